@@ -1,0 +1,180 @@
+/*
+ * paged_kv.h -- C ABI of libpagedkv: paged KV-cache decode attention and the slot-mapping
+ * KV write, for AMD Instinct MI355X (gfx950).
+ *
+ * The problem these calls solve is the one stated by the pages this library follows:
+ *   - "vLLM-Style Llama Inference Engine with Tensor Parallelism", Features and scope /
+ *     Implemented: paged KV caching with block tables and slot mappings, grouped-query
+ *     attention, and a custom kernel for one-token paged decode attention; How it works,
+ *     steps 3-4: each rank writes new K/V into its paged cache, then one-token decode runs a
+ *     paged attention kernel.
+ *   - mini-vLLM LLM-Inference-Engine README, paged KV-cache paragraph: a fixed pool of
+ *     physical blocks, each holding block_size token slots, and a per-sequence block table
+ *     that maps logical positions to physical blocks.
+ *   - "tiny-vLLM" blog, Mastering the Hardware: allocate device memory once and reuse it.
+ *
+ * Conventions for every call:
+ *   - All array arguments are DEVICE pointers to row-major, contiguous arrays, 16-byte
+ *     aligned. bf16 values are passed as their uint16_t bit patterns.
+ *   - The caller owns every buffer (inputs, outputs, workspace). The library allocates and
+ *     frees nothing during a call and keeps no pointer after it returns. Its only state is
+ *     a per-device cache of device properties (compute-unit count), filled on first use.
+ *   - Calls are asynchronous: kernels are enqueued on `stream` (NULL = the null stream) and
+ *     the call returns without synchronising. Ordering between a write and a later
+ *     attention call is the caller's stream order.
+ *   - Calls return a pagedkv_status and never throw. Argument errors are detected on the
+ *     host before anything is enqueued. Data-dependent validity (slot ids, block ids,
+ *     context lengths) is the caller's contract and is not checked on the host, because
+ *     that would need a device-to-host copy; the kernels stay memory-safe on invalid data
+ *     (out-of-range slots are not written, out-of-range block ids are not read, lengths are
+ *     clamped to the table width) but the results for such entries are unspecified.
+ *
+ * Cache layout (both pools): [num_blocks][block_size][num_kv_heads][head_dim] bf16.
+ * Logical position t of a sequence with table row T lives in block T[t / block_size] at
+ * offset t % block_size; the slot number of (block, offset) is block*block_size + offset.
+ * Query head h reads KV head h / (num_q_heads / num_kv_heads).
+ */
+#ifndef PAGED_KV_H
+#define PAGED_KV_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PAGED_KV_ABI_VERSION 1
+
+typedef enum {
+  PAGEDKV_OK = 0,
+  PAGEDKV_ERR_NULL = 1,        /* a required pointer is NULL */
+  PAGEDKV_ERR_SHAPE = 2,       /* a size is out of range or sizes are inconsistent */
+  PAGEDKV_ERR_UNSUPPORTED = 3, /* head_dim / block_size / group size / kernel not built */
+  PAGEDKV_ERR_WORKSPACE = 4,   /* workspace NULL or smaller than required */
+  PAGEDKV_ERR_HIP = 5,         /* a HIP runtime call failed; see paged_kv_last_error() */
+  PAGEDKV_ERR_ALIGN = 6        /* an array pointer is not 16-byte aligned */
+} pagedkv_status;
+
+/* Returns PAGED_KV_ABI_VERSION of the built library. */
+int paged_kv_abi_version(void);
+
+/* Static, NUL-terminated name of a status code ("PAGEDKV_OK", ...); never NULL. */
+const char* paged_kv_status_string(int status);
+
+/* Text of the last error raised on the calling thread (argument problem or HIP error
+ * string); "" if none. Valid until the thread's next call into the library. */
+const char* paged_kv_last_error(void);
+
+/*
+ * paged_kv_write -- store each new token's K and V rows into its slot of the paged pools
+ * (the write step of a decode or prefill step: "vLLM-Style Llama Inference Engine",
+ * How it works, step 3; the mini-vLLM README's per-sequence K/V write loop into the block
+ * pool, done here as one scatter).
+ *
+ *   k, v           bf16 [num_tokens][num_kv_heads][head_dim]           (read)
+ *   slot_mapping   int64 [num_tokens]; token t goes to slot s = slot_mapping[t], i.e. block
+ *                  s / block_size, offset s % block_size. s < 0: token skipped (padding).
+ *                  Non-negative slots must be distinct and < num_blocks*block_size; a slot
+ *                  outside the pool is not written.
+ *   k_cache, v_cache  bf16 [num_blocks][block_size][num_kv_heads][head_dim], modified in
+ *                  place; only the addressed rows change. Bits are copied unchanged (no
+ *                  float conversion), so any payload, NaN included, is preserved.
+ * Requirements: num_tokens >= 0 (0 = no-op), num_blocks >= 1, block_size >= 1,
+ * num_kv_heads >= 1, head_dim >= 1, num_kv_heads*head_dim a multiple of 8.
+ */
+int paged_kv_write(const uint16_t* k, const uint16_t* v, const int64_t* slot_mapping,
+                   int64_t num_tokens, uint16_t* k_cache, uint16_t* v_cache,
+                   int64_t num_blocks, int32_t block_size, int32_t num_kv_heads,
+                   int32_t head_dim, hipStream_t stream);
+
+/*
+ * paged_decode_workspace_bytes -- bytes of device workspace paged_decode_attention needs
+ * for these sizes (0 when the call never splits a sequence). `partition_tokens` has the
+ * same meaning as in paged_decode_attention; for 0 (automatic) the bound covers every
+ * partition size the automatic choice can make.
+ */
+size_t paged_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t head_dim,
+                                    int32_t max_blocks_per_seq, int32_t block_size,
+                                    int32_t partition_tokens);
+
+/*
+ * paged_decode_attention -- one-token grouped-query decode attention over the paged cache
+ * ("vLLM-Style Llama Inference Engine", How it works, step 4; mini-vLLM README, paged
+ * KV-cache paragraph and its test of the paged kernel against dense attention on scattered
+ * blocks; llm-stack, Serving engine / KV cache bullet: the decode query sees every cached
+ * key, no causal mask).
+ *
+ *   out[b][h][:] = sum_t softmax_t(scale * q[b][h] . K_b[t][g]) V_b[t][g],  g = h / G,
+ *   over t = 0 .. context_lens[b]-1, where K_b[t] / V_b[t] is the row at logical position t
+ *   read through block_tables[b]. context_lens[b] == 0 gives out[b] = 0.
+ *
+ *   q              bf16 [batch][num_q_heads][head_dim]
+ *   k_cache, v_cache  bf16 [num_blocks][block_size][num_kv_heads][head_dim]
+ *   block_tables   int32 [batch][max_blocks_per_seq]; entries at j >= ceil(L_b/block_size)
+ *                  are never read (may be -1)
+ *   context_lens   int32 [batch], 0 <= L_b <= max_blocks_per_seq*block_size
+ *   scale          applied in fp32 to the fp32 dot product (typically 1/sqrt(head_dim))
+ *   out            fp32 [batch][num_q_heads][head_dim] (written)
+ *   workspace      device scratch of >= paged_decode_workspace_bytes(...) bytes, 256-byte
+ *                  aligned, or NULL/0 when that size is 0. Contents need no initialisation;
+ *                  calls running concurrently must not share one workspace.
+ *   partition_tokens  0: choose automatically from the sizes and the device; -1: never
+ *                  split a sequence; > 0: split each sequence into partitions of this many
+ *                  tokens (a multiple of block_size) whose partial softmax results are
+ *                  merged by a log-sum-exp reduction.
+ * Supported: head_dim in {64, 128}; block_size 16; num_q_heads / num_kv_heads in
+ * {1, 2, 3, 4, 8} (other ratios up to 16 with the matrix-core kernel).
+ * Accuracy: fp32 accumulation; |out - exact| is a few fp32 ulps of the value scale.
+ */
+int paged_decode_attention(const uint16_t* q, const uint16_t* k_cache,
+                           const uint16_t* v_cache, const int32_t* block_tables,
+                           int32_t max_blocks_per_seq, const int32_t* context_lens,
+                           int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                           int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                           float scale, float* out, void* workspace, size_t workspace_bytes,
+                           int32_t partition_tokens, hipStream_t stream);
+
+/* Kernel families for paged_decode_attention_ex. */
+typedef enum {
+  PAGEDKV_KERNEL_AUTO = 0,  /* the library's choice for the shape (the default path) */
+  PAGEDKV_KERNEL_VALU = 1,  /* fp32 vector-ALU dot products and accumulation */
+  PAGEDKV_KERNEL_MFMA = 2   /* bf16 matrix-core (MFMA) tiles with fp32 accumulation */
+} pagedkv_kernel;
+
+/*
+ * paged_decode_attention_ex -- paged_decode_attention with two extra controls, for
+ * comparison and profiling:
+ *   kernel         a pagedkv_kernel value (PAGEDKV_ERR_UNSUPPORTED if that family has no
+ *                  build for the shape);
+ *   ev_begin, ev_end  if non-NULL, recorded on `stream` immediately before and after the
+ *                  main attention kernel (not the partition merge), so the caller can time
+ *                  that kernel alone with hipEventElapsedTime.
+ */
+int paged_decode_attention_ex(const uint16_t* q, const uint16_t* k_cache,
+                              const uint16_t* v_cache, const int32_t* block_tables,
+                              int32_t max_blocks_per_seq, const int32_t* context_lens,
+                              int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                              int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                              float scale, float* out, void* workspace,
+                              size_t workspace_bytes, int32_t partition_tokens,
+                              int32_t kernel, hipEvent_t ev_begin, hipEvent_t ev_end,
+                              hipStream_t stream);
+
+/*
+ * paged_decode_plan -- the launch the call would make for these sizes on the current
+ * device, without launching: number of sequence partitions and tokens per partition
+ * (partition_tokens as in paged_decode_attention). Returns a status; the outputs are
+ * written on PAGEDKV_OK.
+ */
+int paged_decode_plan(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                      int32_t head_dim, int32_t max_blocks_per_seq, int32_t block_size,
+                      int32_t partition_tokens, int32_t kernel, int32_t* num_partitions,
+                      int32_t* tokens_per_partition);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGED_KV_H */

@@ -1,0 +1,12 @@
+"""CPU oracle (float64, numpy) for paged KV decode attention and the KV write.
+
+Test infrastructure only: imported by the tests, the smoke check and the benchmark's CPU
+baseline leg, never by the HIP product path.
+"""
+from .oracle import (bf16_bits_to_f64, kv_write, kv_head_for, gather_dense, attend_one,
+                     effective_scale, decode_attention, decode_step, partial_stats,
+                     merge_partials, split_attend_one)
+
+__all__ = ["bf16_bits_to_f64", "kv_write", "kv_head_for", "gather_dense", "attend_one",
+           "effective_scale", "decode_attention", "decode_step", "partial_stats",
+           "merge_partials", "split_attend_one"]

@@ -1,0 +1,197 @@
+"""Plain, slow CPU oracle for paged KV decode attention and the slot-mapping KV write.
+
+TEST INFRASTRUCTURE. Only the tests, the package smoke check and the benchmark's CPU
+baseline leg may import this module. The product path (the HIP kernels behind the C ABI)
+never calls it, and it imports nothing from that path.
+
+What it computes, and where the pages state it:
+  * KV write: each new token's K and V row goes to its slot in a pool of physical blocks
+    ("vLLM-Style Llama Inference Engine with Tensor Parallelism", Features and scope /
+    Implemented: paged KV caching with block tables and slot mappings; How it works, step 3:
+    each rank writes to its paged KV cache; mini-vLLM README, benchmarks/baseline_hf.py
+    discussion: the per-sequence loop that writes K/V into the block pool).
+  * Decode attention: one query token per sequence attends to every cached key of that
+    sequence, gathered through its block table (mini-vLLM README, paged KV-cache paragraph:
+    the block table maps logical positions to physical storage; llm-stack, Serving engine /
+    KV cache bullet: a decode query sees all cached keys, no causal mask), with grouped-query
+    heads (vLLM-Style Llama engine, Implemented: grouped-query attention), bf16 inputs and
+    softmax(q K^T * scale) V ("tiny-vLLM" blog, The Precision Trade-off: BF16; llm-stack,
+    Attention kernel).
+
+The method reaches exactly (up to rounding order) the plain definition of softmax
+attention, so this oracle is that definition written out in float64 on the bf16 input
+values. Readings taken where the pages are silent:
+  * cache layout [num_blocks, block_size, num_kv_heads, head_dim]; slot = block*bs + offset;
+  * query head h uses KV head h // (Hq / Hkv) (consecutive grouping);
+  * a negative slot means "no write"; duplicate non-negative slots are a caller error;
+  * context length 0 gives an all-zero output row;
+  * the fp32 scale a GPU receives is applied to the fp64 dot product.
+"""
+from __future__ import annotations
+
+import math
+from typing import Iterable, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+
+# ---------------------------------------------------------------------------------------
+# bf16 decoding ("tiny-vLLM" blog, The Precision Trade-off: BF16 -- 8 exponent bits as in
+# float32, 7 fraction bits; a bf16 value is the top half of a float32 bit pattern).
+# ---------------------------------------------------------------------------------------
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact decode of bf16 bit patterns (uint16) to float64."""
+    bits = np.asarray(bits, dtype=np.uint16)
+    as_f32 = (bits.astype(np.uint32) << np.uint32(16)).view(np.float32)
+    with np.errstate(invalid="ignore"):  # NaN patterns stay NaN
+        return as_f32.astype(np.float64)
+
+
+# ---------------------------------------------------------------------------------------
+# KV write (slot-mapping scatter), on raw bit patterns: no float conversion, so every
+# payload, NaN included, lands unchanged.
+# ---------------------------------------------------------------------------------------
+def kv_write(k_bits: np.ndarray, v_bits: np.ndarray, slot_mapping: np.ndarray,
+             k_cache_bits: np.ndarray, v_cache_bits: np.ndarray
+             ) -> Tuple[np.ndarray, np.ndarray]:
+    """Return copies of the two pools with token t's K/V rows stored at slot_mapping[t].
+
+    k_bits, v_bits: uint16 [T, Hkv, D]; slot_mapping: int [T]; caches: uint16
+    [NB, bs, Hkv, D]. Slot s addresses block s // bs, offset s % bs.
+    """
+    NB, bs, Hkv, D = k_cache_bits.shape
+    kc = np.array(k_cache_bits, dtype=np.uint16, copy=True).reshape(NB * bs, Hkv, D)
+    vc = np.array(v_cache_bits, dtype=np.uint16, copy=True).reshape(NB * bs, Hkv, D)
+    seen = set()
+    for t, s in enumerate(np.asarray(slot_mapping).tolist()):
+        if s < 0:
+            continue  # padding token: nothing to write
+        if s >= NB * bs:
+            raise ValueError(f"slot {s} of token {t} is outside the pool ({NB * bs} slots)")
+        if s in seen:
+            raise ValueError(f"slot {s} is written twice")
+        seen.add(s)
+        kc[s] = k_bits[t]
+        vc[s] = v_bits[t]
+    return kc.reshape(NB, bs, Hkv, D), vc.reshape(NB, bs, Hkv, D)
+
+
+# ---------------------------------------------------------------------------------------
+# Decode attention.
+# ---------------------------------------------------------------------------------------
+def kv_head_for(h: int, num_q_heads: int, num_kv_heads: int) -> int:
+    """KV head shared by query head h: consecutive groups of Hq/Hkv query heads."""
+    return h // (num_q_heads // num_kv_heads)
+
+
+def gather_dense(cache_bits: np.ndarray, table_row: np.ndarray, length: int) -> np.ndarray:
+    """Logical positions 0..length-1 of one sequence as a dense float64 [length, Hkv, D]
+    array, reading physical block table_row[j] for logical block j."""
+    NB, bs, Hkv, D = cache_bits.shape
+    n = (length + bs - 1) // bs
+    ids = np.asarray(table_row[:n], dtype=np.int64)
+    if n > len(table_row):
+        raise ValueError("context needs more blocks than the table holds")
+    if n and (ids.min() < 0 or ids.max() >= NB):
+        raise ValueError("block id outside the pool")
+    dense = bf16_bits_to_f64(cache_bits[ids]).reshape(n * bs, Hkv, D)
+    return dense[:length]
+
+
+def attend_one(qh: np.ndarray, K: np.ndarray, V: np.ndarray, scale_eff: float) -> np.ndarray:
+    """softmax(K qh * scale) V for one query vector; K, V are [L, D] float64."""
+    s = (K @ qh) * scale_eff
+    m = s.max()
+    p = np.exp(s - m)
+    return (p @ V) / p.sum()
+
+
+def effective_scale(scale: float) -> float:
+    """The scale as the GPU receives it: rounded to float32."""
+    return float(np.float32(scale))
+
+
+def decode_attention(q_bits: np.ndarray, k_cache_bits: np.ndarray, v_cache_bits: np.ndarray,
+                     block_tables: np.ndarray, context_lens: np.ndarray, scale: float,
+                     rows: Optional[Iterable[Tuple[int, int]]] = None) -> np.ndarray:
+    """Float64 output [B, Hq, D] of one-token decode attention over the paged cache.
+
+    q_bits uint16 [B, Hq, D]; caches uint16 [NB, bs, Hkv, D]; block_tables int [B, MB];
+    context_lens int [B]. With ``rows`` (an iterable of (b, h) pairs) only those output rows
+    are computed; the others stay zero.
+    """
+    B, Hq, D = q_bits.shape
+    Hkv = k_cache_bits.shape[2]
+    if Hq % Hkv:
+        raise ValueError("query heads must be a multiple of KV heads")
+    scale_eff = effective_scale(scale)
+    out = np.zeros((B, Hq, D), dtype=np.float64)
+    wanted = {}
+    if rows is None:
+        for b in range(B):
+            wanted[b] = list(range(Hq))
+    else:
+        for b, h in rows:
+            wanted.setdefault(int(b), []).append(int(h))
+    for b, heads in sorted(wanted.items()):
+        L = int(context_lens[b])
+        if L == 0:
+            continue
+        K = gather_dense(k_cache_bits, block_tables[b], L)
+        V = gather_dense(v_cache_bits, block_tables[b], L)
+        qd = bf16_bits_to_f64(q_bits[b])
+        for h in heads:
+            g = kv_head_for(h, Hq, Hkv)
+            out[b, h] = attend_one(qd[h], K[:, g, :], V[:, g, :], scale_eff)
+    return out
+
+
+def decode_step(inp: dict, rows=None) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Write the step's new tokens, then attend over the updated pools (the decode step
+    writes position L_b - 1 first and then reads positions 0..L_b-1).
+
+    inp holds host numpy arrays: q, k_cache, v_cache, k_new, v_new (uint16 bits),
+    block_tables, context_lens, slot_mapping, scale. Returns (out, k_cache', v_cache').
+    """
+    kc, vc = kv_write(inp["k_new"], inp["v_new"], inp["slot_mapping"],
+                      inp["k_cache"], inp["v_cache"])
+    out = decode_attention(inp["q"], kc, vc, inp["block_tables"], inp["context_lens"],
+                           inp["scale"], rows=rows)
+    return out, kc, vc
+
+
+# ---------------------------------------------------------------------------------------
+# Partitioned softmax (split-K) identity. The pages never write it out; it is the running
+# max / running sum rescaling behind the tiled online softmax of llm-stack's Attention
+# kernel section and the FlashAttention-2 paper the Llama engine lists under References.
+# For a split of the keys into parts p with m_p = max score, l_p = sum exp(s - m_p),
+# a_p = sum exp(s - m_p) v: out = sum_p e^{m_p - M} a_p / sum_p e^{m_p - M} l_p, M = max m_p.
+# ---------------------------------------------------------------------------------------
+def partial_stats(qh: np.ndarray, K: np.ndarray, V: np.ndarray, scale_eff: float
+                  ) -> Tuple[float, float, np.ndarray]:
+    """(m, l, a) of one part of the keys; an empty part gives (-inf, 0, 0)."""
+    if K.shape[0] == 0:
+        return -math.inf, 0.0, np.zeros(V.shape[1])
+    s = (K @ qh) * scale_eff
+    m = float(s.max())
+    p = np.exp(s - m)
+    return m, float(p.sum()), p @ V
+
+
+def merge_partials(parts: Sequence[Tuple[float, float, np.ndarray]]) -> np.ndarray:
+    """Combine per-part (m, l, a) into the softmax output; parts with l == 0 weigh 0."""
+    live = [(m, l, a) for (m, l, a) in parts if l > 0]
+    if not live:
+        return np.zeros_like(parts[0][2])
+    M = max(m for m, _, _ in live)
+    num = sum(math.exp(m - M) * a for m, _, a in live)
+    den = sum(math.exp(m - M) * l for m, l, _ in live)
+    return num / den
+
+
+def split_attend_one(qh: np.ndarray, K: np.ndarray, V: np.ndarray, scale_eff: float,
+                     bounds: List[int]) -> np.ndarray:
+    """Attention of one query evaluated part by part over keys [bounds[i], bounds[i+1])."""
+    parts = [partial_stats(qh, K[lo:hi], V[lo:hi], scale_eff)
+             for lo, hi in zip(bounds[:-1], bounds[1:])]
+    return merge_partials(parts)

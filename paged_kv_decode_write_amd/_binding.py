@@ -1,0 +1,195 @@
+"""ctypes binding of libpagedkv (declared in include/paged_kv.h).
+
+Argument marshalling only: shape/dtype/device checks, torch tensors to device pointers, the
+current HIP stream. Every step of the computation runs in the library's HIP kernels. There
+is no fallback: if the library is missing or a call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_NAME = "libpagedkv.so"
+
+STATUS_NAMES = {0: "PAGEDKV_OK", 1: "PAGEDKV_ERR_NULL", 2: "PAGEDKV_ERR_SHAPE",
+                3: "PAGEDKV_ERR_UNSUPPORTED", 4: "PAGEDKV_ERR_WORKSPACE", 5: "PAGEDKV_ERR_HIP",
+                6: "PAGEDKV_ERR_ALIGN"}
+KERNELS = {"auto": 0, "valu": 1, "mfma": 2}
+
+_lock = threading.Lock()
+_lib: Optional[ctypes.CDLL] = None
+
+
+class PagedKVError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        self.status = status
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+
+
+def library_path() -> str:
+    return os.environ.get("PAGEDKV_LIBRARY", os.path.join(_HERE, LIB_NAME))
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libpagedkv.so (after torch, so both share one HIP runtime) and declare the
+    C signatures. Raises FileNotFoundError if it has not been built."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        path = library_path()
+        if not os.path.exists(path):
+            raise FileNotFoundError(
+                f"{path} is missing: build it first (python -m paged_kv_decode_write_amd.build)")
+        lib = ctypes.CDLL(path)
+        P, I32, I64, SZ, F32 = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
+                                ctypes.c_size_t, ctypes.c_float)
+        lib.paged_kv_abi_version.restype = ctypes.c_int
+        lib.paged_kv_abi_version.argtypes = []
+        lib.paged_kv_status_string.restype = ctypes.c_char_p
+        lib.paged_kv_status_string.argtypes = [ctypes.c_int]
+        lib.paged_kv_last_error.restype = ctypes.c_char_p
+        lib.paged_kv_last_error.argtypes = []
+        lib.paged_kv_write.restype = ctypes.c_int
+        lib.paged_kv_write.argtypes = [P, P, P, I64, P, P, I64, I32, I32, I32, P]
+        lib.paged_decode_workspace_bytes.restype = SZ
+        lib.paged_decode_workspace_bytes.argtypes = [I32, I32, I32, I32, I32, I32]
+        attn = [P, P, P, P, I32, P, I32, I32, I32, I32, I32, I64, F32, P, P, SZ, I32]
+        lib.paged_decode_attention.restype = ctypes.c_int
+        lib.paged_decode_attention.argtypes = attn + [P]
+        lib.paged_decode_attention_ex.restype = ctypes.c_int
+        lib.paged_decode_attention_ex.argtypes = attn + [I32, P, P, P]
+        lib.paged_decode_plan.restype = ctypes.c_int
+        lib.paged_decode_plan.argtypes = [I32, I32, I32, I32, I32, I32, I32, I32,
+                                          ctypes.POINTER(I32), ctypes.POINTER(I32)]
+        _lib = lib
+        return lib
+
+
+def abi_version() -> int:
+    return load_library().paged_kv_abi_version()
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        msg = load_library().paged_kv_last_error().decode(errors="replace")
+        raise PagedKVError(status, msg)
+
+
+def _stream_handle(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _require(t: torch.Tensor, name: str, dtype: torch.dtype, ndim: int,
+             device: Optional[torch.device] = None) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions, got shape {tuple(t.shape)}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU device, got {t.device}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def paged_kv_write(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,
+                   k_cache: torch.Tensor, v_cache: torch.Tensor) -> None:
+    """Store token t's K/V rows (k[t], v[t]: [Hkv, D] bf16) at slot slot_mapping[t] of the
+    pools k_cache / v_cache ([NB, block_size, Hkv, D] bf16, updated in place).
+    Negative slots are skipped."""
+    _require(k_cache, "k_cache", torch.bfloat16, 4)
+    dev = k_cache.device
+    _require(v_cache, "v_cache", torch.bfloat16, 4, dev)
+    _require(k, "k", torch.bfloat16, 3, dev)
+    _require(v, "v", torch.bfloat16, 3, dev)
+    _require(slot_mapping, "slot_mapping", torch.int64, 1, dev)
+    NB, bs, Hkv, D = k_cache.shape
+    if v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache and v_cache shapes differ")
+    T = k.shape[0]
+    if k.shape != (T, Hkv, D) or v.shape != (T, Hkv, D) or slot_mapping.shape != (T,):
+        raise ValueError(f"k/v must be [T, {Hkv}, {D}] and slot_mapping [T]")
+    lib = load_library()
+    with torch.cuda.device(dev):
+        _check(lib.paged_kv_write(k.data_ptr(), v.data_ptr(), slot_mapping.data_ptr(), T,
+                                  k_cache.data_ptr(), v_cache.data_ptr(), NB, bs, Hkv, D,
+                                  _stream_handle(dev)))
+
+
+def decode_workspace_bytes(batch: int, num_q_heads: int, head_dim: int,
+                           max_blocks_per_seq: int, block_size: int,
+                           partition_tokens: int = 0) -> int:
+    return int(load_library().paged_decode_workspace_bytes(
+        batch, num_q_heads, head_dim, max_blocks_per_seq, block_size, partition_tokens))
+
+
+def decode_plan(batch, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq, block_size,
+                partition_tokens=0, kernel="auto"):
+    """(num_partitions, tokens_per_partition) the call would use on the current device."""
+    n = ctypes.c_int32(0)
+    p = ctypes.c_int32(0)
+    _check(load_library().paged_decode_plan(batch, num_q_heads, num_kv_heads, head_dim,
+                                            max_blocks_per_seq, block_size, partition_tokens,
+                                            KERNELS[kernel], ctypes.byref(n), ctypes.byref(p)))
+    return n.value, p.value
+
+
+def paged_decode_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                           block_tables: torch.Tensor, context_lens: torch.Tensor,
+                           scale: float, out: torch.Tensor, *, partition_tokens: int = 0,
+                           kernel: str = "auto", workspace: Optional[torch.Tensor] = None,
+                           events: Optional[tuple] = None) -> torch.Tensor:
+    """out[b, h] = softmax(scale * q[b, h] . K_b^T) V_b over the context_lens[b] cached
+    positions of sequence b, read through block_tables[b] (KV head h // (Hq/Hkv)).
+
+    q [B, Hq, D] bf16; k_cache/v_cache [NB, block_size, Hkv, D] bf16; block_tables
+    [B, MB] int32; context_lens [B] int32; out [B, Hq, D] fp32 (written and returned).
+    partition_tokens: 0 automatic, -1 never split, >0 split size in tokens (tests).
+    kernel: "auto", "valu" or "mfma". workspace: optional uint8 device buffer (allocated from
+    torch's caching allocator when omitted). events: optional (begin, end) raw hipEvent_t
+    handles recorded around the main kernel.
+    """
+    _require(k_cache, "k_cache", torch.bfloat16, 4)
+    dev = k_cache.device
+    _require(v_cache, "v_cache", torch.bfloat16, 4, dev)
+    _require(q, "q", torch.bfloat16, 3, dev)
+    _require(block_tables, "block_tables", torch.int32, 2, dev)
+    _require(context_lens, "context_lens", torch.int32, 1, dev)
+    _require(out, "out", torch.float32, 3, dev)
+    NB, bs, Hkv, D = k_cache.shape
+    if v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache and v_cache shapes differ")
+    B, Hq, Dq = q.shape
+    if Dq != D:
+        raise ValueError(f"q head_dim {Dq} != cache head_dim {D}")
+    if out.shape != (B, Hq, D):
+        raise ValueError(f"out must be [{B}, {Hq}, {D}]")
+    MB = block_tables.shape[1]
+    if block_tables.shape[0] != B or context_lens.shape != (B,):
+        raise ValueError("block_tables must be [B, MB] and context_lens [B]")
+    if kernel not in KERNELS:
+        raise ValueError(f"kernel must be one of {sorted(KERNELS)}")
+    lib = load_library()
+    need = int(lib.paged_decode_workspace_bytes(B, Hq, D, MB, bs, partition_tokens))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    elif workspace.device != dev or workspace.dtype != torch.uint8:
+        raise ValueError("workspace must be a uint8 tensor on the cache's device")
+    ws_bytes = workspace.numel()
+    ev_b, ev_e = events if events is not None else (None, None)
+    with torch.cuda.device(dev):
+        _check(lib.paged_decode_attention_ex(
+            q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(), MB,
+            context_lens.data_ptr(), B, Hq, Hkv, D, bs, NB, float(scale), out.data_ptr(),
+            workspace.data_ptr() if need else None, ws_bytes if need else 0,
+            partition_tokens, KERNELS[kernel], ev_b, ev_e, _stream_handle(dev)))
+    return out
