@@ -1,0 +1,274 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark on one MI355X: the paged KV write followed by paged decode attention.
+
+A step is one pass of the whole path over one batch of synthetic, seeded inputs that are
+resident in HBM before timing starts. The default workload is the long-context decode pair:
+64 sequences x 8192 tokens, then 2 sequences x 32768 tokens (32 query heads, 8 KV heads,
+head_dim 128, block_size 16, bf16, logits of std ~3); each step writes one new token per
+sequence and then attends over all cached tokens of every sequence.
+
+Prints ONE JSON line. `value` is the whole step's algorithmic HBM throughput (GB/s):
+K and V of every context token (bf16), q (bf16), out (fp32) and the written K/V rows, over
+the measured step time. `roofline` reports the main attention kernel alone, timed with HIP
+events recorded on its own stream around each launch; `cpu_baseline` is the float64 CPU
+oracle timed on a bounded sample of the same workload on this host.
+
+    python bench.py [--steps K] [--warmup W] [--workload c5|c5a|c5b|c1..c4]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, HERE)
+
+METRIC = "paged decode attention µs/call and achieved HBM GB/s (% of MI355X peak)"
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, vendor figure
+TRAFFIC_FILE = os.path.join(HERE, "profiles", "decode_traffic.json")
+
+
+def parse_args():
+    p = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="c5")
+    p.add_argument("--kernel", default="auto", choices=["auto", "valu", "mfma"])
+    p.add_argument("--partition", type=int, default=0,
+                   help="tokens per partition: 0 automatic, -1 never split")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
+                   help="CPU work budget of the oracle baseline sample")
+    p.add_argument("--json-out", default=None)
+    return p.parse_args()
+
+
+class HipEvents:
+    """hipEvent_t handles from the HIP runtime torch has already loaded."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
+                                                 ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.events = []
+
+    def create(self):
+        ev = ctypes.c_void_p()
+        if self.hip.hipEventCreate(ctypes.byref(ev)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        self.events.append(ev.value)
+        return ev.value
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        if self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def close(self):
+        for ev in self.events:
+            self.hip.hipEventDestroy(ev)
+        self.events = []
+
+
+def kernel_source_hash(kernel: str) -> str:
+    csrc = os.path.join(HERE, "paged_kv_decode_write_amd", "csrc")
+    files = ["device_common.h", "launch.h", f"decode_{kernel}.hip"]
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def resolved_kernel(pk, w, requested):
+    if requested != "auto":
+        return requested
+    try:
+        pk.decode_plan(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.max_blocks,
+                       w.block_size, 0, "mfma")
+        return "mfma"
+    except pk.PagedKVError:
+        return "valu"
+
+
+def cpu_baseline(d, seconds):
+    """The float64 oracle, as it stands, on the first sequences of the workload (write +
+    attention, all heads) until `seconds` of CPU time are spent, on one thread."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    from paged_kv_decode_write_amd import workloads as wl
+
+    w = d["workload"]
+    bs = w.block_size
+    tables = d["block_tables"].cpu().numpy()
+    lens = d["context_lens"].cpu().numpy()
+    q = wl.to_bits(d["q"])
+    kn, vn = wl.to_bits(d["k_new"]), wl.to_bits(d["v_new"])
+    spent, nbytes, done = 0.0, 0, 0
+    with threadpool_limits(limits=1):
+        for b in range(w.batch):
+            L = int(lens[b])
+            n = (L + bs - 1) // bs
+            ids = torch.from_numpy(tables[b, :n].astype(np.int64)).to(d["k_cache"].device)
+            kc = wl.to_bits(d["k_cache"].index_select(0, ids))
+            vc = wl.to_bits(d["v_cache"].index_select(0, ids))
+            local = np.arange(n, dtype=np.int32)[None]
+            slot = np.array([(n - 1) * bs + (L - 1) % bs], dtype=np.int64)
+            t0 = time.perf_counter()
+            kc2, vc2 = oracle.kv_write(kn[b:b + 1], vn[b:b + 1], slot, kc, vc)
+            oracle.decode_attention(q[b:b + 1], kc2, vc2, local, lens[b:b + 1], d["scale"])
+            spent += time.perf_counter() - t0
+            ab = wl.algorithmic_bytes(w, [L])
+            nbytes += ab["kv"] + (ab["q"] + ab["out"] + ab["write"]) // w.batch
+            done += 1
+            if spent >= seconds:
+                break
+    return {"value": round(nbytes / spent / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{w.name}: sequences 0..{done - 1} of {w.batch} (KV write + attention, "
+                      f"all {w.num_q_heads} heads), float64 numpy, one BLAS thread, "
+                      f"{spent:.1f} s"}
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the path has no "
+              "multi-GPU leg to time.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    from paged_kv_decode_write_amd import _binding as pk
+    from paged_kv_decode_write_amd import workloads as wl
+
+    pk.load_library()
+    dev = torch.device("cuda:0")
+    names = ["c5a", "c5b"] if args.workload == "c5" else [args.workload]
+    subs = []
+    for name in names:
+        w = wl.WORKLOADS[name]
+        d = wl.make_inputs(w, device="cuda")
+        d["out"] = torch.empty(w.batch, w.num_q_heads, w.head_dim, dtype=torch.float32, device=dev)
+        need = pk.decode_workspace_bytes(w.batch, w.num_q_heads, w.head_dim, w.max_blocks,
+                                         w.block_size, args.partition)
+        d["ws"] = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+        d["bytes"] = wl.algorithmic_bytes(w, d["context_lens"].cpu().tolist())
+        d["plan"] = pk.decode_plan(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim,
+                                   w.max_blocks, w.block_size, args.partition, args.kernel)
+        subs.append(d)
+    torch.cuda.synchronize()
+
+    def step(events=None):
+        for i, d in enumerate(subs):
+            pk.paged_kv_write(d["k_new"], d["v_new"], d["slot_mapping"], d["k_cache"],
+                              d["v_cache"])
+            pk.paged_decode_attention(d["q"], d["k_cache"], d["v_cache"], d["block_tables"],
+                                      d["context_lens"], d["scale"], d["out"],
+                                      partition_tokens=args.partition, kernel=args.kernel,
+                                      workspace=d["ws"],
+                                      events=events[i] if events is not None else None)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    hip = HipEvents()
+    evs = [[(hip.create(), hip.create()) for _ in subs] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+
+    per = []
+    for j, d in enumerate(subs):
+        durs = sorted(hip.elapsed_ms(*evs[i][j]) for i in range(args.steps))
+        mean = sum(durs) / len(durs)
+        w = d["workload"]
+        per.append({
+            "workload": w.name, "description": w.description,
+            "partitions": d["plan"][0], "tokens_per_partition": d["plan"][1],
+            "attn_kernel_us_mean": round(mean * 1e3, 2),
+            "attn_kernel_us_median": round(durs[len(durs) // 2] * 1e3, 2),
+            "attn_kernel_us_min": round(durs[0] * 1e3, 2),
+            "attn_bytes": d["bytes"]["attention"],
+            "attn_kernel_GBps": round(d["bytes"]["attention"] / (mean * 1e-3) / 1e9, 1),
+            "pct_of_peak": round(100 * d["bytes"]["attention"] / (mean * 1e-3) / 1e9
+                                 / PEAK_HBM_GBS, 2),
+        })
+    hip.close()
+
+    step_bytes = sum(d["bytes"]["attention"] + d["bytes"]["write"] for d in subs)
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    launch_bytes = sum(d["bytes"]["attention"] for d in subs) / len(subs)
+    launch_s = sum(p["attn_kernel_us_mean"] for p in per) / len(per) * 1e-6
+    achieved = launch_bytes / launch_s / 1e9
+    kernel = resolved_kernel(pk, subs[0]["workload"], args.kernel)
+
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+        rec = t.get(args.workload, {})
+        if rec.get("kernel_source") == kernel_source_hash(kernel) and rec.get("kernel") == kernel:
+            traffic = rec.get("bytes_per_launch")
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if kernel == "mfma" else "fp32",
+        "data": "synthetic (seeded N(0,1) bf16 K/V pools, shuffled block tables), resident in HBM",
+        "config": {
+            "workload": "+".join(d["workload"].description for d in subs),
+            "kernel": kernel,
+            "partition_tokens": args.partition,
+            "us_per_call": {p["workload"]: p["attn_kernel_us_mean"] for p in per},
+            "pct_of_peak": {p["workload"]: p["pct_of_peak"] for p in per},
+            "step": "KV write + decode attention per sub-workload",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4),
+            "traffic": traffic,
+        },
+        "details": per,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(subs[0], args.cpu_seconds)
+    out = json.dumps(line)
+    print(out, flush=True)
+    if args.json_out:
+        with open(args.json_out, "w") as f:
+            f.write(out + "\n")
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,71 @@
+"""Build libpagedkv.so in-tree with hipcc for gfx950.
+
+    python -m paged_kv_decode_write_amd.build
+
+Every HIP source is compiled for gfx950 only, with packed-fp32 instruction selection
+turned off (-Xclang -target-feature -Xclang -packed-fp32-ops), and linked with the C-ABI
+host layer into one shared library next to this file.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+OUT = os.path.join(HERE, "libpagedkv.so")
+
+SOURCES = ["api.cpp", "kv_write.hip", "decode_valu.hip", "decode_mfma.hip", "decode_reduce.hip"]
+ARCH = os.environ.get("PAGEDKV_ARCH", "gfx950")
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise FileNotFoundError("hipcc not found (set HIPCC)")
+
+
+def common_flags(extra=()):
+    return ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-Wall", "-Wno-unused-command-line-argument",
+            f"-I{INCLUDE}", f"-I{CSRC}", *extra]
+
+
+def compile_one(src: str, obj: str, extra=()) -> None:
+    lang = ["-x", "hip"] if src.endswith(".hip") else []
+    cmd = [hipcc(), *common_flags(extra), *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(" ".join(cmd) + "\n" + res.stdout + res.stderr)
+        raise RuntimeError(f"compiling {src} failed")
+    noise = "packed-fp32-ops"
+    warn = "\n".join(l for l in (res.stderr or "").splitlines() if noise not in l and l.strip())
+    if warn.strip():
+        sys.stderr.write(warn + "\n")
+
+
+def build(out: str = OUT, jobs: int = 8, extra=()) -> str:
+    with tempfile.TemporaryDirectory(prefix="pagedkv_build_") as tmp:
+        objs = [os.path.join(tmp, os.path.splitext(s)[0] + ".o") for s in SOURCES]
+        with ThreadPoolExecutor(max_workers=min(jobs, len(SOURCES))) as ex:
+            list(ex.map(lambda so: compile_one(so[0], so[1], extra), zip(SOURCES, objs)))
+        tmp_out = out + ".tmp"
+        cmd = [hipcc(), *common_flags(extra), "-shared", *objs, "-o", tmp_out]
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            sys.stderr.write(" ".join(cmd) + "\n" + res.stdout + res.stderr)
+            raise RuntimeError("linking libpagedkv.so failed")
+        os.replace(tmp_out, out)
+    return out
+
+
+if __name__ == "__main__":
+    print(build())

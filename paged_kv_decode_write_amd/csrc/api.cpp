@@ -1,0 +1,335 @@
+// C-ABI host layer of libpagedkv: argument validation, status codes, the partition plan and
+// kernel dispatch. Declarations and the contract of every entry point: include/paged_kv.h.
+#include "paged_kv.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <mutex>
+#include <string>
+
+#include "launch.h"
+
+using namespace pagedkv;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(PAGEDKV_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+// Compute-unit count of the current device, queried once per device.
+int cu_count(int* out) {
+  static std::mutex mu;
+  static int counts[256] = {0};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= 256) return fail(PAGEDKV_ERR_HIP, "device ordinal %d out of range", dev);
+  std::lock_guard<std::mutex> lock(mu);
+  if (counts[dev] == 0) {
+    int n = 0;
+    e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
+    counts[dev] = n > 0 ? n : 1;
+  }
+  *out = counts[dev];
+  return PAGEDKV_OK;
+}
+
+// Smallest partition the automatic choice makes, in tokens. Partitions shorter than this
+// spend more on the per-partition set-up and merge than they gain in parallelism.
+constexpr int64_t kMinAutoPartition = 256;
+// Workgroups the automatic choice aims for, per compute unit.
+constexpr int64_t kTargetGroupsPerCU = 4;
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
+
+struct Plan {
+  int32_t nparts;
+  int32_t part_tokens;
+};
+
+// Partition plan. max_len = MB * block_size bounds every context length; the plan never
+// reads context_lens (that would need a device-to-host copy and a sync).
+int make_plan(int32_t batch, int32_t num_kv_heads, int32_t max_blocks, int32_t block_size,
+              int32_t partition_tokens, int cus, Plan* plan) {
+  const int64_t max_len = (int64_t)max_blocks * block_size;
+  if (partition_tokens < -1) return fail(PAGEDKV_ERR_SHAPE, "partition_tokens must be >= -1");
+  int64_t n = 1, P = 0;
+  if (partition_tokens == -1 || max_len == 0) {
+    n = 1;
+  } else if (partition_tokens > 0) {
+    if (partition_tokens % block_size)
+      return fail(PAGEDKV_ERR_SHAPE, "partition_tokens %d is not a multiple of block_size %d",
+                  partition_tokens, block_size);
+    P = partition_tokens;
+    n = ceil_div(max_len, P);
+  } else {
+    const int64_t units = (int64_t)batch * num_kv_heads;
+    const int64_t target = kTargetGroupsPerCU * cus;
+    const int64_t nmax = ceil_div(max_len, kMinAutoPartition);
+    n = units > 0 ? ceil_div(target, units) : 1;
+    if (n > nmax) n = nmax;
+    if (n < 1) n = 1;
+    P = round_up(ceil_div(max_len, n), (int64_t)kWavesPerGroup * block_size);
+    n = ceil_div(max_len, P);
+  }
+  if (n <= 1) {
+    n = 1;
+    P = max_len > 0 ? round_up(max_len, block_size) : block_size;
+  }
+  if (P > INT32_MAX || n > INT32_MAX) return fail(PAGEDKV_ERR_SHAPE, "partition plan overflows");
+  if ((int64_t)batch * num_kv_heads * n > INT32_MAX)
+    return fail(PAGEDKV_ERR_SHAPE, "too many workgroups (batch * kv heads * partitions)");
+  plan->nparts = (int32_t)n;
+  plan->part_tokens = (int32_t)P;
+  return PAGEDKV_OK;
+}
+
+// Upper bound of the partition count for a partition_tokens setting, device-independent.
+int64_t nparts_bound(int64_t max_len, int32_t block_size, int32_t partition_tokens) {
+  if (max_len <= 0 || partition_tokens == -1) return 1;
+  if (partition_tokens > 0) {
+    if (partition_tokens % block_size) return 1;
+    return ceil_div(max_len, partition_tokens);
+  }
+  return ceil_div(max_len, kMinAutoPartition);
+}
+
+size_t acc_bytes(int64_t B, int64_t Hq, int64_t D, int64_t n) {
+  return (size_t)round_up(B * Hq * n * D * 4, 256);
+}
+
+size_t split_workspace_bytes(int64_t B, int64_t Hq, int64_t D, int64_t n) {
+  if (n <= 1) return 0;
+  return acc_bytes(B, Hq, D, n) + (size_t)round_up(B * Hq * n * 2 * 4, 256);
+}
+
+int select_kernel(int32_t kernel, int D, int G, int bs, int* chosen) {
+  switch (kernel) {
+    case PAGEDKV_KERNEL_AUTO:
+      if (supported_mfma(D, G, bs)) { *chosen = PAGEDKV_KERNEL_MFMA; return PAGEDKV_OK; }
+      if (supported_valu(D, G, bs)) { *chosen = PAGEDKV_KERNEL_VALU; return PAGEDKV_OK; }
+      break;
+    case PAGEDKV_KERNEL_VALU:
+      if (supported_valu(D, G, bs)) { *chosen = kernel; return PAGEDKV_OK; }
+      break;
+    case PAGEDKV_KERNEL_MFMA:
+      if (supported_mfma(D, G, bs)) { *chosen = kernel; return PAGEDKV_OK; }
+      break;
+    default:
+      return fail(PAGEDKV_ERR_UNSUPPORTED, "unknown kernel family %d", kernel);
+  }
+  return fail(PAGEDKV_ERR_UNSUPPORTED,
+              "no %s kernel for head_dim %d, block_size %d, group size %d",
+              kernel == PAGEDKV_KERNEL_MFMA ? "MFMA" : kernel == PAGEDKV_KERNEL_VALU ? "VALU" : "",
+              D, bs, G);
+}
+
+int check_decode_sizes(int32_t max_blocks, int32_t batch, int32_t num_q_heads,
+                       int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                       int64_t num_blocks) {
+  if (batch < 0 || max_blocks < 0)
+    return fail(PAGEDKV_ERR_SHAPE, "batch and max_blocks_per_seq must be >= 0");
+  if (num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+      num_blocks <= 0)
+    return fail(PAGEDKV_ERR_SHAPE, "head counts, head_dim, block_size, num_blocks must be > 0");
+  if (num_q_heads % num_kv_heads)
+    return fail(PAGEDKV_ERR_SHAPE, "num_q_heads %d is not a multiple of num_kv_heads %d",
+                num_q_heads, num_kv_heads);
+  if ((int64_t)max_blocks * block_size > INT32_MAX)
+    return fail(PAGEDKV_ERR_SHAPE, "max_blocks_per_seq * block_size exceeds int32");
+  return PAGEDKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int paged_kv_abi_version(void) { return PAGED_KV_ABI_VERSION; }
+
+const char* paged_kv_status_string(int status) {
+  switch (status) {
+    case PAGEDKV_OK: return "PAGEDKV_OK";
+    case PAGEDKV_ERR_NULL: return "PAGEDKV_ERR_NULL";
+    case PAGEDKV_ERR_SHAPE: return "PAGEDKV_ERR_SHAPE";
+    case PAGEDKV_ERR_UNSUPPORTED: return "PAGEDKV_ERR_UNSUPPORTED";
+    case PAGEDKV_ERR_WORKSPACE: return "PAGEDKV_ERR_WORKSPACE";
+    case PAGEDKV_ERR_HIP: return "PAGEDKV_ERR_HIP";
+    case PAGEDKV_ERR_ALIGN: return "PAGEDKV_ERR_ALIGN";
+    default: return "PAGEDKV_UNKNOWN_STATUS";
+  }
+}
+
+const char* paged_kv_last_error(void) { return g_last_error.c_str(); }
+
+int paged_kv_write(const uint16_t* k, const uint16_t* v, const int64_t* slot_mapping,
+                   int64_t num_tokens, uint16_t* k_cache, uint16_t* v_cache,
+                   int64_t num_blocks, int32_t block_size, int32_t num_kv_heads,
+                   int32_t head_dim, hipStream_t stream) {
+  g_last_error.clear();
+  if (num_tokens < 0) return fail(PAGEDKV_ERR_SHAPE, "num_tokens must be >= 0");
+  if (num_blocks <= 0 || block_size <= 0 || num_kv_heads <= 0 || head_dim <= 0)
+    return fail(PAGEDKV_ERR_SHAPE, "num_blocks, block_size, num_kv_heads, head_dim must be > 0");
+  const int64_t row = (int64_t)num_kv_heads * head_dim;
+  if (row % 8)
+    return fail(PAGEDKV_ERR_UNSUPPORTED, "num_kv_heads*head_dim (%lld) must be a multiple of 8",
+                (long long)row);
+  if (row > INT32_MAX) return fail(PAGEDKV_ERR_SHAPE, "row too long");
+  if (num_blocks > INT64_MAX / block_size / row)
+    return fail(PAGEDKV_ERR_SHAPE, "pool size overflows");
+  if (num_tokens == 0) return PAGEDKV_OK;
+  if (!k || !v || !slot_mapping || !k_cache || !v_cache)
+    return fail(PAGEDKV_ERR_NULL, "k, v, slot_mapping, k_cache and v_cache must be non-NULL");
+  if (!aligned(k, 16) || !aligned(v, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+      !aligned(slot_mapping, 8))
+    return fail(PAGEDKV_ERR_ALIGN, "k, v, k_cache, v_cache need 16-byte alignment");
+  hipError_t e = launch_kv_write(k, v, slot_mapping, num_tokens, k_cache, v_cache,
+                                 num_blocks * block_size, (int32_t)row, stream);
+  if (e != hipSuccess) return hip_fail(e, "kv_write launch");
+  return PAGEDKV_OK;
+}
+
+size_t paged_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t head_dim,
+                                    int32_t max_blocks_per_seq, int32_t block_size,
+                                    int32_t partition_tokens) {
+  if (batch <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_blocks_per_seq <= 0 ||
+      block_size <= 0)
+    return 0;
+  const int64_t n = nparts_bound((int64_t)max_blocks_per_seq * block_size, block_size,
+                                 partition_tokens);
+  return split_workspace_bytes(batch, num_q_heads, head_dim, n);
+}
+
+int paged_decode_plan(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                      int32_t head_dim, int32_t max_blocks_per_seq, int32_t block_size,
+                      int32_t partition_tokens, int32_t kernel, int32_t* num_partitions,
+                      int32_t* tokens_per_partition) {
+  g_last_error.clear();
+  int st = check_decode_sizes(max_blocks_per_seq, batch, num_q_heads, num_kv_heads, head_dim,
+                              block_size, 1);
+  if (st) return st;
+  if (!num_partitions || !tokens_per_partition)
+    return fail(PAGEDKV_ERR_NULL, "output pointers must be non-NULL");
+  int chosen = 0;
+  st = select_kernel(kernel, head_dim, num_q_heads / num_kv_heads, block_size, &chosen);
+  if (st) return st;
+  int cus = 0;
+  st = cu_count(&cus);
+  if (st) return st;
+  Plan plan{};
+  st = make_plan(batch, num_kv_heads, max_blocks_per_seq, block_size, partition_tokens, cus,
+                 &plan);
+  if (st) return st;
+  *num_partitions = plan.nparts;
+  *tokens_per_partition = plan.part_tokens;
+  return PAGEDKV_OK;
+}
+
+int paged_decode_attention_ex(const uint16_t* q, const uint16_t* k_cache,
+                              const uint16_t* v_cache, const int32_t* block_tables,
+                              int32_t max_blocks_per_seq, const int32_t* context_lens,
+                              int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                              int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                              float scale, float* out, void* workspace,
+                              size_t workspace_bytes, int32_t partition_tokens,
+                              int32_t kernel, hipEvent_t ev_begin, hipEvent_t ev_end,
+                              hipStream_t stream) {
+  g_last_error.clear();
+  int st = check_decode_sizes(max_blocks_per_seq, batch, num_q_heads, num_kv_heads, head_dim,
+                              block_size, num_blocks);
+  if (st) return st;
+  const int G = num_q_heads / num_kv_heads;
+  int chosen = 0;
+  st = select_kernel(kernel, head_dim, G, block_size, &chosen);
+  if (st) return st;
+  if (batch == 0) return PAGEDKV_OK;
+  if (!q || !k_cache || !v_cache || !context_lens || !out ||
+      (max_blocks_per_seq > 0 && !block_tables))
+    return fail(PAGEDKV_ERR_NULL,
+                "q, k_cache, v_cache, block_tables, context_lens and out must be non-NULL");
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
+      !aligned(block_tables, 4) || !aligned(context_lens, 4))
+    return fail(PAGEDKV_ERR_ALIGN, "q, k_cache, v_cache and out need 16-byte alignment");
+  int cus = 0;
+  st = cu_count(&cus);
+  if (st) return st;
+  Plan plan{};
+  st = make_plan(batch, num_kv_heads, max_blocks_per_seq, block_size, partition_tokens, cus,
+                 &plan);
+  if (st) return st;
+
+  DecodeArgs a{};
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.out = out;
+  a.max_blocks = max_blocks_per_seq;
+  a.batch = batch;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.block_size = block_size;
+  a.num_blocks = num_blocks;
+  a.scale_log2 = scale * kLog2eHost;
+  a.nparts = plan.nparts;
+  a.part_tokens = plan.part_tokens;
+  if (plan.nparts > 1) {
+    const size_t need = split_workspace_bytes(batch, num_q_heads, head_dim, plan.nparts);
+    if (!workspace || workspace_bytes < need)
+      return fail(PAGEDKV_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                  workspace ? workspace_bytes : (size_t)0);
+    if (!aligned(workspace, 16)) return fail(PAGEDKV_ERR_ALIGN, "workspace needs 16-byte alignment");
+    a.ws_acc = static_cast<float*>(workspace);
+    a.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                       acc_bytes(batch, num_q_heads, head_dim, plan.nparts));
+  }
+
+  hipError_t e;
+  if (ev_begin && (e = hipEventRecord(ev_begin, stream)) != hipSuccess)
+    return hip_fail(e, "hipEventRecord(begin)");
+  e = chosen == PAGEDKV_KERNEL_MFMA ? launch_decode_mfma(a, stream) : launch_decode_valu(a, stream);
+  if (e != hipSuccess) return hip_fail(e, "decode attention launch");
+  if (ev_end && (e = hipEventRecord(ev_end, stream)) != hipSuccess)
+    return hip_fail(e, "hipEventRecord(end)");
+  if (plan.nparts > 1) {
+    e = launch_decode_reduce(a, stream);
+    if (e != hipSuccess) return hip_fail(e, "partition merge launch");
+  }
+  return PAGEDKV_OK;
+}
+
+int paged_decode_attention(const uint16_t* q, const uint16_t* k_cache,
+                           const uint16_t* v_cache, const int32_t* block_tables,
+                           int32_t max_blocks_per_seq, const int32_t* context_lens,
+                           int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                           int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                           float scale, float* out, void* workspace, size_t workspace_bytes,
+                           int32_t partition_tokens, hipStream_t stream) {
+  return paged_decode_attention_ex(q, k_cache, v_cache, block_tables, max_blocks_per_seq,
+                                   context_lens, batch, num_q_heads, num_kv_heads, head_dim,
+                                   block_size, num_blocks, scale, out, workspace,
+                                   workspace_bytes, partition_tokens, PAGEDKV_KERNEL_AUTO,
+                                   nullptr, nullptr, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,49 @@
+// Internal interface between the C-ABI host layer (api.cpp) and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pagedkv {
+
+// Arguments of one decode-attention launch, already validated by the host layer.
+struct DecodeArgs {
+  const uint16_t* q;
+  const uint16_t* k_cache;
+  const uint16_t* v_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  float* out;
+  float* ws_acc;    // [B][Hq][nparts][D] unnormalised partial outputs (split only)
+  float* ws_ml;     // [B][Hq][nparts][2] partial (max, sum) in log2 units (split only)
+  int32_t max_blocks;  // MB, block-table row length
+  int32_t batch, num_q_heads, num_kv_heads, head_dim, block_size;
+  int64_t num_blocks;
+  float scale_log2;     // scale * log2(e)
+  int32_t nparts;       // partitions per sequence (1 = write out directly)
+  int32_t part_tokens;  // tokens per partition, a multiple of block_size
+};
+
+// Each launcher returns hipSuccess or the launch error. `supported_*` report whether a
+// compiled instance exists for the shape.
+bool supported_valu(int head_dim, int group, int block_size);
+hipError_t launch_decode_valu(const DecodeArgs& a, hipStream_t stream);
+
+bool supported_mfma(int head_dim, int group, int block_size);
+hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream);
+
+hipError_t launch_decode_reduce(const DecodeArgs& a, hipStream_t stream);
+
+hipError_t launch_kv_write(const uint16_t* k, const uint16_t* v, const int64_t* slots,
+                           int64_t num_tokens, uint16_t* k_cache, uint16_t* v_cache,
+                           int64_t num_slots, int32_t row_elems, hipStream_t stream);
+
+// Waves per workgroup of the decode kernels; partitions are multiples of
+// kWavesPerGroup * block_size tokens when split automatically.
+constexpr int kWavesPerGroup = 4;
+
+// log2(e), to turn natural-log scores into log2 units for v_exp_f32.
+constexpr float kLog2eHost = 1.4426950408889634f;
+
+}  // namespace pagedkv

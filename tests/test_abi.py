@@ -1,0 +1,116 @@
+"""The C-ABI library without a GPU: it loads, exports every declared symbol, and rejects bad
+arguments on the host with the documented status codes before touching the device."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from paged_kv_decode_write_amd import _binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "paged_kv.h")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP, ERR_ALIGN = range(7)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_binding.library_path()):
+        pytest.skip("libpagedkv.so not built")
+    return _binding.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(paged_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for want in ("paged_kv_write", "paged_decode_attention", "paged_decode_attention_ex",
+                 "paged_decode_workspace_bytes", "paged_kv_status_string", "paged_kv_abi_version",
+                 "paged_kv_last_error", "paged_decode_plan"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", _binding.library_path()],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (paged_\w+)", out))
+    assert set(declared_functions()) <= exported
+
+
+def test_version_and_status_strings(lib):
+    assert lib.paged_kv_abi_version() == 1
+    assert lib.paged_kv_status_string(OK) == b"PAGEDKV_OK"
+    assert lib.paged_kv_status_string(ERR_WORKSPACE) == b"PAGEDKV_ERR_WORKSPACE"
+    assert lib.paged_kv_status_string(99) == b"PAGEDKV_UNKNOWN_STATUS"
+
+
+FAKE = 0x10000  # a 16-byte aligned address that is never dereferenced: the host rejects first
+
+
+def _write(lib, k=FAKE, v=FAKE, slots=FAKE, T=4, kc=FAKE, vc=FAKE, NB=8, bs=16, Hkv=8, D=128):
+    return lib.paged_kv_write(k, v, slots, T, kc, vc, NB, bs, Hkv, D, None)
+
+
+def test_write_argument_errors(lib):
+    assert _write(lib, T=-1) == ERR_SHAPE
+    assert _write(lib, NB=0) == ERR_SHAPE
+    assert _write(lib, bs=0) == ERR_SHAPE
+    assert _write(lib, Hkv=1, D=6) == ERR_UNSUPPORTED
+    assert _write(lib, k=None) == ERR_NULL
+    assert _write(lib, vc=None) == ERR_NULL
+    assert _write(lib, k=FAKE + 2) == ERR_ALIGN
+    assert _write(lib, slots=FAKE + 4) == ERR_ALIGN
+    assert _write(lib, T=0, k=None, v=None) == OK  # nothing to do, nothing touched
+    assert b"non-NULL" in (_write(lib, k=None) and lib.paged_kv_last_error())
+
+
+def _attn(lib, q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, MB=8, lens=FAKE, B=2, Hq=32, Hkv=8, D=128,
+          bs=16, NB=64, out=FAKE, ws=None, wsb=0, part=-1, kernel=0):
+    return lib.paged_decode_attention_ex(q, kc, vc, bt, MB, lens, B, Hq, Hkv, D, bs, NB, 0.1,
+                                         out, ws, wsb, part, kernel, None, None, None)
+
+
+def test_attention_argument_errors(lib):
+    assert _attn(lib, B=-1) == ERR_SHAPE
+    assert _attn(lib, Hq=30) == ERR_SHAPE           # not a multiple of Hkv
+    assert _attn(lib, NB=0) == ERR_SHAPE
+    assert _attn(lib, D=96) == ERR_UNSUPPORTED
+    assert _attn(lib, bs=8) == ERR_UNSUPPORTED
+    assert _attn(lib, kernel=7) == ERR_UNSUPPORTED
+    assert _attn(lib, kernel=1, Hq=40) == ERR_UNSUPPORTED  # G=5 has no VALU build
+    assert _attn(lib, q=None) == ERR_NULL
+    assert _attn(lib, out=None) == ERR_NULL
+    assert _attn(lib, q=FAKE + 8) == ERR_ALIGN
+    assert _attn(lib, B=0, q=None, out=None) == OK  # empty batch: no-op
+
+
+def test_workspace_bytes(lib):
+    f = lib.paged_decode_workspace_bytes
+    assert f(64, 32, 128, 512, 16, -1) == 0              # never split
+    assert f(1, 32, 64, 8, 16, 0) == 0                   # 128 tokens: auto never splits
+    # forced 256-token partitions over 32768 tokens: 128 partitions of D+2 floats per head
+    n = 128
+    acc = 2 * 32 * n * 128 * 4
+    ml = 2 * 32 * n * 2 * 4
+    assert f(2, 32, 128, 2048, 16, 256) == acc + ml
+    # auto bound: partitions of at least 256 tokens
+    assert f(2, 32, 128, 2048, 16, 0) == acc + ml
+    assert f(2, 32, 128, 2048, 16, 24) == 0               # not a multiple of block_size
+    assert f(0, 32, 128, 2048, 16, 0) == 0
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    k = torch.zeros(2, 8, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        _binding.paged_kv_write(k, k, torch.zeros(2, dtype=torch.int64),
+                                torch.zeros(4, 16, 8, 128, dtype=torch.bfloat16),
+                                torch.zeros(4, 16, 8, 128, dtype=torch.bfloat16))

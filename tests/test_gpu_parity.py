@@ -1,0 +1,299 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle, on the GPU.
+
+KV write: the whole pools must be bit-identical to the oracle's. Attention: max |out - oracle|
+must stay within 2e-3 (fp32 output against the float64 oracle), in automatic, forced-split
+and never-split modes, for every kernel family built for the shape. Full-size workloads whose
+oracle would be slow are compared on sampled output rows, plus properties that hold at any
+size (split vs unsplit agreement, unread slots never matter, determinism).
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from paged_kv_decode_write_amd import _binding as pk
+from paged_kv_decode_write_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+ATOL = 2e-3
+SUMMARY = {}
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    pk.load_library()  # a missing library is an error on a GPU machine, not a skip
+    return torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _write_summary():
+    yield
+    path = os.environ.get("PAGEDKV_PARITY_SUMMARY")
+    if path:
+        os.makedirs(os.path.dirname(path) or ".", exist_ok=True)
+        with open(path, "w") as f:
+            json.dump(SUMMARY, f, indent=1, sort_keys=True)
+
+
+def kernels_for(w):
+    out = []
+    for k in ("valu", "mfma"):
+        try:
+            pk.decode_plan(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.max_blocks,
+                           w.block_size, 0, k)
+            out.append(k)
+        except pk.PagedKVError:
+            pass
+    assert out, f"no kernel for {w}"
+    return out
+
+
+def to_dev(inp, dev):
+    return {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+
+
+def run_write(d):
+    pk.paged_kv_write(d["k_new"], d["v_new"], d["slot_mapping"], d["k_cache"], d["v_cache"])
+
+
+def run_attention(d, kernel="auto", partition=0):
+    w = d["workload"]
+    out = torch.full((w.batch, w.num_q_heads, w.head_dim), float("nan"), dtype=torch.float32,
+                     device=d["q"].device)
+    pk.paged_decode_attention(d["q"], d["k_cache"], d["v_cache"], d["block_tables"],
+                              d["context_lens"], d["scale"], out, partition_tokens=partition,
+                              kernel=kernel)
+    return out
+
+
+def record(key, err):
+    SUMMARY[key] = float(err)
+    print(f"[parity] {key}: max|err| = {err:.3e}", flush=True)
+
+
+_CASES = {}
+
+
+def case(name, dev, poison=False):
+    """(host numpy inputs, oracle out, oracle pools after the write, device inputs after the
+    GPU write) for a workload; drawn once per session. The write is idempotent, so tests may
+    repeat it on the device copy."""
+    key = (name, poison)
+    if key not in _CASES:
+        inp = wl.make_inputs(wl.WORKLOADS[name], poison=poison)
+        host = wl.to_host_numpy(inp)
+        out, kc, vc = oracle.decode_step(host)
+        d = to_dev(inp, dev)
+        run_write(d)
+        torch.cuda.synchronize()
+        _CASES[key] = (host, out, kc, vc, d)
+    return _CASES[key]
+
+
+SMALL = ["c1", "c2", "c3", "c4"]
+
+
+# ------------------------------------------------------------------------------ KV write
+@pytest.mark.parametrize("name", SMALL)
+def test_kv_write_bit_exact_full_pool(dev, name):
+    host, _, kc_ref, vc_ref, d = case(name, dev)
+    assert np.array_equal(wl.to_bits(d["k_cache"]), kc_ref)
+    assert np.array_equal(wl.to_bits(d["v_cache"]), vc_ref)
+
+
+@pytest.mark.parametrize("name", ["c5a", "c5b"])
+def test_kv_write_bit_exact_full_size(dev, name):
+    w = wl.WORKLOADS[name]
+    d = wl.make_inputs(w, device="cuda")
+    kc0, vc0 = wl.to_bits(d["k_cache"]), wl.to_bits(d["v_cache"])
+    run_write(d)
+    torch.cuda.synchronize()
+    kc_ref, vc_ref = oracle.kv_write(wl.to_bits(d["k_new"]), wl.to_bits(d["v_new"]),
+                                     d["slot_mapping"].cpu().numpy(), kc0, vc0)
+    del kc0, vc0
+    assert np.array_equal(wl.to_bits(d["k_cache"]), kc_ref)
+    assert np.array_equal(wl.to_bits(d["v_cache"]), vc_ref)
+
+
+def test_kv_write_skips_negative_slots_and_keeps_nan_payloads(dev):
+    w = wl.Workload("neg", batch=6, num_q_heads=8, num_kv_heads=2, head_dim=64, block_size=16,
+                    num_blocks=16, max_blocks=4, seed=77, max_context_len=60)
+    inp = wl.make_inputs(w)
+    inp["slot_mapping"][[1, 4]] = -1
+    inp["k_new"].view(torch.int16)[0, 0, 0] = 0x7FA1  # a NaN with a payload
+    host = wl.to_host_numpy(inp)
+    kc_ref, vc_ref = oracle.kv_write(host["k_new"], host["v_new"], host["slot_mapping"],
+                                     host["k_cache"], host["v_cache"])
+    d = to_dev(inp, dev)
+    run_write(d)
+    torch.cuda.synchronize()
+    assert np.array_equal(wl.to_bits(d["k_cache"]), kc_ref)
+    assert np.array_equal(wl.to_bits(d["v_cache"]), vc_ref)
+
+
+def test_kv_write_zero_tokens_is_noop(dev):
+    kc = torch.randn(4, 16, 2, 64, device=dev).to(torch.bfloat16)
+    before = kc.clone()
+    e = torch.empty(0, 2, 64, dtype=torch.bfloat16, device=dev)
+    pk.paged_kv_write(e, e, torch.empty(0, dtype=torch.int64, device=dev), kc, kc)
+    torch.cuda.synchronize()
+    assert torch.equal(kc, before)
+
+
+# ----------------------------------------------------------------------------- attention
+@pytest.mark.parametrize("partition", [0, -1, 64, 256])
+@pytest.mark.parametrize("name", SMALL)
+def test_attention_parity(dev, name, partition):
+    host, ref, _, _, d = case(name, dev)
+    w = wl.WORKLOADS[name]
+    for kernel in kernels_for(w):
+        run_write(d)
+        out = run_attention(d, kernel, partition).cpu().double().numpy()
+        err = np.abs(out - ref).max()
+        record(f"{name}/{kernel}/p{partition}", err)
+        assert np.isfinite(out).all()
+        assert err <= ATOL, (name, kernel, partition, err)
+
+
+@pytest.mark.parametrize("name", SMALL)
+def test_attention_poisoned_pool_matches_clean(dev, name):
+    """Quiet-NaN bits in every slot attention must not read leave the output unchanged."""
+    w = wl.WORKLOADS[name]
+    _, _, _, _, clean = case(name, dev)
+    _, ref, _, _, dirty = case(name, dev, poison=True)
+    for kernel in kernels_for(w):
+        for partition in (0, -1, 64):
+            o1 = run_attention(clean, kernel, partition)
+            o2 = run_attention(dirty, kernel, partition)
+            assert torch.equal(o1, o2), (name, kernel, partition)
+            err = np.abs(o2.cpu().double().numpy() - ref).max()
+            assert err <= ATOL
+
+
+def sample_rows(w, rng, n=24):
+    rows = {(0, 0), (w.batch - 1, w.num_q_heads - 1)}
+    while len(rows) < n:
+        rows.add((int(rng.integers(w.batch)), int(rng.integers(w.num_q_heads))))
+    return sorted(rows)
+
+
+def oracle_rows_from_device(d, rows):
+    """Run the oracle on the sampled rows, reading only the blocks those sequences use."""
+    w = d["workload"]
+    tables = d["block_tables"].cpu().numpy()
+    lens = d["context_lens"].cpu().numpy()
+    q = wl.to_bits(d["q"])
+    res = {}
+    for b in sorted({b for b, _ in rows}):
+        n = (int(lens[b]) + w.block_size - 1) // w.block_size
+        ids = torch.from_numpy(tables[b, :n].astype(np.int64)).to(d["k_cache"].device)
+        kc = wl.to_bits(d["k_cache"].index_select(0, ids))
+        vc = wl.to_bits(d["v_cache"].index_select(0, ids))
+        local = np.arange(n, dtype=np.int32)[None]
+        heads = [h for bb, h in rows if bb == b]
+        o = oracle.decode_attention(q[b:b + 1], kc, vc, local, lens[b:b + 1], d["scale"],
+                                    rows=[(0, h) for h in heads])
+        for h in heads:
+            res[(b, h)] = o[0, h]
+    return res
+
+
+@pytest.mark.parametrize("name", ["c5a", "c5b"])
+def test_attention_full_size_sampled(dev, name):
+    w = wl.WORKLOADS[name]
+    d = wl.make_inputs(w, device="cuda")
+    run_write(d)
+    rows = sample_rows(w, np.random.default_rng(5))
+    ref = oracle_rows_from_device(d, rows)
+    outs = {}
+    for kernel in kernels_for(w):
+        for partition in (0, -1):
+            out = run_attention(d, kernel, partition)
+            outs[(kernel, partition)] = out
+            o = out.cpu().double().numpy()
+            assert np.isfinite(o).all()
+            err = max(np.abs(o[b, h] - ref[(b, h)]).max() for b, h in rows)
+            record(f"{name}/{kernel}/p{partition}/sampled", err)
+            assert err <= ATOL, (name, kernel, partition, err)
+    # properties at full size: split and unsplit agree; every kernel agrees
+    base = outs[(kernels_for(w)[0], -1)]
+    for key, o in outs.items():
+        diff = (o - base).abs().max().item()
+        record(f"{name}/{key[0]}/p{key[1]}/vs_unsplit", diff)
+        assert diff <= 1e-4
+
+
+EDGE_LENGTHS = [1, 15, 16, 17, 256, 257, 4095, 4096, 0, 33]
+
+
+@pytest.mark.parametrize("D,Hq,Hkv", [(128, 32, 8), (64, 24, 8), (128, 8, 8), (64, 16, 2)])
+def test_attention_edge_lengths(dev, D, Hq, Hkv):
+    w = wl.Workload("edge", batch=len(EDGE_LENGTHS), num_q_heads=Hq, num_kv_heads=Hkv,
+                    head_dim=D, block_size=16, num_blocks=1200, max_blocks=260, seed=4242,
+                    q_std=3.0)
+    inp = wl.make_inputs(w, poison=True, lengths=EDGE_LENGTHS)
+    host = wl.to_host_numpy(inp)
+    ref, _, _ = oracle.decode_step(host)
+    for kernel in kernels_for(w):
+        for partition in (0, -1, 16, 256, 272):
+            d = to_dev(inp, dev)
+            run_write(d)
+            out = run_attention(d, kernel, partition).cpu().double().numpy()
+            err = np.abs(out - ref).max()
+            record(f"edge/D{D}/G{Hq // Hkv}/{kernel}/p{partition}", err)
+            assert np.isfinite(out).all()
+            assert err <= ATOL, (kernel, partition, err)
+            assert not out[EDGE_LENGTHS.index(0)].any()  # empty context -> zeros
+
+
+def test_length_one_returns_value_row_exactly(dev):
+    w = wl.Workload("one", batch=5, num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
+                    num_blocks=10, max_blocks=2, seed=99, context_len=1, q_std=3.0)
+    for kernel in kernels_for(w):
+        for partition in (0, -1, 16):
+            d = to_dev(wl.make_inputs(w, poison=True), dev)
+            run_write(d)
+            out = run_attention(d, kernel, partition)
+            vrow = d["v_new"].float().repeat_interleave(4, dim=1)  # [B, Hq, D]
+            assert torch.equal(out, vrow), (kernel, partition)
+
+
+def test_split_agrees_with_unsplit_and_is_deterministic(dev):
+    w = wl.WORKLOADS["c4"]
+    d = case("c4", dev)[4]
+    for kernel in kernels_for(w):
+        base = run_attention(d, kernel, -1)
+        again = run_attention(d, kernel, -1)
+        assert torch.equal(base, again)
+        for partition in (16, 64, 512, 0):
+            o = run_attention(d, kernel, partition)
+            diff = (o - base).abs().max().item()
+            record(f"c4/{kernel}/p{partition}/vs_unsplit", diff)
+            assert diff <= 1e-5, (kernel, partition, diff)
+
+
+def test_kernels_agree(dev):
+    w = wl.WORKLOADS["c2"]
+    ks = kernels_for(w)
+    if len(ks) < 2:
+        pytest.skip("one kernel family built for this shape")
+    d = case("c2", dev)[4]
+    outs = [run_attention(d, k, 0) for k in ks]
+    diff = (outs[0] - outs[1]).abs().max().item()
+    record("c2/kernels_agree", diff)
+    assert diff <= 1e-4
+
+
+def test_empty_batch_is_noop(dev):
+    w = wl.WORKLOADS["c1"]
+    d = case("c1", dev)[4]
+    out = torch.empty(0, w.num_q_heads, w.head_dim, device=dev)
+    pk.paged_decode_attention(d["q"][:0], d["k_cache"], d["v_cache"], d["block_tables"][:0],
+                              d["context_lens"][:0], d["scale"], out)
+    torch.cuda.synchronize()
