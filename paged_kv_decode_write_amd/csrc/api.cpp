@@ -68,8 +68,10 @@ struct Plan {
 
 // Partition plan. max_len = MB * block_size bounds every context length; the plan never
 // reads context_lens (that would need a device-to-host copy and a sync).
+// `granule`: automatic partitions are rounded up to a multiple of this many tokens (the
+// tokens one workgroup step covers: waves x blocks per wave step x block_size).
 int make_plan(int32_t batch, int32_t num_kv_heads, int32_t max_blocks, int32_t block_size,
-              int32_t partition_tokens, int cus, Plan* plan) {
+              int32_t partition_tokens, int cus, int granule, Plan* plan) {
   const int64_t max_len = (int64_t)max_blocks * block_size;
   if (partition_tokens < -1) return fail(PAGEDKV_ERR_SHAPE, "partition_tokens must be >= -1");
   int64_t n = 1, P = 0;
@@ -88,7 +90,7 @@ int make_plan(int32_t batch, int32_t num_kv_heads, int32_t max_blocks, int32_t b
     n = units > 0 ? ceil_div(target, units) : 1;
     if (n > nmax) n = nmax;
     if (n < 1) n = 1;
-    P = round_up(ceil_div(max_len, n), (int64_t)kWavesPerGroup * block_size);
+    P = round_up(ceil_div(max_len, n), (int64_t)granule);
     n = ceil_div(max_len, P);
   }
   if (n <= 1) {
@@ -141,6 +143,10 @@ int select_kernel(int32_t kernel, int D, int G, int bs, int* chosen) {
               "no %s kernel for head_dim %d, block_size %d, group size %d",
               kernel == PAGEDKV_KERNEL_MFMA ? "MFMA" : kernel == PAGEDKV_KERNEL_VALU ? "VALU" : "",
               D, bs, G);
+}
+
+int plan_granule(int kernel, int32_t block_size) {
+  return kWavesPerGroup * block_size * (kernel == PAGEDKV_KERNEL_MFMA ? 2 : 1);
 }
 
 int check_decode_sizes(int32_t max_blocks, int32_t batch, int32_t num_q_heads,
@@ -236,7 +242,7 @@ int paged_decode_plan(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
   if (st) return st;
   Plan plan{};
   st = make_plan(batch, num_kv_heads, max_blocks_per_seq, block_size, partition_tokens, cus,
-                 &plan);
+                 plan_granule(chosen, block_size), &plan);
   if (st) return st;
   *num_partitions = plan.nparts;
   *tokens_per_partition = plan.part_tokens;
@@ -273,7 +279,7 @@ int paged_decode_attention_ex(const uint16_t* q, const uint16_t* k_cache,
   if (st) return st;
   Plan plan{};
   st = make_plan(batch, num_kv_heads, max_blocks_per_seq, block_size, partition_tokens, cus,
-                 &plan);
+                 plan_granule(chosen, block_size), &plan);
   if (st) return st;
 
   DecodeArgs a{};

@@ -123,7 +123,7 @@ def test_kv_write_bit_exact_full_size(dev, name):
 
 def test_kv_write_skips_negative_slots_and_keeps_nan_payloads(dev):
     w = wl.Workload("neg", batch=6, num_q_heads=8, num_kv_heads=2, head_dim=64, block_size=16,
-                    num_blocks=16, max_blocks=4, seed=77, max_context_len=60)
+                    num_blocks=32, max_blocks=4, seed=77, max_context_len=60)
     inp = wl.make_inputs(w)
     inp["slot_mapping"][[1, 4]] = -1
     inp["k_new"].view(torch.int16)[0, 0, 0] = 0x7FA1  # a NaN with a payload
