@@ -39,7 +39,7 @@ def parse_args():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="c5")
-    p.add_argument("--kernel", default="auto", choices=["auto", "valu", "mfma"])
+    p.add_argument("--kernel", default="auto", choices=["auto", "valu", "mfma", "mfma_hw"])
     p.add_argument("--partition", type=int, default=0,
                    help="tokens per partition: 0 automatic, -1 never split")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -81,7 +81,7 @@ class HipEvents:
 
 def kernel_source_hash(kernel: str) -> str:
     csrc = os.path.join(HERE, "paged_kv_decode_write_amd", "csrc")
-    files = ["device_common.h", "launch.h", f"decode_{kernel}.hip"]
+    files = ["device_common.h", "launch.h", "decode_%s.hip" % kernel.split("_")[0]]
     h = hashlib.sha256()
     for f in files:
         with open(os.path.join(csrc, f), "rb") as fh:
@@ -92,12 +92,8 @@ def kernel_source_hash(kernel: str) -> str:
 def resolved_kernel(pk, w, requested):
     if requested != "auto":
         return requested
-    try:
-        pk.decode_plan(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.max_blocks,
-                       w.block_size, 0, "mfma")
-        return "mfma"
-    except pk.PagedKVError:
-        return "valu"
+    return pk.decode_plan(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.max_blocks,
+                          w.block_size, 0, "auto", with_kernel=True)[2]
 
 
 def cpu_baseline(d, seconds):
@@ -166,10 +162,11 @@ def main():
         d["out"] = torch.empty(w.batch, w.num_q_heads, w.head_dim, dtype=torch.float32, device=dev)
         need = pk.decode_workspace_bytes(w.batch, w.num_q_heads, w.head_dim, w.max_blocks,
                                          w.block_size, args.partition)
-        d["ws"] = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+        d["ws"] = pk.new_workspace(need, dev)
         d["bytes"] = wl.algorithmic_bytes(w, d["context_lens"].cpu().tolist())
         d["plan"] = pk.decode_plan(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim,
-                                   w.max_blocks, w.block_size, args.partition, args.kernel)
+                                   w.max_blocks, w.block_size, args.partition, args.kernel,
+                                   with_kernel=True)
         subs.append(d)
     torch.cuda.synchronize()
 
@@ -204,6 +201,7 @@ def main():
         w = d["workload"]
         per.append({
             "workload": w.name, "description": w.description,
+            "kernel": d["plan"][2],
             "partitions": d["plan"][0], "tokens_per_partition": d["plan"][1],
             "attn_kernel_us_mean": round(mean * 1e3, 2),
             "attn_kernel_us_median": round(durs[len(durs) // 2] * 1e3, 2),
@@ -241,7 +239,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if kernel == "mfma" else "fp32",
+        "dtype": "bf16" if kernel.startswith("mfma") else "fp32",
         "data": "synthetic (seeded N(0,1) bf16 K/V pools, shuffled block tables), resident in HBM",
         "config": {
             "workload": "+".join(d["workload"].description for d in subs),
@@ -249,6 +247,7 @@ def main():
             "partition_tokens": args.partition,
             "us_per_call": {p["workload"]: p["attn_kernel_us_mean"] for p in per},
             "pct_of_peak": {p["workload"]: p["pct_of_peak"] for p in per},
+            "kernels": {p["workload"]: p["kernel"] for p in per},
             "step": "KV write + decode attention per sub-workload",
         },
         "roofline": {

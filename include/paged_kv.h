@@ -117,9 +117,9 @@ size_t paged_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t 
  *   context_lens   int32 [batch], 0 <= L_b <= max_blocks_per_seq*block_size
  *   scale          applied in fp32 to the fp32 dot product (typically 1/sqrt(head_dim))
  *   out            fp32 [batch][num_q_heads][head_dim] (written)
- *   workspace      device scratch of >= paged_decode_workspace_bytes(...) bytes, 256-byte
+ *   workspace      device scratch of >= paged_decode_workspace_bytes(...) bytes, 16-byte
  *                  aligned, or NULL/0 when that size is 0. Contents need no initialisation;
- *                  calls running concurrently must not share one workspace.
+ *                  calls that may run concurrently must not share one workspace.
  *   partition_tokens  0: choose automatically from the sizes and the device; -1: never
  *                  split a sequence; > 0: split each sequence into partitions of this many
  *                  tokens (a multiple of block_size) whose partial softmax results are
@@ -138,9 +138,14 @@ int paged_decode_attention(const uint16_t* q, const uint16_t* k_cache,
 
 /* Kernel families for paged_decode_attention_ex. */
 typedef enum {
-  PAGEDKV_KERNEL_AUTO = 0,  /* the library's choice for the shape (the default path) */
-  PAGEDKV_KERNEL_VALU = 1,  /* fp32 vector-ALU dot products and accumulation */
-  PAGEDKV_KERNEL_MFMA = 2   /* bf16 matrix-core (MFMA) tiles with fp32 accumulation */
+  PAGEDKV_KERNEL_AUTO = 0,  /* the library's choice for the shape (the default path):
+                               MFMA_HEADWAVE for contexts over 1024 tokens, else MFMA */
+  PAGEDKV_KERNEL_VALU = 1,  /* fp32 vector-ALU dot products and accumulation; a workgroup's
+                               4 waves split one (sequence, KV head) partition */
+  PAGEDKV_KERNEL_MFMA = 2,  /* bf16 matrix-core (MFMA) tiles, fp32 accumulation; a
+                               workgroup's 4 waves split one (sequence, KV head) partition */
+  PAGEDKV_KERNEL_MFMA_HEADWAVE = 3  /* MFMA tiles; a workgroup's 4 waves take 4 KV heads of
+                               one (sequence, partition), one wave per head */
 } pagedkv_kernel;
 
 /*
@@ -163,15 +168,16 @@ int paged_decode_attention_ex(const uint16_t* q, const uint16_t* k_cache,
                               hipStream_t stream);
 
 /*
- * paged_decode_plan -- the launch the call would make for these sizes on the current
- * device, without launching: number of sequence partitions and tokens per partition
- * (partition_tokens as in paged_decode_attention). Returns a status; the outputs are
- * written on PAGEDKV_OK.
+ * paged_decode_plan -- the launch paged_decode_attention_ex would make for these sizes on
+ * the current device, without launching: number of sequence partitions, tokens per
+ * partition, and the kernel family (a pagedkv_kernel value, never AUTO). partition_tokens
+ * and kernel as in paged_decode_attention_ex. Returns a status; the outputs are written on
+ * PAGEDKV_OK (chosen_kernel may be NULL).
  */
 int paged_decode_plan(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                       int32_t head_dim, int32_t max_blocks_per_seq, int32_t block_size,
                       int32_t partition_tokens, int32_t kernel, int32_t* num_partitions,
-                      int32_t* tokens_per_partition);
+                      int32_t* tokens_per_partition, int32_t* chosen_kernel);
 
 #ifdef __cplusplus
 }

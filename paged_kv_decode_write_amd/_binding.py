@@ -19,10 +19,13 @@ LIB_NAME = "libpagedkv.so"
 STATUS_NAMES = {0: "PAGEDKV_OK", 1: "PAGEDKV_ERR_NULL", 2: "PAGEDKV_ERR_SHAPE",
                 3: "PAGEDKV_ERR_UNSUPPORTED", 4: "PAGEDKV_ERR_WORKSPACE", 5: "PAGEDKV_ERR_HIP",
                 6: "PAGEDKV_ERR_ALIGN"}
-KERNELS = {"auto": 0, "valu": 1, "mfma": 2}
+KERNELS = {"auto": 0, "valu": 1, "mfma": 2, "mfma_hw": 3}
 
 _lock = threading.Lock()
 _lib: Optional[ctypes.CDLL] = None
+# One workspace per (device, stream), grown on demand and reused, so steady-state calls
+# allocate nothing.
+_workspaces = {}
 
 
 class PagedKVError(RuntimeError):
@@ -66,7 +69,8 @@ def load_library() -> ctypes.CDLL:
         lib.paged_decode_attention_ex.argtypes = attn + [I32, P, P, P]
         lib.paged_decode_plan.restype = ctypes.c_int
         lib.paged_decode_plan.argtypes = [I32, I32, I32, I32, I32, I32, I32, I32,
-                                          ctypes.POINTER(I32), ctypes.POINTER(I32)]
+                                          ctypes.POINTER(I32), ctypes.POINTER(I32),
+                                          ctypes.POINTER(I32)]
         _lib = lib
         return lib
 
@@ -132,15 +136,37 @@ def decode_workspace_bytes(batch: int, num_q_heads: int, head_dim: int,
         batch, num_q_heads, head_dim, max_blocks_per_seq, block_size, partition_tokens))
 
 
+KERNEL_NAMES = {v: k for k, v in KERNELS.items()}
+
+
 def decode_plan(batch, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq, block_size,
-                partition_tokens=0, kernel="auto"):
-    """(num_partitions, tokens_per_partition) the call would use on the current device."""
+                partition_tokens=0, kernel="auto", with_kernel=False):
+    """(num_partitions, tokens_per_partition[, kernel name]) the call would use on the
+    current device."""
     n = ctypes.c_int32(0)
     p = ctypes.c_int32(0)
+    k = ctypes.c_int32(0)
     _check(load_library().paged_decode_plan(batch, num_q_heads, num_kv_heads, head_dim,
                                             max_blocks_per_seq, block_size, partition_tokens,
-                                            KERNELS[kernel], ctypes.byref(n), ctypes.byref(p)))
+                                            KERNELS[kernel], ctypes.byref(n), ctypes.byref(p),
+                                            ctypes.byref(k)))
+    if with_kernel:
+        return n.value, p.value, KERNEL_NAMES[k.value]
     return n.value, p.value
+
+
+def _cached_workspace(dev: torch.device, nbytes: int) -> torch.Tensor:
+    key = (dev.index, torch.cuda.current_stream(dev).cuda_stream)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+        _workspaces[key] = ws
+    return ws
+
+
+def new_workspace(nbytes: int, device) -> torch.Tensor:
+    """A workspace of nbytes for explicit reuse across calls on one stream."""
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
 
 
 def paged_decode_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
@@ -154,9 +180,9 @@ def paged_decode_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
     q [B, Hq, D] bf16; k_cache/v_cache [NB, block_size, Hkv, D] bf16; block_tables
     [B, MB] int32; context_lens [B] int32; out [B, Hq, D] fp32 (written and returned).
     partition_tokens: 0 automatic, -1 never split, >0 split size in tokens (tests).
-    kernel: "auto", "valu" or "mfma". workspace: optional uint8 device buffer (allocated from
-    torch's caching allocator when omitted). events: optional (begin, end) raw hipEvent_t
-    handles recorded around the main kernel.
+    kernel: "auto", "valu", "mfma" or "mfma_hw". workspace: optional uint8 device buffer (see
+    new_workspace); when omitted, a cached per-stream workspace is used.
+    events: optional (begin, end) raw hipEvent_t handles recorded around the main kernel.
     """
     _require(k_cache, "k_cache", torch.bfloat16, 4)
     dev = k_cache.device
@@ -181,7 +207,7 @@ def paged_decode_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
     lib = load_library()
     need = int(lib.paged_decode_workspace_bytes(B, Hq, D, MB, bs, partition_tokens))
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        workspace = _cached_workspace(dev, need)
     elif workspace.device != dev or workspace.dtype != torch.uint8:
         raise ValueError("workspace must be a uint8 tensor on the cache's device")
     ws_bytes = workspace.numel()

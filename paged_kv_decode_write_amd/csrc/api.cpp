@@ -55,8 +55,13 @@ int cu_count(int* out) {
 // Smallest partition the automatic choice makes, in tokens. Partitions shorter than this
 // spend more on the per-partition set-up and merge than they gain in parallelism.
 constexpr int64_t kMinAutoPartition = 256;
-// Workgroups the automatic choice aims for, per compute unit.
+// Work the automatic choice aims for, per compute unit: workgroups of the kernels that split
+// a partition over a workgroup's waves, waves of the kernel with one wave per KV head.
 constexpr int64_t kTargetGroupsPerCU = 4;
+constexpr int64_t kTargetHeadWavesPerCU = 8;
+// Contexts longer than this many tokens use the one-wave-per-KV-head kernel by default;
+// shorter ones spread each partition over a workgroup's waves for lower latency.
+constexpr int64_t kHeadWaveMinContext = 1024;
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
@@ -71,7 +76,7 @@ struct Plan {
 // `granule`: automatic partitions are rounded up to a multiple of this many tokens (the
 // tokens one workgroup step covers: waves x blocks per wave step x block_size).
 int make_plan(int32_t batch, int32_t num_kv_heads, int32_t max_blocks, int32_t block_size,
-              int32_t partition_tokens, int cus, int granule, Plan* plan) {
+              int32_t partition_tokens, int cus, int kernel, int granule, Plan* plan) {
   const int64_t max_len = (int64_t)max_blocks * block_size;
   if (partition_tokens < -1) return fail(PAGEDKV_ERR_SHAPE, "partition_tokens must be >= -1");
   int64_t n = 1, P = 0;
@@ -85,7 +90,8 @@ int make_plan(int32_t batch, int32_t num_kv_heads, int32_t max_blocks, int32_t b
     n = ceil_div(max_len, P);
   } else {
     const int64_t units = (int64_t)batch * num_kv_heads;
-    const int64_t target = kTargetGroupsPerCU * cus;
+    const int64_t target =
+        (kernel == PAGEDKV_KERNEL_MFMA_HEADWAVE ? kTargetHeadWavesPerCU : kTargetGroupsPerCU) * cus;
     const int64_t nmax = ceil_div(max_len, kMinAutoPartition);
     n = units > 0 ? ceil_div(target, units) : 1;
     if (n > nmax) n = nmax;
@@ -115,6 +121,7 @@ int64_t nparts_bound(int64_t max_len, int32_t block_size, int32_t partition_toke
   return ceil_div(max_len, kMinAutoPartition);
 }
 
+// Workspace layout of a split call: [partial outputs | partial (max, sum)].
 size_t acc_bytes(int64_t B, int64_t Hq, int64_t D, int64_t n) {
   return (size_t)round_up(B * Hq * n * D * 4, 256);
 }
@@ -124,16 +131,20 @@ size_t split_workspace_bytes(int64_t B, int64_t Hq, int64_t D, int64_t n) {
   return acc_bytes(B, Hq, D, n) + (size_t)round_up(B * Hq * n * 2 * 4, 256);
 }
 
-int select_kernel(int32_t kernel, int D, int G, int bs, int* chosen) {
+int select_kernel(int32_t kernel, int D, int G, int bs, int64_t max_len, int* chosen) {
   switch (kernel) {
     case PAGEDKV_KERNEL_AUTO:
-      if (supported_mfma(D, G, bs)) { *chosen = PAGEDKV_KERNEL_MFMA; return PAGEDKV_OK; }
+      if (supported_mfma(D, G, bs)) {
+        *chosen = max_len > kHeadWaveMinContext ? PAGEDKV_KERNEL_MFMA_HEADWAVE : PAGEDKV_KERNEL_MFMA;
+        return PAGEDKV_OK;
+      }
       if (supported_valu(D, G, bs)) { *chosen = PAGEDKV_KERNEL_VALU; return PAGEDKV_OK; }
       break;
     case PAGEDKV_KERNEL_VALU:
       if (supported_valu(D, G, bs)) { *chosen = kernel; return PAGEDKV_OK; }
       break;
     case PAGEDKV_KERNEL_MFMA:
+    case PAGEDKV_KERNEL_MFMA_HEADWAVE:
       if (supported_mfma(D, G, bs)) { *chosen = kernel; return PAGEDKV_OK; }
       break;
     default:
@@ -146,7 +157,11 @@ int select_kernel(int32_t kernel, int D, int G, int bs, int* chosen) {
 }
 
 int plan_granule(int kernel, int32_t block_size) {
-  return kWavesPerGroup * block_size * (kernel == PAGEDKV_KERNEL_MFMA ? 2 : 1);
+  switch (kernel) {
+    case PAGEDKV_KERNEL_MFMA: return kWavesPerGroup * block_size * 2;
+    case PAGEDKV_KERNEL_MFMA_HEADWAVE: return block_size * 2;
+    default: return kWavesPerGroup * block_size;
+  }
 }
 
 int check_decode_sizes(int32_t max_blocks, int32_t batch, int32_t num_q_heads,
@@ -227,7 +242,7 @@ size_t paged_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t 
 int paged_decode_plan(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                       int32_t head_dim, int32_t max_blocks_per_seq, int32_t block_size,
                       int32_t partition_tokens, int32_t kernel, int32_t* num_partitions,
-                      int32_t* tokens_per_partition) {
+                      int32_t* tokens_per_partition, int32_t* chosen_kernel) {
   g_last_error.clear();
   int st = check_decode_sizes(max_blocks_per_seq, batch, num_q_heads, num_kv_heads, head_dim,
                               block_size, 1);
@@ -235,17 +250,19 @@ int paged_decode_plan(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
   if (!num_partitions || !tokens_per_partition)
     return fail(PAGEDKV_ERR_NULL, "output pointers must be non-NULL");
   int chosen = 0;
-  st = select_kernel(kernel, head_dim, num_q_heads / num_kv_heads, block_size, &chosen);
+  st = select_kernel(kernel, head_dim, num_q_heads / num_kv_heads, block_size,
+                     (int64_t)max_blocks_per_seq * block_size, &chosen);
   if (st) return st;
   int cus = 0;
   st = cu_count(&cus);
   if (st) return st;
   Plan plan{};
   st = make_plan(batch, num_kv_heads, max_blocks_per_seq, block_size, partition_tokens, cus,
-                 plan_granule(chosen, block_size), &plan);
+                 chosen, plan_granule(chosen, block_size), &plan);
   if (st) return st;
   *num_partitions = plan.nparts;
   *tokens_per_partition = plan.part_tokens;
+  if (chosen_kernel) *chosen_kernel = chosen;
   return PAGEDKV_OK;
 }
 
@@ -264,7 +281,8 @@ int paged_decode_attention_ex(const uint16_t* q, const uint16_t* k_cache,
   if (st) return st;
   const int G = num_q_heads / num_kv_heads;
   int chosen = 0;
-  st = select_kernel(kernel, head_dim, G, block_size, &chosen);
+  st = select_kernel(kernel, head_dim, G, block_size, (int64_t)max_blocks_per_seq * block_size,
+                     &chosen);
   if (st) return st;
   if (batch == 0) return PAGEDKV_OK;
   if (!q || !k_cache || !v_cache || !context_lens || !out ||
@@ -279,7 +297,7 @@ int paged_decode_attention_ex(const uint16_t* q, const uint16_t* k_cache,
   if (st) return st;
   Plan plan{};
   st = make_plan(batch, num_kv_heads, max_blocks_per_seq, block_size, partition_tokens, cus,
-                 plan_granule(chosen, block_size), &plan);
+                 chosen, plan_granule(chosen, block_size), &plan);
   if (st) return st;
 
   DecodeArgs a{};
@@ -305,15 +323,19 @@ int paged_decode_attention_ex(const uint16_t* q, const uint16_t* k_cache,
       return fail(PAGEDKV_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
                   workspace ? workspace_bytes : (size_t)0);
     if (!aligned(workspace, 16)) return fail(PAGEDKV_ERR_ALIGN, "workspace needs 16-byte alignment");
-    a.ws_acc = static_cast<float*>(workspace);
-    a.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                       acc_bytes(batch, num_q_heads, head_dim, plan.nparts));
+    char* base = static_cast<char*>(workspace);
+    a.ws_acc = reinterpret_cast<float*>(base);
+    a.ws_ml = reinterpret_cast<float*>(base + acc_bytes(batch, num_q_heads, head_dim, plan.nparts));
   }
 
   hipError_t e;
   if (ev_begin && (e = hipEventRecord(ev_begin, stream)) != hipSuccess)
     return hip_fail(e, "hipEventRecord(begin)");
-  e = chosen == PAGEDKV_KERNEL_MFMA ? launch_decode_mfma(a, stream) : launch_decode_valu(a, stream);
+  switch (chosen) {
+    case PAGEDKV_KERNEL_MFMA: e = launch_decode_mfma(a, stream); break;
+    case PAGEDKV_KERNEL_MFMA_HEADWAVE: e = launch_decode_mfma_hw(a, stream); break;
+    default: e = launch_decode_valu(a, stream); break;
+  }
   if (e != hipSuccess) return hip_fail(e, "decode attention launch");
   if (ev_end && (e = hipEventRecord(ev_end, stream)) != hipSuccess)
     return hip_fail(e, "hipEventRecord(end)");

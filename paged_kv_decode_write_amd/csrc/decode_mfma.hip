@@ -80,16 +80,165 @@ template <> struct VRow<4> {
 // Slack of the lazily updated softmax reference max, in log2 units (weights <= 2^8).
 constexpr float kRescaleSlack = 8.f;
 
+// Per-lane softmax state of one wave: the head is n16 = lane % 16; lanes of the same head
+// (kg = 0..3) share m_run and hold disjoint output columns.
+template <int EPL> struct WaveState {
+  floatx4 acc[EPL];  // O^T: acc[e][i] = out[head n16][EPL*(4kg+i) + e] (unnormalised)
+  float m_run;       // reference max (log2 units)
+  float l_run;       // this lane's share of the running sum
+};
+
+// Registers of one block pair in flight: K rows as the A operand of q.K, V rows as loaded.
+template <int NCH, int EPL> struct PairTile {
+  uint4 ka[NCH], kb[NCH];
+  VRow<EPL> vr[8];
+  int lastA, lastB;  // valid rows in each block (0: block absent or invalid)
+};
+
+template <int D> struct PairCtx {
+  const uint16_t* k_cache;
+  const uint16_t* v_cache;
+  const int32_t* table;  // this sequence's block-table row
+  size_t row_stride;     // elements between token rows (Hkv * D)
+  size_t head_off;       // g * D
+  int64_t num_blocks;
+  int blk0, blk1, tok1, wave, n16, kg;
+};
+
+// Block ids of this wave's pair k (uniform, scalar loads).
+template <int D, int NW>
+__device__ __forceinline__ int2 pair_ids(const PairCtx<D>& c, int k) {
+  const int jA = c.blk0 + 2 * (c.wave + NW * k);
+  const int pA = c.table[jA];
+  const int pB = jA + 1 < c.blk1 ? c.table[jA + 1] : -1;
+  return make_int2(pA, pB);
+}
+
+// Issue the loads of pair k. An invalid or absent block is replaced by block 0 (always in
+// the pool) with no valid rows, so its contents never reach the result.
+template <int D, int NW, int NCH, int EPL>
+__device__ __forceinline__ void pair_load(PairTile<NCH, EPL>& t, const PairCtx<D>& c, int2 ids,
+                                          int k) {
+  constexpr int BS = 16;
+  const int jA = c.blk0 + 2 * (c.wave + NW * k);
+  const bool okA = ids.x >= 0 && (int64_t)ids.x < c.num_blocks;
+  const bool okB = ids.y >= 0 && (int64_t)ids.y < c.num_blocks;
+  const int tA = jA * BS;
+  t.lastA = okA ? min(c.tok1 - tA, BS) : 0;
+  t.lastB = okB ? min(c.tok1 - tA - BS, BS) : 0;
+  const size_t bA = (size_t)(okA ? ids.x : 0) * BS * c.row_stride + c.head_off;
+  const size_t bB = (size_t)(okB ? ids.y : 0) * BS * c.row_stride + c.head_off;
+  const size_t koff = (size_t)c.n16 * c.row_stride + 8 * c.kg;
+#pragma unroll
+  for (int ch = 0; ch < NCH; ++ch) {
+    t.ka[ch] = *reinterpret_cast<const uint4*>(c.k_cache + bA + koff + 32 * ch);
+    t.kb[ch] = *reinterpret_cast<const uint4*>(c.k_cache + bB + koff + 32 * ch);
+  }
+  const size_t voff = (size_t)(4 * c.kg) * c.row_stride + EPL * c.n16;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    t.vr[j].load(c.v_cache + bA + voff + (size_t)j * c.row_stride);
+    t.vr[4 + j].load(c.v_cache + bB + voff + (size_t)j * c.row_stride);
+  }
+}
+
+// q.K, online softmax and p.V for one loaded pair.
+template <int NCH, int EPL>
+__device__ __forceinline__ void pair_compute(PairTile<NCH, EPL>& t, WaveState<EPL>& st,
+                                             const bf16x8 (&qb)[NCH], float sl2, int kg) {
+  constexpr int BS = 16;
+  floatx4 sA = {0.f, 0.f, 0.f, 0.f}, sB = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ch = 0; ch < NCH; ++ch) {
+    sA = mfma16x16x32(as_bf16x8(t.ka[ch]), qb[ch], sA);
+    sB = mfma16x16x32(as_bf16x8(t.kb[ch]), qb[ch], sB);
+  }
+  float s[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    s[i] = sA[i] * sl2;
+    s[4 + i] = sB[i] * sl2;
+  }
+  if (t.lastA < BS || t.lastB < BS) {  // a block holds positions at or past the end
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool va = 4 * kg + i < t.lastA;
+      const bool vb = 4 * kg + i < t.lastB;
+      s[i] = va ? s[i] : kNegInf;
+      s[4 + i] = vb ? s[4 + i] : kNegInf;
+      t.vr[i].keep_if(va);  // stale rows may hold NaN bits; 0 * NaN would poison p.V
+      t.vr[4 + i].keep_if(vb);
+    }
+  }
+  float mx = s[0];
+#pragma unroll
+  for (int i = 1; i < 8; ++i) mx = fmaxf(mx, s[i]);
+  mx = fmaxf(mx, shfl_xor(mx, 16));
+  mx = fmaxf(mx, shfl_xor(mx, 32));
+  // Lazy rescaling: the reference max moves only when a score exceeds it by more than
+  // kRescaleSlack, so weights stay <= 2^kRescaleSlack and the accumulator is rescaled on few
+  // steps instead of every step. Any reference value gives the same softmax; the final
+  // normalisation divides it out.
+  const float mn = fmaxf(st.m_run, mx);
+  const bool upd = mn > st.m_run + kRescaleSlack;  // also true while m_run is -inf
+  if (__any(upd)) {
+    const float m_new = upd ? mn : st.m_run;
+    const float alpha = upd ? fast_exp2(st.m_run - (m_new == kNegInf ? 0.f : m_new)) : 1.f;
+    st.l_run *= alpha;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) st.acc[e] *= alpha;
+    st.m_run = m_new;
+  }
+  const float mu = st.m_run == kNegInf ? 0.f : st.m_run;
+  float p[8];
+  float psum = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    p[i] = fast_exp2(s[i] - mu);
+    psum += p[i];
+  }
+  st.l_run += psum;
+
+  // P^T operand, split into bf16 hi (truncation, exact) + bf16 lo (rounded remainder).
+  uint32_t hw[4], lw[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t u0 = __float_as_uint(p[2 * q]), u1 = __float_as_uint(p[2 * q + 1]);
+    hw[q] = pack_hi(u0, u1);
+    const float r0 = p[2 * q] - __uint_as_float(u0 & 0xffff0000u);
+    const float r1 = p[2 * q + 1] - __uint_as_float(u1 & 0xffff0000u);
+    const __bf16 b0 = (__bf16)r0, b1 = (__bf16)r1;
+    lw[q] = (uint32_t)__builtin_bit_cast(uint16_t, b0) |
+            ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
+  }
+  const bf16x8 phi = as_bf16x8(make_uint4(hw[0], hw[1], hw[2], hw[3]));
+  const bf16x8 plo = as_bf16x8(make_uint4(lw[0], lw[1], lw[2], lw[3]));
+
+  // V^T operand for output column set e: 8 token slots of column EPL*n16 + e.
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) {
+    uint32_t w[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t x = t.vr[2 * q].word(e / 2), y = t.vr[2 * q + 1].word(e / 2);
+      w[q] = (e & 1) ? pack_hi(x, y) : pack_lo(x, y);
+    }
+    const bf16x8 vt = as_bf16x8(make_uint4(w[0], w[1], w[2], w[3]));
+    st.acc[e] = mfma16x16x32(vt, phi, st.acc[e]);
+    st.acc[e] = mfma16x16x32(vt, plo, st.acc[e]);
+  }
+}
+
 template <int D, int NW>
 __global__ void __launch_bounds__(NW * 64)
 decode_mfma_kernel(const DecodeArgs a) {
   constexpr int BS = 16;
   constexpr int NCH = D / 32;  // 32-column chunks of q.K per tile
-  constexpr int EPL = D / 16;  // output columns per lane-row in P.V (= PV MFMAs per step)
+  constexpr int EPL = D / 16;  // output columns per lane-row in p.V (= p.V MFMAs per step)
   constexpr int DP = D + 4;    // padded LDS row
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n16 = lane & 15;
   const int kg = lane >> 4;
 
@@ -124,160 +273,65 @@ decode_mfma_kernel(const DecodeArgs a) {
     }
   }
 
-  float m_run = kNegInf;  // running max of head n16 (log2 units), equal across kg
-  float l_run = 0.f;      // this lane's share of the running sum
-  floatx4 acc[EPL];       // O^T: acc[e][i] = out[head n16][EPL*(4kg+i) + e]
+  WaveState<EPL> st;
+  st.m_run = kNegInf;
+  st.l_run = 0.f;
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) acc[e] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int e = 0; e < EPL; ++e) st.acc[e] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  const size_t row_stride = (size_t)Hkv * D;
-  const int32_t* table = a.block_tables + (size_t)b * a.max_blocks;
+  PairCtx<D> ctx;
+  ctx.k_cache = a.k_cache;
+  ctx.v_cache = a.v_cache;
+  ctx.table = a.block_tables + (size_t)b * a.max_blocks;
+  ctx.row_stride = (size_t)Hkv * D;
+  ctx.head_off = (size_t)g * D;
+  ctx.num_blocks = a.num_blocks;
+  ctx.blk0 = blk0;
+  ctx.blk1 = blk1;
+  ctx.tok1 = tok1;
+  ctx.wave = wave;
+  ctx.n16 = n16;
+  ctx.kg = kg;
   const float sl2 = a.scale_log2;
 
-  // This wave's block pairs: (blk0 + 2*(wave + NW*k), +1), k = 0 .. np-1. Ids are fetched
-  // 64 pairs at a time (lane k holds pair k's two ids) and broadcast with readlane.
-  const int nblk = blk1 - blk0;
-  const int npairs = (nblk + 1) / 2;
+  // This wave's block pairs are (blk0 + 2*(wave + NW*k), +1), k = 0 .. np-1. Two pairs are
+  // kept in flight: pair k+1's loads are issued before pair k is computed, and block ids are
+  // read one pair ahead of the loads. Loads are unconditional (past the last pair they
+  // repeat the last pair's addresses, which hit in cache and are never computed), so the
+  // loop has no branches around memory operations and the wait counts stay exact.
+  const int npairs = (blk1 - blk0 + 1) / 2;
   const int np = wave < npairs ? (npairs - wave + NW - 1) / NW : 0;
-  for (int kb = 0; kb < np; kb += 64) {
-    int idA = -1, idB = -1;
-    {
-      const int jA = blk0 + 2 * (wave + NW * (kb + lane));
-      if (kb + lane < np) {
-        idA = table[jA];
-        if (jA + 1 < blk1) idB = table[jA + 1];
-      }
-    }
-    const int kend = min(np - kb, 64);
-    for (int k = 0; k < kend; ++k) {
-      const int jA = blk0 + 2 * (wave + NW * (kb + k));
-      int pA = __builtin_amdgcn_readlane(idA, k);
-      int pB = __builtin_amdgcn_readlane(idB, k);
-      const bool okA = pA >= 0 && (int64_t)pA < a.num_blocks;
-      const bool okB = pB >= 0 && (int64_t)pB < a.num_blocks;
-      // An invalid or absent block is replaced by block 0 (always in the pool) and all of its
-      // tokens are masked below, so its contents never reach the result.
-      const int tA = jA * BS, tB = tA + BS;
-      const int lastA = okA ? min(tok1 - tA, BS) : 0;  // valid rows in each block
-      const int lastB = okB ? min(tok1 - tB, BS) : 0;
-      pA = okA ? pA : 0;
-      pB = okB ? pB : 0;
-
-      const uint16_t* kA = a.k_cache + ((size_t)pA * BS * Hkv + g) * D;
-      const uint16_t* kB = a.k_cache + ((size_t)pB * BS * Hkv + g) * D;
-      const uint16_t* vA = a.v_cache + ((size_t)pA * BS * Hkv + g) * D;
-      const uint16_t* vB = a.v_cache + ((size_t)pB * BS * Hkv + g) * D;
-
-      uint4 ka[NCH], kbv[NCH];
-      VRow<EPL> vr[8];
-#pragma unroll
-      for (int c = 0; c < NCH; ++c) {
-        ka[c] = *reinterpret_cast<const uint4*>(kA + (size_t)n16 * row_stride + 32 * c + 8 * kg);
-        kbv[c] = *reinterpret_cast<const uint4*>(kB + (size_t)n16 * row_stride + 32 * c + 8 * kg);
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        vr[j].load(vA + (size_t)(4 * kg + j) * row_stride + EPL * n16);
-        vr[4 + j].load(vB + (size_t)(4 * kg + j) * row_stride + EPL * n16);
-      }
-
-      floatx4 sA = {0.f, 0.f, 0.f, 0.f}, sB = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int c = 0; c < NCH; ++c) {
-        sA = mfma16x16x32(as_bf16x8(ka[c]), qb[c], sA);
-        sB = mfma16x16x32(as_bf16x8(kbv[c]), qb[c], sB);
-      }
-      float s[8];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        s[i] = sA[i] * sl2;
-        s[4 + i] = sB[i] * sl2;
-      }
-      if (lastA < BS || lastB < BS) {  // a block holds positions at or past the end
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const bool va = 4 * kg + i < lastA;
-          const bool vb = 4 * kg + i < lastB;
-          s[i] = va ? s[i] : kNegInf;
-          s[4 + i] = vb ? s[4 + i] : kNegInf;
-          vr[i].keep_if(va);  // stale rows may hold NaN bits; 0 * NaN would poison P.V
-          vr[4 + i].keep_if(vb);
-        }
-      }
-      float mx = s[0];
-#pragma unroll
-      for (int i = 1; i < 8; ++i) mx = fmaxf(mx, s[i]);
-      mx = fmaxf(mx, shfl_xor(mx, 16));
-      mx = fmaxf(mx, shfl_xor(mx, 32));
-      // Lazy rescaling: the reference max moves only when a score exceeds it by more than
-      // kRescaleSlack (log2 units), so weights stay <= 2^kRescaleSlack and the accumulator is
-      // rescaled on few steps instead of every step. Any reference value gives the same
-      // softmax; the final normalisation divides it out.
-      const float mn = fmaxf(m_run, mx);
-      const bool upd = mn > m_run + kRescaleSlack;  // also true while m_run is -inf
-      if (__any(upd)) {
-        const float m_new = upd ? mn : m_run;
-        const float alpha = upd ? fast_exp2(m_run - (m_new == kNegInf ? 0.f : m_new)) : 1.f;
-        l_run *= alpha;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[e] *= alpha;
-        m_run = m_new;
-      }
-      const float mu = m_run == kNegInf ? 0.f : m_run;
-      float p[8];
-      float psum = 0.f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        p[i] = fast_exp2(s[i] - mu);
-        psum += p[i];
-      }
-      l_run += psum;
-
-      // P^T operand, split into bf16 hi (truncation, exact) + bf16 lo (rounded remainder).
-      uint32_t hw[4], lw[4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const uint32_t u0 = __float_as_uint(p[2 * t]), u1 = __float_as_uint(p[2 * t + 1]);
-        hw[t] = pack_hi(u0, u1);
-        const float r0 = p[2 * t] - __uint_as_float(u0 & 0xffff0000u);
-        const float r1 = p[2 * t + 1] - __uint_as_float(u1 & 0xffff0000u);
-        const __bf16 b0 = (__bf16)r0, b1 = (__bf16)r1;
-        lw[t] = (uint32_t)__builtin_bit_cast(uint16_t, b0) |
-                ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
-      }
-      const bf16x8 phi = as_bf16x8(make_uint4(hw[0], hw[1], hw[2], hw[3]));
-      const bf16x8 plo = as_bf16x8(make_uint4(lw[0], lw[1], lw[2], lw[3]));
-
-      // V^T operand for output column set e: 8 token slots of column EPL*n16 + e.
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) {
-        uint32_t w[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const uint32_t x = vr[2 * t].word(e / 2), y = vr[2 * t + 1].word(e / 2);
-          w[t] = (e & 1) ? pack_hi(x, y) : pack_lo(x, y);
-        }
-        const bf16x8 vt = as_bf16x8(make_uint4(w[0], w[1], w[2], w[3]));
-        acc[e] = mfma16x16x32(vt, phi, acc[e]);
-        acc[e] = mfma16x16x32(vt, plo, acc[e]);
-      }
+  if (np > 0) {
+    PairTile<NCH, EPL> t0, t1;
+    int2 i0 = pair_ids<D, NW>(ctx, 0);
+    int2 i1 = pair_ids<D, NW>(ctx, min(1, np - 1));
+    pair_load<D, NW>(t0, ctx, i0, 0);
+    for (int k = 0; k < np; k += 2) {
+      const int k1 = min(k + 1, np - 1), k2 = min(k + 2, np - 1), k3 = min(k + 3, np - 1);
+      pair_load<D, NW>(t1, ctx, i1, k1);
+      i0 = pair_ids<D, NW>(ctx, k2);
+      pair_compute(t0, st, qb, sl2, kg);
+      pair_load<D, NW>(t0, ctx, i0, k2);
+      i1 = pair_ids<D, NW>(ctx, k3);
+      if (k + 1 < np) pair_compute(t1, st, qb, sl2, kg);
     }
   }
 
   // Sum of the running sums over the four lanes of a head.
+  float l_run = st.l_run;
   l_run += shfl_xor(l_run, 16);
   l_run += shfl_xor(l_run, 32);
 
   __shared__ float sm_m[NW][16], sm_l[NW][16];
   __shared__ float sm_acc[NW][16][DP];
   if (kg == 0) {
-    sm_m[wave][n16] = m_run;
+    sm_m[wave][n16] = st.m_run;
     sm_l[wave][n16] = l_run;
   }
 #pragma unroll
   for (int e = 0; e < EPL; ++e)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sm_acc[wave][n16][EPL * (4 * kg + i) + e] = acc[e][i];
+    for (int i = 0; i < 4; ++i) sm_acc[wave][n16][EPL * (4 * kg + i) + e] = st.acc[e][i];
   __syncthreads();
 
   for (int x = threadIdx.x; x < G * D; x += NW * 64) {
@@ -308,6 +362,132 @@ decode_mfma_kernel(const DecodeArgs a) {
   }
 }
 
+// Variant with one wave per KV head: a workgroup of HPW waves takes HPW KV heads of the same
+// (sequence, partition), so at any time the workgroup reads HPW*D*2 contiguous bytes of each
+// token row of a block instead of D*2, and every wave walks the whole partition on its own
+// (no cross-wave merge). Each wave writes its heads' output, or its partition partial for
+// the merge kernel.
+template <int D, int HPW>
+__global__ void __launch_bounds__(HPW * 64)
+decode_mfma_hw_kernel(const DecodeArgs a) {
+  constexpr int BS = 16;
+  constexpr int NCH = D / 32;
+  constexpr int EPL = D / 16;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n16 = lane & 15;
+  const int kg = lane >> 4;
+
+  const int nparts = a.nparts;
+  const int Hkv = a.num_kv_heads;
+  const int Hq = a.num_q_heads;
+  const int G = Hq / Hkv;
+  const int ngrp = (Hkv + HPW - 1) / HPW;
+  const int unit = blockIdx.x;
+  const int part = unit % nparts;
+  const int hg = (unit / nparts) % ngrp;
+  const int b = unit / (nparts * ngrp);
+  const int g = hg * HPW + wave;
+  if (g >= Hkv) return;  // no barriers below: waves are independent
+
+  int L = a.context_lens[b];
+  const int Lmax = a.max_blocks * BS;
+  L = L < 0 ? 0 : (L > Lmax ? Lmax : L);
+  const int tok0 = part * a.part_tokens;
+  if (tok0 >= L && !(L == 0 && part == 0)) return;
+  const int tok1 = min(tok0 + a.part_tokens, L);
+  const int blk0 = tok0 / BS;
+  const int blk1 = (tok1 + BS - 1) / BS;
+
+  bf16x8 qb[NCH];
+  {
+    const bool hv = n16 < G;
+    const uint16_t* qrow = a.q + ((size_t)b * Hq + (size_t)g * G + (hv ? n16 : 0)) * D + 8 * kg;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      uint4 w = make_uint4(0, 0, 0, 0);
+      if (hv) w = *reinterpret_cast<const uint4*>(qrow + 32 * c);
+      qb[c] = as_bf16x8(w);
+    }
+  }
+
+  WaveState<EPL> st;
+  st.m_run = kNegInf;
+  st.l_run = 0.f;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) st.acc[e] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  PairCtx<D> ctx;
+  ctx.k_cache = a.k_cache;
+  ctx.v_cache = a.v_cache;
+  ctx.table = a.block_tables + (size_t)b * a.max_blocks;
+  ctx.row_stride = (size_t)Hkv * D;
+  ctx.head_off = (size_t)g * D;
+  ctx.num_blocks = a.num_blocks;
+  ctx.blk0 = blk0;
+  ctx.blk1 = blk1;
+  ctx.tok1 = tok1;
+  ctx.wave = 0;
+  ctx.n16 = n16;
+  ctx.kg = kg;
+  const float sl2 = a.scale_log2;
+
+  // Pairs (blk0 + 2k, blk0 + 2k + 1), k = 0 .. np-1, two in flight (see the kernel above).
+  const int np = (blk1 - blk0 + 1) / 2;
+  if (np > 0) {
+    PairTile<NCH, EPL> t0, t1;
+    int2 i0 = pair_ids<D, 1>(ctx, 0);
+    int2 i1 = pair_ids<D, 1>(ctx, min(1, np - 1));
+    pair_load<D, 1>(t0, ctx, i0, 0);
+    for (int k = 0; k < np; k += 2) {
+      const int k1 = min(k + 1, np - 1), k2 = min(k + 2, np - 1), k3 = min(k + 3, np - 1);
+      pair_load<D, 1>(t1, ctx, i1, k1);
+      i0 = pair_ids<D, 1>(ctx, k2);
+      pair_compute(t0, st, qb, sl2, kg);
+      pair_load<D, 1>(t0, ctx, i0, k2);
+      i1 = pair_ids<D, 1>(ctx, k3);
+      if (k + 1 < np) pair_compute(t1, st, qb, sl2, kg);
+    }
+  }
+
+  float l_run = st.l_run;
+  l_run += shfl_xor(l_run, 16);
+  l_run += shfl_xor(l_run, 32);
+  const bool hv = n16 < G;
+  const size_t row0 = (size_t)b * Hq + (size_t)g * G;  // first query head of KV head g
+  if (nparts == 1) {
+    if (hv) {
+      const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+      float* o = a.out + (row0 + n16) * D;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int e = 0; e < EPL; e += 4)
+          *reinterpret_cast<float4*>(o + EPL * (4 * kg + i) + e) =
+              make_float4(st.acc[e][i] * inv, st.acc[e + 1][i] * inv, st.acc[e + 2][i] * inv,
+                          st.acc[e + 3][i] * inv);
+    }
+    return;
+  }
+  // Split: leave this partition's partial (unnormalised output, reference max, sum) for the
+  // merge kernel.
+  if (hv) {
+    const size_t pr = (row0 + n16) * nparts + part;
+    float* o = a.ws_acc + pr * D;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < EPL; e += 4)
+        *reinterpret_cast<float4*>(o + EPL * (4 * kg + i) + e) =
+            make_float4(st.acc[e][i], st.acc[e + 1][i], st.acc[e + 2][i], st.acc[e + 3][i]);
+    if (kg == 0) {
+      a.ws_ml[pr * 2 + 0] = st.m_run;
+      a.ws_ml[pr * 2 + 1] = l_run;
+    }
+  }
+}
+
 bool supported_mfma(int head_dim, int group, int block_size) {
   return block_size == 16 && (head_dim == 64 || head_dim == 128) && group >= 1 && group <= 16;
 }
@@ -321,6 +501,21 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream) {
   else if (a.head_dim == 64)
     hipLaunchKernelGGL((decode_mfma_kernel<64, NW>), dim3((unsigned)units), dim3(NW * 64), 0,
                        stream, a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_mfma_hw(const DecodeArgs& a, hipStream_t stream) {
+  constexpr int HPW = kHeadsPerGroup;
+  const long long ngrp = (a.num_kv_heads + HPW - 1) / HPW;
+  const long long units = (long long)a.batch * ngrp * a.nparts;
+  if (a.head_dim == 128)
+    hipLaunchKernelGGL((decode_mfma_hw_kernel<128, HPW>), dim3((unsigned)units), dim3(HPW * 64),
+                       0, stream, a);
+  else if (a.head_dim == 64)
+    hipLaunchKernelGGL((decode_mfma_hw_kernel<64, HPW>), dim3((unsigned)units), dim3(HPW * 64),
+                       0, stream, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

@@ -32,6 +32,8 @@ hipError_t launch_decode_valu(const DecodeArgs& a, hipStream_t stream);
 
 bool supported_mfma(int head_dim, int group, int block_size);
 hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream);
+// One wave per KV head, kHeadsPerGroup heads of a (sequence, partition) per workgroup.
+hipError_t launch_decode_mfma_hw(const DecodeArgs& a, hipStream_t stream);
 
 hipError_t launch_decode_reduce(const DecodeArgs& a, hipStream_t stream);
 
@@ -42,6 +44,11 @@ hipError_t launch_kv_write(const uint16_t* k, const uint16_t* v, const int64_t* 
 // Waves per workgroup of the decode kernels; partitions are multiples of
 // kWavesPerGroup * block_size tokens when split automatically.
 constexpr int kWavesPerGroup = 4;
+// KV heads (one wave each) per workgroup of the head-per-wave MFMA kernel.
+#ifndef PAGEDKV_HEADS_PER_GROUP
+#define PAGEDKV_HEADS_PER_GROUP 4
+#endif
+constexpr int kHeadsPerGroup = PAGEDKV_HEADS_PER_GROUP;
 
 // log2(e), to turn natural-log scores into log2 units for v_exp_f32.
 constexpr float kLog2eHost = 1.4426950408889634f;

@@ -43,7 +43,7 @@ def _write_summary():
 
 def kernels_for(w):
     out = []
-    for k in ("valu", "mfma"):
+    for k in ("valu", "mfma", "mfma_hw"):
         try:
             pk.decode_plan(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.max_blocks,
                            w.block_size, 0, k)
@@ -297,3 +297,33 @@ def test_empty_batch_is_noop(dev):
     pk.paged_decode_attention(d["q"][:0], d["k_cache"], d["v_cache"], d["block_tables"][:0],
                               d["context_lens"][:0], d["scale"], out)
     torch.cuda.synchronize()
+
+
+def test_one_workspace_across_shapes(dev):
+    """One workspace reused by split calls of different batch sizes and partition counts
+    (its contents are scratch: nothing carries over from call to call)."""
+    w4, w5 = wl.WORKLOADS["c4"], wl.WORKLOADS["c5b"]
+    _, ref4, _, _, d4 = case("c4", dev)
+    need = max(pk.decode_workspace_bytes(w.batch, w.num_q_heads, w.head_dim, w.max_blocks,
+                                         w.block_size, 16) for w in (w4, w5))
+    ws = pk.new_workspace(need, dev)
+    ws.fill_(0x7F)  # garbage
+    d5 = wl.make_inputs(w5, device="cuda")
+    run_write(d5)
+    for kernel in kernels_for(w5):
+        base5 = run_attention(d5, kernel, -1)
+        for partition in (16, 256, 0, 48, 1024):
+            for d, ref in ((d4, ref4), (d5, None)):
+                w = d["workload"]
+                out = torch.full((w.batch, w.num_q_heads, w.head_dim), float("nan"), device=dev)
+                pk.paged_decode_attention(d["q"], d["k_cache"], d["v_cache"], d["block_tables"],
+                                          d["context_lens"], d["scale"], out,
+                                          partition_tokens=partition, kernel=kernel,
+                                          workspace=ws)
+                if ref is not None:
+                    err = np.abs(out.cpu().double().numpy() - ref).max()
+                    assert err <= ATOL, (kernel, partition, err)
+                else:
+                    diff = (out - base5).abs().max().item()
+                    record(f"c5b/{kernel}/p{partition}/vs_unsplit", diff)
+                    assert diff <= 1e-4, (kernel, partition, diff)
