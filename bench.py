@@ -46,6 +46,13 @@ def parse_args():
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="CPU work budget of the oracle baseline sample")
     p.add_argument("--json-out", default=None)
+    p.add_argument("--flush-mib", type=int, default=0,
+                   help="before every step, read a buffer of this many MiB so no input stays "
+                        "in the 256 MB last-level cache (cold-cache timing; the read is inside "
+                        "the measured step time, the kernel times exclude it)")
+    p.add_argument("--copy-calibration-mib", type=int, default=0,
+                   help="run one plain device-to-device copy of this many MiB before the "
+                        "steps (reference dispatch for hardware byte counters)")
     return p.parse_args()
 
 
@@ -170,7 +177,14 @@ def main():
         subs.append(d)
     torch.cuda.synchronize()
 
+    # Eviction by reading only: a written buffer would leave dirty lines whose write-back
+    # would then compete with the measured kernel.
+    flush = (torch.zeros((args.flush_mib << 20) // 4, dtype=torch.float32, device=dev)
+             if args.flush_mib > 0 else None)
+
     def step(events=None):
+        if flush is not None:
+            torch.sum(flush)
         for i, d in enumerate(subs):
             pk.paged_kv_write(d["k_new"], d["v_new"], d["slot_mapping"], d["k_cache"],
                               d["v_cache"])
@@ -179,6 +193,16 @@ def main():
                                       partition_tokens=args.partition, kernel=args.kernel,
                                       workspace=d["ws"],
                                       events=events[i] if events is not None else None)
+
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     for _ in range(args.warmup):
         step()

@@ -391,15 +391,15 @@ decode_mfma_hw_kernel(const DecodeArgs a) {
   const int g = hg * HPW + wave;
   if (g >= Hkv) return;  // no barriers below: waves are independent
 
-  int L = a.context_lens[b];
-  const int Lmax = a.max_blocks * BS;
-  L = L < 0 ? 0 : (L > Lmax ? Lmax : L);
+  // Loads that do not depend on the context length are issued before it arrives, so a
+  // wave's start costs two dependent round trips (length and ids together, then K/V)
+  // instead of three: q, and the first pair's block ids (every entry of the table row is in
+  // bounds to read; entries past the context are ignored below).
+  const int32_t* table = a.block_tables + (size_t)b * a.max_blocks;
   const int tok0 = part * a.part_tokens;
-  if (tok0 >= L && !(L == 0 && part == 0)) return;
-  const int tok1 = min(tok0 + a.part_tokens, L);
   const int blk0 = tok0 / BS;
-  const int blk1 = (tok1 + BS - 1) / BS;
-
+  const int idA0 = blk0 < a.max_blocks ? table[blk0] : -1;
+  const int idB0 = blk0 + 1 < a.max_blocks ? table[blk0 + 1] : -1;
   bf16x8 qb[NCH];
   {
     const bool hv = n16 < G;
@@ -412,6 +412,13 @@ decode_mfma_hw_kernel(const DecodeArgs a) {
     }
   }
 
+  int L = a.context_lens[b];
+  const int Lmax = a.max_blocks * BS;
+  L = L < 0 ? 0 : (L > Lmax ? Lmax : L);
+  if (tok0 >= L && !(L == 0 && part == 0)) return;
+  const int tok1 = min(tok0 + a.part_tokens, L);
+  const int blk1 = (tok1 + BS - 1) / BS;
+
   WaveState<EPL> st;
   st.m_run = kNegInf;
   st.l_run = 0.f;
@@ -421,7 +428,7 @@ decode_mfma_hw_kernel(const DecodeArgs a) {
   PairCtx<D> ctx;
   ctx.k_cache = a.k_cache;
   ctx.v_cache = a.v_cache;
-  ctx.table = a.block_tables + (size_t)b * a.max_blocks;
+  ctx.table = table;
   ctx.row_stride = (size_t)Hkv * D;
   ctx.head_off = (size_t)g * D;
   ctx.num_blocks = a.num_blocks;
@@ -437,7 +444,7 @@ decode_mfma_hw_kernel(const DecodeArgs a) {
   const int np = (blk1 - blk0 + 1) / 2;
   if (np > 0) {
     PairTile<NCH, EPL> t0, t1;
-    int2 i0 = pair_ids<D, 1>(ctx, 0);
+    int2 i0 = make_int2(idA0, blk0 + 1 < blk1 ? idB0 : -1);
     int2 i1 = pair_ids<D, 1>(ctx, min(1, np - 1));
     pair_load<D, 1>(t0, ctx, i0, 0);
     for (int k = 0; k < np; k += 2) {
