@@ -56,9 +56,13 @@ int cu_count(int* out) {
 // spend more on the per-partition set-up and merge than they gain in parallelism.
 constexpr int64_t kMinAutoPartition = 256;
 // Work the automatic choice aims for, per compute unit: workgroups of the kernels that split
-// a partition over a workgroup's waves, waves of the kernel with one wave per KV head.
+// a partition over a workgroup's waves; waves of the kernel with one wave per KV head (two
+// per SIMD, one full residency round). With few (sequence, KV head) units, i.e. few long
+// contexts, that kernel aims for one wave per SIMD instead: fewer, longer partitions, which
+// measured faster there (less per-wave start-up, a smaller merge).
 constexpr int64_t kTargetGroupsPerCU = 4;
 constexpr int64_t kTargetHeadWavesPerCU = 8;
+constexpr int64_t kTargetHeadWavesPerCUFewUnits = 4;
 // Contexts longer than this many tokens use the one-wave-per-KV-head kernel by default;
 // shorter ones spread each partition over a workgroup's waves for lower latency.
 constexpr int64_t kHeadWaveMinContext = 1024;
@@ -90,8 +94,9 @@ int make_plan(int32_t batch, int32_t num_kv_heads, int32_t max_blocks, int32_t b
     n = ceil_div(max_len, P);
   } else {
     const int64_t units = (int64_t)batch * num_kv_heads;
-    const int64_t target =
-        (kernel == PAGEDKV_KERNEL_MFMA_HEADWAVE ? kTargetHeadWavesPerCU : kTargetGroupsPerCU) * cus;
+    int64_t target = kTargetGroupsPerCU * cus;
+    if (kernel == PAGEDKV_KERNEL_MFMA_HEADWAVE)
+      target = (units * 4 <= cus ? kTargetHeadWavesPerCUFewUnits : kTargetHeadWavesPerCU) * cus;
     const int64_t nmax = ceil_div(max_len, kMinAutoPartition);
     n = units > 0 ? ceil_div(target, units) : 1;
     if (n > nmax) n = nmax;

@@ -367,8 +367,8 @@ decode_mfma_kernel(const DecodeArgs a) {
 // token row of a block instead of D*2, and every wave walks the whole partition on its own
 // (no cross-wave merge). Each wave writes its heads' output, or its partition partial for
 // the merge kernel.
-template <int D, int HPW>
-__global__ void __launch_bounds__(HPW * 64)
+template <int D, int HPW, int NBUF, int MINW>
+__global__ void __launch_bounds__(HPW * 64, MINW)
 decode_mfma_hw_kernel(const DecodeArgs a) {
   constexpr int BS = 16;
   constexpr int NCH = D / 32;
@@ -440,21 +440,31 @@ decode_mfma_hw_kernel(const DecodeArgs a) {
   ctx.kg = kg;
   const float sl2 = a.scale_log2;
 
-  // Pairs (blk0 + 2k, blk0 + 2k + 1), k = 0 .. np-1, two in flight (see the kernel above).
+  // Pairs (blk0 + 2k, blk0 + 2k + 1), k = 0 .. np-1, NBUF pairs in flight. Pair j lives in
+  // register buffer j % NBUF; the loop is unrolled NBUF times so every buffer index is static.
+  // At the step that computes pair j, pair j+NBUF-1 is loaded into the buffer pair j-1 just
+  // left, with block ids read one pair ahead of their loads. Past the last pair the loads
+  // repeat the last pair's addresses (cache hits, never computed), so no memory operation sits
+  // behind a branch and the wait counts stay exact.
   const int np = (blk1 - blk0 + 1) / 2;
   if (np > 0) {
-    PairTile<NCH, EPL> t0, t1;
-    int2 i0 = make_int2(idA0, blk0 + 1 < blk1 ? idB0 : -1);
-    int2 i1 = pair_ids<D, 1>(ctx, min(1, np - 1));
-    pair_load<D, 1>(t0, ctx, i0, 0);
-    for (int k = 0; k < np; k += 2) {
-      const int k1 = min(k + 1, np - 1), k2 = min(k + 2, np - 1), k3 = min(k + 3, np - 1);
-      pair_load<D, 1>(t1, ctx, i1, k1);
-      i0 = pair_ids<D, 1>(ctx, k2);
-      pair_compute(t0, st, qb, sl2, kg);
-      pair_load<D, 1>(t0, ctx, i0, k2);
-      i1 = pair_ids<D, 1>(ctx, k3);
-      if (k + 1 < np) pair_compute(t1, st, qb, sl2, kg);
+    PairTile<NCH, EPL> t[NBUF];
+    int2 ids[NBUF];
+    ids[0] = make_int2(idA0, blk0 + 1 < blk1 ? idB0 : -1);
+#pragma unroll
+    for (int u = 1; u < NBUF; ++u) ids[u] = pair_ids<D, 1>(ctx, min(u, np - 1));
+#pragma unroll
+    for (int u = 0; u < NBUF - 1; ++u) pair_load<D, 1>(t[u], ctx, ids[u], min(u, np - 1));
+    for (int k = 0; k < np; k += NBUF) {
+#pragma unroll
+      for (int u = 0; u < NBUF; ++u) {
+        const int j = k + u;
+        const int jl = min(j + NBUF - 1, np - 1);
+        const int ub = (u + NBUF - 1) % NBUF;
+        pair_load<D, 1>(t[ub], ctx, ids[ub], jl);
+        ids[u] = pair_ids<D, 1>(ctx, min(jl + 1, np - 1));
+        if (j < np) pair_compute(t[u], st, qb, sl2, kg);
+      }
     }
   }
 
@@ -515,14 +525,17 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream) {
 
 hipError_t launch_decode_mfma_hw(const DecodeArgs& a, hipStream_t stream) {
   constexpr int HPW = kHeadsPerGroup;
+  // Two block pairs in flight per wave: measured as fast as four (which needs occupancy 1)
+  // on every workload, and it keeps two waves per SIMD.
+  constexpr int NBUF = 2;
   const long long ngrp = (a.num_kv_heads + HPW - 1) / HPW;
   const long long units = (long long)a.batch * ngrp * a.nparts;
   if (a.head_dim == 128)
-    hipLaunchKernelGGL((decode_mfma_hw_kernel<128, HPW>), dim3((unsigned)units), dim3(HPW * 64),
-                       0, stream, a);
+    hipLaunchKernelGGL((decode_mfma_hw_kernel<128, HPW, NBUF, 2>), dim3((unsigned)units),
+                       dim3(HPW * 64), 0, stream, a);
   else if (a.head_dim == 64)
-    hipLaunchKernelGGL((decode_mfma_hw_kernel<64, HPW>), dim3((unsigned)units), dim3(HPW * 64),
-                       0, stream, a);
+    hipLaunchKernelGGL((decode_mfma_hw_kernel<64, HPW, NBUF, 2>), dim3((unsigned)units),
+                       dim3(HPW * 64), 0, stream, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
