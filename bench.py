@@ -46,6 +46,9 @@ def parse_args():
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="CPU work budget of the oracle baseline sample")
     p.add_argument("--json-out", default=None)
+    p.add_argument("--graph", action="store_true",
+                   help="also capture one step in a HIP graph and time K replays "
+                        "(reported as graph_ms_per_step)")
     p.add_argument("--flush-mib", type=int, default=0,
                    help="before every step, read a buffer of this many MiB so no input stays "
                         "in the 256 MB last-level cache (cold-cache timing; the read is inside "
@@ -237,6 +240,26 @@ def main():
         })
     hip.close()
 
+    graph_ms = None
+    if args.graph:
+        side = torch.cuda.Stream(device=dev)
+        side.wait_stream(torch.cuda.current_stream(dev))
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream(dev).wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        g0 = time.perf_counter()
+        for _ in range(args.steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        graph_ms = (time.perf_counter() - g0) * 1e3 / args.steps
+
     step_bytes = sum(d["bytes"]["attention"] + d["bytes"]["write"] for d in subs)
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     launch_bytes = sum(d["bytes"]["attention"] for d in subs) / len(subs)
@@ -284,6 +307,8 @@ def main():
         },
         "details": per,
     }
+    if graph_ms is not None:
+        line["graph_ms_per_step"] = round(graph_ms, 4)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(subs[0], args.cpu_seconds)
     out = json.dumps(line)

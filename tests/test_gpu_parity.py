@@ -327,3 +327,47 @@ def test_one_workspace_across_shapes(dev):
                     diff = (out - base5).abs().max().item()
                     record(f"c5b/{kernel}/p{partition}/vs_unsplit", diff)
                     assert diff <= 1e-4, (kernel, partition, diff)
+
+
+@pytest.mark.parametrize("name,partition", [("c2", 0), ("c4", 64)])
+def test_graph_capture_replays_match_eager(dev, name, partition):
+    """The write + attention step captured in a HIP graph (no allocation, no memset inside the
+    library calls) replays to the eager result, replay after replay, with eager work and
+    synchronisations in between."""
+    w = wl.WORKLOADS[name]
+    inp = wl.make_inputs(w)
+    d = to_dev(inp, dev)
+    out = torch.empty(w.batch, w.num_q_heads, w.head_dim, dtype=torch.float32, device=dev)
+    ws = pk.new_workspace(pk.decode_workspace_bytes(w.batch, w.num_q_heads, w.head_dim,
+                                                    w.max_blocks, w.block_size, partition), dev)
+
+    def step():
+        pk.paged_kv_write(d["k_new"], d["v_new"], d["slot_mapping"], d["k_cache"], d["v_cache"])
+        pk.paged_decode_attention(d["q"], d["k_cache"], d["v_cache"], d["block_tables"],
+                                  d["context_lens"], d["scale"], out,
+                                  partition_tokens=partition, workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    eager = out.clone()
+    _, ref, kc_ref, vc_ref, _ = case(name, dev)
+    assert np.abs(eager.cpu().double().numpy() - ref).max() <= ATOL
+
+    side = torch.cuda.Stream(device=dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream(dev).wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for r in range(4):
+        out.fill_(float("nan"))
+        d["k_cache"].view(torch.int16)[0, 0, 0, 0] += 0  # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {r}"
+    assert np.array_equal(wl.to_bits(d["k_cache"]), kc_ref)
+    assert np.array_equal(wl.to_bits(d["v_cache"]), vc_ref)
