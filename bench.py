@@ -91,7 +91,7 @@ class HipEvents:
 
 def kernel_source_hash(kernel: str) -> str:
     csrc = os.path.join(HERE, "paged_kv_decode_write_amd", "csrc")
-    files = ["device_common.h", "launch.h", "decode_%s.hip" % kernel.split("_")[0]]
+    files = ["device_common.h", "launch.h", "mfma_tiles.h", "decode_%s.hip" % kernel.split("_")[0]]
     h = hashlib.sha256()
     for f in files:
         with open(os.path.join(csrc, f), "rb") as fh:
@@ -148,6 +148,63 @@ def cpu_baseline(d, seconds):
                       f"{spent:.1f} s"}
 
 
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix throughput, vendor figure
+
+
+def bench_prefill(args, torch, pk, wl):
+    """Multi-query causal workloads: step = write the chunk's K/V + causal attention."""
+    dev = torch.device("cuda:0")
+    w = wl.PREFILL_WORKLOADS[args.workload]
+    d = wl.make_prefill_inputs(w, device="cuda")
+    T, Hq, D = d["q"].shape
+    out = torch.empty(T, Hq, D, dtype=torch.float32, device=dev)
+    alg = wl.prefill_algorithmic(w)
+    write_bytes = T * w.num_kv_heads * w.head_dim * 2 * 2 * 2
+
+    def step(ev=None):
+        pk.paged_kv_write(d["k_new"], d["v_new"], d["slot_mapping"], d["k_cache"], d["v_cache"])
+        if ev is not None:
+            ev[0].record()
+        pk.paged_prefill_attention(d["q"], d["cu_seqlens_q"], d["k_cache"], d["v_cache"],
+                                   d["block_tables"], d["context_lens"], d["scale"], out,
+                                   max_q_len=d["max_q_len"])
+        if ev is not None:
+            ev[1].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    durs = sorted(a.elapsed_time(b) for a, b in evs)
+    mean = sum(durs) / len(durs)
+    tflops = alg["flops"] / (mean * 1e-3) / 1e12
+    line = {
+        "metric": "paged multi-query causal attention us/call and achieved TFLOP/s",
+        "value": round(alg["flops"] / (ms_per_step * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16), resident in HBM",
+        "config": {"workload": w.description, "kernel": "prefill_mfma",
+                   "us_per_call": round(mean * 1e3, 2),
+                   "GBps": round(alg["bytes"] / (mean * 1e-3) / 1e9, 1),
+                   "step": "KV write of the chunk + multi-query causal attention"},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None},
+        "details": {"flops": alg["flops"], "bytes": alg["bytes"], "write_bytes": write_bytes,
+                    "attn_us_median": round(durs[len(durs) // 2] * 1e3, 2)},
+    }
+    return line
+
+
 def main():
     args = parse_args()
     if args.gpus != 1:
@@ -164,6 +221,14 @@ def main():
 
     pk.load_library()
     dev = torch.device("cuda:0")
+    if args.workload in wl.PREFILL_WORKLOADS:
+        line = bench_prefill(args, torch, pk, wl)
+        out = json.dumps(line)
+        print(out, flush=True)
+        if args.json_out:
+            with open(args.json_out, "w") as f:
+                f.write(out + "\n")
+        return
     names = ["c5a", "c5b"] if args.workload == "c5" else [args.workload]
     subs = []
     for name in names:

@@ -179,6 +179,34 @@ int paged_decode_plan(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                       int32_t partition_tokens, int32_t kernel, int32_t* num_partitions,
                       int32_t* tokens_per_partition, int32_t* chosen_kernel);
 
+/*
+ * paged_prefill_attention -- multi-query causal attention over the paged cache: prefill,
+ * chunked prefill and recompute (the Llama engine's causal prefill / recomputation,
+ * "vLLM-Style Llama Inference Engine with Tensor Parallelism", Features and scope /
+ * Implemented; the ragged attention without padding, gathering by block table, planned in
+ * llm-stack's Roadmap).
+ *
+ *   Sequence b owns query rows cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 (Q_b rows), which are
+ *   its last Q_b logical positions: row i sits at position p = context_lens[b] - Q_b + i and
+ *   out[row][h][:] = sum_{t<=p} softmax_t(scale * q[row][h] . K_b[t][g]) V_b[t][g], g = h/G.
+ *   The rows' own keys must already be in the cache (write them with paged_kv_write first).
+ *
+ *   q              bf16 [num_tokens][num_q_heads][head_dim], the sequences' rows back to back
+ *   cu_seqlens_q   int32 [batch+1], 0 = cu[0] <= cu[1] <= ... <= cu[batch] = num_tokens
+ *   max_q_len      >= max_b Q_b (sizes the grid on the host without reading cu_seqlens_q)
+ *   k_cache, v_cache, block_tables, context_lens, scale: as in paged_decode_attention;
+ *                  Q_b <= context_lens[b] (rows whose position would be negative get 0)
+ *   out            fp32 [num_tokens][num_q_heads][head_dim] (written)
+ * Supported: head_dim in {64, 128}; block_size 16; num_q_heads / num_kv_heads in 1..16.
+ * Needs no workspace. Asynchronous on `stream`; status codes as above.
+ */
+int paged_prefill_attention(const uint16_t* q, const int32_t* cu_seqlens_q, int64_t num_tokens,
+                            int32_t max_q_len, const uint16_t* k_cache, const uint16_t* v_cache,
+                            const int32_t* block_tables, int32_t max_blocks_per_seq,
+                            const int32_t* context_lens, int32_t batch, int32_t num_q_heads,
+                            int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                            int64_t num_blocks, float scale, float* out, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -4,9 +4,10 @@ Test infrastructure only: imported by the tests, the smoke check and the benchma
 baseline leg, never by the HIP product path.
 """
 from .oracle import (bf16_bits_to_f64, kv_write, kv_head_for, gather_dense, attend_one,
-                     effective_scale, decode_attention, decode_step, partial_stats,
+                     effective_scale, decode_attention, decode_step, prefill_attention,
+                     partial_stats,
                      merge_partials, split_attend_one)
 
 __all__ = ["bf16_bits_to_f64", "kv_write", "kv_head_for", "gather_dense", "attend_one",
-           "effective_scale", "decode_attention", "decode_step", "partial_stats",
+           "effective_scale", "decode_attention", "decode_step", "prefill_attention", "partial_stats",
            "merge_partials", "split_attend_one"]

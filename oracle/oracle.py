@@ -146,6 +146,59 @@ def decode_attention(q_bits: np.ndarray, k_cache_bits: np.ndarray, v_cache_bits:
     return out
 
 
+def prefill_attention(q_bits: np.ndarray, cu_seqlens_q: np.ndarray, k_cache_bits: np.ndarray,
+                      v_cache_bits: np.ndarray, block_tables: np.ndarray,
+                      context_lens: np.ndarray, scale: float,
+                      rows: Optional[Iterable[Tuple[int, int]]] = None) -> np.ndarray:
+    """Float64 output [T, Hq, D] of multi-query causal attention over the paged cache.
+
+    Sequence b owns query rows cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 (Q_b of them), which are
+    its last Q_b logical positions: query i sits at position p = L_b - Q_b + i and attends to
+    positions 0..p (causal). Q_b = L_b is a full prefill or recompute; Q_b < L_b is a chunk
+    appended to a cached prefix; Q_b = 1 is the decode case. This is the causal SDPA the
+    Llama engine uses for prefill and recomputation ("vLLM-Style Llama Inference Engine with
+    Tensor Parallelism", Features and scope / Implemented, How it works step 4) with keys
+    gathered through the block table, the ragged attention over block tables that llm-stack's
+    Roadmap plans. Its keys must already be in the cache (write them first). With ``rows``
+    (an iterable of (query row, head) pairs) only those outputs are computed.
+    """
+    T, Hq, D = q_bits.shape
+    B = len(context_lens)
+    Hkv = k_cache_bits.shape[2]
+    if Hq % Hkv:
+        raise ValueError("query heads must be a multiple of KV heads")
+    cu = np.asarray(cu_seqlens_q, dtype=np.int64)
+    if len(cu) != B + 1 or cu[0] != 0 or cu[-1] != T or np.any(np.diff(cu) < 0):
+        raise ValueError("cu_seqlens_q must be [B+1] non-decreasing offsets from 0 to T")
+    scale_eff = effective_scale(scale)
+    out = np.zeros((T, Hq, D), dtype=np.float64)
+    wanted = None
+    if rows is not None:
+        wanted = {}
+        for r, h in rows:
+            wanted.setdefault(int(r), []).append(int(h))
+    for b in range(B):
+        L = int(context_lens[b])
+        Q = int(cu[b + 1] - cu[b])
+        if Q == 0:
+            continue
+        if Q > L:
+            raise ValueError(f"sequence {b}: {Q} queries but only {L} cached positions")
+        if wanted is not None and not any(cu[b] <= r < cu[b + 1] for r in wanted):
+            continue
+        K = gather_dense(k_cache_bits, block_tables[b], L)
+        V = gather_dense(v_cache_bits, block_tables[b], L)
+        qd = bf16_bits_to_f64(q_bits[cu[b]:cu[b + 1]])
+        for i in range(Q):
+            p = L - Q + i
+            heads = range(Hq) if wanted is None else wanted.get(int(cu[b]) + i, [])
+            for h in heads:
+                g = kv_head_for(h, Hq, Hkv)
+                out[cu[b] + i, h] = attend_one(qd[i, h], K[:p + 1, g, :], V[:p + 1, g, :],
+                                               scale_eff)
+    return out
+
+
 def decode_step(inp: dict, rows=None) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
     """Write the step's new tokens, then attend over the updated pools (the decode step
     writes position L_b - 1 first and then reads positions 0..L_b-1).

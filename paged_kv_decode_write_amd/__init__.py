@@ -5,8 +5,10 @@ The compute runs in hand-written HIP kernels behind a C ABI (``libpagedkv.so``, 
 tensors into pointers and the current stream, and nothing else. The library is loaded on
 first use; if it is missing the call raises, there is no fallback.
 """
-from ._binding import (paged_kv_write, paged_decode_attention, decode_workspace_bytes, decode_plan,
+from ._binding import (paged_kv_write, paged_decode_attention, paged_prefill_attention,
+                       decode_workspace_bytes, decode_plan,
                        library_path, load_library, abi_version, PagedKVError)
 
-__all__ = ["paged_kv_write", "paged_decode_attention", "decode_workspace_bytes", "decode_plan",
+__all__ = ["paged_kv_write", "paged_decode_attention", "paged_prefill_attention",
+           "decode_workspace_bytes", "decode_plan",
            "library_path", "load_library", "abi_version", "PagedKVError"]

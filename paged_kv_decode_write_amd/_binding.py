@@ -67,6 +67,9 @@ def load_library() -> ctypes.CDLL:
         lib.paged_decode_attention.argtypes = attn + [P]
         lib.paged_decode_attention_ex.restype = ctypes.c_int
         lib.paged_decode_attention_ex.argtypes = attn + [I32, P, P, P]
+        lib.paged_prefill_attention.restype = ctypes.c_int
+        lib.paged_prefill_attention.argtypes = [P, P, I64, I32, P, P, P, I32, P, I32, I32, I32,
+                                                I32, I32, I64, F32, P, P]
         lib.paged_decode_plan.restype = ctypes.c_int
         lib.paged_decode_plan.argtypes = [I32, I32, I32, I32, I32, I32, I32, I32,
                                           ctypes.POINTER(I32), ctypes.POINTER(I32),
@@ -218,4 +221,42 @@ def paged_decode_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
             context_lens.data_ptr(), B, Hq, Hkv, D, bs, NB, float(scale), out.data_ptr(),
             workspace.data_ptr() if need else None, ws_bytes if need else 0,
             partition_tokens, KERNELS[kernel], ev_b, ev_e, _stream_handle(dev)))
+    return out
+
+
+def paged_prefill_attention(q: torch.Tensor, cu_seqlens_q: torch.Tensor, k_cache: torch.Tensor,
+                            v_cache: torch.Tensor, block_tables: torch.Tensor,
+                            context_lens: torch.Tensor, scale: float, out: torch.Tensor, *,
+                            max_q_len: Optional[int] = None) -> torch.Tensor:
+    """Multi-query causal attention over the paged cache (prefill / chunked prefill).
+
+    Sequence b's query rows are q[cu_seqlens_q[b]:cu_seqlens_q[b+1]], its last Q_b positions;
+    row i attends to positions 0 .. context_lens[b] - Q_b + i. q [T, Hq, D] bf16, cu_seqlens_q
+    [B+1] int32, out [T, Hq, D] fp32. max_q_len (the largest Q_b) sizes the launch; when
+    omitted it is read from cu_seqlens_q, which synchronises with the device.
+    """
+    _require(k_cache, "k_cache", torch.bfloat16, 4)
+    dev = k_cache.device
+    _require(v_cache, "v_cache", torch.bfloat16, 4, dev)
+    _require(q, "q", torch.bfloat16, 3, dev)
+    _require(cu_seqlens_q, "cu_seqlens_q", torch.int32, 1, dev)
+    _require(block_tables, "block_tables", torch.int32, 2, dev)
+    _require(context_lens, "context_lens", torch.int32, 1, dev)
+    _require(out, "out", torch.float32, 3, dev)
+    NB, bs, Hkv, D = k_cache.shape
+    T, Hq, Dq = q.shape
+    B = context_lens.shape[0]
+    if v_cache.shape != k_cache.shape or Dq != D or out.shape != q.shape:
+        raise ValueError("shape mismatch between q, out and the caches")
+    if cu_seqlens_q.shape != (B + 1,) or block_tables.shape[0] != B:
+        raise ValueError("cu_seqlens_q must be [B+1] and block_tables [B, MB]")
+    if max_q_len is None:
+        max_q_len = int((cu_seqlens_q[1:] - cu_seqlens_q[:-1]).max().item()) if B else 0
+    lib = load_library()
+    with torch.cuda.device(dev):
+        _check(lib.paged_prefill_attention(
+            q.data_ptr(), cu_seqlens_q.data_ptr(), T, int(max_q_len), k_cache.data_ptr(),
+            v_cache.data_ptr(), block_tables.data_ptr(), block_tables.shape[1],
+            context_lens.data_ptr(), B, Hq, Hkv, D, bs, NB, float(scale), out.data_ptr(),
+            _stream_handle(dev)))
     return out

@@ -21,7 +21,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(HERE, "libpagedkv.so")
 
-SOURCES = ["api.cpp", "kv_write.hip", "decode_valu.hip", "decode_mfma.hip", "decode_reduce.hip"]
+SOURCES = ["api.cpp", "kv_write.hip", "decode_valu.hip", "decode_mfma.hip", "decode_reduce.hip",
+           "prefill_mfma.hip"]
 ARCH = os.environ.get("PAGEDKV_ARCH", "gfx950")
 
 

@@ -365,4 +365,56 @@ int paged_decode_attention(const uint16_t* q, const uint16_t* k_cache,
                                    nullptr, nullptr, stream);
 }
 
+int paged_prefill_attention(const uint16_t* q, const int32_t* cu_seqlens_q, int64_t num_tokens,
+                            int32_t max_q_len, const uint16_t* k_cache, const uint16_t* v_cache,
+                            const int32_t* block_tables, int32_t max_blocks_per_seq,
+                            const int32_t* context_lens, int32_t batch, int32_t num_q_heads,
+                            int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                            int64_t num_blocks, float scale, float* out, hipStream_t stream) {
+  g_last_error.clear();
+  int st = check_decode_sizes(max_blocks_per_seq, batch, num_q_heads, num_kv_heads, head_dim,
+                              block_size, num_blocks);
+  if (st) return st;
+  if (num_tokens < 0 || max_q_len < 0)
+    return fail(PAGEDKV_ERR_SHAPE, "num_tokens and max_q_len must be >= 0");
+  if (num_tokens > INT32_MAX) return fail(PAGEDKV_ERR_SHAPE, "num_tokens exceeds int32");
+  const int G = num_q_heads / num_kv_heads;
+  if (!supported_prefill(head_dim, G, block_size))
+    return fail(PAGEDKV_ERR_UNSUPPORTED,
+                "no multi-query kernel for head_dim %d, block_size %d, group size %d", head_dim,
+                block_size, G);
+  if (batch == 0 || num_tokens == 0 || max_q_len == 0) return PAGEDKV_OK;
+  if (!q || !cu_seqlens_q || !k_cache || !v_cache || !context_lens || !out ||
+      (max_blocks_per_seq > 0 && !block_tables))
+    return fail(PAGEDKV_ERR_NULL, "q, cu_seqlens_q, k_cache, v_cache, block_tables, "
+                                  "context_lens and out must be non-NULL");
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
+      !aligned(block_tables, 4) || !aligned(context_lens, 4) || !aligned(cu_seqlens_q, 4))
+    return fail(PAGEDKV_ERR_ALIGN, "q, k_cache, v_cache and out need 16-byte alignment");
+  const int64_t per_group = prefill_tokens_per_group(G);
+  const int64_t ntiles = ceil_div(max_q_len, per_group);
+  if ((int64_t)batch * num_kv_heads * ntiles > INT32_MAX)
+    return fail(PAGEDKV_ERR_SHAPE, "too many workgroups (batch * kv heads * query tiles)");
+  PrefillArgs a{};
+  a.q = q;
+  a.cu_seqlens_q = cu_seqlens_q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.out = out;
+  a.max_blocks = max_blocks_per_seq;
+  a.batch = batch;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.block_size = block_size;
+  a.num_blocks = num_blocks;
+  a.scale_log2 = scale * kLog2eHost;
+  a.ntiles = (int32_t)ntiles;
+  hipError_t e = launch_prefill_mfma(a, stream);
+  if (e != hipSuccess) return hip_fail(e, "prefill attention launch");
+  return PAGEDKV_OK;
+}
+
 }  // extern "C"

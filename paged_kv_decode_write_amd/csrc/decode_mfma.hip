@@ -33,201 +33,10 @@
 // the running sum stays per lane and is reduced once at the end. Waves are merged through
 // LDS with the log-sum-exp rule and the result is written out, or left as a partition
 // partial for the merge kernel.
-#include "device_common.h"
 #include "launch.h"
+#include "mfma_tiles.h"
 
 namespace pagedkv {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float floatx4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ bf16x8 as_bf16x8(const uint4& w) {
-  return __builtin_bit_cast(bf16x8, w);
-}
-
-__device__ __forceinline__ floatx4 mfma16x16x32(const bf16x8& a, const bf16x8& b,
-                                                const floatx4& c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-// Low / high bf16 halves of two words packed into one word (x's half first).
-__device__ __forceinline__ uint32_t pack_lo(uint32_t x, uint32_t y) {
-  return __builtin_amdgcn_perm(y, x, 0x05040100u);
-}
-__device__ __forceinline__ uint32_t pack_hi(uint32_t x, uint32_t y) {
-  return __builtin_amdgcn_perm(y, x, 0x07060302u);
-}
-
-// Row of EPL consecutive bf16 values (EPL = 8: 16 bytes, EPL = 4: 8 bytes).
-template <int EPL> struct VRow;
-template <> struct VRow<8> {
-  uint4 w;
-  __device__ __forceinline__ void load(const uint16_t* p) { w = *reinterpret_cast<const uint4*>(p); }
-  __device__ __forceinline__ void keep_if(bool v) {
-    w.x = v ? w.x : 0u; w.y = v ? w.y : 0u; w.z = v ? w.z : 0u; w.w = v ? w.w : 0u;
-  }
-  __device__ __forceinline__ uint32_t word(int i) const {
-    return i == 0 ? w.x : i == 1 ? w.y : i == 2 ? w.z : w.w;
-  }
-};
-template <> struct VRow<4> {
-  uint2 w;
-  __device__ __forceinline__ void load(const uint16_t* p) { w = *reinterpret_cast<const uint2*>(p); }
-  __device__ __forceinline__ void keep_if(bool v) { w.x = v ? w.x : 0u; w.y = v ? w.y : 0u; }
-  __device__ __forceinline__ uint32_t word(int i) const { return i == 0 ? w.x : w.y; }
-};
-
-// Slack of the lazily updated softmax reference max, in log2 units (weights <= 2^8).
-constexpr float kRescaleSlack = 8.f;
-
-// Per-lane softmax state of one wave: the head is n16 = lane % 16; lanes of the same head
-// (kg = 0..3) share m_run and hold disjoint output columns.
-template <int EPL> struct WaveState {
-  floatx4 acc[EPL];  // O^T: acc[e][i] = out[head n16][EPL*(4kg+i) + e] (unnormalised)
-  float m_run;       // reference max (log2 units)
-  float l_run;       // this lane's share of the running sum
-};
-
-// Registers of one block pair in flight: K rows as the A operand of q.K, V rows as loaded.
-template <int NCH, int EPL> struct PairTile {
-  uint4 ka[NCH], kb[NCH];
-  VRow<EPL> vr[8];
-  int lastA, lastB;  // valid rows in each block (0: block absent or invalid)
-};
-
-template <int D> struct PairCtx {
-  const uint16_t* k_cache;
-  const uint16_t* v_cache;
-  const int32_t* table;  // this sequence's block-table row
-  size_t row_stride;     // elements between token rows (Hkv * D)
-  size_t head_off;       // g * D
-  int64_t num_blocks;
-  int blk0, blk1, tok1, wave, n16, kg;
-};
-
-// Block ids of this wave's pair k (uniform, scalar loads).
-template <int D, int NW>
-__device__ __forceinline__ int2 pair_ids(const PairCtx<D>& c, int k) {
-  const int jA = c.blk0 + 2 * (c.wave + NW * k);
-  const int pA = c.table[jA];
-  const int pB = jA + 1 < c.blk1 ? c.table[jA + 1] : -1;
-  return make_int2(pA, pB);
-}
-
-// Issue the loads of pair k. An invalid or absent block is replaced by block 0 (always in
-// the pool) with no valid rows, so its contents never reach the result.
-template <int D, int NW, int NCH, int EPL>
-__device__ __forceinline__ void pair_load(PairTile<NCH, EPL>& t, const PairCtx<D>& c, int2 ids,
-                                          int k) {
-  constexpr int BS = 16;
-  const int jA = c.blk0 + 2 * (c.wave + NW * k);
-  const bool okA = ids.x >= 0 && (int64_t)ids.x < c.num_blocks;
-  const bool okB = ids.y >= 0 && (int64_t)ids.y < c.num_blocks;
-  const int tA = jA * BS;
-  t.lastA = okA ? min(c.tok1 - tA, BS) : 0;
-  t.lastB = okB ? min(c.tok1 - tA - BS, BS) : 0;
-  const size_t bA = (size_t)(okA ? ids.x : 0) * BS * c.row_stride + c.head_off;
-  const size_t bB = (size_t)(okB ? ids.y : 0) * BS * c.row_stride + c.head_off;
-  const size_t koff = (size_t)c.n16 * c.row_stride + 8 * c.kg;
-#pragma unroll
-  for (int ch = 0; ch < NCH; ++ch) {
-    t.ka[ch] = *reinterpret_cast<const uint4*>(c.k_cache + bA + koff + 32 * ch);
-    t.kb[ch] = *reinterpret_cast<const uint4*>(c.k_cache + bB + koff + 32 * ch);
-  }
-  const size_t voff = (size_t)(4 * c.kg) * c.row_stride + EPL * c.n16;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    t.vr[j].load(c.v_cache + bA + voff + (size_t)j * c.row_stride);
-    t.vr[4 + j].load(c.v_cache + bB + voff + (size_t)j * c.row_stride);
-  }
-}
-
-// q.K, online softmax and p.V for one loaded pair.
-template <int NCH, int EPL>
-__device__ __forceinline__ void pair_compute(PairTile<NCH, EPL>& t, WaveState<EPL>& st,
-                                             const bf16x8 (&qb)[NCH], float sl2, int kg) {
-  constexpr int BS = 16;
-  floatx4 sA = {0.f, 0.f, 0.f, 0.f}, sB = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int ch = 0; ch < NCH; ++ch) {
-    sA = mfma16x16x32(as_bf16x8(t.ka[ch]), qb[ch], sA);
-    sB = mfma16x16x32(as_bf16x8(t.kb[ch]), qb[ch], sB);
-  }
-  float s[8];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    s[i] = sA[i] * sl2;
-    s[4 + i] = sB[i] * sl2;
-  }
-  if (t.lastA < BS || t.lastB < BS) {  // a block holds positions at or past the end
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const bool va = 4 * kg + i < t.lastA;
-      const bool vb = 4 * kg + i < t.lastB;
-      s[i] = va ? s[i] : kNegInf;
-      s[4 + i] = vb ? s[4 + i] : kNegInf;
-      t.vr[i].keep_if(va);  // stale rows may hold NaN bits; 0 * NaN would poison p.V
-      t.vr[4 + i].keep_if(vb);
-    }
-  }
-  float mx = s[0];
-#pragma unroll
-  for (int i = 1; i < 8; ++i) mx = fmaxf(mx, s[i]);
-  mx = fmaxf(mx, shfl_xor(mx, 16));
-  mx = fmaxf(mx, shfl_xor(mx, 32));
-  // Lazy rescaling: the reference max moves only when a score exceeds it by more than
-  // kRescaleSlack, so weights stay <= 2^kRescaleSlack and the accumulator is rescaled on few
-  // steps instead of every step. Any reference value gives the same softmax; the final
-  // normalisation divides it out.
-  const float mn = fmaxf(st.m_run, mx);
-  const bool upd = mn > st.m_run + kRescaleSlack;  // also true while m_run is -inf
-  if (__any(upd)) {
-    const float m_new = upd ? mn : st.m_run;
-    const float alpha = upd ? fast_exp2(st.m_run - (m_new == kNegInf ? 0.f : m_new)) : 1.f;
-    st.l_run *= alpha;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) st.acc[e] *= alpha;
-    st.m_run = m_new;
-  }
-  const float mu = st.m_run == kNegInf ? 0.f : st.m_run;
-  float p[8];
-  float psum = 0.f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    p[i] = fast_exp2(s[i] - mu);
-    psum += p[i];
-  }
-  st.l_run += psum;
-
-  // P^T operand, split into bf16 hi (truncation, exact) + bf16 lo (rounded remainder).
-  uint32_t hw[4], lw[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const uint32_t u0 = __float_as_uint(p[2 * q]), u1 = __float_as_uint(p[2 * q + 1]);
-    hw[q] = pack_hi(u0, u1);
-    const float r0 = p[2 * q] - __uint_as_float(u0 & 0xffff0000u);
-    const float r1 = p[2 * q + 1] - __uint_as_float(u1 & 0xffff0000u);
-    const __bf16 b0 = (__bf16)r0, b1 = (__bf16)r1;
-    lw[q] = (uint32_t)__builtin_bit_cast(uint16_t, b0) |
-            ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
-  }
-  const bf16x8 phi = as_bf16x8(make_uint4(hw[0], hw[1], hw[2], hw[3]));
-  const bf16x8 plo = as_bf16x8(make_uint4(lw[0], lw[1], lw[2], lw[3]));
-
-  // V^T operand for output column set e: 8 token slots of column EPL*n16 + e.
-#pragma unroll
-  for (int e = 0; e < EPL; ++e) {
-    uint32_t w[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t x = t.vr[2 * q].word(e / 2), y = t.vr[2 * q + 1].word(e / 2);
-      w[q] = (e & 1) ? pack_hi(x, y) : pack_lo(x, y);
-    }
-    const bf16x8 vt = as_bf16x8(make_uint4(w[0], w[1], w[2], w[3]));
-    st.acc[e] = mfma16x16x32(vt, phi, st.acc[e]);
-    st.acc[e] = mfma16x16x32(vt, plo, st.acc[e]);
-  }
-}
 
 template <int D, int NW>
 __global__ void __launch_bounds__(NW * 64)

@@ -25,6 +25,22 @@ struct DecodeArgs {
   int32_t part_tokens;  // tokens per partition, a multiple of block_size
 };
 
+// Arguments of one multi-query causal (prefill) launch, already validated.
+struct PrefillArgs {
+  const uint16_t* q;             // [T][Hq][D]
+  const int32_t* cu_seqlens_q;   // [B+1]
+  const uint16_t* k_cache;
+  const uint16_t* v_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  float* out;                    // [T][Hq][D]
+  int32_t max_blocks;
+  int32_t batch, num_q_heads, num_kv_heads, head_dim, block_size;
+  int64_t num_blocks;
+  float scale_log2;
+  int32_t ntiles;  // query tiles per sequence (ceil(max_q_len / tokens per workgroup))
+};
+
 // Each launcher returns hipSuccess or the launch error. `supported_*` report whether a
 // compiled instance exists for the shape.
 bool supported_valu(int head_dim, int group, int block_size);
@@ -36,6 +52,10 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_mfma_hw(const DecodeArgs& a, hipStream_t stream);
 
 hipError_t launch_decode_reduce(const DecodeArgs& a, hipStream_t stream);
+
+bool supported_prefill(int head_dim, int group, int block_size);
+int prefill_tokens_per_group(int group);  // query tokens one workgroup covers
+hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t stream);
 
 hipError_t launch_kv_write(const uint16_t* k, const uint16_t* v, const int64_t* slots,
                            int64_t num_tokens, uint16_t* k_cache, uint16_t* v_cache,

@@ -191,8 +191,9 @@ def to_host_numpy(inp: Dict[str, object]) -> Dict[str, object]:
     out = {"workload": inp["workload"], "scale": inp["scale"]}
     for key in ("q", "k_cache", "v_cache", "k_new", "v_new"):
         out[key] = to_bits(inp[key])
-    for key in ("block_tables", "context_lens", "slot_mapping"):
-        out[key] = inp[key].detach().to("cpu").numpy()
+    for key in ("block_tables", "context_lens", "slot_mapping", "cu_seqlens_q"):
+        if key in inp:
+            out[key] = inp[key].detach().to("cpu").numpy()
     return out
 
 
@@ -207,3 +208,115 @@ def algorithmic_bytes(w: Workload, context_lens) -> Dict[str, int]:
     write = B * Hkv * D * 2 * 2 * 2
     return {"kv": kv, "q": q, "out": o, "attention": kv + q + o, "write": write,
             "tokens": total_tokens}
+
+
+# --------------------------------------------------------------------------------------------
+# Multi-query (prefill / chunked prefill) workloads. Sequence b has a cached prefix of
+# L_b - Q_b tokens and appends a chunk of Q_b new tokens (Q_b = L_b: full prefill or
+# recompute). Recipe (one torch.Generator per workload, draws in this order): block-id
+# permutation, q [T, Hq, D] * q_std, pool K, pool V, new k [T, Hkv, D], new v; T = sum Q_b.
+# The new tokens occupy positions L_b - Q_b .. L_b - 1, so token i of sequence b goes to
+# slot table[b][p // bs] * bs + p % bs with p = L_b - Q_b + i.
+# --------------------------------------------------------------------------------------------
+@dataclasses.dataclass(frozen=True)
+class PrefillWorkload:
+    name: str
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    block_size: int
+    num_blocks: int
+    max_blocks: int
+    seed: int
+    context_lens: tuple
+    query_lens: tuple
+    q_std: float = 1.0
+    description: str = ""
+
+    @property
+    def batch(self) -> int:
+        return len(self.context_lens)
+
+    @property
+    def gqa(self) -> int:
+        return self.num_q_heads // self.num_kv_heads
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.head_dim)
+
+
+PREFILL_WORKLOADS: Dict[str, PrefillWorkload] = {
+    "p1": PrefillWorkload("p1", num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
+                          num_blocks=2048, max_blocks=256, seed=2001,
+                          context_lens=(4096,) * 8, query_lens=(512,) * 8,
+                          description="chunked prefill: 8 sequences, 3584 cached + 512 new "
+                                      "tokens each, 32q:8kv, D=128"),
+    "p2": PrefillWorkload("p2", num_q_heads=24, num_kv_heads=8, head_dim=128, block_size=16,
+                          num_blocks=600, max_blocks=256, seed=2002,
+                          context_lens=(1, 17, 300, 1000, 2048, 4000),
+                          query_lens=(1, 17, 64, 1000, 256, 100),
+                          description="ragged mix of full prefills and chunks, 24q:8kv, D=128"),
+    "p3": PrefillWorkload("p3", num_q_heads=32, num_kv_heads=8, head_dim=64, block_size=16,
+                          num_blocks=300, max_blocks=128, seed=2003,
+                          context_lens=(2048, 2048), query_lens=(2048, 2048),
+                          description="full prefill (recompute) of 2 x 2048 tokens, 32q:8kv, "
+                                      "D=64"),
+}
+
+
+def make_prefill_inputs(w: PrefillWorkload, device: str = "cpu", poison: bool = False
+                        ) -> Dict[str, object]:
+    gen = torch.Generator(device=device)
+    gen.manual_seed(w.seed)
+    B, bs, NB, MB = w.batch, w.block_size, w.num_blocks, w.max_blocks
+    Hq, Hkv, D = w.num_q_heads, w.num_kv_heads, w.head_dim
+    ctx = torch.tensor(w.context_lens, dtype=torch.int32)
+    ql = torch.tensor(w.query_lens, dtype=torch.int32)
+    if (ql > ctx).any() or (ql < 0).any():
+        raise ValueError("query lengths must be within [0, context length]")
+    perm = torch.randperm(NB, generator=gen, device=device).to("cpu")
+    nblk = [(int(L) + bs - 1) // bs for L in ctx.tolist()]
+    if sum(nblk) > NB or max(nblk) > MB:
+        raise ValueError(f"{w.name}: lengths need {sum(nblk)} blocks (pool {NB})")
+    tables = torch.full((B, MB), -1, dtype=torch.int32)
+    pos = 0
+    for b, n in enumerate(nblk):
+        tables[b, :n] = perm[pos:pos + n].to(torch.int32)
+        pos += n
+    T = int(ql.sum())
+    q = _bf16_normal((T, Hq, D), gen, device, w.q_std)
+    k_cache = _bf16_normal((NB, bs, Hkv, D), gen, device)
+    v_cache = _bf16_normal((NB, bs, Hkv, D), gen, device)
+    k_new = _bf16_normal((T, Hkv, D), gen, device)
+    v_new = _bf16_normal((T, Hkv, D), gen, device)
+    cu = torch.zeros(B + 1, dtype=torch.int32)
+    cu[1:] = torch.cumsum(ql, 0)
+    slots = torch.empty(T, dtype=torch.int64)
+    for b in range(B):
+        L, Q = int(ctx[b]), int(ql[b])
+        for i in range(Q):
+            p = L - Q + i
+            slots[int(cu[b]) + i] = int(tables[b, p // bs]) * bs + p % bs
+    if poison:
+        poison_unread_slots(k_cache, v_cache, tables, ctx, bs)
+    dev = torch.device(device)
+    return {"workload": w, "q": q, "k_cache": k_cache, "v_cache": v_cache,
+            "block_tables": tables.to(dev), "context_lens": ctx.to(dev),
+            "cu_seqlens_q": cu.to(dev), "k_new": k_new, "v_new": v_new,
+            "slot_mapping": slots.to(dev), "scale": w.scale, "max_q_len": int(ql.max()) if B else 0}
+
+
+def prefill_algorithmic(w: PrefillWorkload) -> Dict[str, int]:
+    """Useful work of one multi-query call: flops of q.K and p.V over the causal keys of
+    every query row (4 * (p+1) * D per row and query head), and bytes of K/V of every cached
+    position read once, q (bf16) and out (fp32)."""
+    flops = 0
+    for L, Q in zip(w.context_lens, w.query_lens):
+        keys = sum(L - Q + i + 1 for i in range(Q))
+        flops += 4 * keys * w.head_dim * w.num_q_heads
+    T = sum(w.query_lens)
+    kv = sum(w.context_lens) * w.num_kv_heads * w.head_dim * 2 * 2
+    return {"flops": flops, "kv": kv, "q": T * w.num_q_heads * w.head_dim * 2,
+            "out": T * w.num_q_heads * w.head_dim * 4,
+            "bytes": kv + T * w.num_q_heads * w.head_dim * 6}

@@ -371,3 +371,105 @@ def test_graph_capture_replays_match_eager(dev, name, partition):
         assert torch.equal(out, eager), f"replay {r}"
     assert np.array_equal(wl.to_bits(d["k_cache"]), kc_ref)
     assert np.array_equal(wl.to_bits(d["v_cache"]), vc_ref)
+
+
+# ------------------------------------------------------- multi-query causal (prefill)
+_PCASES = {}
+
+
+def prefill_case(name, dev, poison=False, rows=None):
+    key = (name, poison)
+    if key not in _PCASES:
+        w = wl.PREFILL_WORKLOADS[name]
+        inp = wl.make_prefill_inputs(w, poison=poison)
+        host = wl.to_host_numpy(inp)
+        kc, vc = oracle.kv_write(host["k_new"], host["v_new"], host["slot_mapping"],
+                                 host["k_cache"], host["v_cache"])
+        ref = oracle.prefill_attention(host["q"], host["cu_seqlens_q"], kc, vc,
+                                       host["block_tables"], host["context_lens"],
+                                       host["scale"], rows=rows)
+        d = to_dev(inp, dev)
+        run_write(d)
+        torch.cuda.synchronize()
+        assert np.array_equal(wl.to_bits(d["k_cache"]), kc)
+        _PCASES[key] = (ref, d)
+    return _PCASES[key]
+
+
+def run_prefill(d):
+    T, Hq, D = d["q"].shape
+    out = torch.full((T, Hq, D), float("nan"), dtype=torch.float32, device=d["q"].device)
+    pk.paged_prefill_attention(d["q"], d["cu_seqlens_q"], d["k_cache"], d["v_cache"],
+                               d["block_tables"], d["context_lens"], d["scale"], out,
+                               max_q_len=d["max_q_len"])
+    return out
+
+
+@pytest.mark.parametrize("name", ["p2", "p3"])
+def test_prefill_parity(dev, name):
+    ref, d = prefill_case(name, dev)
+    out = run_prefill(d).cpu().double().numpy()
+    err = np.abs(out - ref).max()
+    record(f"{name}/prefill", err)
+    assert np.isfinite(out).all()
+    assert err <= ATOL, err
+
+
+def test_prefill_chunked_sampled(dev):
+    w = wl.PREFILL_WORKLOADS["p1"]
+    rng = np.random.default_rng(17)
+    T = sum(w.query_lens)
+    rows = sorted({(0, 0), (T - 1, w.num_q_heads - 1)} |
+                  {(int(rng.integers(T)), int(rng.integers(w.num_q_heads))) for _ in range(40)})
+    ref, d = prefill_case("p1", dev, rows=rows)
+    out = run_prefill(d).cpu().double().numpy()
+    assert np.isfinite(out).all()
+    err = max(np.abs(out[r, h] - ref[r, h]).max() for r, h in rows)
+    record("p1/prefill/sampled", err)
+    assert err <= ATOL, err
+
+
+def test_prefill_poisoned_pool_matches_clean(dev):
+    _, clean = prefill_case("p2", dev)
+    ref, dirty = prefill_case("p2", dev, poison=True)
+    o1, o2 = run_prefill(clean), run_prefill(dirty)
+    assert torch.equal(o1, o2)
+    assert np.abs(o2.cpu().double().numpy() - ref).max() <= ATOL
+
+
+@pytest.mark.parametrize("name", ["c2", "c4"])
+def test_prefill_single_query_matches_decode(dev, name):
+    """One query row per sequence at its last position is the decode case."""
+    w = wl.WORKLOADS[name]
+    _, ref, _, _, d = case(name, dev)
+    cu = torch.arange(w.batch + 1, dtype=torch.int32, device=dev)
+    out = torch.empty(w.batch, w.num_q_heads, w.head_dim, dtype=torch.float32, device=dev)
+    pk.paged_prefill_attention(d["q"], cu, d["k_cache"], d["v_cache"], d["block_tables"],
+                               d["context_lens"], d["scale"], out, max_q_len=1)
+    dec = run_attention(d, "auto", -1)
+    diff = (out - dec).abs().max().item()
+    record(f"{name}/prefill_q1_vs_decode", diff)
+    assert diff <= 1e-4
+    assert np.abs(out.cpu().double().numpy() - ref).max() <= ATOL
+
+
+@pytest.mark.parametrize("Hq,Hkv,D", [(24, 8, 64), (16, 16, 128), (32, 2, 128)])
+def test_prefill_group_sizes_and_edges(dev, Hq, Hkv, D):
+    """G = 3, 1 and 16 (5, 16 and 1 query tokens per wave), lengths at block edges, single
+    tokens, full prefills and chunks, on a poisoned pool."""
+    w = wl.PrefillWorkload("edge", num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, block_size=16,
+                           num_blocks=200, max_blocks=80, seed=77,
+                           context_lens=(1, 16, 17, 33, 300, 1000),
+                           query_lens=(1, 16, 5, 33, 47, 129), q_std=3.0)
+    inp = wl.make_prefill_inputs(w, poison=True)
+    host = wl.to_host_numpy(inp)
+    kc, vc = oracle.kv_write(host["k_new"], host["v_new"], host["slot_mapping"],
+                             host["k_cache"], host["v_cache"])
+    ref = oracle.prefill_attention(host["q"], host["cu_seqlens_q"], kc, vc, host["block_tables"],
+                                   host["context_lens"], host["scale"])
+    d = to_dev(inp, dev)
+    run_write(d)
+    out = run_prefill(d).cpu().double().numpy()
+    err = np.abs(out - ref).max()
+    record(f"edge_prefill/D{D}/G{Hq // Hkv}", err)
+    assert np.isfinite(out).all() and err <= ATOL, err

@@ -503,3 +503,136 @@ def test_decode_step_orders_write_before_attention():
     for b in range(3):
         for h in range(4):
             assert np.array_equal(out[b, h], vn[b, h // 2])
+
+
+# ----------------------------------------------- multi-query causal (prefill) oracle pins
+def prefill_case(seed, lens, qlens, Hq=8, Hkv=2, D=16, bs=4):
+    rng = np.random.default_rng(seed)
+    dense_k = [rand_bits(rng, (L, Hkv, D)) for L in lens]
+    dense_v = [rand_bits(rng, (L, Hkv, D)) for L in lens]
+    MB = max(1, max((L + bs - 1) // bs for L in lens))
+    NB = sum((L + bs - 1) // bs for L in lens) + 3
+    kc, vc, tables = scatter_to_pool(rng, dense_k, dense_v, lens, NB, bs, MB)
+    T = sum(qlens)
+    q = rand_bits(rng, (T, Hq, D))
+    cu = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
+    return dict(q=q, cu=cu, kc=kc, vc=vc, tables=tables, lens=np.array(lens, np.int32),
+                qlens=qlens, dense_k=dense_k, dense_v=dense_v, Hq=Hq, Hkv=Hkv, D=D,
+                scale=1 / math.sqrt(D))
+
+
+def run_prefill(c):
+    return oracle.prefill_attention(c["q"], c["cu"], c["kc"], c["vc"], c["tables"], c["lens"],
+                                    c["scale"])
+
+
+def sdpa_prefill(c, offset=0):
+    """torch SDPA in float64 with an explicit causal mask (row i sees keys <= L-Q+i+offset)."""
+    out = np.zeros((c["q"].shape[0], c["Hq"], c["D"]))
+    for b, (L, Q) in enumerate(zip(c["lens"].tolist(), c["qlens"])):
+        if Q == 0:
+            continue
+        q = torch.from_numpy(oracle.bf16_bits_to_f64(c["q"][c["cu"][b]:c["cu"][b + 1]]))
+        k = torch.from_numpy(oracle.bf16_bits_to_f64(c["dense_k"][b]))
+        v = torch.from_numpy(oracle.bf16_bits_to_f64(c["dense_v"][b]))
+        i = torch.arange(Q)[:, None]
+        j = torch.arange(L)[None, :]
+        mask = j <= (L - Q + i + offset)
+        o = F.scaled_dot_product_attention(q.permute(1, 0, 2)[None], k.permute(1, 0, 2)[None],
+                                           v.permute(1, 0, 2)[None], attn_mask=mask,
+                                           scale=float(np.float32(c["scale"])), enable_gqa=True)
+        out[c["cu"][b]:c["cu"][b + 1]] = o[0].permute(1, 0, 2).numpy()
+    return out
+
+
+@pytest.mark.parametrize("seed,lens,qlens,Hq,Hkv,D,bs", [
+    (301, [40, 7, 33], [40, 3, 16], 8, 2, 16, 4),
+    (302, [100, 64], [1, 64], 12, 4, 32, 16),
+    (303, [257, 1, 18], [31, 1, 18], 6, 2, 8, 8),
+    (304, [600], [120], 16, 1, 64, 16)])
+def test_P13_prefill_equals_masked_sdpa(seed, lens, qlens, Hq, Hkv, D, bs):
+    c = prefill_case(seed, lens, qlens, Hq, Hkv, D, bs)
+    np.testing.assert_allclose(run_prefill(c), sdpa_prefill(c), rtol=0, atol=1e-12)
+
+
+def test_P14_full_prefill_equals_is_causal():
+    c = prefill_case(311, [50, 33], [50, 33], 8, 2, 16, 4)
+    out = run_prefill(c)
+    for b in range(2):
+        q = torch.from_numpy(oracle.bf16_bits_to_f64(c["q"][c["cu"][b]:c["cu"][b + 1]]))
+        k = torch.from_numpy(oracle.bf16_bits_to_f64(c["dense_k"][b]))
+        v = torch.from_numpy(oracle.bf16_bits_to_f64(c["dense_v"][b]))
+        o = F.scaled_dot_product_attention(q.permute(1, 0, 2)[None], k.permute(1, 0, 2)[None],
+                                           v.permute(1, 0, 2)[None], is_causal=True,
+                                           scale=float(np.float32(c["scale"])), enable_gqa=True)
+        np.testing.assert_allclose(out[c["cu"][b]:c["cu"][b + 1]], o[0].permute(1, 0, 2).numpy(),
+                                   rtol=0, atol=1e-12)
+
+
+def test_P15_single_query_prefill_equals_decode():
+    c = prefill_case(321, [70, 5, 128], [1, 1, 1], 8, 2, 16, 16)
+    dec = oracle.decode_attention(c["q"], c["kc"], c["vc"], c["tables"], c["lens"], c["scale"])
+    assert np.array_equal(run_prefill(c), dec)
+
+
+def brute_force_prefill(c):
+    q, cu, kc, vc, tables, lens = c["q"], c["cu"], c["kc"], c["vc"], c["tables"], c["lens"]
+    T, Hq, D = q.shape
+    bs, Hkv = kc.shape[1], kc.shape[2]
+    G = Hq // Hkv
+    s32 = struct.unpack("f", struct.pack("f", c["scale"]))[0]
+    out = [[[0.0] * D for _ in range(Hq)] for _ in range(T)]
+    for b in range(len(lens)):
+        L = int(lens[b])
+        Q = int(cu[b + 1] - cu[b])
+        pages = [int(x) for x in tables[b] if x >= 0]
+        for i in range(Q):
+            row = int(cu[b]) + i
+            last = L - Q + i
+            for h in range(Hq):
+                g = h // G
+                sc = [math.fsum(_brute_bf16(int(q[row][h][d])) *
+                                _brute_bf16(int(kc[pages[t // bs]][t % bs][g][d])) for d in range(D)) * s32
+                      for t in range(last + 1)]
+                mx = max(sc)
+                wts = [math.exp(x - mx) for x in sc]
+                den = math.fsum(wts)
+                for d in range(D):
+                    out[row][h][d] = math.fsum(
+                        wts[t] * _brute_bf16(int(vc[pages[t // bs]][t % bs][g][d]))
+                        for t in range(last + 1)) / den
+    return np.array(out)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_P16_prefill_brute_force_tiny(seed):
+    rng = np.random.default_rng(3000 + seed)
+    B = int(rng.integers(1, 4))
+    lens = [int(x) for x in rng.integers(1, 10, size=B)]
+    qlens = [int(rng.integers(0, L + 1)) for L in lens]
+    Hkv = int(rng.integers(1, 3))
+    c = prefill_case(4000 + seed, lens, qlens, Hq=Hkv * int(rng.integers(1, 3)), Hkv=Hkv,
+                     D=int(rng.integers(1, 5)), bs=int(rng.choice([1, 2, 4])))
+    np.testing.assert_allclose(run_prefill(c), brute_force_prefill(c), rtol=0, atol=1e-12)
+
+
+def test_P17_prefill_mutations_are_caught():
+    c = prefill_case(331, [300, 120], [64, 120], 24, 8, 32, 16)
+    ref = sdpa_prefill(c)
+    np.testing.assert_allclose(run_prefill(c), ref, rtol=0, atol=1e-12)
+    # causal offset off by one in either direction, and a mask that ignores the offset
+    for off in (-1, 1):
+        assert np.abs(sdpa_prefill(c, offset=off) - ref).max() > 2e-3
+    qswap = dict(c)
+    qswap["q"] = c["q"][::-1].copy()  # rows attached to the wrong positions
+    assert np.abs(run_prefill(qswap) - ref).max() > 2e-3
+
+
+def test_prefill_rejects_bad_arguments():
+    c = prefill_case(341, [10, 10], [4, 4])
+    with pytest.raises(ValueError):
+        oracle.prefill_attention(c["q"], np.array([0, 4, 9], np.int32), c["kc"], c["vc"],
+                                 c["tables"], c["lens"], c["scale"])
+    with pytest.raises(ValueError):  # more queries than cached positions
+        oracle.prefill_attention(c["q"], c["cu"], c["kc"], c["vc"], c["tables"],
+                                 np.array([3, 10], np.int32), c["scale"])
