@@ -46,6 +46,9 @@ def parse_args():
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="CPU work budget of the oracle baseline sample")
     p.add_argument("--json-out", default=None)
+    p.add_argument("--rope", action="store_true",
+                   help="write with the fused rotary embedding (positions L-1, Llama 3 base "
+                        "500000 frequencies) and attend with the rotated q")
     p.add_argument("--graph", action="store_true",
                    help="also capture one step in a HIP graph and time K replays "
                         "(reported as graph_ms_per_step)")
@@ -242,6 +245,12 @@ def main():
         d["plan"] = pk.decode_plan(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim,
                                    w.max_blocks, w.block_size, args.partition, args.kernel,
                                    with_kernel=True)
+        if args.rope:
+            d["pos"] = (d["context_lens"] - 1).to(torch.int32)
+            d["inv_freq"] = (500000.0 ** (-torch.arange(0, w.head_dim, 2, device=dev,
+                                                          dtype=torch.float64) / w.head_dim)
+                             ).to(torch.float32)
+            d["q_rot"] = torch.empty_like(d["q"])
         subs.append(d)
     torch.cuda.synchronize()
 
@@ -254,9 +263,15 @@ def main():
         if flush is not None:
             torch.sum(flush)
         for i, d in enumerate(subs):
-            pk.paged_kv_write(d["k_new"], d["v_new"], d["slot_mapping"], d["k_cache"],
-                              d["v_cache"])
-            pk.paged_decode_attention(d["q"], d["k_cache"], d["v_cache"], d["block_tables"],
+            if args.rope:
+                pk.paged_kv_write_rope(d["q"], d["k_new"], d["v_new"], d["pos"], d["inv_freq"],
+                                       d["slot_mapping"], d["k_cache"], d["v_cache"],
+                                       q_out=d["q_rot"])
+            else:
+                pk.paged_kv_write(d["k_new"], d["v_new"], d["slot_mapping"], d["k_cache"],
+                                  d["v_cache"])
+            pk.paged_decode_attention(d["q_rot"] if args.rope else d["q"], d["k_cache"],
+                                      d["v_cache"], d["block_tables"],
                                       d["context_lens"], d["scale"], d["out"],
                                       partition_tokens=args.partition, kernel=args.kernel,
                                       workspace=d["ws"],
@@ -360,7 +375,8 @@ def main():
             "us_per_call": {p["workload"]: p["attn_kernel_us_mean"] for p in per},
             "pct_of_peak": {p["workload"]: p["pct_of_peak"] for p in per},
             "kernels": {p["workload"]: p["kernel"] for p in per},
-            "step": "KV write + decode attention per sub-workload",
+            "step": ("RoPE + KV write" if args.rope else "KV write") +
+                    " + decode attention per sub-workload",
         },
         "roofline": {
             "bound": "hbm",

@@ -90,6 +90,32 @@ int paged_kv_write(const uint16_t* k, const uint16_t* v, const int64_t* slot_map
                    int32_t head_dim, hipStream_t stream);
 
 /*
+ * paged_kv_write_rope -- rotary position embedding at absolute positions fused with the KV
+ * write: keys are rotated at their absolute positions before they enter the cache (llm-stack,
+ * Serving engine / KV cache bullet), by a rotation of pairs of components with sine and cosine
+ * ("tiny-vLLM" blog, CUDA Kernel Engineering: RoPE).
+ *
+ *   For token t at position positions[t] and pair i of every head vector:
+ *     theta = fp32(positions[t]) * inv_freq[i]   (fp32 product)
+ *     (x0, x1) -> (x0*cos(theta) - x1*sin(theta), x1*cos(theta) + x0*sin(theta))
+ *   computed in fp32 and rounded to bf16 (nearest even). Pairs are (i, i + D/2) when
+ *   interleaved == 0 (half split) or (2i, 2i+1) when interleaved == 1.
+ *   q [T][Hq][D] -> q_out [T][Hq][D] (rotated; q_out may be q itself);
+ *   k [T][Hkv][D] rotated and v [T][Hkv][D] copied to slot slot_mapping[t] of the pools, as
+ *   paged_kv_write does (negative slot: nothing stored; q_out is still written).
+ *   inv_freq       fp32 [D/2], the caller's per-pair frequencies (e.g. base^(-2i/D), with any
+ *                  long-context rescaling already applied)
+ * Requirements: head_dim a multiple of 8, at most 512; v and v_cache 16-byte aligned. Status
+ * codes and asynchrony as above.
+ */
+int paged_kv_write_rope(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                        const int32_t* positions, const float* inv_freq, int32_t interleaved,
+                        const int64_t* slot_mapping, int64_t num_tokens, uint16_t* q_out,
+                        uint16_t* k_cache, uint16_t* v_cache, int64_t num_blocks,
+                        int32_t block_size, int32_t num_q_heads, int32_t num_kv_heads,
+                        int32_t head_dim, hipStream_t stream);
+
+/*
  * paged_decode_workspace_bytes -- bytes of device workspace paged_decode_attention needs
  * for these sizes (0 when the call never splits a sequence). `partition_tokens` has the
  * same meaning as in paged_decode_attention; for 0 (automatic) the bound covers every

@@ -6,8 +6,10 @@ baseline leg, never by the HIP product path.
 from .oracle import (bf16_bits_to_f64, kv_write, kv_head_for, gather_dense, attend_one,
                      effective_scale, decode_attention, decode_step, prefill_attention,
                      partial_stats,
-                     merge_partials, split_attend_one)
+                     merge_partials, split_attend_one, rope_pairs, rope_angles, rope_rotate,
+                     f64_to_bf16_bits, kv_write_rope)
 
 __all__ = ["bf16_bits_to_f64", "kv_write", "kv_head_for", "gather_dense", "attend_one",
            "effective_scale", "decode_attention", "decode_step", "prefill_attention", "partial_stats",
-           "merge_partials", "split_attend_one"]
+           "merge_partials", "split_attend_one", "rope_pairs", "rope_angles", "rope_rotate",
+           "f64_to_bf16_bits", "kv_write_rope"]

@@ -214,6 +214,88 @@ def decode_step(inp: dict, rows=None) -> Tuple[np.ndarray, np.ndarray, np.ndarra
 
 
 # ---------------------------------------------------------------------------------------
+# Rotary position embedding at absolute positions, applied before keys enter the cache
+# (llm-stack, Serving engine / KV cache bullet: RoPE at absolute positions before the keys
+# are cached; "tiny-vLLM" blog, CUDA Kernel Engineering: RoPE rotates pairs of hidden-state
+# components by position-dependent angles with sine and cosine).
+# Pair i of a head vector is rotated by angle theta_i = position * inv_freq[i]. Pairs are
+# (i, i + D/2) ("half" pairing) or (2i, 2i+1) ("interleaved"). The angle is formed in fp32
+# (as a GPU receives position and frequency), everything after it in float64; the rotated
+# value is rounded to bf16 (round-to-nearest-even) when it is stored.
+# ---------------------------------------------------------------------------------------
+def rope_pairs(D: int, interleaved: bool) -> Tuple[np.ndarray, np.ndarray]:
+    """Index arrays (first, second) of the D/2 rotated pairs."""
+    i = np.arange(D // 2)
+    if interleaved:
+        return 2 * i, 2 * i + 1
+    return i, i + D // 2
+
+
+def rope_angles(position: int, inv_freq: np.ndarray) -> np.ndarray:
+    """theta_i = fp32(position) * fp32(inv_freq[i]), the product rounded to fp32."""
+    return (np.float32(position) * np.asarray(inv_freq, dtype=np.float32)).astype(np.float64)
+
+
+def rope_rotate(x: np.ndarray, position: int, inv_freq: np.ndarray, interleaved: bool
+                ) -> np.ndarray:
+    """Rotate the last axis (D) of float64 array x by the angles of `position`."""
+    D = x.shape[-1]
+    a, b = rope_pairs(D, interleaved)
+    th = rope_angles(position, inv_freq)
+    c, s = np.cos(th), np.sin(th)
+    y = np.array(x, dtype=np.float64, copy=True)
+    y[..., a] = x[..., a] * c - x[..., b] * s
+    y[..., b] = x[..., b] * c + x[..., a] * s
+    return y
+
+
+def f64_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float64 values to bf16 (round-to-nearest-even) bit patterns, via an exact
+    float64 -> fp32 rounding first only where that cannot double-round: the rounding is
+    done directly on the float64 value's bits."""
+    x = np.asarray(x, dtype=np.float64)
+    bits = x.view(np.uint64)
+    sign = (bits >> np.uint64(63)).astype(np.uint16) << np.uint16(15)
+    ax = np.abs(x)
+    out = np.empty(x.shape, dtype=np.uint16)
+    # exact decomposition: ax = m * 2^e with m in [1, 2)
+    m, e = np.frexp(ax)          # m in [0.5, 1)
+    m = m * 2.0
+    e = e - 1
+    # bf16 keeps 8 significant bits; spacing 2^(e-7) for normals, 2^-133 for subnormals
+    e_eff = np.maximum(e, -126)
+    ulp = np.ldexp(1.0, (e_eff - 7).astype(np.int64))
+    q = ax / ulp                  # exact (power-of-two scaling)
+    r = np.rint(q)                # round half to even
+    val = r * ulp
+    with np.errstate(over="ignore", invalid="ignore"):
+        f32 = val.astype(np.float32)
+    fbits = f32.view(np.uint32)
+    out[:] = (fbits >> np.uint32(16)).astype(np.uint16) & np.uint16(0x7FFF)
+    out[ax == 0] = 0
+    out[ax >= np.ldexp(1.0, 128) - np.ldexp(1.0, 119)] = 0x7F80  # rounds to infinity
+    out[np.isnan(x)] = 0x7FC0
+    return (out | sign).astype(np.uint16)
+
+
+def kv_write_rope(q_bits: np.ndarray, k_bits: np.ndarray, v_bits: np.ndarray,
+                  positions: np.ndarray, inv_freq: np.ndarray, interleaved: bool,
+                  slot_mapping: np.ndarray, k_cache_bits: np.ndarray, v_cache_bits: np.ndarray
+                  ) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Rotate q and k of token t at positions[t], write rotated k and raw v to slot
+    slot_mapping[t] (negative: no write). Returns (q rotated bits, k_cache', v_cache')."""
+    q_rot = np.empty_like(q_bits)
+    k_rot = np.empty_like(k_bits)
+    for t, p in enumerate(np.asarray(positions).tolist()):
+        q_rot[t] = f64_to_bf16_bits(rope_rotate(bf16_bits_to_f64(q_bits[t]), p, inv_freq,
+                                                interleaved))
+        k_rot[t] = f64_to_bf16_bits(rope_rotate(bf16_bits_to_f64(k_bits[t]), p, inv_freq,
+                                                interleaved))
+    kc, vc = kv_write(k_rot, v_bits, slot_mapping, k_cache_bits, v_cache_bits)
+    return q_rot, kc, vc
+
+
+# ---------------------------------------------------------------------------------------
 # Partitioned softmax (split-K) identity. The pages never write it out; it is the running
 # max / running sum rescaling behind the tiled online softmax of llm-stack's Attention
 # kernel section and the FlashAttention-2 paper the Llama engine lists under References.

@@ -67,6 +67,9 @@ def load_library() -> ctypes.CDLL:
         lib.paged_decode_attention.argtypes = attn + [P]
         lib.paged_decode_attention_ex.restype = ctypes.c_int
         lib.paged_decode_attention_ex.argtypes = attn + [I32, P, P, P]
+        lib.paged_kv_write_rope.restype = ctypes.c_int
+        lib.paged_kv_write_rope.argtypes = [P, P, P, P, P, I32, P, I64, P, P, P, I64, I32, I32,
+                                            I32, I32, P]
         lib.paged_prefill_attention.restype = ctypes.c_int
         lib.paged_prefill_attention.argtypes = [P, P, I64, I32, P, P, P, I32, P, I32, I32, I32,
                                                 I32, I32, I64, F32, P, P]
@@ -260,3 +263,40 @@ def paged_prefill_attention(q: torch.Tensor, cu_seqlens_q: torch.Tensor, k_cache
             context_lens.data_ptr(), B, Hq, Hkv, D, bs, NB, float(scale), out.data_ptr(),
             _stream_handle(dev)))
     return out
+
+
+def paged_kv_write_rope(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                        positions: torch.Tensor, inv_freq: torch.Tensor,
+                        slot_mapping: torch.Tensor, k_cache: torch.Tensor,
+                        v_cache: torch.Tensor, *, q_out: Optional[torch.Tensor] = None,
+                        interleaved: bool = False) -> torch.Tensor:
+    """Rotate q and k of token t at positions[t] (pair i by positions[t] * inv_freq[i]), store
+    the rotated k and the raw v at slot slot_mapping[t], return the rotated q (q_out, or a new
+    tensor). q [T, Hq, D], k/v [T, Hkv, D] bf16; positions [T] int32; inv_freq [D/2] fp32."""
+    _require(k_cache, "k_cache", torch.bfloat16, 4)
+    dev = k_cache.device
+    _require(v_cache, "v_cache", torch.bfloat16, 4, dev)
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _require(t, name, torch.bfloat16, 3, dev)
+    _require(positions, "positions", torch.int32, 1, dev)
+    _require(inv_freq, "inv_freq", torch.float32, 1, dev)
+    _require(slot_mapping, "slot_mapping", torch.int64, 1, dev)
+    NB, bs, Hkv, D = k_cache.shape
+    T, Hq, _ = q.shape
+    if (k.shape != (T, Hkv, D) or v.shape != (T, Hkv, D) or q.shape[2] != D or
+            positions.shape != (T,) or slot_mapping.shape != (T,) or inv_freq.shape != (D // 2,)
+            or v_cache.shape != k_cache.shape):
+        raise ValueError("shape mismatch in paged_kv_write_rope arguments")
+    if q_out is None:
+        q_out = torch.empty_like(q)
+    _require(q_out, "q_out", torch.bfloat16, 3, dev)
+    if q_out.shape != q.shape:
+        raise ValueError("q_out must have q's shape")
+    lib = load_library()
+    with torch.cuda.device(dev):
+        _check(lib.paged_kv_write_rope(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                       positions.data_ptr(), inv_freq.data_ptr(),
+                                       int(bool(interleaved)), slot_mapping.data_ptr(), T,
+                                       q_out.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                       NB, bs, Hq, Hkv, D, _stream_handle(dev)))
+    return q_out

@@ -22,7 +22,7 @@ INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(HERE, "libpagedkv.so")
 
 SOURCES = ["api.cpp", "kv_write.hip", "decode_valu.hip", "decode_mfma.hip", "decode_reduce.hip",
-           "prefill_mfma.hip"]
+           "prefill_mfma.hip", "kv_write_rope.hip"]
 ARCH = os.environ.get("PAGEDKV_ARCH", "gfx950")
 
 

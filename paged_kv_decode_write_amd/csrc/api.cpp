@@ -233,6 +233,56 @@ int paged_kv_write(const uint16_t* k, const uint16_t* v, const int64_t* slot_map
   return PAGEDKV_OK;
 }
 
+int paged_kv_write_rope(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                        const int32_t* positions, const float* inv_freq, int32_t interleaved,
+                        const int64_t* slot_mapping, int64_t num_tokens, uint16_t* q_out,
+                        uint16_t* k_cache, uint16_t* v_cache, int64_t num_blocks,
+                        int32_t block_size, int32_t num_q_heads, int32_t num_kv_heads,
+                        int32_t head_dim, hipStream_t stream) {
+  g_last_error.clear();
+  if (num_tokens < 0) return fail(PAGEDKV_ERR_SHAPE, "num_tokens must be >= 0");
+  if (num_blocks <= 0 || block_size <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
+      head_dim <= 0)
+    return fail(PAGEDKV_ERR_SHAPE, "sizes must be > 0");
+  if (head_dim % 8 || head_dim > 512)
+    return fail(PAGEDKV_ERR_UNSUPPORTED, "head_dim (%d) must be a multiple of 8, at most 512",
+                head_dim);
+  if (interleaved != 0 && interleaved != 1)
+    return fail(PAGEDKV_ERR_SHAPE, "interleaved must be 0 or 1");
+  const int64_t row = (int64_t)num_kv_heads * head_dim;
+  if ((int64_t)num_q_heads * head_dim > INT32_MAX || row > INT32_MAX)
+    return fail(PAGEDKV_ERR_SHAPE, "rows too long");
+  if (num_blocks > INT64_MAX / block_size / row)
+    return fail(PAGEDKV_ERR_SHAPE, "pool size overflows");
+  if (num_tokens == 0) return PAGEDKV_OK;
+  if (!q || !k || !v || !positions || !inv_freq || !slot_mapping || !q_out || !k_cache ||
+      !v_cache)
+    return fail(PAGEDKV_ERR_NULL, "every array argument must be non-NULL");
+  if (!aligned(v, 16) || !aligned(v_cache, 16) || !aligned(q, 2) || !aligned(k, 2) ||
+      !aligned(q_out, 2) || !aligned(k_cache, 2) || !aligned(positions, 4) ||
+      !aligned(inv_freq, 4) || !aligned(slot_mapping, 8))
+    return fail(PAGEDKV_ERR_ALIGN, "v and v_cache need 16-byte alignment");
+  RopeArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.positions = positions;
+  a.inv_freq = inv_freq;
+  a.slot_mapping = slot_mapping;
+  a.q_out = q_out;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.num_tokens = num_tokens;
+  a.num_slots = num_blocks * block_size;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.interleaved = interleaved;
+  hipError_t e = launch_kv_write_rope(a, stream);
+  if (e != hipSuccess) return hip_fail(e, "rope + kv_write launch");
+  return PAGEDKV_OK;
+}
+
 size_t paged_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t head_dim,
                                     int32_t max_blocks_per_seq, int32_t block_size,
                                     int32_t partition_tokens) {

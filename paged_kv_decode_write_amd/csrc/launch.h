@@ -41,6 +41,22 @@ struct PrefillArgs {
   int32_t ntiles;  // query tiles per sequence (ceil(max_q_len / tokens per workgroup))
 };
 
+// Arguments of one rotary-embedding + KV-write launch, already validated.
+struct RopeArgs {
+  const uint16_t* q;        // [T][Hq][D]
+  const uint16_t* k;        // [T][Hkv][D]
+  const uint16_t* v;        // [T][Hkv][D]
+  const int32_t* positions; // [T]
+  const float* inv_freq;    // [D/2]
+  const int64_t* slot_mapping;
+  uint16_t* q_out;          // [T][Hq][D] (may alias q)
+  uint16_t* k_cache;
+  uint16_t* v_cache;
+  int64_t num_tokens, num_slots;
+  int32_t num_q_heads, num_kv_heads, head_dim;
+  int32_t interleaved;
+};
+
 // Each launcher returns hipSuccess or the launch error. `supported_*` report whether a
 // compiled instance exists for the shape.
 bool supported_valu(int head_dim, int group, int block_size);
@@ -56,6 +72,8 @@ hipError_t launch_decode_reduce(const DecodeArgs& a, hipStream_t stream);
 bool supported_prefill(int head_dim, int group, int block_size);
 int prefill_tokens_per_group(int group);  // query tokens one workgroup covers
 hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t stream);
+
+hipError_t launch_kv_write_rope(const RopeArgs& a, hipStream_t stream);
 
 hipError_t launch_kv_write(const uint16_t* k, const uint16_t* v, const int64_t* slots,
                            int64_t num_tokens, uint16_t* k_cache, uint16_t* v_cache,

@@ -473,3 +473,93 @@ def test_prefill_group_sizes_and_edges(dev, Hq, Hkv, D):
     err = np.abs(out - ref).max()
     record(f"edge_prefill/D{D}/G{Hq // Hkv}", err)
     assert np.isfinite(out).all() and err <= ATOL, err
+
+
+# ---------------------------------------------------------- RoPE fused with the KV write
+def llama_inv_freq(D, base=500000.0):
+    return (base ** (-np.arange(D // 2, dtype=np.float64) * 2 / D)).astype(np.float32)
+
+
+def bf16_ulp_diff(a_bits, b_bits):
+    """|a - b| in units of the larger operand's bf16 spacing (NaN-free inputs)."""
+    a = oracle.bf16_bits_to_f64(a_bits)
+    b = oracle.bf16_bits_to_f64(b_bits)
+    mag = np.maximum(np.abs(a), np.abs(b))
+    e = np.floor(np.log2(np.where(mag > 0, mag, 1.0)))
+    ulp = np.ldexp(1.0, (np.maximum(e, -126) - 7).astype(np.int64))
+    return np.abs(a - b) / ulp
+
+
+@pytest.mark.parametrize("name,interleaved", [("c2", False), ("c4", True), ("c5b", False)])
+def test_rope_write_matches_oracle(dev, name, interleaved):
+    """Rotated q and the pools after the fused write agree with the oracle's float64 rotation
+    rounded to bf16 to within one bf16 unit in the last place (the kernel rounds its fp32
+    result, the oracle its float64 result), and almost everywhere exactly."""
+    w = wl.WORKLOADS[name]
+    if name == "c5b":
+        inp = wl.make_inputs(w, device="cuda")
+        d = inp
+    else:
+        inp = wl.make_inputs(w)
+        d = to_dev(inp, dev)
+    kc0, vc0 = wl.to_bits(d["k_cache"]), wl.to_bits(d["v_cache"])
+    pos = (d["context_lens"] - 1).to(torch.int32)
+    inv = torch.from_numpy(llama_inv_freq(w.head_dim)).to(dev)
+    q_rot = pk.paged_kv_write_rope(d["q"], d["k_new"], d["v_new"], pos, inv, d["slot_mapping"],
+                                   d["k_cache"], d["v_cache"], interleaved=interleaved)
+    torch.cuda.synchronize()
+    q_ref, kc_ref, vc_ref = oracle.kv_write_rope(
+        wl.to_bits(d["q"]), wl.to_bits(d["k_new"]), wl.to_bits(d["v_new"]), pos.cpu().numpy(),
+        inv.cpu().numpy(), interleaved, d["slot_mapping"].cpu().numpy(), kc0, vc0)
+    assert np.array_equal(wl.to_bits(d["v_cache"]), vc_ref)  # v is copied bit for bit
+    for got, ref, what in ((wl.to_bits(q_rot), q_ref, "q"), (wl.to_bits(d["k_cache"]), kc_ref, "k")):
+        diff = bf16_ulp_diff(got, ref)
+        frac = float((got != ref).mean())
+        record(f"rope/{name}/{what}/max_ulp", float(diff.max()))
+        assert diff.max() <= 1.0, (what, diff.max())
+        assert frac <= 0.01, (what, frac)
+
+
+def test_decode_step_with_rope(dev):
+    """Rotate + write the new token at position L-1, then attend with the rotated q."""
+    w = wl.WORKLOADS["c4"]
+    inp = wl.make_inputs(w)
+    host = wl.to_host_numpy(inp)
+    d = to_dev(inp, dev)
+    pos = (d["context_lens"] - 1).to(torch.int32)
+    inv_np = llama_inv_freq(w.head_dim)
+    q_rot = pk.paged_kv_write_rope(d["q"], d["k_new"], d["v_new"], pos,
+                                   torch.from_numpy(inv_np).to(dev), d["slot_mapping"],
+                                   d["k_cache"], d["v_cache"])
+    d2 = dict(d)
+    d2["q"] = q_rot
+    out = run_attention(d2).cpu().double().numpy()
+    q_ref, kc, vc = oracle.kv_write_rope(host["q"], host["k_new"], host["v_new"],
+                                         pos.cpu().numpy(), inv_np, False, host["slot_mapping"],
+                                         host["k_cache"], host["v_cache"])
+    ref = oracle.decode_attention(q_ref, kc, vc, host["block_tables"], host["context_lens"],
+                                  host["scale"])
+    err = np.abs(out - ref).max()
+    record("c4/rope_decode_step", err)
+    assert err <= ATOL, err
+
+
+def test_rope_in_place_and_large_positions(dev):
+    w = wl.Workload("rope", batch=8, num_q_heads=8, num_kv_heads=2, head_dim=64, block_size=16,
+                    num_blocks=64, max_blocks=8, seed=5, context_len=100)
+    inp = wl.make_inputs(w)
+    d = to_dev(inp, dev)
+    pos = torch.tensor([0, 1, 2, 1000, 8191, 32767, 131071, 65535], dtype=torch.int32, device=dev)
+    inv = torch.from_numpy(llama_inv_freq(64, 10000.0)).to(dev)
+    q_in = d["q"].clone()
+    kc0, vc0 = wl.to_bits(d["k_cache"]), wl.to_bits(d["v_cache"])
+    q_out = pk.paged_kv_write_rope(d["q"], d["k_new"], d["v_new"], pos, inv, d["slot_mapping"],
+                                   d["k_cache"], d["v_cache"], q_out=d["q"])  # in place
+    torch.cuda.synchronize()
+    q_ref, kc_ref, _ = oracle.kv_write_rope(wl.to_bits(q_in), wl.to_bits(d["k_new"]),
+                                            wl.to_bits(d["v_new"]), pos.cpu().numpy(),
+                                            inv.cpu().numpy(), False,
+                                            d["slot_mapping"].cpu().numpy(), kc0, vc0)
+    assert q_out.data_ptr() == d["q"].data_ptr()
+    assert bf16_ulp_diff(wl.to_bits(q_out), q_ref).max() <= 1.0
+    assert bf16_ulp_diff(wl.to_bits(d["k_cache"]), kc_ref).max() <= 1.0

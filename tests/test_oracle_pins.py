@@ -636,3 +636,100 @@ def test_prefill_rejects_bad_arguments():
     with pytest.raises(ValueError):  # more queries than cached positions
         oracle.prefill_attention(c["q"], c["cu"], c["kc"], c["vc"], c["tables"],
                                  np.array([3, 10], np.int32), c["scale"])
+
+
+# ------------------------------------------------------------ RoPE + write oracle pins
+def _all_finite_bf16():
+    bits = np.arange(65536, dtype=np.uint16)
+    vals = oracle.bf16_bits_to_f64(bits)
+    keep = np.isfinite(vals) & ~((vals == 0) & (bits == 0x8000))
+    order = np.argsort(vals[keep], kind="stable")
+    return vals[keep][order], bits[keep][order]
+
+
+def test_f64_to_bf16_rounding_against_neighbour_search():
+    vals, bits = _all_finite_bf16()
+    rng = np.random.default_rng(5)
+    x = np.concatenate([rng.standard_normal(20000) * 3, rng.standard_normal(2000) * 1e-38,
+                        (vals[1:-1] + vals[2:]) / 2,  # exact midpoints: ties
+                        [0.0, 1.0, -1.0, 3.3e38]])
+    got = oracle.f64_to_bf16_bits(x)
+    for xi, gi in zip(x, got):
+        ax = abs(xi)
+        j = np.searchsorted(vals, ax)
+        lo, hi = vals[j - 1], vals[min(j, len(vals) - 1)]
+        if ax == hi:
+            want = bits[min(j, len(vals) - 1)]
+        elif ax - lo < hi - ax:
+            want = bits[j - 1]
+        elif ax - lo > hi - ax:
+            want = bits[j]
+        else:  # tie: even significand
+            want = bits[j - 1] if bits[j - 1] % 2 == 0 else bits[j]
+        if xi < 0 or (xi == 0 and math.copysign(1, xi) < 0):
+            want = want | 0x8000
+        assert gi == want, (xi, hex(gi), hex(want))
+
+
+def test_rope_known_values_and_identity():
+    x = np.array([[1.0, 0.0], [0.0, 1.0]])
+    for inter in (False, True):
+        y = oracle.rope_rotate(x, 1, np.array([1.0]), inter)
+        np.testing.assert_allclose(y[0], [math.cos(1), math.sin(1)], rtol=0, atol=1e-15)
+        np.testing.assert_allclose(y[1], [-math.sin(1), math.cos(1)], rtol=0, atol=1e-15)
+    rng = np.random.default_rng(7)
+    qb = rand_bits(rng, (3, 4, 16))
+    inv = (10000.0 ** (-np.arange(8) * 2 / 16)).astype(np.float32)
+    q_rot, _, _ = oracle.kv_write_rope(qb, qb[:, :2], qb[:, :2], np.zeros(3, np.int32), inv,
+                                       False, -np.ones(3, np.int64),
+                                       np.zeros((2, 4, 2, 16), np.uint16),
+                                       np.zeros((2, 4, 2, 16), np.uint16))
+    assert np.array_equal(q_rot, qb)  # position 0 rotates nothing
+
+
+def test_rope_preserves_pair_norms_and_relative_positions():
+    rng = np.random.default_rng(8)
+    D = 64
+    inv = 2.0 ** -np.arange(D // 2, dtype=np.float64)  # exact angles for small positions
+    q, k = rng.standard_normal(D), rng.standard_normal(D)
+    for inter in (False, True):
+        a, b = oracle.rope_pairs(D, inter)
+        y = oracle.rope_rotate(q, 37, inv, inter)
+        np.testing.assert_allclose(y[a] ** 2 + y[b] ** 2, q[a] ** 2 + q[b] ** 2, rtol=1e-13)
+        d1 = oracle.rope_rotate(q, 40, inv, inter) @ oracle.rope_rotate(k, 25, inv, inter)
+        d2 = oracle.rope_rotate(q, 1040, inv, inter) @ oracle.rope_rotate(k, 1025, inv, inter)
+        assert abs(d1 - d2) < 1e-9
+
+
+def test_rope_interleaved_is_permuted_half():
+    rng = np.random.default_rng(9)
+    D = 16
+    x = rng.standard_normal(D)
+    inv = rng.random(D // 2).astype(np.float32)
+    perm = np.concatenate([np.arange(0, D, 2), np.arange(1, D, 2)])  # evens then odds
+    inter = oracle.rope_rotate(x, 123, inv, True)
+    half = oracle.rope_rotate(x[perm], 123, inv, False)
+    np.testing.assert_allclose(inter[perm], half, rtol=0, atol=1e-15)
+
+
+def test_kv_write_rope_stores_rotated_k_and_raw_v():
+    rng = np.random.default_rng(10)
+    T, Hq, Hkv, D, NB, bs = 5, 4, 2, 16, 6, 4
+    q, k, v = rand_bits(rng, (T, Hq, D)), rand_bits(rng, (T, Hkv, D)), rand_bits(rng, (T, Hkv, D))
+    kc, vc = rand_bits(rng, (NB, bs, Hkv, D)), rand_bits(rng, (NB, bs, Hkv, D))
+    pos = np.array([0, 5, 17, 1000, 3], np.int32)
+    slots = np.array([3, -1, 20, 7, 0], np.int64)
+    inv = (500000.0 ** (-np.arange(D // 2) * 2 / D)).astype(np.float32)
+    q_rot, kc2, vc2 = oracle.kv_write_rope(q, k, v, pos, inv, False, slots, kc, vc)
+    flat_k, flat_v = kc2.reshape(NB * bs, Hkv, D), vc2.reshape(NB * bs, Hkv, D)
+    for t in range(T):
+        kr = oracle.f64_to_bf16_bits(oracle.rope_rotate(oracle.bf16_bits_to_f64(k[t]), pos[t],
+                                                          inv, False))
+        if slots[t] >= 0:
+            assert np.array_equal(flat_k[slots[t]], kr)
+            assert np.array_equal(flat_v[slots[t]], v[t])
+    # slot -1: nothing stored, but q is still rotated
+    assert not np.array_equal(q_rot[1], q[1])
+    untouched = np.ones(NB * bs, bool)
+    untouched[[3, 20, 7, 0]] = False
+    assert np.array_equal(flat_k[untouched], kc.reshape(NB * bs, Hkv, D)[untouched])
