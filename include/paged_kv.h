@@ -233,6 +233,21 @@ int paged_prefill_attention(const uint16_t* q, const int32_t* cu_seqlens_q, int6
                             int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                             int64_t num_blocks, float scale, float* out, hipStream_t stream);
 
+/*
+ * paged_prefill_attention_ex -- paged_prefill_attention with the work split chosen by the
+ * caller: row_blocks = number of 16-row blocks of queries each wave carries through one pass
+ * over the keys (1, 2 or 4), or 0 to let the library choose from the sizes and the device
+ * (what paged_prefill_attention does). Results agree across choices up to fp32 rounding of
+ * the same sums. Any other row_blocks value returns PAGEDKV_ERR_SHAPE.
+ */
+int paged_prefill_attention_ex(const uint16_t* q, const int32_t* cu_seqlens_q,
+                               int64_t num_tokens, int32_t max_q_len, const uint16_t* k_cache,
+                               const uint16_t* v_cache, const int32_t* block_tables,
+                               int32_t max_blocks_per_seq, const int32_t* context_lens,
+                               int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                               int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                               float scale, float* out, int32_t row_blocks, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

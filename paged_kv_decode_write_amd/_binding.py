@@ -73,6 +73,9 @@ def load_library() -> ctypes.CDLL:
         lib.paged_prefill_attention.restype = ctypes.c_int
         lib.paged_prefill_attention.argtypes = [P, P, I64, I32, P, P, P, I32, P, I32, I32, I32,
                                                 I32, I32, I64, F32, P, P]
+        lib.paged_prefill_attention_ex.restype = ctypes.c_int
+        lib.paged_prefill_attention_ex.argtypes = [P, P, I64, I32, P, P, P, I32, P, I32, I32,
+                                                   I32, I32, I32, I64, F32, P, I32, P]
         lib.paged_decode_plan.restype = ctypes.c_int
         lib.paged_decode_plan.argtypes = [I32, I32, I32, I32, I32, I32, I32, I32,
                                           ctypes.POINTER(I32), ctypes.POINTER(I32),
@@ -230,13 +233,14 @@ def paged_decode_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
 def paged_prefill_attention(q: torch.Tensor, cu_seqlens_q: torch.Tensor, k_cache: torch.Tensor,
                             v_cache: torch.Tensor, block_tables: torch.Tensor,
                             context_lens: torch.Tensor, scale: float, out: torch.Tensor, *,
-                            max_q_len: Optional[int] = None) -> torch.Tensor:
+                            max_q_len: Optional[int] = None, row_blocks: int = 0) -> torch.Tensor:
     """Multi-query causal attention over the paged cache (prefill / chunked prefill).
 
     Sequence b's query rows are q[cu_seqlens_q[b]:cu_seqlens_q[b+1]], its last Q_b positions;
     row i attends to positions 0 .. context_lens[b] - Q_b + i. q [T, Hq, D] bf16, cu_seqlens_q
     [B+1] int32, out [T, Hq, D] fp32. max_q_len (the largest Q_b) sizes the launch; when
-    omitted it is read from cu_seqlens_q, which synchronises with the device.
+    omitted it is read from cu_seqlens_q, which synchronises with the device. row_blocks
+    (1, 2 or 4; 0 = chosen by the library) is the number of 16-row query blocks per wave.
     """
     _require(k_cache, "k_cache", torch.bfloat16, 4)
     dev = k_cache.device
@@ -257,11 +261,11 @@ def paged_prefill_attention(q: torch.Tensor, cu_seqlens_q: torch.Tensor, k_cache
         max_q_len = int((cu_seqlens_q[1:] - cu_seqlens_q[:-1]).max().item()) if B else 0
     lib = load_library()
     with torch.cuda.device(dev):
-        _check(lib.paged_prefill_attention(
+        _check(lib.paged_prefill_attention_ex(
             q.data_ptr(), cu_seqlens_q.data_ptr(), T, int(max_q_len), k_cache.data_ptr(),
             v_cache.data_ptr(), block_tables.data_ptr(), block_tables.shape[1],
             context_lens.data_ptr(), B, Hq, Hkv, D, bs, NB, float(scale), out.data_ptr(),
-            _stream_handle(dev)))
+            int(row_blocks), _stream_handle(dev)))
     return out
 
 

@@ -415,13 +415,17 @@ int paged_decode_attention(const uint16_t* q, const uint16_t* k_cache,
                                    nullptr, nullptr, stream);
 }
 
-int paged_prefill_attention(const uint16_t* q, const int32_t* cu_seqlens_q, int64_t num_tokens,
-                            int32_t max_q_len, const uint16_t* k_cache, const uint16_t* v_cache,
-                            const int32_t* block_tables, int32_t max_blocks_per_seq,
-                            const int32_t* context_lens, int32_t batch, int32_t num_q_heads,
-                            int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
-                            int64_t num_blocks, float scale, float* out, hipStream_t stream) {
+int paged_prefill_attention_ex(const uint16_t* q, const int32_t* cu_seqlens_q,
+                               int64_t num_tokens, int32_t max_q_len, const uint16_t* k_cache,
+                               const uint16_t* v_cache, const int32_t* block_tables,
+                               int32_t max_blocks_per_seq, const int32_t* context_lens,
+                               int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                               int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                               float scale, float* out, int32_t row_blocks,
+                               hipStream_t stream) {
   g_last_error.clear();
+  if (row_blocks != 0 && row_blocks != 1 && row_blocks != 2 && row_blocks != 4)
+    return fail(PAGEDKV_ERR_SHAPE, "row_blocks must be 0 (auto), 1, 2 or 4, got %d", row_blocks);
   int st = check_decode_sizes(max_blocks_per_seq, batch, num_q_heads, num_kv_heads, head_dim,
                               block_size, num_blocks);
   if (st) return st;
@@ -441,7 +445,12 @@ int paged_prefill_attention(const uint16_t* q, const int32_t* cu_seqlens_q, int6
   if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
       !aligned(block_tables, 4) || !aligned(context_lens, 4) || !aligned(cu_seqlens_q, 4))
     return fail(PAGEDKV_ERR_ALIGN, "q, k_cache, v_cache and out need 16-byte alignment");
-  const int64_t per_group = prefill_tokens_per_group(G);
+  int cus = 0;
+  st = cu_count(&cus);
+  if (st) return st;
+  const int nb = row_blocks > 0 ? row_blocks
+                               : prefill_rows_per_wave(num_tokens, num_kv_heads, head_dim, G, cus);
+  const int64_t per_group = prefill_tokens_per_group(G, nb);
   const int64_t ntiles = ceil_div(max_q_len, per_group);
   if ((int64_t)batch * num_kv_heads * ntiles > INT32_MAX)
     return fail(PAGEDKV_ERR_SHAPE, "too many workgroups (batch * kv heads * query tiles)");
@@ -462,9 +471,22 @@ int paged_prefill_attention(const uint16_t* q, const int32_t* cu_seqlens_q, int6
   a.num_blocks = num_blocks;
   a.scale_log2 = scale * kLog2eHost;
   a.ntiles = (int32_t)ntiles;
+  a.nb = nb;
   hipError_t e = launch_prefill_mfma(a, stream);
   if (e != hipSuccess) return hip_fail(e, "prefill attention launch");
   return PAGEDKV_OK;
+}
+
+int paged_prefill_attention(const uint16_t* q, const int32_t* cu_seqlens_q, int64_t num_tokens,
+                            int32_t max_q_len, const uint16_t* k_cache, const uint16_t* v_cache,
+                            const int32_t* block_tables, int32_t max_blocks_per_seq,
+                            const int32_t* context_lens, int32_t batch, int32_t num_q_heads,
+                            int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                            int64_t num_blocks, float scale, float* out, hipStream_t stream) {
+  return paged_prefill_attention_ex(q, cu_seqlens_q, num_tokens, max_q_len, k_cache, v_cache,
+                                    block_tables, max_blocks_per_seq, context_lens, batch,
+                                    num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                                    scale, out, 0, stream);
 }
 
 }  // extern "C"

@@ -39,6 +39,7 @@ struct PrefillArgs {
   int64_t num_blocks;
   float scale_log2;
   int32_t ntiles;  // query tiles per sequence (ceil(max_q_len / tokens per workgroup))
+  int32_t nb;      // 16-row N blocks per wave: 1, 2 or 4
 };
 
 // Arguments of one rotary-embedding + KV-write launch, already validated.
@@ -70,7 +71,8 @@ hipError_t launch_decode_mfma_hw(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_reduce(const DecodeArgs& a, hipStream_t stream);
 
 bool supported_prefill(int head_dim, int group, int block_size);
-int prefill_tokens_per_group(int group);  // query tokens one workgroup covers
+int prefill_rows_per_wave(int64_t num_tokens, int num_kv_heads, int head_dim, int group, int cus);
+int prefill_tokens_per_group(int group, int nb);  // query tokens one workgroup covers
 hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t stream);
 
 hipError_t launch_kv_write_rope(const RopeArgs& a, hipStream_t stream);

@@ -223,4 +223,108 @@ __device__ __forceinline__ void pair_compute(PairTile<NCH, EPL>& t, WaveState<EP
   }
 }
 
+// Several N blocks of 16 query rows against one loaded pair (multi-query kernels): the K
+// tiles and the transposed V operand are formed once and serve all NB blocks, so one pass
+// over the keys feeds 16*NB rows. Block nb's rows sit at positions row_pos[nb] (per lane);
+// causal masking applies when `active` (uniform) says some key of the pair lies after the
+// earliest row.
+template <int NCH, int EPL, int NB>
+__device__ __forceinline__ void pair_compute_nb(PairTile<NCH, EPL>& t, WaveState<EPL> (&st)[NB],
+                                                const bf16x8 (&qb)[NB][NCH], float sl2, int kg,
+                                                const int (&row_pos)[NB], int key0,
+                                                bool active) {
+  constexpr int BS = 16;
+  const bool tail = t.lastA < BS || t.lastB < BS;
+  if (tail) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      t.vr[i].keep_if(4 * kg + i < t.lastA);  // stale rows may hold NaN bits
+      t.vr[4 + i].keep_if(4 * kg + i < t.lastB);
+    }
+  }
+  bf16x8 vt[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) {
+    uint32_t w[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t x = t.vr[2 * q].word(e / 2), y = t.vr[2 * q + 1].word(e / 2);
+      w[q] = (e & 1) ? pack_hi(x, y) : pack_lo(x, y);
+    }
+    vt[e] = as_bf16x8(make_uint4(w[0], w[1], w[2], w[3]));
+  }
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    floatx4 sA = {0.f, 0.f, 0.f, 0.f}, sB = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ch = 0; ch < NCH; ++ch) {
+      sA = mfma16x16x32(as_bf16x8(t.ka[ch]), qb[nb][ch], sA);
+      sB = mfma16x16x32(as_bf16x8(t.kb[ch]), qb[nb][ch], sB);
+    }
+    float s[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      s[i] = sA[i] * sl2;
+      s[4 + i] = sB[i] * sl2;
+    }
+    if (tail) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        s[i] = 4 * kg + i < t.lastA ? s[i] : kNegInf;
+        s[4 + i] = 4 * kg + i < t.lastB ? s[4 + i] : kNegInf;
+      }
+    }
+    if (active) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        s[i] = key0 + 4 * kg + i <= row_pos[nb] ? s[i] : kNegInf;
+        s[4 + i] = key0 + BS + 4 * kg + i <= row_pos[nb] ? s[4 + i] : kNegInf;
+      }
+    }
+    float mx = s[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) mx = fmaxf(mx, s[i]);
+    mx = fmaxf(mx, shfl_xor(mx, 16));
+    mx = fmaxf(mx, shfl_xor(mx, 32));
+    const float mn = fmaxf(st[nb].m_run, mx);
+    const bool upd = mn > st[nb].m_run + kRescaleSlack;
+    if (__any(upd)) {
+      const float m_new = upd ? mn : st[nb].m_run;
+      const float alpha =
+          upd ? fast_exp2(st[nb].m_run - (m_new == kNegInf ? 0.f : m_new)) : 1.f;
+      st[nb].l_run *= alpha;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) st[nb].acc[e] *= alpha;
+      st[nb].m_run = m_new;
+    }
+    const float mu = st[nb].m_run == kNegInf ? 0.f : st[nb].m_run;
+    float p[8];
+    float psum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      p[i] = fast_exp2(s[i] - mu);
+      psum += p[i];
+    }
+    st[nb].l_run += psum;
+    uint32_t hw[4], lw[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t u0 = __float_as_uint(p[2 * q]), u1 = __float_as_uint(p[2 * q + 1]);
+      hw[q] = pack_hi(u0, u1);
+      const float r0 = p[2 * q] - __uint_as_float(u0 & 0xffff0000u);
+      const float r1 = p[2 * q + 1] - __uint_as_float(u1 & 0xffff0000u);
+      const __bf16 b0 = (__bf16)r0, b1 = (__bf16)r1;
+      lw[q] = (uint32_t)__builtin_bit_cast(uint16_t, b0) |
+              ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
+    }
+    const bf16x8 phi = as_bf16x8(make_uint4(hw[0], hw[1], hw[2], hw[3]));
+    const bf16x8 plo = as_bf16x8(make_uint4(lw[0], lw[1], lw[2], lw[3]));
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      st[nb].acc[e] = mfma16x16x32(vt[e], phi, st[nb].acc[e]);
+      st[nb].acc[e] = mfma16x16x32(vt[e], plo, st[nb].acc[e]);
+    }
+  }
+}
+
 }  // namespace pagedkv

@@ -7,18 +7,21 @@
 // step 4), done over the paged cache as the ragged, padding-free attention over block tables
 // that llm-stack's Roadmap plans, with grouped-query heads.
 //
-// Work decomposition: a workgroup of NW waves takes one KV head g of one sequence and NW*R
-// consecutive query tokens; each wave owns R = 16/G tokens x the G query heads of g, i.e. the
-// 16 query rows of one MFMA N block. The wave streams the key blocks 0..(its last row's
-// position) in pairs, exactly as the decode kernel does (mfma_tiles.h), with a per-lane causal
-// mask on the pairs that reach past its first row, and writes its rows normalised.
+// Work decomposition: a workgroup of NW waves takes one KV head g of one sequence and
+// NW*NB*R consecutive query tokens; each wave owns NB MFMA N blocks of 16 query rows, each
+// block R = 16/G tokens x the G query heads of g. The wave streams the key blocks 0..(its
+// last row's position) in pairs, as the decode kernels do (mfma_tiles.h); each loaded pair
+// (K tiles and the transposed V operand) serves all NB blocks, with a per-lane causal mask on
+// the pairs that reach past the wave's first row. Rows are written normalised.
 #include "launch.h"
 #include "mfma_tiles.h"
 
+#include <mutex>
+
 namespace pagedkv {
 
-template <int D, int NW>
-__global__ void __launch_bounds__(NW * 64)
+template <int D, int NW, int NB, int MINW>
+__global__ void __launch_bounds__(NW * 64, MINW)
 prefill_mfma_kernel(const PrefillArgs a) {
   constexpr int BS = 16;
   constexpr int NCH = D / 32;
@@ -32,48 +35,65 @@ prefill_mfma_kernel(const PrefillArgs a) {
   const int Hq = a.num_q_heads;
   const int Hkv = a.num_kv_heads;
   const int G = Hq / Hkv;
-  const int R = 16 / G;  // query tokens per wave
+  const int R = 16 / G;  // query tokens per N block
+  // Tiles are counted from the end of each sequence and the tile index is the slowest grid
+  // dimension, so every sequence's last tile (the one with the most keys under the causal
+  // mask) is dispatched first and the light leading tiles fill in behind: a
+  // longest-job-first order for the uneven causal work.
   const int unit = blockIdx.x;
-  const int tile = unit % a.ntiles;
-  const int g = (unit / a.ntiles) % Hkv;
-  const int b = unit / (a.ntiles * Hkv);
+  const int bg = unit % (a.batch * Hkv);
+  const int tile = unit / (a.batch * Hkv);
+  const int g = bg % Hkv;
+  const int b = bg / Hkv;
 
   const int q0 = a.cu_seqlens_q[b];
   int Q = a.cu_seqlens_q[b + 1] - q0;
   Q = Q < 0 ? 0 : Q;
-  const int tok_base = (tile * NW + wave) * R;  // first query token (in the sequence) of this wave
-  if (tok_base >= Q) return;                     // no barriers below: waves are independent
+  const int tok_end = Q - (tile * NW + wave) * NB * R;  // one past this wave's last token
+  if (tok_end <= 0) return;                             // no barriers: waves are independent
+  const int tok_base = tok_end - NB * R;                // may be negative: rows < 0 are idle
   int L = a.context_lens[b];
   const int Lmax = a.max_blocks * BS;
   L = L < 0 ? 0 : (L > Lmax ? Lmax : L);
 
-  const int tok = tok_base + n16 / G;
+  // Lane row of N block nb: token tok_base + nb*R + n16/G, head n16 % G.
   const int head = n16 % G;
-  const bool row_ok = n16 < R * G && tok < Q;
-  const int row_pos = row_ok ? L - Q + tok : -1;  // < 0: no key (only when Q > L)
-  const int last_tok = min(tok_base + R, Q) - 1;
-  const int p_min = L - Q + tok_base;
-  const int p_max = L - Q + last_tok;
+  int tok[NB], row_pos[NB];
+  bool row_ok[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    tok[nb] = tok_base + nb * R + n16 / G;
+    row_ok[nb] = n16 < R * G && tok[nb] >= 0;
+    row_pos[nb] = row_ok[nb] ? L - Q + tok[nb] : -1;  // < 0: no key (only when Q > L)
+  }
+  const int first_tok = tok_base > 0 ? tok_base : 0;
+  const int p_min = L - Q + first_tok;
+  const int p_max = L - Q + tok_end - 1;
   const int tok1 = p_max + 1 > 0 ? p_max + 1 : 0;  // keys 0 .. tok1-1 can matter to this wave
   const int blk1 = (tok1 + BS - 1) / BS;
 
-  bf16x8 qb[NCH];
-  {
+  bf16x8 qb[NB][NCH];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
     const uint16_t* qrow =
-        a.q + ((size_t)(q0 + (row_ok ? tok : tok_base)) * Hq + (size_t)g * G + head) * D + 8 * kg;
+        a.q + ((size_t)(q0 + (row_ok[nb] ? tok[nb] : first_tok)) * Hq + (size_t)g * G + head) * D +
+        8 * kg;
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
       uint4 w = make_uint4(0, 0, 0, 0);
-      if (row_ok) w = *reinterpret_cast<const uint4*>(qrow + 32 * c);
-      qb[c] = as_bf16x8(w);
+      if (row_ok[nb]) w = *reinterpret_cast<const uint4*>(qrow + 32 * c);
+      qb[nb][c] = as_bf16x8(w);
     }
   }
 
-  WaveState<EPL> st;
-  st.m_run = kNegInf;
-  st.l_run = 0.f;
+  WaveState<EPL> st[NB];
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) st.acc[e] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int nb = 0; nb < NB; ++nb) {
+    st[nb].m_run = kNegInf;
+    st[nb].l_run = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) st[nb].acc[e] = floatx4{0.f, 0.f, 0.f, 0.f};
+  }
 
   PairCtx<D> ctx;
   ctx.k_cache = a.k_cache;
@@ -108,26 +128,29 @@ prefill_mfma_kernel(const PrefillArgs a) {
         ids[u] = pair_ids<D, 1>(ctx, min(jl + 1, np - 1));
         if (j < np) {
           const int key0 = 2 * BS * j;
-          const CausalMask cm{row_pos, key0, key0 + 2 * BS - 1 > p_min};
-          pair_compute<NCH, EPL, true>(t[u], st, qb, sl2, kg, cm);
+          pair_compute_nb<NCH, EPL, NB>(t[u], st, qb, sl2, kg, row_pos, key0,
+                                        key0 + 2 * BS - 1 > p_min);
         }
       }
     }
   }
 
-  float l_run = st.l_run;
-  l_run += shfl_xor(l_run, 16);
-  l_run += shfl_xor(l_run, 32);
-  if (row_ok) {
-    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-    float* o = a.out + ((size_t)(q0 + tok) * Hq + (size_t)g * G + head) * D;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+  for (int nb = 0; nb < NB; ++nb) {
+    float l_run = st[nb].l_run;
+    l_run += shfl_xor(l_run, 16);
+    l_run += shfl_xor(l_run, 32);
+    if (row_ok[nb]) {
+      const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+      float* o = a.out + ((size_t)(q0 + tok[nb]) * Hq + (size_t)g * G + head) * D;
 #pragma unroll
-      for (int e = 0; e < EPL; e += 4)
-        *reinterpret_cast<float4*>(o + EPL * (4 * kg + i) + e) =
-            make_float4(st.acc[e][i] * inv, st.acc[e + 1][i] * inv, st.acc[e + 2][i] * inv,
-                        st.acc[e + 3][i] * inv);
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int e = 0; e < EPL; e += 4)
+          *reinterpret_cast<float4*>(o + EPL * (4 * kg + i) + e) =
+              make_float4(st[nb].acc[e][i] * inv, st[nb].acc[e + 1][i] * inv,
+                          st[nb].acc[e + 2][i] * inv, st[nb].acc[e + 3][i] * inv);
+    }
   }
 }
 
@@ -135,20 +158,79 @@ bool supported_prefill(int head_dim, int group, int block_size) {
   return block_size == 16 && (head_dim == 64 || head_dim == 128) && group >= 1 && group <= 16;
 }
 
-int prefill_tokens_per_group(int group) { return kWavesPerGroup * (16 / group); }
+int prefill_tokens_per_group(int group, int nb) { return kWavesPerGroup * nb * (16 / group); }
+
+template <int D, int NB>
+static const void* prefill_kernel_ptr() {
+  return reinterpret_cast<const void*>(&prefill_mfma_kernel<D, kWavesPerGroup, NB, NB == 1 ? 2 : 1>);
+}
+
+// Workgroups of the (D, NB) variant one CU holds at once, asked of the runtime once per
+// device (it follows from the variant's register count).
+static int prefill_groups_per_cu(int head_dim, int nb_index) {
+  static std::mutex mu;
+  static int cache[256][2][3];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 256) return 1;
+  const int di = head_dim == 128 ? 1 : 0;
+  std::lock_guard<std::mutex> lock(mu);
+  int& slot = cache[dev][di][nb_index];
+  if (slot == 0) {
+    static const void* const ptrs[2][3] = {
+        {prefill_kernel_ptr<64, 1>(), prefill_kernel_ptr<64, 2>(), prefill_kernel_ptr<64, 4>()},
+        {prefill_kernel_ptr<128, 1>(), prefill_kernel_ptr<128, 2>(), prefill_kernel_ptr<128, 4>()}};
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, ptrs[di][nb_index], kWavesPerGroup * 64,
+                                                     0) != hipSuccess)
+      n = 1;
+    slot = n > 0 ? n : 1;
+  }
+  return slot;
+}
+
+// N blocks of 16 query rows per wave (1, 2 or 4). A larger NB reuses every loaded key/value
+// pair for more rows but holds more registers, so fewer workgroups fit on a CU, and it cuts
+// the query rows into fewer workgroups. The launch takes the largest NB whose workgroups
+// (counted from the total query rows, a lower bound for ragged batches) still fill the
+// resident slots at least twice, so the longest-first order can balance them. NB stops at 2
+// for head_dim 64: there NB = 4 drops the variant from two waves per SIMD to one, which
+// measured slower than the extra reuse gains; at head_dim 128 NB = 2 and 4 both hold one wave
+// per SIMD. A build may pin NB with PAGEDKV_PREFILL_NB.
+int prefill_rows_per_wave(int64_t num_tokens, int num_kv_heads, int head_dim, int group,
+                          int cus) {
+#ifdef PAGEDKV_PREFILL_NB
+  (void)num_tokens; (void)num_kv_heads; (void)head_dim; (void)group; (void)cus;
+  return PAGEDKV_PREFILL_NB;
+#else
+  const int max_index = head_dim >= 128 ? 2 : 1;
+  for (int i = max_index; i > 0; --i) {
+    const int nb = 1 << i;
+    const int64_t per_group = prefill_tokens_per_group(group, nb);
+    const int64_t units = (int64_t)num_kv_heads * ((num_tokens + per_group - 1) / per_group);
+    const int64_t slots = (int64_t)cus * prefill_groups_per_cu(head_dim, i);
+    if (units >= 2 * slots) return nb;
+  }
+  return 1;
+#endif
+}
+
+template <int D>
+static hipError_t launch_prefill_d(const PrefillArgs& a, unsigned grid, hipStream_t stream) {
+  constexpr int NW = kWavesPerGroup;
+  switch (a.nb) {
+    case 1: hipLaunchKernelGGL((prefill_mfma_kernel<D, NW, 1, 2>), dim3(grid), dim3(NW * 64), 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((prefill_mfma_kernel<D, NW, 2, 1>), dim3(grid), dim3(NW * 64), 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((prefill_mfma_kernel<D, NW, 4, 1>), dim3(grid), dim3(NW * 64), 0, stream, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t stream) {
-  constexpr int NW = kWavesPerGroup;
   const long long units = (long long)a.batch * a.num_kv_heads * a.ntiles;
-  if (a.head_dim == 128)
-    hipLaunchKernelGGL((prefill_mfma_kernel<128, NW>), dim3((unsigned)units), dim3(NW * 64), 0,
-                       stream, a);
-  else if (a.head_dim == 64)
-    hipLaunchKernelGGL((prefill_mfma_kernel<64, NW>), dim3((unsigned)units), dim3(NW * 64), 0,
-                       stream, a);
-  else
-    return hipErrorInvalidValue;
-  return hipGetLastError();
+  if (a.head_dim == 128) return launch_prefill_d<128>(a, (unsigned)units, stream);
+  if (a.head_dim == 64) return launch_prefill_d<64>(a, (unsigned)units, stream);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace pagedkv

@@ -92,6 +92,26 @@ def test_attention_argument_errors(lib):
     assert _attn(lib, B=0, q=None, out=None) == OK  # empty batch: no-op
 
 
+def _prefill(lib, q=FAKE, cu=FAKE, T=8, maxq=4, kc=FAKE, vc=FAKE, bt=FAKE, MB=8, lens=FAKE,
+             B=2, Hq=32, Hkv=8, D=128, bs=16, NB=64, out=FAKE, rb=0):
+    return lib.paged_prefill_attention_ex(q, cu, T, maxq, kc, vc, bt, MB, lens, B, Hq, Hkv, D,
+                                          bs, NB, 0.1, out, rb, None)
+
+
+def test_prefill_argument_errors(lib):
+    assert _prefill(lib, rb=3) == ERR_SHAPE
+    assert _prefill(lib, rb=8) == ERR_SHAPE
+    assert _prefill(lib, T=-1) == ERR_SHAPE
+    assert _prefill(lib, maxq=-1) == ERR_SHAPE
+    assert _prefill(lib, Hq=30) == ERR_SHAPE
+    assert _prefill(lib, D=96) == ERR_UNSUPPORTED
+    assert _prefill(lib, Hq=34, Hkv=2) == ERR_UNSUPPORTED  # group of 17 query heads
+    assert _prefill(lib, q=None) == ERR_NULL
+    assert _prefill(lib, cu=None) == ERR_NULL
+    assert _prefill(lib, out=FAKE + 4) == ERR_ALIGN
+    assert _prefill(lib, T=0, q=None, out=None) == OK  # no query rows: no-op
+
+
 def test_workspace_bytes(lib):
     f = lib.paged_decode_workspace_bytes
     assert f(64, 32, 128, 512, 16, -1) == 0              # never split

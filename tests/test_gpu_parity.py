@@ -396,21 +396,22 @@ def prefill_case(name, dev, poison=False, rows=None):
     return _PCASES[key]
 
 
-def run_prefill(d):
+def run_prefill(d, row_blocks=0):
     T, Hq, D = d["q"].shape
     out = torch.full((T, Hq, D), float("nan"), dtype=torch.float32, device=d["q"].device)
     pk.paged_prefill_attention(d["q"], d["cu_seqlens_q"], d["k_cache"], d["v_cache"],
                                d["block_tables"], d["context_lens"], d["scale"], out,
-                               max_q_len=d["max_q_len"])
+                               max_q_len=d["max_q_len"], row_blocks=row_blocks)
     return out
 
 
+@pytest.mark.parametrize("row_blocks", [0, 1, 2, 4])
 @pytest.mark.parametrize("name", ["p2", "p3"])
-def test_prefill_parity(dev, name):
+def test_prefill_parity(dev, name, row_blocks):
     ref, d = prefill_case(name, dev)
-    out = run_prefill(d).cpu().double().numpy()
+    out = run_prefill(d, row_blocks).cpu().double().numpy()
     err = np.abs(out - ref).max()
-    record(f"{name}/prefill", err)
+    record(f"{name}/prefill/rb{row_blocks}", err)
     assert np.isfinite(out).all()
     assert err <= ATOL, err
 
@@ -453,8 +454,9 @@ def test_prefill_single_query_matches_decode(dev, name):
     assert np.abs(out.cpu().double().numpy() - ref).max() <= ATOL
 
 
+@pytest.mark.parametrize("row_blocks", [1, 4])
 @pytest.mark.parametrize("Hq,Hkv,D", [(24, 8, 64), (16, 16, 128), (32, 2, 128)])
-def test_prefill_group_sizes_and_edges(dev, Hq, Hkv, D):
+def test_prefill_group_sizes_and_edges(dev, Hq, Hkv, D, row_blocks):
     """G = 3, 1 and 16 (5, 16 and 1 query tokens per wave), lengths at block edges, single
     tokens, full prefills and chunks, on a poisoned pool."""
     w = wl.PrefillWorkload("edge", num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, block_size=16,
@@ -469,9 +471,9 @@ def test_prefill_group_sizes_and_edges(dev, Hq, Hkv, D):
                                    host["context_lens"], host["scale"])
     d = to_dev(inp, dev)
     run_write(d)
-    out = run_prefill(d).cpu().double().numpy()
+    out = run_prefill(d, row_blocks).cpu().double().numpy()
     err = np.abs(out - ref).max()
-    record(f"edge_prefill/D{D}/G{Hq // Hkv}", err)
+    record(f"edge_prefill/D{D}/G{Hq // Hkv}/rb{row_blocks}", err)
     assert np.isfinite(out).all() and err <= ATOL, err
 
 
