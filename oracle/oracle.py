@@ -48,6 +48,37 @@ def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
 
 
 # ---------------------------------------------------------------------------------------
+# fp16 decoding (IEEE 754 binary16: sign bit, 5 exponent bits with bias 15, 10 fraction
+# bits; exponent field 0 holds zero and the subnormals, 31 holds infinity and NaN). The
+# fp16-input variant of the path reads its q and caches in this format, as the T4 kernel of
+# the mini-vLLM benchmark ran in fp16 ("mini-vLLM" README, benchmark notes on the T4 run).
+# ---------------------------------------------------------------------------------------
+def f16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact decode of binary16 bit patterns (uint16) to float64, from the field layout."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.int64)
+    sign = np.where((b >> 15) & 1, -1.0, 1.0)
+    e = (b >> 10) & 0x1F
+    f = (b & 0x3FF).astype(np.float64)
+    normal = np.ldexp(1.0 + f / 1024.0, e - 15)
+    subnormal = np.ldexp(f / 1024.0, -14)
+    val = np.where(e == 0, subnormal, normal)
+    val = np.where(e == 31, np.where(f == 0, np.inf, np.nan), val)
+    return sign * val
+
+
+INPUT_DTYPES = ("bf16", "f16")
+
+
+def decode_bits(bits: np.ndarray, dtype: str = "bf16") -> np.ndarray:
+    """Exact float64 values of 16-bit input bit patterns of the given format."""
+    if dtype == "bf16":
+        return bf16_bits_to_f64(bits)
+    if dtype == "f16":
+        return f16_bits_to_f64(bits)
+    raise ValueError(f"unknown input format {dtype!r} (expected one of {INPUT_DTYPES})")
+
+
+# ---------------------------------------------------------------------------------------
 # KV write (slot-mapping scatter), on raw bit patterns: no float conversion, so every
 # payload, NaN included, lands unchanged.
 # ---------------------------------------------------------------------------------------
@@ -84,7 +115,8 @@ def kv_head_for(h: int, num_q_heads: int, num_kv_heads: int) -> int:
     return h // (num_q_heads // num_kv_heads)
 
 
-def gather_dense(cache_bits: np.ndarray, table_row: np.ndarray, length: int) -> np.ndarray:
+def gather_dense(cache_bits: np.ndarray, table_row: np.ndarray, length: int,
+                 dtype: str = "bf16") -> np.ndarray:
     """Logical positions 0..length-1 of one sequence as a dense float64 [length, Hkv, D]
     array, reading physical block table_row[j] for logical block j."""
     NB, bs, Hkv, D = cache_bits.shape
@@ -94,7 +126,7 @@ def gather_dense(cache_bits: np.ndarray, table_row: np.ndarray, length: int) -> 
         raise ValueError("context needs more blocks than the table holds")
     if n and (ids.min() < 0 or ids.max() >= NB):
         raise ValueError("block id outside the pool")
-    dense = bf16_bits_to_f64(cache_bits[ids]).reshape(n * bs, Hkv, D)
+    dense = decode_bits(cache_bits[ids], dtype).reshape(n * bs, Hkv, D)
     return dense[:length]
 
 
@@ -113,12 +145,13 @@ def effective_scale(scale: float) -> float:
 
 def decode_attention(q_bits: np.ndarray, k_cache_bits: np.ndarray, v_cache_bits: np.ndarray,
                      block_tables: np.ndarray, context_lens: np.ndarray, scale: float,
-                     rows: Optional[Iterable[Tuple[int, int]]] = None) -> np.ndarray:
+                     rows: Optional[Iterable[Tuple[int, int]]] = None,
+                     dtype: str = "bf16") -> np.ndarray:
     """Float64 output [B, Hq, D] of one-token decode attention over the paged cache.
 
     q_bits uint16 [B, Hq, D]; caches uint16 [NB, bs, Hkv, D]; block_tables int [B, MB];
-    context_lens int [B]. With ``rows`` (an iterable of (b, h) pairs) only those output rows
-    are computed; the others stay zero.
+    context_lens int [B]; dtype: format of q and the caches ("bf16" or "f16"). With ``rows``
+    (an iterable of (b, h) pairs) only those output rows are computed; the others stay zero.
     """
     B, Hq, D = q_bits.shape
     Hkv = k_cache_bits.shape[2]
@@ -137,9 +170,9 @@ def decode_attention(q_bits: np.ndarray, k_cache_bits: np.ndarray, v_cache_bits:
         L = int(context_lens[b])
         if L == 0:
             continue
-        K = gather_dense(k_cache_bits, block_tables[b], L)
-        V = gather_dense(v_cache_bits, block_tables[b], L)
-        qd = bf16_bits_to_f64(q_bits[b])
+        K = gather_dense(k_cache_bits, block_tables[b], L, dtype)
+        V = gather_dense(v_cache_bits, block_tables[b], L, dtype)
+        qd = decode_bits(q_bits[b], dtype)
         for h in heads:
             g = kv_head_for(h, Hq, Hkv)
             out[b, h] = attend_one(qd[h], K[:, g, :], V[:, g, :], scale_eff)
@@ -149,7 +182,8 @@ def decode_attention(q_bits: np.ndarray, k_cache_bits: np.ndarray, v_cache_bits:
 def prefill_attention(q_bits: np.ndarray, cu_seqlens_q: np.ndarray, k_cache_bits: np.ndarray,
                       v_cache_bits: np.ndarray, block_tables: np.ndarray,
                       context_lens: np.ndarray, scale: float,
-                      rows: Optional[Iterable[Tuple[int, int]]] = None) -> np.ndarray:
+                      rows: Optional[Iterable[Tuple[int, int]]] = None,
+                      dtype: str = "bf16") -> np.ndarray:
     """Float64 output [T, Hq, D] of multi-query causal attention over the paged cache.
 
     Sequence b owns query rows cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 (Q_b of them), which are
@@ -160,7 +194,8 @@ def prefill_attention(q_bits: np.ndarray, cu_seqlens_q: np.ndarray, k_cache_bits
     Tensor Parallelism", Features and scope / Implemented, How it works step 4) with keys
     gathered through the block table, the ragged attention over block tables that llm-stack's
     Roadmap plans. Its keys must already be in the cache (write them first). With ``rows``
-    (an iterable of (query row, head) pairs) only those outputs are computed.
+    (an iterable of (query row, head) pairs) only those outputs are computed. dtype is the
+    format of q and the caches ("bf16" or "f16").
     """
     T, Hq, D = q_bits.shape
     B = len(context_lens)
@@ -186,9 +221,9 @@ def prefill_attention(q_bits: np.ndarray, cu_seqlens_q: np.ndarray, k_cache_bits
             raise ValueError(f"sequence {b}: {Q} queries but only {L} cached positions")
         if wanted is not None and not any(cu[b] <= r < cu[b + 1] for r in wanted):
             continue
-        K = gather_dense(k_cache_bits, block_tables[b], L)
-        V = gather_dense(v_cache_bits, block_tables[b], L)
-        qd = bf16_bits_to_f64(q_bits[cu[b]:cu[b + 1]])
+        K = gather_dense(k_cache_bits, block_tables[b], L, dtype)
+        V = gather_dense(v_cache_bits, block_tables[b], L, dtype)
+        qd = decode_bits(q_bits[cu[b]:cu[b + 1]], dtype)
         for i in range(Q):
             p = L - Q + i
             heads = range(Hq) if wanted is None else wanted.get(int(cu[b]) + i, [])
@@ -276,6 +311,36 @@ def f64_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     out[ax >= np.ldexp(1.0, 128) - np.ldexp(1.0, 119)] = 0x7F80  # rounds to infinity
     out[np.isnan(x)] = 0x7FC0
     return (out | sign).astype(np.uint16)
+
+
+def f64_to_f16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float64 values to binary16 (round-to-nearest-even) bit patterns: 11 significant
+    bits for normals (exponents -14..15), spacing 2^-24 below 2^-14, overflow to infinity
+    from 65520 (the midpoint above 65504, whose tie goes to the even, infinite, side)."""
+    x = np.asarray(x, dtype=np.float64)
+    neg = np.signbit(x)
+    ax = np.abs(x)
+    m, e = np.frexp(np.where(np.isfinite(ax), ax, 0.0))  # ax = m 2^e, m in [0.5, 1)
+    e_eff = np.maximum(e - 1, -14)
+    ulp = np.ldexp(1.0, (e_eff - 10).astype(np.int64))
+    val = np.rint(ax / ulp) * ulp  # exact scaling, round half to even; val is an fp16 value
+    with np.errstate(over="ignore", invalid="ignore"):
+        out = np.where(val >= 65536.0, np.inf, val).astype(np.float16).view(np.uint16)
+    out = np.where(np.isinf(ax), np.uint16(0x7C00), out)
+    out = np.where(np.isnan(x), np.uint16(0x7E00), out).astype(np.uint16)
+    return np.where(neg & ~np.isnan(x), out | np.uint16(0x8000), out).astype(np.uint16)
+
+
+def round_output(x: np.ndarray, out_dtype: str) -> np.ndarray:
+    """Float64 values as the output format stores them (float64 again): "f32" rounds to fp32,
+    "bf16" and "f16" to those formats, all round-to-nearest-even."""
+    if out_dtype == "f32":
+        return np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)
+    if out_dtype == "bf16":
+        return bf16_bits_to_f64(f64_to_bf16_bits(x))
+    if out_dtype == "f16":
+        return f16_bits_to_f64(f64_to_f16_bits(x))
+    raise ValueError(f"unknown output format {out_dtype!r}")
 
 
 def kv_write_rope(q_bits: np.ndarray, k_bits: np.ndarray, v_bits: np.ndarray,

@@ -86,15 +86,20 @@ WORKLOADS: Dict[str, Workload] = {
 }
 
 
-def _bf16_normal(shape, gen: torch.Generator, device, std: float = 1.0) -> torch.Tensor:
+INPUT_DTYPES = {"bf16": torch.bfloat16, "f16": torch.float16}
+
+
+def _bf16_normal(shape, gen: torch.Generator, device, std: float = 1.0,
+                 dtype: str = "bf16") -> torch.Tensor:
+    """Normal draws in fp32, rounded (nearest-even) to the 16-bit input format."""
     x = torch.randn(shape, generator=gen, device=device, dtype=torch.float32)
     if std != 1.0:
         x.mul_(std)
-    return x.to(torch.bfloat16)  # round-to-nearest-even
+    return x.to(INPUT_DTYPES[dtype])
 
 
 def make_inputs(w: Workload, device: str = "cpu", poison: bool = False,
-                lengths: Optional[list] = None) -> Dict[str, object]:
+                lengths: Optional[list] = None, dtype: str = "bf16") -> Dict[str, object]:
     """Draw one decode step's inputs for workload ``w``.
 
     device: where the random numbers are drawn ("cpu" gives the canonical inputs; "cuda"
@@ -104,6 +109,8 @@ def make_inputs(w: Workload, device: str = "cpu", poison: bool = False,
             and the stale slots after position L_b - 1 in a sequence's last block) with a
             quiet-NaN bit pattern.
     lengths: optional explicit per-sequence context lengths (overrides the workload's).
+    dtype:  format of q, the pools and the new rows: "bf16" or "f16" (the same fp32 draws,
+            rounded to that format).
     """
     gen = torch.Generator(device=device)
     gen.manual_seed(w.seed)
@@ -129,11 +136,11 @@ def make_inputs(w: Workload, device: str = "cpu", poison: bool = False,
         tables[b, :n] = perm[pos:pos + n].to(torch.int32)
         pos += n
 
-    q = _bf16_normal((B, Hq, D), gen, device, w.q_std)
-    k_cache = _bf16_normal((NB, bs, Hkv, D), gen, device)
-    v_cache = _bf16_normal((NB, bs, Hkv, D), gen, device)
-    k_new = _bf16_normal((B, Hkv, D), gen, device)
-    v_new = _bf16_normal((B, Hkv, D), gen, device)
+    q = _bf16_normal((B, Hq, D), gen, device, w.q_std, dtype)
+    k_cache = _bf16_normal((NB, bs, Hkv, D), gen, device, dtype=dtype)
+    v_cache = _bf16_normal((NB, bs, Hkv, D), gen, device, dtype=dtype)
+    k_new = _bf16_normal((B, Hkv, D), gen, device, dtype=dtype)
+    v_new = _bf16_normal((B, Hkv, D), gen, device, dtype=dtype)
 
     slots = torch.empty(B, dtype=torch.int64)
     for b, L in enumerate(ctx.tolist()):
@@ -157,6 +164,7 @@ def make_inputs(w: Workload, device: str = "cpu", poison: bool = False,
         "v_new": v_new,
         "slot_mapping": slots.to(dev),
         "scale": w.scale,
+        "dtype": dtype,
     }
 
 
@@ -182,13 +190,13 @@ def poison_unread_slots(k_cache: torch.Tensor, v_cache: torch.Tensor, tables: to
 
 
 def to_bits(t: torch.Tensor) -> np.ndarray:
-    """bf16 tensor -> numpy uint16 array of its raw bit patterns (host copy)."""
+    """16-bit float tensor -> numpy uint16 array of its raw bit patterns (host copy)."""
     return t.detach().to("cpu").contiguous().view(torch.int16).numpy().view(np.uint16)
 
 
 def to_host_numpy(inp: Dict[str, object]) -> Dict[str, object]:
     """Host numpy views of an input dict: bf16 as uint16 bits, indices as integers."""
-    out = {"workload": inp["workload"], "scale": inp["scale"]}
+    out = {"workload": inp["workload"], "scale": inp["scale"], "dtype": inp.get("dtype", "bf16")}
     for key in ("q", "k_cache", "v_cache", "k_new", "v_new"):
         out[key] = to_bits(inp[key])
     for key in ("block_tables", "context_lens", "slot_mapping", "cu_seqlens_q"):
@@ -265,8 +273,8 @@ PREFILL_WORKLOADS: Dict[str, PrefillWorkload] = {
 }
 
 
-def make_prefill_inputs(w: PrefillWorkload, device: str = "cpu", poison: bool = False
-                        ) -> Dict[str, object]:
+def make_prefill_inputs(w: PrefillWorkload, device: str = "cpu", poison: bool = False,
+                        dtype: str = "bf16") -> Dict[str, object]:
     gen = torch.Generator(device=device)
     gen.manual_seed(w.seed)
     B, bs, NB, MB = w.batch, w.block_size, w.num_blocks, w.max_blocks
@@ -285,11 +293,11 @@ def make_prefill_inputs(w: PrefillWorkload, device: str = "cpu", poison: bool = 
         tables[b, :n] = perm[pos:pos + n].to(torch.int32)
         pos += n
     T = int(ql.sum())
-    q = _bf16_normal((T, Hq, D), gen, device, w.q_std)
-    k_cache = _bf16_normal((NB, bs, Hkv, D), gen, device)
-    v_cache = _bf16_normal((NB, bs, Hkv, D), gen, device)
-    k_new = _bf16_normal((T, Hkv, D), gen, device)
-    v_new = _bf16_normal((T, Hkv, D), gen, device)
+    q = _bf16_normal((T, Hq, D), gen, device, w.q_std, dtype)
+    k_cache = _bf16_normal((NB, bs, Hkv, D), gen, device, dtype=dtype)
+    v_cache = _bf16_normal((NB, bs, Hkv, D), gen, device, dtype=dtype)
+    k_new = _bf16_normal((T, Hkv, D), gen, device, dtype=dtype)
+    v_new = _bf16_normal((T, Hkv, D), gen, device, dtype=dtype)
     cu = torch.zeros(B + 1, dtype=torch.int32)
     cu[1:] = torch.cumsum(ql, 0)
     slots = torch.empty(T, dtype=torch.int64)
@@ -304,7 +312,8 @@ def make_prefill_inputs(w: PrefillWorkload, device: str = "cpu", poison: bool = 
     return {"workload": w, "q": q, "k_cache": k_cache, "v_cache": v_cache,
             "block_tables": tables.to(dev), "context_lens": ctx.to(dev),
             "cu_seqlens_q": cu.to(dev), "k_new": k_new, "v_new": v_new,
-            "slot_mapping": slots.to(dev), "scale": w.scale, "max_q_len": int(ql.max()) if B else 0}
+            "slot_mapping": slots.to(dev), "scale": w.scale,
+            "max_q_len": int(ql.max()) if B else 0, "dtype": dtype}
 
 
 def prefill_algorithmic(w: PrefillWorkload) -> Dict[str, int]:

@@ -377,13 +377,13 @@ _REAL_ATTEND = orc.attend_one
 
 
 def _wrap_gather(tf):
-    def g(cache_bits, row, L):
+    def g(cache_bits, row, L, *fmt):
         cb, r, L2 = tf(cache_bits, row, L)
         NB, bs = cb.shape[:2]
         n = (L2 + bs - 1) // bs
         r = np.where(np.asarray(r[:n]) < 0, 0, np.asarray(r[:n]))  # keep the mutant runnable
         full = np.concatenate([r, np.zeros(max(0, n - len(r)), dtype=r.dtype)])
-        return _REAL_GATHER(cb, full, L2)
+        return _REAL_GATHER(cb, full, L2, *fmt)
     return g
 
 
@@ -733,3 +733,161 @@ def test_kv_write_rope_stores_rotated_k_and_raw_v():
     untouched = np.ones(NB * bs, bool)
     untouched[[3, 20, 7, 0]] = False
     assert np.array_equal(flat_k[untouched], kc.reshape(NB * bs, Hkv, D)[untouched])
+
+
+# --------------------------------------------------- fp16 inputs and 16-bit output formats
+F16_KNOWN = {0x0000: 0.0, 0x3C00: 1.0, 0xC000: -2.0, 0x3800: 0.5, 0x3555: 1365 / 4096,
+             0x7BFF: 65504.0, 0x0400: 2.0 ** -14, 0x03FF: 1023 * 2.0 ** -24,
+             0x0001: 2.0 ** -24, 0x8001: -(2.0 ** -24), 0x7C00: math.inf, 0xFC00: -math.inf}
+
+
+def test_f16_decode_closed_forms():
+    bits = np.array(list(F16_KNOWN), dtype=np.uint16)
+    got = oracle.f16_bits_to_f64(bits)
+    assert got.tolist() == list(F16_KNOWN.values())
+    neg0 = oracle.f16_bits_to_f64(np.array([0x8000], np.uint16))[0]
+    assert neg0 == 0.0 and math.copysign(1.0, neg0) < 0
+    assert np.isnan(oracle.f16_bits_to_f64(np.array([0x7E00, 0x7C01, 0xFE00, 0xFFFF],
+                                                    np.uint16))).all()
+
+
+def test_f16_decode_matches_library_on_every_pattern():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    lib = bits.view(np.float16).astype(np.float64)
+    assert np.array_equal(oracle.f16_bits_to_f64(bits), lib, equal_nan=True)
+
+
+def test_decode_bits_dispatches_on_format():
+    assert oracle.decode_bits(np.array([0x3C00], np.uint16), "f16")[0] == 1.0
+    assert oracle.decode_bits(np.array([0x3F80], np.uint16), "bf16")[0] == 1.0
+    with pytest.raises(ValueError):
+        oracle.decode_bits(np.array([0], np.uint16), "fp8")
+
+
+def _all_finite_f16():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    vals = oracle.f16_bits_to_f64(bits)
+    keep = np.isfinite(vals) & (vals >= 0) & ~((vals == 0) & (bits == 0x8000))
+    order = np.argsort(vals[keep], kind="stable")
+    return vals[keep][order], bits[keep][order]
+
+
+def test_f64_to_f16_rounding_against_neighbour_search():
+    vals, bits = _all_finite_f16()
+    rng = np.random.default_rng(6)
+    x = np.concatenate([rng.standard_normal(20000) * 30, rng.standard_normal(2000) * 1e-6,
+                        (vals[1:-1] + vals[2:]) / 2,  # exact midpoints: ties
+                        -(vals[1:200] + vals[2:201]) / 2, [0.0, 1.0, -1.0, 65504.0]])
+    got = oracle.f64_to_f16_bits(x)
+    for xi, gi in zip(x, got):
+        ax = abs(xi)
+        j = np.searchsorted(vals, ax)
+        lo, hi = vals[j - 1], vals[min(j, len(vals) - 1)]
+        if ax == hi:
+            want = bits[min(j, len(vals) - 1)]
+        elif ax - lo < hi - ax:
+            want = bits[j - 1]
+        elif ax - lo > hi - ax:
+            want = bits[j]
+        else:  # tie: even significand
+            want = bits[j - 1] if bits[j - 1] % 2 == 0 else bits[j]
+        if xi < 0:
+            want = want | 0x8000
+        assert gi == want, (xi, hex(gi), hex(want))
+
+
+def test_f64_to_f16_overflow_and_specials():
+    x = np.array([65519.99, 65520.0, 1e6, -1e6, math.inf, 2.0 ** -25, 1.5 * 2.0 ** -25, -0.0])
+    assert [int(b) for b in oracle.f64_to_f16_bits(x)] == [0x7BFF, 0x7C00, 0x7C00, 0xFC00,
+                                                           0x7C00, 0x0000, 0x0001, 0x8000]
+    n = oracle.f64_to_f16_bits(np.array([math.nan]))[0]
+    assert (n & 0x7C00) == 0x7C00 and (n & 0x3FF) != 0
+
+
+def test_round_output_closed_forms():
+    one = np.array([1.0 + 2.0 ** -30, 1.0 + 2.0 ** -24, 1.0 + 3 * 2.0 ** -24])
+    assert oracle.round_output(one, "f32").tolist() == [1.0, 1.0, 1.0 + 2.0 ** -22]
+    assert oracle.round_output(np.array([1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8]),
+                               "bf16").tolist() == [1.0, 1.0 + 2.0 ** -6]
+    assert oracle.round_output(np.array([1.0 + 2.0 ** -11, 1.0 + 3 * 2.0 ** -11]),
+                               "f16").tolist() == [1.0, 1.0 + 2.0 ** -9]
+    with pytest.raises(ValueError):
+        oracle.round_output(np.zeros(1), "f64")
+
+
+def _shared_value_case(seed, B=3, Hq=8, Hkv=2, D=16, bs=4):
+    """Inputs whose values (multiples of 1/8 up to 3) are exact in bf16 and in fp16, encoded
+    both ways, in the same paged layout."""
+    rng = np.random.default_rng(seed)
+    lengths = [int(x) for x in rng.integers(1, 30, size=B)]
+    MB = max((L + bs - 1) // bs for L in lengths)
+    NB = sum((L + bs - 1) // bs for L in lengths) + 3
+    q = rng.integers(-24, 25, size=(B, Hq, D)) / 8.0
+    dk = [rng.integers(-24, 25, size=(L, Hkv, D)) / 8.0 for L in lengths]
+    dv = [rng.integers(-24, 25, size=(L, Hkv, D)) / 8.0 for L in lengths]
+    enc = {"bf16": lambda a: f32_to_bf16_bits(np.asarray(a, np.float32)),
+           "f16": lambda a: np.asarray(a, np.float16).view(np.uint16)}
+    out = {}
+    for name, e in enc.items():
+        kc, vc, tables = scatter_to_pool(np.random.default_rng(seed + 1), [e(x) for x in dk],
+                                         [e(x) for x in dv], lengths, NB, bs, MB)
+        out[name] = (e(q), kc, vc, tables)
+    return out, np.array(lengths, np.int32), q, dk, dv
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_f16_attention_equals_bf16_on_values_exact_in_both(seed):
+    enc, lens, _, _, _ = _shared_value_case(seed)
+    res = {}
+    for name, (q, kc, vc, tables) in enc.items():
+        res[name] = oracle.decode_attention(q, kc, vc, tables, lens, 0.25, dtype=name)
+    assert np.array_equal(res["bf16"], res["f16"])
+    # the format argument matters: fp16 bits read as bf16 are other numbers entirely
+    q, kc, vc, tables = enc["f16"]
+    wrong = oracle.decode_attention(q, kc, vc, tables, lens, 0.25, dtype="bf16")
+    assert not np.allclose(np.nan_to_num(wrong), res["f16"], atol=1e-3)
+
+
+def test_f16_attention_equals_sdpa_on_library_decoded_values():
+    rng = np.random.default_rng(12)
+    B, Hq, Hkv, D, bs = 3, 6, 2, 16, 4
+    lengths = [5, 1, 23]
+    f16 = lambda a: np.asarray(a, np.float16).view(np.uint16)
+    q = f16(rng.standard_normal((B, Hq, D)) * 2)
+    dk = [f16(rng.standard_normal((L, Hkv, D))) for L in lengths]
+    dv = [f16(rng.standard_normal((L, Hkv, D))) for L in lengths]
+    MB = max((L + bs - 1) // bs for L in lengths)
+    kc, vc, tables = scatter_to_pool(rng, dk, dv, lengths, 20, bs, MB)
+    got = oracle.decode_attention(q, kc, vc, tables, np.array(lengths), 0.3, dtype="f16")
+    dec = lambda b: torch.from_numpy(b.view(np.float16).astype(np.float64))
+    for b, L in enumerate(lengths):
+        o = F.scaled_dot_product_attention(dec(q[b])[None, :, None, :],
+                                           dec(dk[b]).permute(1, 0, 2)[None],
+                                           dec(dv[b]).permute(1, 0, 2)[None],
+                                           scale=float(np.float32(0.3)), enable_gqa=True)
+        np.testing.assert_allclose(got[b], o[0, :, 0, :].numpy(), rtol=0, atol=1e-12)
+
+
+def test_f16_prefill_equals_bf16_on_values_exact_in_both():
+    enc, lens, _, _, _ = _shared_value_case(4, B=2)
+    qlens = [min(int(L), 3) for L in lens]
+    cu = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
+    res = {}
+    for name, (_, kc, vc, tables) in enc.items():
+        rng = np.random.default_rng(9)
+        qv = rng.integers(-24, 25, size=(int(cu[-1]), 8, 16)) / 8.0
+        qb = (f32_to_bf16_bits(qv.astype(np.float32)) if name == "bf16"
+              else qv.astype(np.float16).view(np.uint16))
+        res[name] = oracle.prefill_attention(qb, cu, kc, vc, tables, lens, 0.25, dtype=name)
+    assert np.array_equal(res["bf16"], res["f16"])
+
+
+def test_workload_f16_inputs_are_the_same_draws_rounded():
+    w = wl.WORKLOADS["c1"]
+    a = wl.make_inputs(w, dtype="bf16")
+    b = wl.make_inputs(w, dtype="f16")
+    assert b["q"].dtype == torch.float16 and b["k_cache"].dtype == torch.float16
+    assert torch.equal(a["block_tables"], b["block_tables"])
+    assert torch.equal(a["slot_mapping"], b["slot_mapping"])
+    # both are roundings of the same fp32 draws: they agree to bf16 precision
+    assert (a["k_cache"].float() - b["k_cache"].float()).abs().max() <= 2.0 ** -7 * 4
