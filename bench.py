@@ -31,6 +31,7 @@ sys.path.insert(0, HERE)
 METRIC = "paged decode attention µs/call and achieved HBM GB/s (% of MI355X peak)"
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, vendor figure
 TRAFFIC_FILE = os.path.join(HERE, "profiles", "decode_traffic.json")
+OUT_TORCH = {"f32": "float32", "bf16": "bfloat16", "f16": "float16"}  # torch dtype names
 
 
 def parse_args():
@@ -42,6 +43,10 @@ def parse_args():
     p.add_argument("--kernel", default="auto", choices=["auto", "valu", "mfma", "mfma_hw"])
     p.add_argument("--partition", type=int, default=0,
                    help="tokens per partition: 0 automatic, -1 never split")
+    p.add_argument("--in-dtype", default="bf16", choices=["bf16", "f16"],
+                   help="format of q and the K/V pools")
+    p.add_argument("--out-dtype", default="f32", choices=["f32", "bf16", "f16"],
+                   help="attention output format: f32 or the input format")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="CPU work budget of the oracle baseline sample")
@@ -158,9 +163,9 @@ def bench_prefill(args, torch, pk, wl):
     """Multi-query causal workloads: step = write the chunk's K/V + causal attention."""
     dev = torch.device("cuda:0")
     w = wl.PREFILL_WORKLOADS[args.workload]
-    d = wl.make_prefill_inputs(w, device="cuda")
+    d = wl.make_prefill_inputs(w, device="cuda", dtype=args.in_dtype)
     T, Hq, D = d["q"].shape
-    out = torch.empty(T, Hq, D, dtype=torch.float32, device=dev)
+    out = torch.empty(T, Hq, D, dtype=getattr(torch, OUT_TORCH[args.out_dtype]), device=dev)
     alg = wl.prefill_algorithmic(w)
     write_bytes = T * w.num_kv_heads * w.head_dim * 2 * 2 * 2
 
@@ -193,9 +198,10 @@ def bench_prefill(args, torch, pk, wl):
         "unit": "TFLOP/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16",
-        "data": "synthetic (seeded N(0,1) bf16), resident in HBM",
+        "vs_baseline": None, "dtype": args.in_dtype,
+        "data": f"synthetic (seeded N(0,1) {args.in_dtype}), resident in HBM",
         "config": {"workload": w.description, "kernel": "prefill_mfma",
+                   "formats": f"{args.in_dtype} in, {args.out_dtype} out",
                    "us_per_call": round(mean * 1e3, 2),
                    "GBps": round(alg["bytes"] / (mean * 1e-3) / 1e9, 1),
                    "step": "KV write of the chunk + multi-query causal attention"},
@@ -224,6 +230,10 @@ def main():
 
     pk.load_library()
     dev = torch.device("cuda:0")
+    if args.out_dtype not in ("f32", args.in_dtype):
+        print(f"output format {args.out_dtype} is not built for {args.in_dtype} inputs "
+              "(fp32 or the input format)", file=sys.stderr)
+        sys.exit(2)
     if args.workload in wl.PREFILL_WORKLOADS:
         line = bench_prefill(args, torch, pk, wl)
         out = json.dumps(line)
@@ -236,12 +246,14 @@ def main():
     subs = []
     for name in names:
         w = wl.WORKLOADS[name]
-        d = wl.make_inputs(w, device="cuda")
-        d["out"] = torch.empty(w.batch, w.num_q_heads, w.head_dim, dtype=torch.float32, device=dev)
+        d = wl.make_inputs(w, device="cuda", dtype=args.in_dtype)
+        d["out"] = torch.empty(w.batch, w.num_q_heads, w.head_dim,
+                               dtype=getattr(torch, OUT_TORCH[args.out_dtype]), device=dev)
         need = pk.decode_workspace_bytes(w.batch, w.num_q_heads, w.head_dim, w.max_blocks,
                                          w.block_size, args.partition)
         d["ws"] = pk.new_workspace(need, dev)
-        d["bytes"] = wl.algorithmic_bytes(w, d["context_lens"].cpu().tolist())
+        d["bytes"] = wl.algorithmic_bytes(w, d["context_lens"].cpu().tolist(),
+                                          out_bytes=4 if args.out_dtype == "f32" else 2)
         d["plan"] = pk.decode_plan(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim,
                                    w.max_blocks, w.block_size, args.partition, args.kernel,
                                    with_kernel=True)
@@ -352,7 +364,8 @@ def main():
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
         rec = t.get(args.workload, {})
-        if rec.get("kernel_source") == kernel_source_hash(kernel) and rec.get("kernel") == kernel:
+        if (rec.get("kernel_source") == kernel_source_hash(kernel) and rec.get("kernel") == kernel
+                and (args.in_dtype, args.out_dtype) == ("bf16", "f32")):
             traffic = rec.get("bytes_per_launch")
 
     line = {
@@ -366,12 +379,14 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if kernel.startswith("mfma") else "fp32",
-        "data": "synthetic (seeded N(0,1) bf16 K/V pools, shuffled block tables), resident in HBM",
+        "dtype": args.in_dtype if kernel.startswith("mfma") else "fp32",
+        "data": (f"synthetic (seeded N(0,1) {args.in_dtype} K/V pools, shuffled block tables), "
+                 "resident in HBM"),
         "config": {
             "workload": "+".join(d["workload"].description for d in subs),
             "kernel": kernel,
             "partition_tokens": args.partition,
+            "formats": f"{args.in_dtype} in, {args.out_dtype} out",
             "us_per_call": {p["workload"]: p["attn_kernel_us_mean"] for p in per},
             "pct_of_peak": {p["workload"]: p["pct_of_peak"] for p in per},
             "kernels": {p["workload"]: p["kernel"] for p in per},
@@ -390,7 +405,7 @@ def main():
     }
     if graph_ms is not None:
         line["graph_ms_per_step"] = round(graph_ms, 4)
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and (args.in_dtype, args.out_dtype) == ("bf16", "f32"):
         line["cpu_baseline"] = cpu_baseline(subs[0], args.cpu_seconds)
     out = json.dumps(line)
     print(out, flush=True)

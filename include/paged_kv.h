@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define PAGED_KV_ABI_VERSION 1
+#define PAGED_KV_ABI_VERSION 2
 
 typedef enum {
   PAGEDKV_OK = 0,
@@ -56,6 +56,20 @@ typedef enum {
   PAGEDKV_ERR_HIP = 5,         /* a HIP runtime call failed; see paged_kv_last_error() */
   PAGEDKV_ERR_ALIGN = 6        /* an array pointer is not 16-byte aligned */
 } pagedkv_status;
+
+/*
+ * Element formats of the attention inputs and outputs. q and both caches share one 16-bit
+ * format: bf16 (8 exponent bits, 7 fraction bits) or fp16 (IEEE binary16: 5 and 10), the two
+ * half-width formats the pages weigh against each other ("tiny-vLLM" blog, The Precision
+ * Trade-off: BF16; the mini-vLLM README's Results were measured with an fp16 model). The
+ * output is fp32, or the input format itself, rounded to nearest even, for a consumer that
+ * takes the attention output as the next matrix product's 16-bit operand.
+ */
+typedef enum {
+  PAGEDKV_DTYPE_BF16 = 0,
+  PAGEDKV_DTYPE_F16 = 1,
+  PAGEDKV_DTYPE_F32 = 2
+} pagedkv_dtype;
 
 /* Returns PAGED_KV_ABI_VERSION of the built library. */
 int paged_kv_abi_version(void);
@@ -73,12 +87,13 @@ const char* paged_kv_last_error(void);
  * How it works, step 3; the mini-vLLM README's per-sequence K/V write loop into the block
  * pool, done here as one scatter).
  *
- *   k, v           bf16 [num_tokens][num_kv_heads][head_dim]           (read)
+ *   k, v           16-bit elements [num_tokens][num_kv_heads][head_dim]  (read); bf16 or
+ *                  fp16 alike, the call moves bit patterns
  *   slot_mapping   int64 [num_tokens]; token t goes to slot s = slot_mapping[t], i.e. block
  *                  s / block_size, offset s % block_size. s < 0: token skipped (padding).
  *                  Non-negative slots must be distinct and < num_blocks*block_size; a slot
  *                  outside the pool is not written.
- *   k_cache, v_cache  bf16 [num_blocks][block_size][num_kv_heads][head_dim], modified in
+ *   k_cache, v_cache  [num_blocks][block_size][num_kv_heads][head_dim], same format as k/v, modified in
  *                  place; only the addressed rows change. Bits are copied unchanged (no
  *                  float conversion), so any payload, NaN included, is preserved.
  * Requirements: num_tokens >= 0 (0 = no-op), num_blocks >= 1, block_size >= 1,
@@ -162,6 +177,27 @@ int paged_decode_attention(const uint16_t* q, const uint16_t* k_cache,
                            float scale, float* out, void* workspace, size_t workspace_bytes,
                            int32_t partition_tokens, hipStream_t stream);
 
+/*
+ * paged_decode_attention_typed -- paged_decode_attention in other formats:
+ *   kv_dtype       format of q, k_cache and v_cache: PAGEDKV_DTYPE_BF16 or PAGEDKV_DTYPE_F16
+ *   out            [batch][num_q_heads][head_dim] in out_dtype (written)
+ *   out_dtype      PAGEDKV_DTYPE_F32, or kv_dtype (the fp32 result rounded to nearest even)
+ * Other pairs return PAGEDKV_ERR_UNSUPPORTED. Everything else, the workspace included, is as
+ * in paged_decode_attention (whose formats are bf16 in, fp32 out). Accumulation is fp32 in
+ * every format. With fp16 inputs the attention weights enter the matrix product as an fp16
+ * hi + lo pair scaled by 2^7 (the scale cancels in the normalisation), so weights down to
+ * 2^-31 of the largest still count; a 16-bit output adds its own rounding, at most half a
+ * unit in its last place.
+ */
+int paged_decode_attention_typed(const uint16_t* q, const uint16_t* k_cache,
+                                 const uint16_t* v_cache, const int32_t* block_tables,
+                                 int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                 int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                                 float scale, int32_t kv_dtype, void* out, int32_t out_dtype,
+                                 void* workspace, size_t workspace_bytes,
+                                 int32_t partition_tokens, hipStream_t stream);
+
 /* Kernel families for paged_decode_attention_ex. */
 typedef enum {
   PAGEDKV_KERNEL_AUTO = 0,  /* the library's choice for the shape (the default path):
@@ -175,7 +211,7 @@ typedef enum {
 } pagedkv_kernel;
 
 /*
- * paged_decode_attention_ex -- paged_decode_attention with two extra controls, for
+ * paged_decode_attention_ex -- paged_decode_attention_typed with two extra controls, for
  * comparison and profiling:
  *   kernel         a pagedkv_kernel value (PAGEDKV_ERR_UNSUPPORTED if that family has no
  *                  build for the shape);
@@ -188,10 +224,10 @@ int paged_decode_attention_ex(const uint16_t* q, const uint16_t* k_cache,
                               int32_t max_blocks_per_seq, const int32_t* context_lens,
                               int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                               int32_t head_dim, int32_t block_size, int64_t num_blocks,
-                              float scale, float* out, void* workspace,
-                              size_t workspace_bytes, int32_t partition_tokens,
-                              int32_t kernel, hipEvent_t ev_begin, hipEvent_t ev_end,
-                              hipStream_t stream);
+                              float scale, int32_t kv_dtype, void* out, int32_t out_dtype,
+                              void* workspace, size_t workspace_bytes,
+                              int32_t partition_tokens, int32_t kernel, hipEvent_t ev_begin,
+                              hipEvent_t ev_end, hipStream_t stream);
 
 /*
  * paged_decode_plan -- the launch paged_decode_attention_ex would make for these sizes on
@@ -234,11 +270,15 @@ int paged_prefill_attention(const uint16_t* q, const int32_t* cu_seqlens_q, int6
                             int64_t num_blocks, float scale, float* out, hipStream_t stream);
 
 /*
- * paged_prefill_attention_ex -- paged_prefill_attention with the work split chosen by the
- * caller: row_blocks = number of 16-row blocks of queries each wave carries through one pass
- * over the keys (1, 2 or 4), or 0 to let the library choose from the sizes and the device
- * (what paged_prefill_attention does). Results agree across choices up to fp32 rounding of
- * the same sums. Any other row_blocks value returns PAGEDKV_ERR_SHAPE.
+ * paged_prefill_attention_ex -- paged_prefill_attention in other formats and with the work
+ * split chosen by the caller:
+ *   kv_dtype, out_dtype  formats of q and the caches, and of out, as in
+ *                  paged_decode_attention_typed (paged_prefill_attention is bf16 in, fp32 out)
+ *   row_blocks     number of 16-row blocks of queries each wave carries through one pass
+ *                  over the keys (1, 2 or 4), or 0 to let the library choose from the sizes
+ *                  and the device (what paged_prefill_attention does). Results agree across
+ *                  choices up to fp32 rounding of the same sums. Any other value returns
+ *                  PAGEDKV_ERR_SHAPE.
  */
 int paged_prefill_attention_ex(const uint16_t* q, const int32_t* cu_seqlens_q,
                                int64_t num_tokens, int32_t max_q_len, const uint16_t* k_cache,
@@ -246,7 +286,8 @@ int paged_prefill_attention_ex(const uint16_t* q, const int32_t* cu_seqlens_q,
                                int32_t max_blocks_per_seq, const int32_t* context_lens,
                                int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                                int32_t head_dim, int32_t block_size, int64_t num_blocks,
-                               float scale, float* out, int32_t row_blocks, hipStream_t stream);
+                               float scale, int32_t kv_dtype, void* out, int32_t out_dtype,
+                               int32_t row_blocks, hipStream_t stream);
 
 #ifdef __cplusplus
 }

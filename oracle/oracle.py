@@ -50,8 +50,10 @@ def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
 # ---------------------------------------------------------------------------------------
 # fp16 decoding (IEEE 754 binary16: sign bit, 5 exponent bits with bias 15, 10 fraction
 # bits; exponent field 0 holds zero and the subnormals, 31 holds infinity and NaN). The
-# fp16-input variant of the path reads its q and caches in this format, as the T4 kernel of
-# the mini-vLLM benchmark ran in fp16 ("mini-vLLM" README, benchmark notes on the T4 run).
+# fp16-input variant of the path reads its q and caches in this format: the mini-vLLM
+# serving results were measured with an fp16 model (mini-vLLM README, Results, hardware
+# line), and the "tiny-vLLM" blog (The Precision Trade-off: BF16) sets fp16's narrower
+# exponent against bf16's.
 # ---------------------------------------------------------------------------------------
 def f16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
     """Exact decode of binary16 bit patterns (uint16) to float64, from the field layout."""

@@ -20,6 +20,9 @@ STATUS_NAMES = {0: "PAGEDKV_OK", 1: "PAGEDKV_ERR_NULL", 2: "PAGEDKV_ERR_SHAPE",
                 3: "PAGEDKV_ERR_UNSUPPORTED", 4: "PAGEDKV_ERR_WORKSPACE", 5: "PAGEDKV_ERR_HIP",
                 6: "PAGEDKV_ERR_ALIGN"}
 KERNELS = {"auto": 0, "valu": 1, "mfma": 2, "mfma_hw": 3}
+# pagedkv_dtype values of the tensor element types the library takes.
+DTYPES = {torch.bfloat16: 0, torch.float16: 1, torch.float32: 2}
+INPUT_TYPES = (torch.bfloat16, torch.float16)
 
 _lock = threading.Lock()
 _lib: Optional[ctypes.CDLL] = None
@@ -65,8 +68,11 @@ def load_library() -> ctypes.CDLL:
         attn = [P, P, P, P, I32, P, I32, I32, I32, I32, I32, I64, F32, P, P, SZ, I32]
         lib.paged_decode_attention.restype = ctypes.c_int
         lib.paged_decode_attention.argtypes = attn + [P]
+        typed = attn[:13] + [I32, P, I32, P, SZ, I32]
+        lib.paged_decode_attention_typed.restype = ctypes.c_int
+        lib.paged_decode_attention_typed.argtypes = typed + [P]
         lib.paged_decode_attention_ex.restype = ctypes.c_int
-        lib.paged_decode_attention_ex.argtypes = attn + [I32, P, P, P]
+        lib.paged_decode_attention_ex.argtypes = typed + [I32, P, P, P]
         lib.paged_kv_write_rope.restype = ctypes.c_int
         lib.paged_kv_write_rope.argtypes = [P, P, P, P, P, I32, P, I64, P, P, P, I64, I32, I32,
                                             I32, I32, P]
@@ -75,7 +81,8 @@ def load_library() -> ctypes.CDLL:
                                                 I32, I32, I64, F32, P, P]
         lib.paged_prefill_attention_ex.restype = ctypes.c_int
         lib.paged_prefill_attention_ex.argtypes = [P, P, I64, I32, P, P, P, I32, P, I32, I32,
-                                                   I32, I32, I32, I64, F32, P, I32, P]
+                                                   I32, I32, I32, I64, F32, I32, P, I32, I32,
+                                                   P]
         lib.paged_decode_plan.restype = ctypes.c_int
         lib.paged_decode_plan.argtypes = [I32, I32, I32, I32, I32, I32, I32, I32,
                                           ctypes.POINTER(I32), ctypes.POINTER(I32),
@@ -98,12 +105,14 @@ def _stream_handle(device: torch.device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
 
-def _require(t: torch.Tensor, name: str, dtype: torch.dtype, ndim: int,
+def _require(t: torch.Tensor, name: str, dtype, ndim: int,
              device: Optional[torch.device] = None) -> None:
+    """dtype: one torch dtype, or a tuple of accepted ones."""
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
-    if t.dtype != dtype:
-        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    accepted = dtype if isinstance(dtype, tuple) else (dtype,)
+    if t.dtype not in accepted:
+        raise ValueError(f"{name} must be {' or '.join(map(str, accepted))}, got {t.dtype}")
     if t.dim() != ndim:
         raise ValueError(f"{name} must have {ndim} dimensions, got shape {tuple(t.shape)}")
     if t.device.type != "cuda":
@@ -116,14 +125,14 @@ def _require(t: torch.Tensor, name: str, dtype: torch.dtype, ndim: int,
 
 def paged_kv_write(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,
                    k_cache: torch.Tensor, v_cache: torch.Tensor) -> None:
-    """Store token t's K/V rows (k[t], v[t]: [Hkv, D] bf16) at slot slot_mapping[t] of the
-    pools k_cache / v_cache ([NB, block_size, Hkv, D] bf16, updated in place).
-    Negative slots are skipped."""
-    _require(k_cache, "k_cache", torch.bfloat16, 4)
-    dev = k_cache.device
-    _require(v_cache, "v_cache", torch.bfloat16, 4, dev)
-    _require(k, "k", torch.bfloat16, 3, dev)
-    _require(v, "v", torch.bfloat16, 3, dev)
+    """Store token t's K/V rows (k[t], v[t]: [Hkv, D]) at slot slot_mapping[t] of the pools
+    k_cache / v_cache ([NB, block_size, Hkv, D], updated in place), all bf16 or all fp16
+    (bit patterns are copied). Negative slots are skipped."""
+    _require(k_cache, "k_cache", INPUT_TYPES, 4)
+    dev, dt = k_cache.device, k_cache.dtype
+    _require(v_cache, "v_cache", dt, 4, dev)
+    _require(k, "k", dt, 3, dev)
+    _require(v, "v", dt, 3, dev)
     _require(slot_mapping, "slot_mapping", torch.int64, 1, dev)
     NB, bs, Hkv, D = k_cache.shape
     if v_cache.shape != k_cache.shape:
@@ -186,20 +195,21 @@ def paged_decode_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
     """out[b, h] = softmax(scale * q[b, h] . K_b^T) V_b over the context_lens[b] cached
     positions of sequence b, read through block_tables[b] (KV head h // (Hq/Hkv)).
 
-    q [B, Hq, D] bf16; k_cache/v_cache [NB, block_size, Hkv, D] bf16; block_tables
-    [B, MB] int32; context_lens [B] int32; out [B, Hq, D] fp32 (written and returned).
+    q [B, Hq, D] and k_cache/v_cache [NB, block_size, Hkv, D]: all bf16 or all fp16;
+    block_tables [B, MB] int32; context_lens [B] int32; out [B, Hq, D] fp32 or the input
+    type (written and returned).
     partition_tokens: 0 automatic, -1 never split, >0 split size in tokens (tests).
     kernel: "auto", "valu", "mfma" or "mfma_hw". workspace: optional uint8 device buffer (see
     new_workspace); when omitted, a cached per-stream workspace is used.
     events: optional (begin, end) raw hipEvent_t handles recorded around the main kernel.
     """
-    _require(k_cache, "k_cache", torch.bfloat16, 4)
-    dev = k_cache.device
-    _require(v_cache, "v_cache", torch.bfloat16, 4, dev)
-    _require(q, "q", torch.bfloat16, 3, dev)
+    _require(k_cache, "k_cache", INPUT_TYPES, 4)
+    dev, dt = k_cache.device, k_cache.dtype
+    _require(v_cache, "v_cache", dt, 4, dev)
+    _require(q, "q", dt, 3, dev)
     _require(block_tables, "block_tables", torch.int32, 2, dev)
     _require(context_lens, "context_lens", torch.int32, 1, dev)
-    _require(out, "out", torch.float32, 3, dev)
+    _require(out, "out", (torch.float32, dt), 3, dev)
     NB, bs, Hkv, D = k_cache.shape
     if v_cache.shape != k_cache.shape:
         raise ValueError("k_cache and v_cache shapes differ")
@@ -224,9 +234,10 @@ def paged_decode_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
     with torch.cuda.device(dev):
         _check(lib.paged_decode_attention_ex(
             q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(), MB,
-            context_lens.data_ptr(), B, Hq, Hkv, D, bs, NB, float(scale), out.data_ptr(),
-            workspace.data_ptr() if need else None, ws_bytes if need else 0,
-            partition_tokens, KERNELS[kernel], ev_b, ev_e, _stream_handle(dev)))
+            context_lens.data_ptr(), B, Hq, Hkv, D, bs, NB, float(scale), DTYPES[dt],
+            out.data_ptr(), DTYPES[out.dtype], workspace.data_ptr() if need else None,
+            ws_bytes if need else 0, partition_tokens, KERNELS[kernel], ev_b, ev_e,
+            _stream_handle(dev)))
     return out
 
 
@@ -237,19 +248,20 @@ def paged_prefill_attention(q: torch.Tensor, cu_seqlens_q: torch.Tensor, k_cache
     """Multi-query causal attention over the paged cache (prefill / chunked prefill).
 
     Sequence b's query rows are q[cu_seqlens_q[b]:cu_seqlens_q[b+1]], its last Q_b positions;
-    row i attends to positions 0 .. context_lens[b] - Q_b + i. q [T, Hq, D] bf16, cu_seqlens_q
-    [B+1] int32, out [T, Hq, D] fp32. max_q_len (the largest Q_b) sizes the launch; when
+    row i attends to positions 0 .. context_lens[b] - Q_b + i. q [T, Hq, D] and the caches
+    bf16 or fp16 alike, cu_seqlens_q [B+1] int32, out [T, Hq, D] fp32 or the input type.
+    max_q_len (the largest Q_b) sizes the launch; when
     omitted it is read from cu_seqlens_q, which synchronises with the device. row_blocks
     (1, 2 or 4; 0 = chosen by the library) is the number of 16-row query blocks per wave.
     """
-    _require(k_cache, "k_cache", torch.bfloat16, 4)
-    dev = k_cache.device
-    _require(v_cache, "v_cache", torch.bfloat16, 4, dev)
-    _require(q, "q", torch.bfloat16, 3, dev)
+    _require(k_cache, "k_cache", INPUT_TYPES, 4)
+    dev, dt = k_cache.device, k_cache.dtype
+    _require(v_cache, "v_cache", dt, 4, dev)
+    _require(q, "q", dt, 3, dev)
     _require(cu_seqlens_q, "cu_seqlens_q", torch.int32, 1, dev)
     _require(block_tables, "block_tables", torch.int32, 2, dev)
     _require(context_lens, "context_lens", torch.int32, 1, dev)
-    _require(out, "out", torch.float32, 3, dev)
+    _require(out, "out", (torch.float32, dt), 3, dev)
     NB, bs, Hkv, D = k_cache.shape
     T, Hq, Dq = q.shape
     B = context_lens.shape[0]
@@ -264,8 +276,8 @@ def paged_prefill_attention(q: torch.Tensor, cu_seqlens_q: torch.Tensor, k_cache
         _check(lib.paged_prefill_attention_ex(
             q.data_ptr(), cu_seqlens_q.data_ptr(), T, int(max_q_len), k_cache.data_ptr(),
             v_cache.data_ptr(), block_tables.data_ptr(), block_tables.shape[1],
-            context_lens.data_ptr(), B, Hq, Hkv, D, bs, NB, float(scale), out.data_ptr(),
-            int(row_blocks), _stream_handle(dev)))
+            context_lens.data_ptr(), B, Hq, Hkv, D, bs, NB, float(scale), DTYPES[dt],
+            out.data_ptr(), DTYPES[out.dtype], int(row_blocks), _stream_handle(dev)))
     return out
 
 

@@ -169,6 +169,16 @@ int plan_granule(int kernel, int32_t block_size) {
   }
 }
 
+int check_formats(int32_t kv_dtype, int32_t out_dtype) {
+  if (kv_dtype != PAGEDKV_DTYPE_BF16 && kv_dtype != PAGEDKV_DTYPE_F16)
+    return fail(PAGEDKV_ERR_UNSUPPORTED, "q and cache format %d is not bf16 or fp16", kv_dtype);
+  if (out_dtype != PAGEDKV_DTYPE_F32 && out_dtype != kv_dtype)
+    return fail(PAGEDKV_ERR_UNSUPPORTED,
+                "output format %d: fp32 or the input format (%d) are supported", out_dtype,
+                kv_dtype);
+  return PAGEDKV_OK;
+}
+
 int check_decode_sizes(int32_t max_blocks, int32_t batch, int32_t num_q_heads,
                        int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                        int64_t num_blocks) {
@@ -326,13 +336,15 @@ int paged_decode_attention_ex(const uint16_t* q, const uint16_t* k_cache,
                               int32_t max_blocks_per_seq, const int32_t* context_lens,
                               int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                               int32_t head_dim, int32_t block_size, int64_t num_blocks,
-                              float scale, float* out, void* workspace,
-                              size_t workspace_bytes, int32_t partition_tokens,
-                              int32_t kernel, hipEvent_t ev_begin, hipEvent_t ev_end,
-                              hipStream_t stream) {
+                              float scale, int32_t kv_dtype, void* out, int32_t out_dtype,
+                              void* workspace, size_t workspace_bytes,
+                              int32_t partition_tokens, int32_t kernel, hipEvent_t ev_begin,
+                              hipEvent_t ev_end, hipStream_t stream) {
   g_last_error.clear();
-  int st = check_decode_sizes(max_blocks_per_seq, batch, num_q_heads, num_kv_heads, head_dim,
-                              block_size, num_blocks);
+  int st = check_formats(kv_dtype, out_dtype);
+  if (st) return st;
+  st = check_decode_sizes(max_blocks_per_seq, batch, num_q_heads, num_kv_heads, head_dim,
+                          block_size, num_blocks);
   if (st) return st;
   const int G = num_q_heads / num_kv_heads;
   int chosen = 0;
@@ -372,6 +384,8 @@ int paged_decode_attention_ex(const uint16_t* q, const uint16_t* k_cache,
   a.scale_log2 = scale * kLog2eHost;
   a.nparts = plan.nparts;
   a.part_tokens = plan.part_tokens;
+  a.kv_dtype = kv_dtype;
+  a.out_dtype = out_dtype;
   if (plan.nparts > 1) {
     const size_t need = split_workspace_bytes(batch, num_q_heads, head_dim, plan.nparts);
     if (!workspace || workspace_bytes < need)
@@ -410,9 +424,25 @@ int paged_decode_attention(const uint16_t* q, const uint16_t* k_cache,
                            int32_t partition_tokens, hipStream_t stream) {
   return paged_decode_attention_ex(q, k_cache, v_cache, block_tables, max_blocks_per_seq,
                                    context_lens, batch, num_q_heads, num_kv_heads, head_dim,
-                                   block_size, num_blocks, scale, out, workspace,
-                                   workspace_bytes, partition_tokens, PAGEDKV_KERNEL_AUTO,
-                                   nullptr, nullptr, stream);
+                                   block_size, num_blocks, scale, PAGEDKV_DTYPE_BF16, out,
+                                   PAGEDKV_DTYPE_F32, workspace, workspace_bytes,
+                                   partition_tokens, PAGEDKV_KERNEL_AUTO, nullptr, nullptr,
+                                   stream);
+}
+
+int paged_decode_attention_typed(const uint16_t* q, const uint16_t* k_cache,
+                                 const uint16_t* v_cache, const int32_t* block_tables,
+                                 int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                 int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                                 float scale, int32_t kv_dtype, void* out, int32_t out_dtype,
+                                 void* workspace, size_t workspace_bytes,
+                                 int32_t partition_tokens, hipStream_t stream) {
+  return paged_decode_attention_ex(q, k_cache, v_cache, block_tables, max_blocks_per_seq,
+                                   context_lens, batch, num_q_heads, num_kv_heads, head_dim,
+                                   block_size, num_blocks, scale, kv_dtype, out, out_dtype,
+                                   workspace, workspace_bytes, partition_tokens,
+                                   PAGEDKV_KERNEL_AUTO, nullptr, nullptr, stream);
 }
 
 int paged_prefill_attention_ex(const uint16_t* q, const int32_t* cu_seqlens_q,
@@ -421,13 +451,15 @@ int paged_prefill_attention_ex(const uint16_t* q, const int32_t* cu_seqlens_q,
                                int32_t max_blocks_per_seq, const int32_t* context_lens,
                                int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                                int32_t head_dim, int32_t block_size, int64_t num_blocks,
-                               float scale, float* out, int32_t row_blocks,
-                               hipStream_t stream) {
+                               float scale, int32_t kv_dtype, void* out, int32_t out_dtype,
+                               int32_t row_blocks, hipStream_t stream) {
   g_last_error.clear();
+  int st = check_formats(kv_dtype, out_dtype);
+  if (st) return st;
   if (row_blocks != 0 && row_blocks != 1 && row_blocks != 2 && row_blocks != 4)
     return fail(PAGEDKV_ERR_SHAPE, "row_blocks must be 0 (auto), 1, 2 or 4, got %d", row_blocks);
-  int st = check_decode_sizes(max_blocks_per_seq, batch, num_q_heads, num_kv_heads, head_dim,
-                              block_size, num_blocks);
+  st = check_decode_sizes(max_blocks_per_seq, batch, num_q_heads, num_kv_heads, head_dim,
+                          block_size, num_blocks);
   if (st) return st;
   if (num_tokens < 0 || max_q_len < 0)
     return fail(PAGEDKV_ERR_SHAPE, "num_tokens and max_q_len must be >= 0");
@@ -472,6 +504,8 @@ int paged_prefill_attention_ex(const uint16_t* q, const int32_t* cu_seqlens_q,
   a.scale_log2 = scale * kLog2eHost;
   a.ntiles = (int32_t)ntiles;
   a.nb = nb;
+  a.kv_dtype = kv_dtype;
+  a.out_dtype = out_dtype;
   hipError_t e = launch_prefill_mfma(a, stream);
   if (e != hipSuccess) return hip_fail(e, "prefill attention launch");
   return PAGEDKV_OK;
@@ -486,7 +520,7 @@ int paged_prefill_attention(const uint16_t* q, const int32_t* cu_seqlens_q, int6
   return paged_prefill_attention_ex(q, cu_seqlens_q, num_tokens, max_q_len, k_cache, v_cache,
                                     block_tables, max_blocks_per_seq, context_lens, batch,
                                     num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
-                                    scale, out, 0, stream);
+                                    scale, PAGEDKV_DTYPE_BF16, out, PAGEDKV_DTYPE_F32, 0, stream);
 }
 
 }  // extern "C"

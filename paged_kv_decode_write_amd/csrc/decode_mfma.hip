@@ -1,4 +1,5 @@
-// Paged one-token decode attention on the matrix cores (bf16 MFMA, fp32 accumulate).
+// Paged one-token decode attention on the matrix cores (bf16 or fp16 MFMA, fp32 accumulate;
+// output in fp32 or in the input format).
 //
 // Same computation as the vector-ALU kernel: for every sequence b and query head h,
 // softmax(scale * q[b,h] . K^T) V over the context_lens[b] positions read through
@@ -27,8 +28,10 @@
 //                        row 4kg+j-4). P^T is then built in place with no data movement;
 //                        V^T needs 8 token rows per lane, loaded as EPL contiguous bf16 per
 //                        row and transposed in registers with v_perm_b32.
-//   P is split as p = hi + lo with both parts in bf16 (hi = p truncated to bf16, exact;
-//   lo = bf16(p - hi)), two MFMAs per tile, so the weights keep ~16 bits of precision.
+//   P is split as p = hi + lo with both parts in the input format (bf16: hi = p truncated,
+//   exact, lo = bf16(p - hi); fp16: both rounded toward zero, weights lifted by 2^7 to stay
+//   clear of fp16's small range), two MFMAs per tile, so the weights keep ~16 bits of
+//   precision.
 // The running max is shared by the four lanes of a head (two cross-lane maxima per step);
 // the running sum stays per lane and is reduced once at the end. Waves are merged through
 // LDS with the log-sum-exp rule and the result is written out, or left as a partition
@@ -38,7 +41,7 @@
 
 namespace pagedkv {
 
-template <int D, int NW>
+template <int D, int NW, int KT, int OT>
 __global__ void __launch_bounds__(NW * 64)
 decode_mfma_kernel(const DecodeArgs a) {
   constexpr int BS = 16;
@@ -70,15 +73,14 @@ decode_mfma_kernel(const DecodeArgs a) {
   const int blk1 = (tok1 + BS - 1) / BS;
 
   // Q^T operand: lane (n16, kg) holds q[head n16][32c + 8kg .. +7] for chunk c (0 if n16>=G).
-  bf16x8 qb[NCH];
+  uint4 qb[NCH];
   {
     const bool hv = n16 < G;
     const uint16_t* qrow = a.q + ((size_t)b * Hq + (size_t)g * G + (hv ? n16 : 0)) * D + 8 * kg;
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
-      uint4 w = make_uint4(0, 0, 0, 0);
-      if (hv) w = *reinterpret_cast<const uint4*>(qrow + 32 * c);
-      qb[c] = as_bf16x8(w);
+      qb[c] = make_uint4(0, 0, 0, 0);
+      if (hv) qb[c] = *reinterpret_cast<const uint4*>(qrow + 32 * c);
     }
   }
 
@@ -119,10 +121,10 @@ decode_mfma_kernel(const DecodeArgs a) {
       const int k1 = min(k + 1, np - 1), k2 = min(k + 2, np - 1), k3 = min(k + 3, np - 1);
       pair_load<D, NW>(t1, ctx, i1, k1);
       i0 = pair_ids<D, NW>(ctx, k2);
-      pair_compute(t0, st, qb, sl2, kg);
+      pair_compute<KT>(t0, st, qb, sl2, kg);
       pair_load<D, NW>(t0, ctx, i0, k2);
       i1 = pair_ids<D, NW>(ctx, k3);
-      if (k + 1 < np) pair_compute(t1, st, qb, sl2, kg);
+      if (k + 1 < np) pair_compute<KT>(t1, st, qb, sl2, kg);
     }
   }
 
@@ -159,7 +161,7 @@ decode_mfma_kernel(const DecodeArgs a) {
     }
     const size_t row = (size_t)b * Hq + (size_t)g * G + h;
     if (nparts == 1) {
-      a.out[row * D + d] = den > 0.f ? num / den : 0.f;
+      store_out<OT>(a.out, row * D + d, den > 0.f ? num / den : 0.f);
     } else {
       const size_t pr = row * nparts + part;
       a.ws_acc[pr * D + d] = num;
@@ -176,7 +178,7 @@ decode_mfma_kernel(const DecodeArgs a) {
 // token row of a block instead of D*2, and every wave walks the whole partition on its own
 // (no cross-wave merge). Each wave writes its heads' output, or its partition partial for
 // the merge kernel.
-template <int D, int HPW, int NBUF, int MINW>
+template <int D, int HPW, int NBUF, int MINW, int KT, int OT>
 __global__ void __launch_bounds__(HPW * 64, MINW)
 decode_mfma_hw_kernel(const DecodeArgs a) {
   constexpr int BS = 16;
@@ -209,15 +211,14 @@ decode_mfma_hw_kernel(const DecodeArgs a) {
   const int blk0 = tok0 / BS;
   const int idA0 = blk0 < a.max_blocks ? table[blk0] : -1;
   const int idB0 = blk0 + 1 < a.max_blocks ? table[blk0 + 1] : -1;
-  bf16x8 qb[NCH];
+  uint4 qb[NCH];
   {
     const bool hv = n16 < G;
     const uint16_t* qrow = a.q + ((size_t)b * Hq + (size_t)g * G + (hv ? n16 : 0)) * D + 8 * kg;
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
-      uint4 w = make_uint4(0, 0, 0, 0);
-      if (hv) w = *reinterpret_cast<const uint4*>(qrow + 32 * c);
-      qb[c] = as_bf16x8(w);
+      qb[c] = make_uint4(0, 0, 0, 0);
+      if (hv) qb[c] = *reinterpret_cast<const uint4*>(qrow + 32 * c);
     }
   }
 
@@ -272,7 +273,7 @@ decode_mfma_hw_kernel(const DecodeArgs a) {
         const int ub = (u + NBUF - 1) % NBUF;
         pair_load<D, 1>(t[ub], ctx, ids[ub], jl);
         ids[u] = pair_ids<D, 1>(ctx, min(jl + 1, np - 1));
-        if (j < np) pair_compute(t[u], st, qb, sl2, kg);
+        if (j < np) pair_compute<KT>(t[u], st, qb, sl2, kg);
       }
     }
   }
@@ -285,14 +286,13 @@ decode_mfma_hw_kernel(const DecodeArgs a) {
   if (nparts == 1) {
     if (hv) {
       const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-      float* o = a.out + (row0 + n16) * D;
+      const size_t o = (row0 + n16) * D;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int e = 0; e < EPL; e += 4)
-          *reinterpret_cast<float4*>(o + EPL * (4 * kg + i) + e) =
-              make_float4(st.acc[e][i] * inv, st.acc[e + 1][i] * inv, st.acc[e + 2][i] * inv,
-                          st.acc[e + 3][i] * inv);
+          store_out4<OT>(a.out, o + EPL * (4 * kg + i) + e, st.acc[e][i] * inv,
+                         st.acc[e + 1][i] * inv, st.acc[e + 2][i] * inv, st.acc[e + 3][i] * inv);
     }
     return;
   }
@@ -320,16 +320,19 @@ bool supported_mfma(int head_dim, int group, int block_size) {
 
 hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream) {
   constexpr int NW = kWavesPerGroup;
-  const long long units = (long long)a.batch * a.num_kv_heads * a.nparts;
-  if (a.head_dim == 128)
-    hipLaunchKernelGGL((decode_mfma_kernel<128, NW>), dim3((unsigned)units), dim3(NW * 64), 0,
-                       stream, a);
-  else if (a.head_dim == 64)
-    hipLaunchKernelGGL((decode_mfma_kernel<64, NW>), dim3((unsigned)units), dim3(NW * 64), 0,
-                       stream, a);
-  else
-    return hipErrorInvalidValue;
-  return hipGetLastError();
+  const unsigned units = (unsigned)((long long)a.batch * a.num_kv_heads * a.nparts);
+  return with_formats(a.kv_dtype, a.out_dtype, [&](auto kt, auto ot) {
+    constexpr int KT = decltype(kt)::value, OT = decltype(ot)::value;
+    if (a.head_dim == 128)
+      hipLaunchKernelGGL((decode_mfma_kernel<128, NW, KT, OT>), dim3(units), dim3(NW * 64), 0,
+                         stream, a);
+    else if (a.head_dim == 64)
+      hipLaunchKernelGGL((decode_mfma_kernel<64, NW, KT, OT>), dim3(units), dim3(NW * 64), 0,
+                         stream, a);
+    else
+      return hipErrorInvalidValue;
+    return hipGetLastError();
+  });
 }
 
 hipError_t launch_decode_mfma_hw(const DecodeArgs& a, hipStream_t stream) {
@@ -338,16 +341,19 @@ hipError_t launch_decode_mfma_hw(const DecodeArgs& a, hipStream_t stream) {
   // on every workload, and it keeps two waves per SIMD.
   constexpr int NBUF = 2;
   const long long ngrp = (a.num_kv_heads + HPW - 1) / HPW;
-  const long long units = (long long)a.batch * ngrp * a.nparts;
-  if (a.head_dim == 128)
-    hipLaunchKernelGGL((decode_mfma_hw_kernel<128, HPW, NBUF, 2>), dim3((unsigned)units),
-                       dim3(HPW * 64), 0, stream, a);
-  else if (a.head_dim == 64)
-    hipLaunchKernelGGL((decode_mfma_hw_kernel<64, HPW, NBUF, 2>), dim3((unsigned)units),
-                       dim3(HPW * 64), 0, stream, a);
-  else
-    return hipErrorInvalidValue;
-  return hipGetLastError();
+  const unsigned units = (unsigned)((long long)a.batch * ngrp * a.nparts);
+  return with_formats(a.kv_dtype, a.out_dtype, [&](auto kt, auto ot) {
+    constexpr int KT = decltype(kt)::value, OT = decltype(ot)::value;
+    if (a.head_dim == 128)
+      hipLaunchKernelGGL((decode_mfma_hw_kernel<128, HPW, NBUF, 2, KT, OT>), dim3(units),
+                         dim3(HPW * 64), 0, stream, a);
+    else if (a.head_dim == 64)
+      hipLaunchKernelGGL((decode_mfma_hw_kernel<64, HPW, NBUF, 2, KT, OT>), dim3(units),
+                         dim3(HPW * 64), 0, stream, a);
+    else
+      return hipErrorInvalidValue;
+    return hipGetLastError();
+  });
 }
 
 }  // namespace pagedkv

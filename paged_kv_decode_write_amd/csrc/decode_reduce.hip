@@ -12,7 +12,8 @@
 // One workgroup of 256 threads per (sequence, query head). The partition statistics are
 // reduced across the whole workgroup; the weighted sum of the partial outputs splits the
 // partitions over 256/D thread groups (thread = (column d, group)), whose loads of a_p are
-// coalesced along d and independent across p.
+// coalesced along d and independent across p. The partials are fp32 whatever the formats;
+// the result is stored in the output format.
 #include "device_common.h"
 #include "launch.h"
 
@@ -31,6 +32,7 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+template <int OT>
 __global__ void __launch_bounds__(kReduceThreads)
 decode_reduce_kernel(const DecodeArgs a) {
   constexpr int NWV = kReduceThreads / 64;
@@ -45,9 +47,9 @@ decode_reduce_kernel(const DecodeArgs a) {
   int L = a.context_lens[b];
   const int Lmax = a.max_blocks * a.block_size;
   L = L < 0 ? 0 : (L > Lmax ? Lmax : L);
-  float* o = a.out + (size_t)row * D;
+  const size_t o = (size_t)row * D;
   if (L == 0) {
-    for (int d = tid; d < D; d += kReduceThreads) o[d] = 0.f;
+    for (int d = tid; d < D; d += kReduceThreads) store_out<OT>(a.out, o + d, 0.f);
     return;
   }
   const int np = (L + a.part_tokens - 1) / a.part_tokens;  // partitions holding keys
@@ -90,14 +92,18 @@ decode_reduce_kernel(const DecodeArgs a) {
   __syncthreads();
   if (grp == 0) {
     for (int q = 1; q < groups; ++q) num += part[q * D + d];
-    o[d] = den > 0.f ? num / den : 0.f;
+    store_out<OT>(a.out, o + d, den > 0.f ? num / den : 0.f);
   }
 }
 
 hipError_t launch_decode_reduce(const DecodeArgs& a, hipStream_t stream) {
-  const long long rows = (long long)a.batch * a.num_q_heads;
-  hipLaunchKernelGGL(decode_reduce_kernel, dim3((unsigned)rows), dim3(kReduceThreads), 0,
-                     stream, a);
+  const unsigned rows = (unsigned)((long long)a.batch * a.num_q_heads);
+  switch (a.out_dtype) {
+    case kDtF32: hipLaunchKernelGGL(decode_reduce_kernel<kDtF32>, dim3(rows), dim3(kReduceThreads), 0, stream, a); break;
+    case kDtBf16: hipLaunchKernelGGL(decode_reduce_kernel<kDtBf16>, dim3(rows), dim3(kReduceThreads), 0, stream, a); break;
+    case kDtF16: hipLaunchKernelGGL(decode_reduce_kernel<kDtF16>, dim3(rows), dim3(kReduceThreads), 0, stream, a); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

@@ -1,4 +1,5 @@
-// Paged one-token decode attention, vector-ALU kernel (fp32 dot products and accumulate).
+// Paged one-token decode attention, vector-ALU kernel (fp32 dot products and accumulate; bf16
+// or fp16 inputs, output in fp32 or in the input format).
 //
 // Computes, for every sequence b and query head h, softmax(scale * q[b,h] . K^T) V over the
 // context_lens[b] positions read through block_tables[b] (mini-vLLM README, paged KV-cache
@@ -26,7 +27,7 @@
 
 namespace pagedkv {
 
-template <int D, int G, int BS, int NW>
+template <int D, int G, int BS, int NW, int KT, int OT>
 __global__ void __launch_bounds__(NW * 64)
 decode_valu_kernel(const DecodeArgs a) {
   constexpr int LPR = D / 8;        // lanes per token row
@@ -62,7 +63,7 @@ decode_valu_kernel(const DecodeArgs a) {
   for (int h = 0; h < G; ++h) {
     const uint4 w = *reinterpret_cast<const uint4*>(
         a.q + ((size_t)b * Hq + (size_t)g * G + h) * D + col * 8);
-    unpack8(w, qf[h]);
+    unpack8<KT>(w, qf[h]);
   }
 
   float m[G], l[G], acc[G][8];
@@ -105,7 +106,7 @@ decode_valu_kernel(const DecodeArgs a) {
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
         float kf[8];
-        unpack8(kr[i], kf);
+        unpack8<KT>(kr[i], kf);
 #pragma unroll
         for (int h = 0; h < G; ++h) {
           float d = 0.f;
@@ -141,7 +142,7 @@ decode_valu_kernel(const DecodeArgs a) {
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
         float vf[8];
-        unpack8(vr[i], vf);
+        unpack8<KT>(vr[i], vf);
 #pragma unroll
         for (int h = 0; h < G; ++h) {
           l[h] += s[h][i];
@@ -204,7 +205,7 @@ decode_valu_kernel(const DecodeArgs a) {
     }
     const size_t row = (size_t)b * Hq + (size_t)g * G + h;
     if (nparts == 1) {
-      a.out[row * D + d] = den > 0.f ? num / den : 0.f;
+      store_out<OT>(a.out, row * D + d, den > 0.f ? num / den : 0.f);
     } else {
       const size_t pr = row * nparts + part;
       a.ws_acc[pr * D + d] = num;
@@ -219,10 +220,13 @@ decode_valu_kernel(const DecodeArgs a) {
 template <int D, int G>
 static hipError_t launch_dg(const DecodeArgs& a, hipStream_t stream) {
   constexpr int NW = kWavesPerGroup;
-  const long long units = (long long)a.batch * a.num_kv_heads * a.nparts;
-  hipLaunchKernelGGL((decode_valu_kernel<D, G, 16, NW>), dim3((unsigned)units), dim3(NW * 64),
-                     0, stream, a);
-  return hipGetLastError();
+  const unsigned units = (unsigned)((long long)a.batch * a.num_kv_heads * a.nparts);
+  return with_formats(a.kv_dtype, a.out_dtype, [&](auto kt, auto ot) {
+    constexpr int KT = decltype(kt)::value, OT = decltype(ot)::value;
+    hipLaunchKernelGGL((decode_valu_kernel<D, G, 16, NW, KT, OT>), dim3(units), dim3(NW * 64),
+                       0, stream, a);
+    return hipGetLastError();
+  });
 }
 
 bool supported_valu(int head_dim, int group, int block_size) {

@@ -9,15 +9,69 @@ namespace pagedkv {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -__builtin_inff();
 
-// bf16 -> fp32 is exact: a bf16 value is the upper half of an fp32 bit pattern.
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+// Element formats (the values of the C ABI's pagedkv_dtype).
+enum : int { kDtBf16 = 0, kDtF16 = 1, kDtF32 = 2 };
 
-__device__ __forceinline__ void unpack8(const uint4& w, float (&f)[8]) {
-  f[0] = bf16_lo(w.x); f[1] = bf16_hi(w.x);
-  f[2] = bf16_lo(w.y); f[3] = bf16_hi(w.y);
-  f[4] = bf16_lo(w.z); f[5] = bf16_hi(w.z);
-  f[6] = bf16_lo(w.w); f[7] = bf16_hi(w.w);
+// 16-bit input element -> fp32, exact for both formats: a bf16 value is the upper half of an
+// fp32 bit pattern; an fp16 value converts with v_cvt_f32_f16.
+template <int KT> __device__ __forceinline__ float in_lo(uint32_t w) {
+  if constexpr (KT == kDtF16) return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+  else return __uint_as_float(w << 16);
+}
+template <int KT> __device__ __forceinline__ float in_hi(uint32_t w) {
+  if constexpr (KT == kDtF16) return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+  else return __uint_as_float(w & 0xffff0000u);
+}
+
+template <int KT> __device__ __forceinline__ void unpack8(const uint4& w, float (&f)[8]) {
+  f[0] = in_lo<KT>(w.x); f[1] = in_hi<KT>(w.x);
+  f[2] = in_lo<KT>(w.y); f[3] = in_hi<KT>(w.y);
+  f[4] = in_lo<KT>(w.z); f[5] = in_hi<KT>(w.z);
+  f[6] = in_lo<KT>(w.w); f[7] = in_hi<KT>(w.w);
+}
+
+// Makes an fp32 value opaque to the optimiser, so the operation that produced it is rounded
+// to fp32 first. Without it, a product feeding an fp16 conversion may be contracted into one
+// v_fma_mix*_f16 (a single rounding of the exact product): close, but not the fp32 result
+// rounded, which is what a 16-bit output is defined to hold.
+__device__ __forceinline__ float materialize_f32(float f) {
+  asm volatile("" : "+v"(f));
+  return f;
+}
+
+// fp32 -> bf16 with the hardware conversion (v_cvt_pk_bf16_f32: round to nearest even).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  return __builtin_bit_cast(uint16_t, (__bf16)materialize_f32(f));
+}
+// fp32 -> fp16 with v_cvt_f16_f32 (round to nearest even; overflow gives infinity).
+__device__ __forceinline__ uint16_t f32_to_f16_rne(float f) {
+  return __builtin_bit_cast(uint16_t, (_Float16)materialize_f32(f));
+}
+
+// Output stores: one value, or four consecutive values (index a multiple of 4), in the
+// output format OT.
+template <int OT> __device__ __forceinline__ void store_out(void* out, size_t i, float v) {
+  if constexpr (OT == kDtF32) static_cast<float*>(out)[i] = v;
+  else if constexpr (OT == kDtBf16) static_cast<uint16_t*>(out)[i] = f32_to_bf16_rne(v);
+  else static_cast<uint16_t*>(out)[i] = f32_to_f16_rne(v);
+}
+template <int OT>
+__device__ __forceinline__ void store_out4(void* out, size_t i, float a, float b, float c,
+                                           float d) {
+  if constexpr (OT == kDtF32) {
+    *reinterpret_cast<float4*>(static_cast<float*>(out) + i) = make_float4(a, b, c, d);
+  } else {
+    uint16_t h[4];
+    if constexpr (OT == kDtBf16) {
+      h[0] = f32_to_bf16_rne(a); h[1] = f32_to_bf16_rne(b);
+      h[2] = f32_to_bf16_rne(c); h[3] = f32_to_bf16_rne(d);
+    } else {
+      h[0] = f32_to_f16_rne(a); h[1] = f32_to_f16_rne(b);
+      h[2] = f32_to_f16_rne(c); h[3] = f32_to_f16_rne(d);
+    }
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + i) =
+        make_uint2(h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16));
+  }
 }
 
 // v_exp_f32: 2^x, with 2^-inf = 0.

@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace pagedkv {
 
 // Arguments of one decode-attention launch, already validated by the host layer.
@@ -14,7 +16,7 @@ struct DecodeArgs {
   const uint16_t* v_cache;
   const int32_t* block_tables;
   const int32_t* context_lens;
-  float* out;
+  void* out;        // [B][Hq][D] in the output format
   float* ws_acc;    // [B][Hq][nparts][D] unnormalised partial outputs (split only)
   float* ws_ml;     // [B][Hq][nparts][2] partial (max, sum) in log2 units (split only)
   int32_t max_blocks;  // MB, block-table row length
@@ -23,6 +25,8 @@ struct DecodeArgs {
   float scale_log2;     // scale * log2(e)
   int32_t nparts;       // partitions per sequence (1 = write out directly)
   int32_t part_tokens;  // tokens per partition, a multiple of block_size
+  int32_t kv_dtype;     // format of q and the caches: kDtBf16 or kDtF16
+  int32_t out_dtype;    // kDtF32 or kv_dtype
 };
 
 // Arguments of one multi-query causal (prefill) launch, already validated.
@@ -33,13 +37,14 @@ struct PrefillArgs {
   const uint16_t* v_cache;
   const int32_t* block_tables;
   const int32_t* context_lens;
-  float* out;                    // [T][Hq][D]
+  void* out;                     // [T][Hq][D] in the output format
   int32_t max_blocks;
   int32_t batch, num_q_heads, num_kv_heads, head_dim, block_size;
   int64_t num_blocks;
   float scale_log2;
   int32_t ntiles;  // query tiles per sequence (ceil(max_q_len / tokens per workgroup))
   int32_t nb;      // 16-row N blocks per wave: 1, 2 or 4
+  int32_t kv_dtype, out_dtype;  // as in DecodeArgs
 };
 
 // Arguments of one rotary-embedding + KV-write launch, already validated.
@@ -57,6 +62,20 @@ struct RopeArgs {
   int32_t num_q_heads, num_kv_heads, head_dim;
   int32_t interleaved;
 };
+
+// Calls f(integral_constant<KT>, integral_constant<OT>) for the compiled (input, output)
+// format pairs: bf16 or fp16 inputs, fp32 output or the input's own format.
+template <class F>
+hipError_t with_formats(int kv_dtype, int out_dtype, F&& f) {
+  using B16 = std::integral_constant<int, 0>;
+  using F16 = std::integral_constant<int, 1>;
+  using F32 = std::integral_constant<int, 2>;
+  if (kv_dtype == 0 && out_dtype == 2) return f(B16{}, F32{});
+  if (kv_dtype == 0 && out_dtype == 0) return f(B16{}, B16{});
+  if (kv_dtype == 1 && out_dtype == 2) return f(F16{}, F32{});
+  if (kv_dtype == 1 && out_dtype == 1) return f(F16{}, F16{});
+  return hipErrorInvalidValue;
+}
 
 // Each launcher returns hipSuccess or the launch error. `supported_*` report whether a
 // compiled instance exists for the shape.

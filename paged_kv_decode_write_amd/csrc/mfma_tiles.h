@@ -1,12 +1,14 @@
 // Register tiles shared by the matrix-core attention kernels (decode and multi-query causal):
 // one wave streams pairs of 16-token blocks of one KV head and runs, per pair,
-//   S^T = K_tile . Q^T   (v_mfma_f32_16x16x32_bf16: M = 16 keys, N = 16 query rows, K = 32
-//                        columns of D; K rows feed the A operand from global memory),
+//   S^T = K_tile . Q^T   (v_mfma_f32_16x16x32_bf16 or _f16 for fp16 inputs: M = 16 keys,
+//                        N = 16 query rows, K = 32 columns of D; K rows feed the A operand
+//                        from global memory),
 //   online softmax per query row (lazily rescaled reference max, shared by the 4 lanes of
 //   a row), and
 //   O^T += V^T . P^T     (M = 16 output columns, N = 16 rows, K = 32 keys; keys contracted in
 //                        the order the scores already sit in the lanes, V^T transposed in
-//                        registers with v_perm_b32, p split into bf16 hi + lo).
+//                        registers with v_perm_b32, p split into a hi + lo pair in the
+//                        input format).
 // Lane (n16 = lane % 16, kg = lane / 16) owns query row n16; it holds scores of keys
 // 4kg..4kg+3 of each block of the pair and output columns EPL*(4kg+i)+e of its row.
 #pragma once
@@ -16,15 +18,21 @@
 namespace pagedkv {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __fp16 fp16x2 __attribute__((ext_vector_type(2)));  // v_cvt_pkrtz result
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ bf16x8 as_bf16x8(const uint4& w) {
-  return __builtin_bit_cast(bf16x8, w);
-}
-
-__device__ __forceinline__ floatx4 mfma16x16x32(const bf16x8& a, const bf16x8& b,
+// One 16x16x32 product with fp32 accumulate; a and b hold 8 packed 16-bit values of the input
+// format KT (bf16 or fp16).
+template <int KT>
+__device__ __forceinline__ floatx4 mfma16x16x32(const uint4& a, const uint4& b,
                                                 const floatx4& c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  if constexpr (KT == kDtF16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
 // Low / high bf16 halves of two words packed into one word (x's half first).
@@ -56,6 +64,40 @@ template <> struct VRow<4> {
 
 // Slack of the lazily updated softmax reference max, in log2 units (weights <= 2^8).
 constexpr float kRescaleSlack = 8.f;
+
+// Exponent lift (log2) of the weights that enter p.V. bf16 has fp32's exponent range and
+// needs none. fp16 stops at 2^-24: weights are taken as 2^(s - m + 7) (largest 2^15, below
+// the fp16 maximum 65504), so a weight still counts down to 2^-31 of the reference. The sum
+// carries the same factor, so it cancels in acc / l and in the partition merge.
+template <int KT> constexpr float kWeightLift = KT == kDtF16 ? 7.f : 0.f;
+
+// Weights p[0..7] (token slots of the P^T operand) as hi + lo in the input format, with
+// p = hi + lo + O(2^-16 p): bf16 hi is p truncated (exact), lo the rounded remainder; fp16
+// hi is p rounded toward zero (v_cvt_pkrtz_f16_f32), lo the remainder likewise.
+template <int KT>
+__device__ __forceinline__ void split_weights(const float (&p)[8], uint4& hi, uint4& lo) {
+  uint32_t hw[4], lw[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    if constexpr (KT == kDtF16) {
+      const fp16x2 h = __builtin_amdgcn_cvt_pkrtz(p[2 * q], p[2 * q + 1]);
+      const fp16x2 l = __builtin_amdgcn_cvt_pkrtz(p[2 * q] - (float)h[0],
+                                                  p[2 * q + 1] - (float)h[1]);
+      hw[q] = __builtin_bit_cast(uint32_t, h);
+      lw[q] = __builtin_bit_cast(uint32_t, l);
+    } else {
+      const uint32_t u0 = __float_as_uint(p[2 * q]), u1 = __float_as_uint(p[2 * q + 1]);
+      hw[q] = __builtin_amdgcn_perm(u1, u0, 0x07060302u);
+      const float r0 = p[2 * q] - __uint_as_float(u0 & 0xffff0000u);
+      const float r1 = p[2 * q + 1] - __uint_as_float(u1 & 0xffff0000u);
+      const __bf16 b0 = (__bf16)r0, b1 = (__bf16)r1;
+      lw[q] = (uint32_t)__builtin_bit_cast(uint16_t, b0) |
+              ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
+    }
+  }
+  hi = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+  lo = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+}
 
 // Per-lane softmax state of one wave: the head is n16 = lane % 16; lanes of the same head
 // (kg = 0..3) share m_run and hold disjoint output columns.
@@ -119,60 +161,72 @@ __device__ __forceinline__ void pair_load(PairTile<NCH, EPL>& t, const PairCtx<D
   }
 }
 
-// Optional causal mask of a pair: the lane's query row sits at position row_pos; key
-// positions of the pair start at key0 (first block) and key0 + 16 (second block). `active`
-// (uniform) says whether any key of the pair lies after the earliest row of the wave.
-struct CausalMask {
-  int row_pos;
-  int key0;
-  bool active;
-};
+// V^T operand of output column set e: 8 token slots of column EPL*n16 + e, gathered from the
+// 8 loaded V rows with v_perm_b32 (a 16-bit shuffle, the same for both input formats).
+template <int NCH, int EPL>
+__device__ __forceinline__ uint4 vt_operand(const PairTile<NCH, EPL>& t, int e) {
+  uint32_t w[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t x = t.vr[2 * q].word(e / 2), y = t.vr[2 * q + 1].word(e / 2);
+    w[q] = (e & 1) ? pack_hi(x, y) : pack_lo(x, y);
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
 
-// q.K, online softmax and p.V for one loaded pair.
-template <int NCH, int EPL, bool CAUSAL = false>
-__device__ __forceinline__ void pair_compute(PairTile<NCH, EPL>& t, WaveState<EPL>& st,
-                                             const bf16x8 (&qb)[NCH], float sl2, int kg,
-                                             CausalMask cm = CausalMask{0, 0, false}) {
-  constexpr int BS = 16;
+// Zero the V rows past a block's valid rows: stale slots may hold NaN bits, and 0 * NaN would
+// poison p.V even where the weight is 0.
+template <int NCH, int EPL>
+__device__ __forceinline__ void clear_stale_rows(PairTile<NCH, EPL>& t, int kg) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    t.vr[i].keep_if(4 * kg + i < t.lastA);
+    t.vr[4 + i].keep_if(4 * kg + i < t.lastB);
+  }
+}
+
+// Scores of one pair for one 16-row N block: q.K on the matrix cores, scaled to log2 units.
+template <int KT, int NCH, int EPL>
+__device__ __forceinline__ void pair_scores(const PairTile<NCH, EPL>& t, const uint4 (&qb)[NCH],
+                                            float sl2, float (&s)[8]) {
   floatx4 sA = {0.f, 0.f, 0.f, 0.f}, sB = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int ch = 0; ch < NCH; ++ch) {
-    sA = mfma16x16x32(as_bf16x8(t.ka[ch]), qb[ch], sA);
-    sB = mfma16x16x32(as_bf16x8(t.kb[ch]), qb[ch], sB);
+    sA = mfma16x16x32<KT>(t.ka[ch], qb[ch], sA);
+    sB = mfma16x16x32<KT>(t.kb[ch], qb[ch], sB);
   }
-  float s[8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     s[i] = sA[i] * sl2;
     s[4 + i] = sB[i] * sl2;
   }
-  if (t.lastA < BS || t.lastB < BS) {  // a block holds positions at or past the end
+}
+
+// Positions past a block's valid rows: score -inf.
+template <int NCH, int EPL>
+__device__ __forceinline__ void mask_stale_scores(const PairTile<NCH, EPL>& t, int kg,
+                                                  float (&s)[8]) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const bool va = 4 * kg + i < t.lastA;
-      const bool vb = 4 * kg + i < t.lastB;
-      s[i] = va ? s[i] : kNegInf;
-      s[4 + i] = vb ? s[4 + i] : kNegInf;
-      t.vr[i].keep_if(va);  // stale rows may hold NaN bits; 0 * NaN would poison p.V
-      t.vr[4 + i].keep_if(vb);
-    }
+  for (int i = 0; i < 4; ++i) {
+    s[i] = 4 * kg + i < t.lastA ? s[i] : kNegInf;
+    s[4 + i] = 4 * kg + i < t.lastB ? s[4 + i] : kNegInf;
   }
-  if (CAUSAL && cm.active) {  // keys after the lane's own query position get weight 0
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      s[i] = cm.key0 + 4 * kg + i <= cm.row_pos ? s[i] : kNegInf;
-      s[4 + i] = cm.key0 + BS + 4 * kg + i <= cm.row_pos ? s[4 + i] : kNegInf;
-    }
-  }
+}
+
+// Online-softmax update of one N block with the pair's scores s; returns the weights (lifted
+// by kWeightLift) split into the hi / lo P^T operands.
+template <int KT, int EPL>
+__device__ __forceinline__ void softmax_step(WaveState<EPL>& st, const float (&s)[8], uint4& phi,
+                                             uint4& plo) {
   float mx = s[0];
 #pragma unroll
   for (int i = 1; i < 8; ++i) mx = fmaxf(mx, s[i]);
   mx = fmaxf(mx, shfl_xor(mx, 16));
   mx = fmaxf(mx, shfl_xor(mx, 32));
   // Lazy rescaling: the reference max moves only when a score exceeds it by more than
-  // kRescaleSlack, so weights stay <= 2^kRescaleSlack and the accumulator is rescaled on few
-  // steps instead of every step. Any reference value gives the same softmax; the final
-  // normalisation divides it out.
+  // kRescaleSlack, so weights stay <= 2^kRescaleSlack (times the lift) and the accumulator is
+  // rescaled on few steps instead of every step. Any reference value gives the same softmax;
+  // the final normalisation divides it out.
   const float mn = fmaxf(st.m_run, mx);
   const bool upd = mn > st.m_run + kRescaleSlack;  // also true while m_run is -inf
   if (__any(upd)) {
@@ -183,7 +237,7 @@ __device__ __forceinline__ void pair_compute(PairTile<NCH, EPL>& t, WaveState<EP
     for (int e = 0; e < EPL; ++e) st.acc[e] *= alpha;
     st.m_run = m_new;
   }
-  const float mu = st.m_run == kNegInf ? 0.f : st.m_run;
+  const float mu = (st.m_run == kNegInf ? 0.f : st.m_run) - kWeightLift<KT>;
   float p[8];
   float psum = 0.f;
 #pragma unroll
@@ -192,88 +246,51 @@ __device__ __forceinline__ void pair_compute(PairTile<NCH, EPL>& t, WaveState<EP
     psum += p[i];
   }
   st.l_run += psum;
+  split_weights<KT>(p, phi, plo);
+}
 
-  // P^T operand, split into bf16 hi (truncation, exact) + bf16 lo (rounded remainder).
-  uint32_t hw[4], lw[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const uint32_t u0 = __float_as_uint(p[2 * q]), u1 = __float_as_uint(p[2 * q + 1]);
-    hw[q] = pack_hi(u0, u1);
-    const float r0 = p[2 * q] - __uint_as_float(u0 & 0xffff0000u);
-    const float r1 = p[2 * q + 1] - __uint_as_float(u1 & 0xffff0000u);
-    const __bf16 b0 = (__bf16)r0, b1 = (__bf16)r1;
-    lw[q] = (uint32_t)__builtin_bit_cast(uint16_t, b0) |
-            ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
+// q.K, online softmax and p.V for one loaded pair and one 16-row N block (decode).
+template <int KT, int NCH, int EPL>
+__device__ __forceinline__ void pair_compute(PairTile<NCH, EPL>& t, WaveState<EPL>& st,
+                                             const uint4 (&qb)[NCH], float sl2, int kg) {
+  constexpr int BS = 16;
+  float s[8];
+  pair_scores<KT>(t, qb, sl2, s);
+  if (t.lastA < BS || t.lastB < BS) {  // a block holds positions at or past the end
+    mask_stale_scores(t, kg, s);
+    clear_stale_rows(t, kg);
   }
-  const bf16x8 phi = as_bf16x8(make_uint4(hw[0], hw[1], hw[2], hw[3]));
-  const bf16x8 plo = as_bf16x8(make_uint4(lw[0], lw[1], lw[2], lw[3]));
-
-  // V^T operand for output column set e: 8 token slots of column EPL*n16 + e.
+  uint4 phi, plo;
+  softmax_step<KT>(st, s, phi, plo);
 #pragma unroll
   for (int e = 0; e < EPL; ++e) {
-    uint32_t w[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t x = t.vr[2 * q].word(e / 2), y = t.vr[2 * q + 1].word(e / 2);
-      w[q] = (e & 1) ? pack_hi(x, y) : pack_lo(x, y);
-    }
-    const bf16x8 vt = as_bf16x8(make_uint4(w[0], w[1], w[2], w[3]));
-    st.acc[e] = mfma16x16x32(vt, phi, st.acc[e]);
-    st.acc[e] = mfma16x16x32(vt, plo, st.acc[e]);
+    const uint4 vt = vt_operand(t, e);
+    st.acc[e] = mfma16x16x32<KT>(vt, phi, st.acc[e]);
+    st.acc[e] = mfma16x16x32<KT>(vt, plo, st.acc[e]);
   }
 }
 
 // Several N blocks of 16 query rows against one loaded pair (multi-query kernels): the K
 // tiles and the transposed V operand are formed once and serve all NB blocks, so one pass
 // over the keys feeds 16*NB rows. Block nb's rows sit at positions row_pos[nb] (per lane);
-// causal masking applies when `active` (uniform) says some key of the pair lies after the
-// earliest row.
-template <int NCH, int EPL, int NB>
+// keys after a row's position get weight 0 when `active` (uniform) says some key of the pair
+// lies after the earliest row.
+template <int KT, int NCH, int EPL, int NB>
 __device__ __forceinline__ void pair_compute_nb(PairTile<NCH, EPL>& t, WaveState<EPL> (&st)[NB],
-                                                const bf16x8 (&qb)[NB][NCH], float sl2, int kg,
+                                                const uint4 (&qb)[NB][NCH], float sl2, int kg,
                                                 const int (&row_pos)[NB], int key0,
                                                 bool active) {
   constexpr int BS = 16;
   const bool tail = t.lastA < BS || t.lastB < BS;
-  if (tail) {
+  if (tail) clear_stale_rows(t, kg);
+  uint4 vt[EPL];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      t.vr[i].keep_if(4 * kg + i < t.lastA);  // stale rows may hold NaN bits
-      t.vr[4 + i].keep_if(4 * kg + i < t.lastB);
-    }
-  }
-  bf16x8 vt[EPL];
-#pragma unroll
-  for (int e = 0; e < EPL; ++e) {
-    uint32_t w[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t x = t.vr[2 * q].word(e / 2), y = t.vr[2 * q + 1].word(e / 2);
-      w[q] = (e & 1) ? pack_hi(x, y) : pack_lo(x, y);
-    }
-    vt[e] = as_bf16x8(make_uint4(w[0], w[1], w[2], w[3]));
-  }
+  for (int e = 0; e < EPL; ++e) vt[e] = vt_operand(t, e);
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-    floatx4 sA = {0.f, 0.f, 0.f, 0.f}, sB = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ch = 0; ch < NCH; ++ch) {
-      sA = mfma16x16x32(as_bf16x8(t.ka[ch]), qb[nb][ch], sA);
-      sB = mfma16x16x32(as_bf16x8(t.kb[ch]), qb[nb][ch], sB);
-    }
     float s[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      s[i] = sA[i] * sl2;
-      s[4 + i] = sB[i] * sl2;
-    }
-    if (tail) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        s[i] = 4 * kg + i < t.lastA ? s[i] : kNegInf;
-        s[4 + i] = 4 * kg + i < t.lastB ? s[4 + i] : kNegInf;
-      }
-    }
+    pair_scores<KT>(t, qb[nb], sl2, s);
+    if (tail) mask_stale_scores(t, kg, s);
     if (active) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -281,48 +298,12 @@ __device__ __forceinline__ void pair_compute_nb(PairTile<NCH, EPL>& t, WaveState
         s[4 + i] = key0 + BS + 4 * kg + i <= row_pos[nb] ? s[4 + i] : kNegInf;
       }
     }
-    float mx = s[0];
-#pragma unroll
-    for (int i = 1; i < 8; ++i) mx = fmaxf(mx, s[i]);
-    mx = fmaxf(mx, shfl_xor(mx, 16));
-    mx = fmaxf(mx, shfl_xor(mx, 32));
-    const float mn = fmaxf(st[nb].m_run, mx);
-    const bool upd = mn > st[nb].m_run + kRescaleSlack;
-    if (__any(upd)) {
-      const float m_new = upd ? mn : st[nb].m_run;
-      const float alpha =
-          upd ? fast_exp2(st[nb].m_run - (m_new == kNegInf ? 0.f : m_new)) : 1.f;
-      st[nb].l_run *= alpha;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) st[nb].acc[e] *= alpha;
-      st[nb].m_run = m_new;
-    }
-    const float mu = st[nb].m_run == kNegInf ? 0.f : st[nb].m_run;
-    float p[8];
-    float psum = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      p[i] = fast_exp2(s[i] - mu);
-      psum += p[i];
-    }
-    st[nb].l_run += psum;
-    uint32_t hw[4], lw[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t u0 = __float_as_uint(p[2 * q]), u1 = __float_as_uint(p[2 * q + 1]);
-      hw[q] = pack_hi(u0, u1);
-      const float r0 = p[2 * q] - __uint_as_float(u0 & 0xffff0000u);
-      const float r1 = p[2 * q + 1] - __uint_as_float(u1 & 0xffff0000u);
-      const __bf16 b0 = (__bf16)r0, b1 = (__bf16)r1;
-      lw[q] = (uint32_t)__builtin_bit_cast(uint16_t, b0) |
-              ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
-    }
-    const bf16x8 phi = as_bf16x8(make_uint4(hw[0], hw[1], hw[2], hw[3]));
-    const bf16x8 plo = as_bf16x8(make_uint4(lw[0], lw[1], lw[2], lw[3]));
+    uint4 phi, plo;
+    softmax_step<KT>(st[nb], s, phi, plo);
 #pragma unroll
     for (int e = 0; e < EPL; ++e) {
-      st[nb].acc[e] = mfma16x16x32(vt[e], phi, st[nb].acc[e]);
-      st[nb].acc[e] = mfma16x16x32(vt[e], plo, st[nb].acc[e]);
+      st[nb].acc[e] = mfma16x16x32<KT>(vt[e], phi, st[nb].acc[e]);
+      st[nb].acc[e] = mfma16x16x32<KT>(vt[e], plo, st[nb].acc[e]);
     }
   }
 }

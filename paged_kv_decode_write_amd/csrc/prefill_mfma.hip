@@ -20,7 +20,7 @@
 
 namespace pagedkv {
 
-template <int D, int NW, int NB, int MINW>
+template <int D, int NW, int NB, int MINW, int KT, int OT>
 __global__ void __launch_bounds__(NW * 64, MINW)
 prefill_mfma_kernel(const PrefillArgs a) {
   constexpr int BS = 16;
@@ -72,7 +72,7 @@ prefill_mfma_kernel(const PrefillArgs a) {
   const int tok1 = p_max + 1 > 0 ? p_max + 1 : 0;  // keys 0 .. tok1-1 can matter to this wave
   const int blk1 = (tok1 + BS - 1) / BS;
 
-  bf16x8 qb[NB][NCH];
+  uint4 qb[NB][NCH];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     const uint16_t* qrow =
@@ -80,9 +80,8 @@ prefill_mfma_kernel(const PrefillArgs a) {
         8 * kg;
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
-      uint4 w = make_uint4(0, 0, 0, 0);
-      if (row_ok[nb]) w = *reinterpret_cast<const uint4*>(qrow + 32 * c);
-      qb[nb][c] = as_bf16x8(w);
+      qb[nb][c] = make_uint4(0, 0, 0, 0);
+      if (row_ok[nb]) qb[nb][c] = *reinterpret_cast<const uint4*>(qrow + 32 * c);
     }
   }
 
@@ -128,8 +127,7 @@ prefill_mfma_kernel(const PrefillArgs a) {
         ids[u] = pair_ids<D, 1>(ctx, min(jl + 1, np - 1));
         if (j < np) {
           const int key0 = 2 * BS * j;
-          pair_compute_nb<NCH, EPL, NB>(t[u], st, qb, sl2, kg, row_pos, key0,
-                                        key0 + 2 * BS - 1 > p_min);
+          pair_compute_nb<KT>(t[u], st, qb, sl2, kg, row_pos, key0, key0 + 2 * BS - 1 > p_min);
         }
       }
     }
@@ -142,14 +140,14 @@ prefill_mfma_kernel(const PrefillArgs a) {
     l_run += shfl_xor(l_run, 32);
     if (row_ok[nb]) {
       const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-      float* o = a.out + ((size_t)(q0 + tok[nb]) * Hq + (size_t)g * G + head) * D;
+      const size_t o = ((size_t)(q0 + tok[nb]) * Hq + (size_t)g * G + head) * D;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int e = 0; e < EPL; e += 4)
-          *reinterpret_cast<float4*>(o + EPL * (4 * kg + i) + e) =
-              make_float4(st[nb].acc[e][i] * inv, st[nb].acc[e + 1][i] * inv,
-                          st[nb].acc[e + 2][i] * inv, st[nb].acc[e + 3][i] * inv);
+          store_out4<OT>(a.out, o + EPL * (4 * kg + i) + e, st[nb].acc[e][i] * inv,
+                         st[nb].acc[e + 1][i] * inv, st[nb].acc[e + 2][i] * inv,
+                         st[nb].acc[e + 3][i] * inv);
     }
   }
 }
@@ -160,9 +158,12 @@ bool supported_prefill(int head_dim, int group, int block_size) {
 
 int prefill_tokens_per_group(int group, int nb) { return kWavesPerGroup * nb * (16 / group); }
 
+// Register use (and so occupancy) is taken from the bf16 -> fp32 instance of each (D, NB);
+// the other formats differ only in conversions and the output store.
 template <int D, int NB>
 static const void* prefill_kernel_ptr() {
-  return reinterpret_cast<const void*>(&prefill_mfma_kernel<D, kWavesPerGroup, NB, NB == 1 ? 2 : 1>);
+  return reinterpret_cast<const void*>(
+      &prefill_mfma_kernel<D, kWavesPerGroup, NB, NB == 1 ? 2 : 1, kDtBf16, kDtF32>);
 }
 
 // Workgroups of the (D, NB) variant one CU holds at once, asked of the runtime once per
@@ -214,23 +215,26 @@ int prefill_rows_per_wave(int64_t num_tokens, int num_kv_heads, int head_dim, in
 #endif
 }
 
-template <int D>
+template <int D, int KT, int OT>
 static hipError_t launch_prefill_d(const PrefillArgs& a, unsigned grid, hipStream_t stream) {
   constexpr int NW = kWavesPerGroup;
   switch (a.nb) {
-    case 1: hipLaunchKernelGGL((prefill_mfma_kernel<D, NW, 1, 2>), dim3(grid), dim3(NW * 64), 0, stream, a); break;
-    case 2: hipLaunchKernelGGL((prefill_mfma_kernel<D, NW, 2, 1>), dim3(grid), dim3(NW * 64), 0, stream, a); break;
-    case 4: hipLaunchKernelGGL((prefill_mfma_kernel<D, NW, 4, 1>), dim3(grid), dim3(NW * 64), 0, stream, a); break;
+    case 1: hipLaunchKernelGGL((prefill_mfma_kernel<D, NW, 1, 2, KT, OT>), dim3(grid), dim3(NW * 64), 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((prefill_mfma_kernel<D, NW, 2, 1, KT, OT>), dim3(grid), dim3(NW * 64), 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((prefill_mfma_kernel<D, NW, 4, 1, KT, OT>), dim3(grid), dim3(NW * 64), 0, stream, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
 hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t stream) {
-  const long long units = (long long)a.batch * a.num_kv_heads * a.ntiles;
-  if (a.head_dim == 128) return launch_prefill_d<128>(a, (unsigned)units, stream);
-  if (a.head_dim == 64) return launch_prefill_d<64>(a, (unsigned)units, stream);
-  return hipErrorInvalidValue;
+  const unsigned units = (unsigned)((long long)a.batch * a.num_kv_heads * a.ntiles);
+  return with_formats(a.kv_dtype, a.out_dtype, [&](auto kt, auto ot) {
+    constexpr int KT = decltype(kt)::value, OT = decltype(ot)::value;
+    if (a.head_dim == 128) return launch_prefill_d<128, KT, OT>(a, units, stream);
+    if (a.head_dim == 64) return launch_prefill_d<64, KT, OT>(a, units, stream);
+    return hipErrorInvalidValue;
+  });
 }
 
 }  // namespace pagedkv

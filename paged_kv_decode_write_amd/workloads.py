@@ -205,14 +205,15 @@ def to_host_numpy(inp: Dict[str, object]) -> Dict[str, object]:
     return out
 
 
-def algorithmic_bytes(w: Workload, context_lens) -> Dict[str, int]:
-    """Bytes the decode step must move at minimum: K and V of every context token (bf16),
-    q (bf16) and out (fp32); the write moves T rows of K and V in and out."""
+def algorithmic_bytes(w: Workload, context_lens, out_bytes: int = 4) -> Dict[str, int]:
+    """Bytes the decode step must move at minimum: K and V of every context token (16-bit),
+    q (16-bit) and out (out_bytes per element: 4 for fp32, 2 for a 16-bit output); the write
+    moves T rows of K and V in and out."""
     total_tokens = int(sum(int(x) for x in context_lens))
     Hq, Hkv, D, B = w.num_q_heads, w.num_kv_heads, w.head_dim, w.batch
     kv = total_tokens * Hkv * D * 2 * 2
     q = B * Hq * D * 2
-    o = B * Hq * D * 4
+    o = B * Hq * D * out_bytes
     write = B * Hkv * D * 2 * 2 * 2
     return {"kv": kv, "q": q, "out": o, "attention": kv + q + o, "write": write,
             "tokens": total_tokens}

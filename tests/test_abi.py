@@ -31,6 +31,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for want in ("paged_kv_write", "paged_decode_attention", "paged_decode_attention_ex",
+                 "paged_decode_attention_typed", "paged_prefill_attention",
+                 "paged_prefill_attention_ex", "paged_kv_write_rope",
                  "paged_decode_workspace_bytes", "paged_kv_status_string", "paged_kv_abi_version",
                  "paged_kv_last_error", "paged_decode_plan"):
         assert want in names
@@ -46,7 +48,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.paged_kv_abi_version() == 1
+    assert lib.paged_kv_abi_version() == 2
     assert lib.paged_kv_status_string(OK) == b"PAGEDKV_OK"
     assert lib.paged_kv_status_string(ERR_WORKSPACE) == b"PAGEDKV_ERR_WORKSPACE"
     assert lib.paged_kv_status_string(99) == b"PAGEDKV_UNKNOWN_STATUS"
@@ -72,10 +74,13 @@ def test_write_argument_errors(lib):
     assert b"non-NULL" in (_write(lib, k=None) and lib.paged_kv_last_error())
 
 
+BF16, F16, F32 = 0, 1, 2
+
+
 def _attn(lib, q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, MB=8, lens=FAKE, B=2, Hq=32, Hkv=8, D=128,
-          bs=16, NB=64, out=FAKE, ws=None, wsb=0, part=-1, kernel=0):
+          bs=16, NB=64, out=FAKE, ws=None, wsb=0, part=-1, kernel=0, kvt=BF16, ot=F32):
     return lib.paged_decode_attention_ex(q, kc, vc, bt, MB, lens, B, Hq, Hkv, D, bs, NB, 0.1,
-                                         out, ws, wsb, part, kernel, None, None, None)
+                                         kvt, out, ot, ws, wsb, part, kernel, None, None, None)
 
 
 def test_attention_argument_errors(lib):
@@ -92,10 +97,27 @@ def test_attention_argument_errors(lib):
     assert _attn(lib, B=0, q=None, out=None) == OK  # empty batch: no-op
 
 
+def test_format_pairs(lib):
+    # bf16 or fp16 inputs; fp32 output or the input's own format (checked before any sizes)
+    for kvt, ot in ((BF16, F32), (BF16, BF16), (F16, F32), (F16, F16)):
+        assert _attn(lib, B=0, q=None, out=None, kvt=kvt, ot=ot) == OK
+        assert _prefill(lib, T=0, q=None, out=None, kvt=kvt, ot=ot) == OK
+    for kvt, ot in ((BF16, F16), (F16, BF16), (F32, F32), (3, F32), (BF16, 7), (-1, F32)):
+        assert _attn(lib, kvt=kvt, ot=ot) == ERR_UNSUPPORTED
+        assert _prefill(lib, kvt=kvt, ot=ot) == ERR_UNSUPPORTED
+    assert b"format" in lib.paged_kv_last_error()
+    st = lib.paged_decode_attention_typed(FAKE, FAKE, FAKE, FAKE, 8, FAKE, 0, 32, 8, 128, 16, 64,
+                                          0.1, F16, None, F16, None, 0, 0, None)
+    assert st == OK
+    st = lib.paged_decode_attention_typed(FAKE, FAKE, FAKE, FAKE, 8, FAKE, 2, 32, 8, 128, 16, 64,
+                                          0.1, F16, FAKE, BF16, None, 0, 0, None)
+    assert st == ERR_UNSUPPORTED
+
+
 def _prefill(lib, q=FAKE, cu=FAKE, T=8, maxq=4, kc=FAKE, vc=FAKE, bt=FAKE, MB=8, lens=FAKE,
-             B=2, Hq=32, Hkv=8, D=128, bs=16, NB=64, out=FAKE, rb=0):
+             B=2, Hq=32, Hkv=8, D=128, bs=16, NB=64, out=FAKE, rb=0, kvt=BF16, ot=F32):
     return lib.paged_prefill_attention_ex(q, cu, T, maxq, kc, vc, bt, MB, lens, B, Hq, Hkv, D,
-                                          bs, NB, 0.1, out, rb, None)
+                                          bs, NB, 0.1, kvt, out, ot, rb, None)
 
 
 def test_prefill_argument_errors(lib):
