@@ -48,6 +48,8 @@ def parse_args():
     p.add_argument("--out-dtype", default="f32", choices=["f32", "bf16", "f16"],
                    help="attention output format: f32 or the input format")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-read-probe", action="store_true",
+                   help="skip the plain streaming-read reference after the timed steps")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="CPU work budget of the oracle baseline sample")
     p.add_argument("--json-out", default=None)
@@ -68,11 +70,17 @@ def parse_args():
 
 
 class HipEvents:
-    """hipEvent_t handles from the HIP runtime torch has already loaded."""
+    """hipEvent_t handles from the HIP runtime torch has already loaded. They are created
+    timing-only (hipEventDisableSystemFence): recording them performs no system-scope fence,
+    so they neither add a cache write-back to the measured interval nor disturb the next
+    kernel; the host reads them only after a full device synchronisation."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000  # hipEventDisableSystemFence (hip_runtime_api.h)
 
     def __init__(self):
         self.hip = ctypes.CDLL("libamdhip64.so.7")
-        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p),
+                                                     ctypes.c_uint]
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
                                                  ctypes.c_void_p, ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
@@ -80,8 +88,8 @@ class HipEvents:
 
     def create(self):
         ev = ctypes.c_void_p()
-        if self.hip.hipEventCreate(ctypes.byref(ev)) != 0:
-            raise RuntimeError("hipEventCreate failed")
+        if self.hip.hipEventCreateWithFlags(ctypes.byref(ev), self.DISABLE_SYSTEM_FENCE) != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed")
         self.events.append(ev.value)
         return ev.value
 
@@ -112,6 +120,39 @@ def resolved_kernel(pk, w, requested):
         return requested
     return pk.decode_plan(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.max_blocks,
                           w.block_size, 0, "auto", with_kernel=True)[2]
+
+
+def read_probe(torch, dev, nbytes, reps=5):
+    """Achievable streaming-read rate at this byte count: a plain grid-stride read kernel
+    (libpagedkv_probe.so) over a buffer of nbytes, cold (a 1 GiB buffer is read in between so
+    neither L2 nor the MALL holds it), timed with events. Returns (median us, GB/s)."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(HERE, "paged_kv_decode_write_amd", "libpagedkv_probe.so"))
+    lib.pagedkv_read_probe.restype = ctypes.c_int
+    lib.pagedkv_read_probe.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                       ctypes.c_int32, ctypes.c_void_p]
+    grid = 256 * 16
+    nbytes = (nbytes + 15) // 16 * 16
+    buf = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    flush = torch.ones((1 << 30) // 4, dtype=torch.float32, device=dev)
+    sink = torch.zeros(grid, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    times = []
+    for i in range(reps + 1):
+        if lib.pagedkv_read_probe(flush.data_ptr(), flush.numel() * 4, sink.data_ptr(), grid,
+                                  stream):
+            raise RuntimeError("read probe launch failed")
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        if lib.pagedkv_read_probe(buf.data_ptr(), nbytes, sink.data_ptr(), grid, stream):
+            raise RuntimeError("read probe launch failed")
+        b.record()
+        torch.cuda.synchronize()
+        if i:
+            times.append(a.elapsed_time(b) * 1e3)
+    del buf, flush, sink
+    us = sorted(times)[len(times) // 2]
+    return us, nbytes / (us * 1e-6) / 1e9
 
 
 def cpu_baseline(d, seconds):
@@ -352,6 +393,12 @@ def main():
         torch.cuda.synchronize()
         graph_ms = (time.perf_counter() - g0) * 1e3 / args.steps
 
+    probe = {}
+    if not args.no_read_probe:
+        for d in subs:
+            us, gbs = read_probe(torch, dev, d["bytes"]["attention"])
+            probe[d["workload"].name] = {"us": round(us, 2), "GBps": round(gbs, 1)}
+
     step_bytes = sum(d["bytes"]["attention"] + d["bytes"]["write"] for d in subs)
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     launch_bytes = sum(d["bytes"]["attention"] for d in subs) / len(subs)
@@ -405,6 +452,10 @@ def main():
     }
     if graph_ms is not None:
         line["graph_ms_per_step"] = round(graph_ms, 4)
+    if probe:
+        # plain streaming read (cold) of the attention's algorithmic bytes: the rate HBM
+        # delivers to a simple kernel on this part, beside the 8 TB/s vendor peak
+        line["read_probe"] = probe
     if not args.no_cpu_baseline and (args.in_dtype, args.out_dtype) == ("bf16", "f32"):
         line["cpu_baseline"] = cpu_baseline(subs[0], args.cpu_seconds)
     out = json.dumps(line)

@@ -1,0 +1,30 @@
+/*
+ * paged_kv_probe.h -- measurement utility, libpagedkv_probe.so (not part of the attention
+ * path or of libpagedkv.so).
+ *
+ * pagedkv_read_probe -- read `bytes` (rounded down to a multiple of 16) of device memory at
+ * `buf` (16-byte aligned) with a grid-stride kernel of `grid` workgroups of 256 threads, on
+ * `stream`, asynchronously. `sink` (device, >= grid uint32 words) receives a word only in the
+ * rare case that a block's XOR of its data equals a fixed sentinel; it exists so the loads
+ * cannot be optimised away. Time the launch with events to obtain the achievable streaming-read
+ * rate. Returns 0, 1 for a bad argument, or 5 if the launch failed.
+ */
+#ifndef PAGED_KV_PROBE_H
+#define PAGED_KV_PROBE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+int pagedkv_read_probe(const void* buf, size_t bytes, uint32_t* sink, int32_t grid,
+                       hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGED_KV_PROBE_H */

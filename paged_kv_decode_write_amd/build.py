@@ -20,6 +20,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(HERE, "libpagedkv.so")
+PROBE_OUT = os.path.join(HERE, "libpagedkv_probe.so")
+PROBE_SOURCES = ["read_probe.hip"]  # measurement utility, a library of its own
 
 SOURCES = ["api.cpp", "kv_write.hip", "decode_valu.hip", "decode_mfma.hip", "decode_reduce.hip",
            "prefill_mfma.hip", "kv_write_rope.hip"]
@@ -53,20 +55,31 @@ def compile_one(src: str, obj: str, extra=()) -> None:
         sys.stderr.write(warn + "\n")
 
 
-def build(out: str = OUT, jobs: int = 8, extra=()) -> str:
+def link(sources, out: str, jobs: int = 8, extra=()) -> str:
     with tempfile.TemporaryDirectory(prefix="pagedkv_build_") as tmp:
-        objs = [os.path.join(tmp, os.path.splitext(s)[0] + ".o") for s in SOURCES]
-        with ThreadPoolExecutor(max_workers=min(jobs, len(SOURCES))) as ex:
-            list(ex.map(lambda so: compile_one(so[0], so[1], extra), zip(SOURCES, objs)))
+        objs = [os.path.join(tmp, os.path.splitext(s)[0] + ".o") for s in sources]
+        with ThreadPoolExecutor(max_workers=min(jobs, len(sources))) as ex:
+            list(ex.map(lambda so: compile_one(so[0], so[1], extra), zip(sources, objs)))
         tmp_out = out + ".tmp"
         cmd = [hipcc(), *common_flags(extra), "-shared", *objs, "-o", tmp_out]
         res = subprocess.run(cmd, capture_output=True, text=True)
         if res.returncode != 0:
             sys.stderr.write(" ".join(cmd) + "\n" + res.stdout + res.stderr)
-            raise RuntimeError("linking libpagedkv.so failed")
+            raise RuntimeError(f"linking {os.path.basename(out)} failed")
         os.replace(tmp_out, out)
     return out
 
 
+def build(out: str = OUT, jobs: int = 8, extra=()) -> str:
+    """Build libpagedkv.so (the path) at `out`."""
+    return link(SOURCES, out, jobs, extra)
+
+
+def build_probe(out: str = PROBE_OUT) -> str:
+    """Build libpagedkv_probe.so (the streaming-read measurement utility)."""
+    return link(PROBE_SOURCES, out)
+
+
 if __name__ == "__main__":
     print(build())
+    print(build_probe())
