@@ -47,6 +47,8 @@ def parse_args():
                    help="format of q and the K/V pools")
     p.add_argument("--out-dtype", default="f32", choices=["f32", "bf16", "f16"],
                    help="attention output format: f32 or the input format")
+    p.add_argument("--row-blocks", type=int, default=0, choices=[0, 1, 2, 4],
+                   help="multi-query workloads: 16-row query blocks per wave (0 = library's choice)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-read-probe", action="store_true",
                    help="skip the plain streaming-read reference after the timed steps")
@@ -216,7 +218,7 @@ def bench_prefill(args, torch, pk, wl):
             ev[0].record()
         pk.paged_prefill_attention(d["q"], d["cu_seqlens_q"], d["k_cache"], d["v_cache"],
                                    d["block_tables"], d["context_lens"], d["scale"], out,
-                                   max_q_len=d["max_q_len"])
+                                   max_q_len=d["max_q_len"], row_blocks=args.row_blocks)
         if ev is not None:
             ev[1].record()
 
@@ -242,6 +244,7 @@ def bench_prefill(args, torch, pk, wl):
         "vs_baseline": None, "dtype": args.in_dtype,
         "data": f"synthetic (seeded N(0,1) {args.in_dtype}), resident in HBM",
         "config": {"workload": w.description, "kernel": "prefill_mfma",
+                   "row_blocks": args.row_blocks,
                    "formats": f"{args.in_dtype} in, {args.out_dtype} out",
                    "us_per_call": round(mean * 1e3, 2),
                    "GBps": round(alg["bytes"] / (mean * 1e-3) / 1e9, 1),

@@ -130,8 +130,7 @@ decode_mfma_kernel(const DecodeArgs a) {
 
   // Sum of the running sums over the four lanes of a head.
   float l_run = st.l_run;
-  l_run += shfl_xor(l_run, 16);
-  l_run += shfl_xor(l_run, 32);
+  l_run = row4_sum(l_run);
 
   __shared__ float sm_m[NW][16], sm_l[NW][16];
   __shared__ float sm_acc[NW][16][DP];
@@ -279,8 +278,7 @@ decode_mfma_hw_kernel(const DecodeArgs a) {
   }
 
   float l_run = st.l_run;
-  l_run += shfl_xor(l_run, 16);
-  l_run += shfl_xor(l_run, 32);
+  l_run = row4_sum(l_run);
   const bool hv = n16 < G;
   const size_t row0 = (size_t)b * Hq + (size_t)g * G;  // first query head of KV head g
   if (nparts == 1) {

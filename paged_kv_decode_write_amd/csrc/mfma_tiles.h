@@ -21,6 +21,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __fp16 fp16x2 __attribute__((ext_vector_type(2)));  // v_cvt_pkrtz result
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // One 16x16x32 product with fp32 accumulate; a and b hold 8 packed 16-bit values of the input
 // format KT (bf16 or fp16).
@@ -88,11 +90,9 @@ __device__ __forceinline__ void split_weights(const float (&p)[8], uint4& hi, ui
     } else {
       const uint32_t u0 = __float_as_uint(p[2 * q]), u1 = __float_as_uint(p[2 * q + 1]);
       hw[q] = __builtin_amdgcn_perm(u1, u0, 0x07060302u);
-      const float r0 = p[2 * q] - __uint_as_float(u0 & 0xffff0000u);
-      const float r1 = p[2 * q + 1] - __uint_as_float(u1 & 0xffff0000u);
-      const __bf16 b0 = (__bf16)r0, b1 = (__bf16)r1;
-      lw[q] = (uint32_t)__builtin_bit_cast(uint16_t, b0) |
-              ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
+      const floatx2 r = {p[2 * q] - __uint_as_float(u0 & 0xffff0000u),
+                         p[2 * q + 1] - __uint_as_float(u1 & 0xffff0000u)};
+      lw[q] = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2));  // one cvt_pk
     }
   }
   hi = make_uint4(hw[0], hw[1], hw[2], hw[3]);
@@ -213,16 +213,18 @@ __device__ __forceinline__ void mask_stale_scores(const PairTile<NCH, EPL>& t, i
   }
 }
 
-// Online-softmax update of one N block with the pair's scores s; returns the weights (lifted
-// by kWeightLift) split into the hi / lo P^T operands.
+// Online-softmax update of one N block with the pair's scores s (log2 units, masked ones
+// -inf); returns the weights (lifted by kWeightLift) split into the hi / lo P^T operands. The
+// exponent of a weight is the difference s - m of two fp32 values, so the weight of a score
+// equal to the reference max is exactly 1 (a one-token context returns its value row
+// exactly); a fused s * sl2 - m would leave the product's rounding error in that exponent.
 template <int KT, int EPL>
 __device__ __forceinline__ void softmax_step(WaveState<EPL>& st, const float (&s)[8], uint4& phi,
                                              uint4& plo) {
   float mx = s[0];
 #pragma unroll
   for (int i = 1; i < 8; ++i) mx = fmaxf(mx, s[i]);
-  mx = fmaxf(mx, shfl_xor(mx, 16));
-  mx = fmaxf(mx, shfl_xor(mx, 32));
+  mx = row4_max(mx);
   // Lazy rescaling: the reference max moves only when a score exceeds it by more than
   // kRescaleSlack, so weights stay <= 2^kRescaleSlack (times the lift) and the accumulator is
   // rescaled on few steps instead of every step. Any reference value gives the same softmax;

@@ -7,12 +7,22 @@
 // step 4), done over the paged cache as the ragged, padding-free attention over block tables
 // that llm-stack's Roadmap plans, with grouped-query heads.
 //
-// Work decomposition: a workgroup of NW waves takes one KV head g of one sequence and
-// NW*NB*R consecutive query tokens; each wave owns NB MFMA N blocks of 16 query rows, each
-// block R = 16/G tokens x the G query heads of g. The wave streams the key blocks 0..(its
-// last row's position) in pairs, as the decode kernels do (mfma_tiles.h); each loaded pair
-// (K tiles and the transposed V operand) serves all NB blocks, with a per-lane causal mask on
-// the pairs that reach past the wave's first row. Rows are written normalised.
+// Work decomposition: a workgroup of 4 waves takes one KV head g of one sequence and
+// 4*NB*R consecutive query tokens; each wave owns NB MFMA N blocks of 16 query rows, each
+// block R = 16/G tokens x the G query heads of g. Query tiles are counted from the end of each
+// sequence and the tile index is the slowest grid dimension, so every sequence's last tile
+// (the most keys under the causal mask) is dispatched first: a longest-job-first order for the
+// uneven causal work.
+//
+// The four waves read the same keys. Each 32-key pair (both 16-token blocks, K and V) is
+// brought from memory once per workgroup: every thread loads 16-byte pieces into registers,
+// which are written to one of two LDS buffers while the waves compute on the other; one
+// barrier per pair. Each wave then takes its MFMA operands from LDS (K rows, and V rows for the
+// in-register transpose) and runs the tiles of mfma_tiles.h on its NB blocks, with a per-lane
+// causal mask on the pairs that reach past its first row. Key slots at or past the
+// workgroup's last position are stored as zeros, so stale cache contents (NaN included) never
+// reach p.V; every such key is after every row's position, so the causal mask gives it
+// weight 0. Rows are written normalised.
 #include "launch.h"
 #include "mfma_tiles.h"
 
@@ -20,12 +30,111 @@
 
 namespace pagedkv {
 
+namespace {
+
+constexpr int kPairRows = 32;  // keys per staged pair
+
+// LDS row pitch in bytes: a token row of D 16-bit values plus 16 bytes, so the 16 rows that
+// one ds_read_b128 wave access touches start in different banks.
+template <int D> constexpr int lds_pitch() { return D * 2 + 16; }
+
+template <int D> struct LdsPair {
+  alignas(16) unsigned char k[kPairRows * lds_pitch<D>()];
+  alignas(16) unsigned char v[kPairRows * lds_pitch<D>()];
+};
+
+// One thread's share of a pair, kPieces 16-byte pieces of K and of V. Piece x of thread t is
+// row r = (t + 256x) / (D/8) of the pair (rows 0-15: first block, 16-31: second) and 16 bytes
+// at column (t + 256x) % (D/8). With 64 threads covering 64/(D/8) whole rows, the block a
+// piece falls in is the same for the whole wave, so block base addresses stay scalar and a
+// load is a scalar base plus a per-thread 32-bit offset fixed for the whole kernel.
+template <int D> struct Stager {
+  static constexpr int kCPR = D / 8;                           // pieces per row
+  static constexpr int kPieces = kPairRows * kCPR / 256;      // per thread: D 64 -> 1, 128 -> 2
+  uint4 k[kPieces], v[kPieces];
+  uint32_t goff[kPieces];  // byte offset of the piece inside its block (row, head, column)
+  uint32_t loff[kPieces];  // byte offset of the piece in an LdsPair buffer
+  int row[kPieces];        // r
+  int blk[kPieces];        // 0 or 1: block of the pair (uniform over the wave)
+
+  __device__ __forceinline__ void init(int wave, size_t row_stride, size_t head_off) {
+#pragma unroll
+    for (int x = 0; x < kPieces; ++x) {
+      const int idx = threadIdx.x + 256 * x;
+      const int r = idx / kCPR, c = idx % kCPR;
+      row[x] = r;
+      blk[x] = (wave * (64 / kCPR) + x * (256 / kCPR)) / 16;
+      goff[x] = (uint32_t)(((size_t)(r & 15) * row_stride + head_off + 8 * c) * 2);
+      loff[x] = (uint32_t)(r * lds_pitch<D>() + 16 * c);
+    }
+  }
+
+  // Load pair `pair`. A block id outside the pool, and rows at or past tok1 (only in the last
+  // pair), give zeros; their loads read block 0 instead.
+  __device__ __forceinline__ void load(const PrefillArgs& a, const int32_t* table, int nblk,
+                                       int tok1, size_t row_stride, int pair) {
+    const int jA = 2 * pair;
+    const int idA = table[jA];
+    const int idB = jA + 1 < nblk ? table[jA + 1] : -1;
+    const bool okA = idA >= 0 && (int64_t)idA < a.num_blocks;
+    const bool okB = idB >= 0 && (int64_t)idB < a.num_blocks;
+    const size_t bbytes = (size_t)16 * row_stride * 2;  // bytes of one block
+    const char* kc = reinterpret_cast<const char*>(a.k_cache);
+    const char* vc = reinterpret_cast<const char*>(a.v_cache);
+    const bool tail = 32 * pair + 32 > tok1;  // uniform
+#pragma unroll
+    for (int x = 0; x < kPieces; ++x) {
+      const bool okb = blk[x] ? okB : okA;
+      const size_t base = (size_t)(okb ? (blk[x] ? idB : idA) : 0) * bbytes;
+      const uint4 kw = *reinterpret_cast<const uint4*>(kc + base + goff[x]);
+      const uint4 vw = *reinterpret_cast<const uint4*>(vc + base + goff[x]);
+      const bool ok = okb && (!tail || 32 * pair + row[x] < tok1);
+      k[x] = ok ? kw : make_uint4(0, 0, 0, 0);
+      v[x] = ok ? vw : make_uint4(0, 0, 0, 0);
+    }
+  }
+
+  __device__ __forceinline__ void commit(LdsPair<D>& p) const {
+#pragma unroll
+    for (int x = 0; x < kPieces; ++x) {
+      *reinterpret_cast<uint4*>(p.k + loff[x]) = k[x];
+      *reinterpret_cast<uint4*>(p.v + loff[x]) = v[x];
+    }
+  }
+};
+
+// A wave's MFMA operands of a staged pair, in the register tile the shared tiles expect:
+// K rows n16 (first block) and 16 + n16 (second), columns 32ch + 8kg .. +7; V rows 4kg + j
+// and 16 + 4kg + j, columns EPL*n16 .. +EPL-1. Both blocks count as full (lastA = lastB = 16):
+// the zeros and the causal mask take care of positions past the end.
+template <int D, int NCH, int EPL>
+__device__ __forceinline__ void read_pair(PairTile<NCH, EPL>& t, const LdsPair<D>& p, int n16,
+                                          int kg) {
+  constexpr int P = lds_pitch<D>();
+#pragma unroll
+  for (int ch = 0; ch < NCH; ++ch) {
+    t.ka[ch] = *reinterpret_cast<const uint4*>(p.k + n16 * P + 2 * (32 * ch + 8 * kg));
+    t.kb[ch] = *reinterpret_cast<const uint4*>(p.k + (16 + n16) * P + 2 * (32 * ch + 8 * kg));
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    t.vr[j].load(reinterpret_cast<const uint16_t*>(p.v + (4 * kg + j) * P + 2 * EPL * n16));
+    t.vr[4 + j].load(
+        reinterpret_cast<const uint16_t*>(p.v + (16 + 4 * kg + j) * P + 2 * EPL * n16));
+  }
+  t.lastA = 16;
+  t.lastB = 16;
+}
+
+}  // namespace
+
 template <int D, int NW, int NB, int MINW, int KT, int OT>
 __global__ void __launch_bounds__(NW * 64, MINW)
 prefill_mfma_kernel(const PrefillArgs a) {
-  constexpr int BS = 16;
   constexpr int NCH = D / 32;
   constexpr int EPL = D / 16;
+  static_assert(NW == 4, "the staging split assumes 256 threads");
+  __shared__ LdsPair<D> buf[2];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -36,10 +145,7 @@ prefill_mfma_kernel(const PrefillArgs a) {
   const int Hkv = a.num_kv_heads;
   const int G = Hq / Hkv;
   const int R = 16 / G;  // query tokens per N block
-  // Tiles are counted from the end of each sequence and the tile index is the slowest grid
-  // dimension, so every sequence's last tile (the one with the most keys under the causal
-  // mask) is dispatched first and the light leading tiles fill in behind: a
-  // longest-job-first order for the uneven causal work.
+  // Tiles counted from the end of each sequence, tile index slowest (see the top of the file).
   const int unit = blockIdx.x;
   const int bg = unit % (a.batch * Hkv);
   const int tile = unit / (a.batch * Hkv);
@@ -49,14 +155,16 @@ prefill_mfma_kernel(const PrefillArgs a) {
   const int q0 = a.cu_seqlens_q[b];
   int Q = a.cu_seqlens_q[b + 1] - q0;
   Q = Q < 0 ? 0 : Q;
-  const int tok_end = Q - (tile * NW + wave) * NB * R;  // one past this wave's last token
-  if (tok_end <= 0) return;                             // no barriers: waves are independent
-  const int tok_base = tok_end - NB * R;                // may be negative: rows < 0 are idle
+  const int wg_end = Q - tile * NW * NB * R;  // one past the workgroup's last token
+  if (wg_end <= 0) return;                    // uniform over the workgroup: before any barrier
   int L = a.context_lens[b];
-  const int Lmax = a.max_blocks * BS;
+  const int Lmax = a.max_blocks * 16;
   L = L < 0 ? 0 : (L > Lmax ? Lmax : L);
 
-  // Lane row of N block nb: token tok_base + nb*R + n16/G, head n16 % G.
+  // This wave's tokens (possibly none: it still loads and meets every barrier).
+  const int tok_end = wg_end - wave * NB * R;
+  const int tok_base = tok_end - NB * R;
+  const bool wave_rows = tok_end > 0;
   const int head = n16 % G;
   int tok[NB], row_pos[NB];
   bool row_ok[NB];
@@ -64,13 +172,15 @@ prefill_mfma_kernel(const PrefillArgs a) {
   for (int nb = 0; nb < NB; ++nb) {
     tok[nb] = tok_base + nb * R + n16 / G;
     row_ok[nb] = n16 < R * G && tok[nb] >= 0;
-    row_pos[nb] = row_ok[nb] ? L - Q + tok[nb] : -1;  // < 0: no key (only when Q > L)
+    row_pos[nb] = row_ok[nb] ? L - Q + tok[nb] : -1;
   }
   const int first_tok = tok_base > 0 ? tok_base : 0;
   const int p_min = L - Q + first_tok;
-  const int p_max = L - Q + tok_end - 1;
-  const int tok1 = p_max + 1 > 0 ? p_max + 1 : 0;  // keys 0 .. tok1-1 can matter to this wave
-  const int blk1 = (tok1 + BS - 1) / BS;
+  const int p_max = L - Q + tok_end - 1;        // this wave's last position
+  const int wg_p_max = L - Q + wg_end - 1;      // the workgroup's (wave 0's) last position
+  const int tok1 = wg_p_max + 1 > 0 ? wg_p_max + 1 : 0;
+  const int nblk = (tok1 + 15) / 16;
+  const int np = (nblk + 1) / 2;
 
   uint4 qb[NB][NCH];
 #pragma unroll
@@ -94,50 +204,35 @@ prefill_mfma_kernel(const PrefillArgs a) {
     for (int e = 0; e < EPL; ++e) st[nb].acc[e] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
 
-  PairCtx<D> ctx;
-  ctx.k_cache = a.k_cache;
-  ctx.v_cache = a.v_cache;
-  ctx.table = a.block_tables + (size_t)b * a.max_blocks;
-  ctx.row_stride = (size_t)Hkv * D;
-  ctx.head_off = (size_t)g * D;
-  ctx.num_blocks = a.num_blocks;
-  ctx.blk0 = 0;
-  ctx.blk1 = blk1;
-  ctx.tok1 = tok1;
-  ctx.wave = 0;
-  ctx.n16 = n16;
-  ctx.kg = kg;
+  const int32_t* table = a.block_tables + (size_t)b * a.max_blocks;
+  const size_t row_stride = (size_t)Hkv * D;
+  const size_t head_off = (size_t)g * D;
   const float sl2 = a.scale_log2;
 
-  // Key pairs (2k, 2k+1), two in flight, loads unconditional (see the decode kernels).
-  const int np = (blk1 + 1) / 2;
   if (np > 0) {
-    PairTile<NCH, EPL> t[2];
-    int2 ids[2];
-    ids[0] = pair_ids<D, 1>(ctx, 0);
-    ids[1] = pair_ids<D, 1>(ctx, min(1, np - 1));
-    pair_load<D, 1>(t[0], ctx, ids[0], 0);
-    for (int k = 0; k < np; k += 2) {
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int j = k + u;
-        const int jl = min(j + 1, np - 1);
-        const int ub = (u + 1) % 2;
-        pair_load<D, 1>(t[ub], ctx, ids[ub], jl);
-        ids[u] = pair_ids<D, 1>(ctx, min(jl + 1, np - 1));
-        if (j < np) {
-          const int key0 = 2 * BS * j;
-          pair_compute_nb<KT>(t[u], st, qb, sl2, kg, row_pos, key0, key0 + 2 * BS - 1 > p_min);
-        }
+    Stager<D> s;
+    s.init(wave, row_stride, head_off);
+    s.load(a, table, nblk, tok1, row_stride, 0);
+    s.commit(buf[0]);
+    __syncthreads();
+    for (int k = 0; k < np; ++k) {
+      const bool more = k + 1 < np;  // uniform
+      if (more) s.load(a, table, nblk, tok1, row_stride, k + 1);
+      const int key0 = 32 * k;
+      if (wave_rows && key0 <= p_max) {
+        PairTile<NCH, EPL> t;
+        read_pair<D>(t, buf[k & 1], n16, kg);
+        pair_compute_nb<KT>(t, st, qb, sl2, kg, row_pos, key0, key0 + 31 > p_min);
       }
+      if (more) s.commit(buf[(k + 1) & 1]);
+      __syncthreads();
     }
   }
 
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     float l_run = st[nb].l_run;
-    l_run += shfl_xor(l_run, 16);
-    l_run += shfl_xor(l_run, 32);
+    l_run = row4_sum(l_run);
     if (row_ok[nb]) {
       const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
       const size_t o = ((size_t)(q0 + tok[nb]) * Hq + (size_t)g * G + head) * D;
@@ -158,16 +253,18 @@ bool supported_prefill(int head_dim, int group, int block_size) {
 
 int prefill_tokens_per_group(int group, int nb) { return kWavesPerGroup * nb * (16 / group); }
 
+template <int NB> constexpr int prefill_min_waves() { return NB == 4 ? 1 : 2; }
+
 // Register use (and so occupancy) is taken from the bf16 -> fp32 instance of each (D, NB);
 // the other formats differ only in conversions and the output store.
 template <int D, int NB>
 static const void* prefill_kernel_ptr() {
   return reinterpret_cast<const void*>(
-      &prefill_mfma_kernel<D, kWavesPerGroup, NB, NB == 1 ? 2 : 1, kDtBf16, kDtF32>);
+      &prefill_mfma_kernel<D, kWavesPerGroup, NB, prefill_min_waves<NB>(), kDtBf16, kDtF32>);
 }
 
 // Workgroups of the (D, NB) variant one CU holds at once, asked of the runtime once per
-// device (it follows from the variant's register count).
+// device (it follows from the variant's registers and LDS).
 static int prefill_groups_per_cu(int head_dim, int nb_index) {
   static std::mutex mu;
   static int cache[256][2][3];
@@ -189,29 +286,23 @@ static int prefill_groups_per_cu(int head_dim, int nb_index) {
   return slot;
 }
 
-// N blocks of 16 query rows per wave (1, 2 or 4). A larger NB reuses every loaded key/value
-// pair for more rows but holds more registers, so fewer workgroups fit on a CU, and it cuts
-// the query rows into fewer workgroups. The launch takes the largest NB whose workgroups
-// (counted from the total query rows, a lower bound for ragged batches) still fill the
-// resident slots at least twice, so the longest-first order can balance them. NB stops at 2
-// for head_dim 64: there NB = 4 drops the variant from two waves per SIMD to one, which
-// measured slower than the extra reuse gains; at head_dim 128 NB = 2 and 4 both hold one wave
-// per SIMD. A build may pin NB with PAGEDKV_PREFILL_NB.
+// N blocks of 16 query rows per wave. A larger NB computes more rows per staged pair but holds
+// more registers, and it cuts the query rows into fewer workgroups. The launch takes NB = 2
+// when its workgroups (counted from the total query rows, a lower bound for ragged batches)
+// fill the resident slots at least twice, so the longest-first order can balance them, and
+// NB = 1 otherwise. NB = 4 (callers may ask for it) needs more registers than a SIMD holds
+// for two waves and measured slower on every workload. A build may pin NB with
+// PAGEDKV_PREFILL_NB.
 int prefill_rows_per_wave(int64_t num_tokens, int num_kv_heads, int head_dim, int group,
                           int cus) {
 #ifdef PAGEDKV_PREFILL_NB
   (void)num_tokens; (void)num_kv_heads; (void)head_dim; (void)group; (void)cus;
   return PAGEDKV_PREFILL_NB;
 #else
-  const int max_index = head_dim >= 128 ? 2 : 1;
-  for (int i = max_index; i > 0; --i) {
-    const int nb = 1 << i;
-    const int64_t per_group = prefill_tokens_per_group(group, nb);
-    const int64_t units = (int64_t)num_kv_heads * ((num_tokens + per_group - 1) / per_group);
-    const int64_t slots = (int64_t)cus * prefill_groups_per_cu(head_dim, i);
-    if (units >= 2 * slots) return nb;
-  }
-  return 1;
+  const int64_t per_group = prefill_tokens_per_group(group, 2);
+  const int64_t units = (int64_t)num_kv_heads * ((num_tokens + per_group - 1) / per_group);
+  const int64_t slots = (int64_t)cus * prefill_groups_per_cu(head_dim, 1);
+  return units >= 2 * slots ? 2 : 1;
 #endif
 }
 
@@ -219,9 +310,9 @@ template <int D, int KT, int OT>
 static hipError_t launch_prefill_d(const PrefillArgs& a, unsigned grid, hipStream_t stream) {
   constexpr int NW = kWavesPerGroup;
   switch (a.nb) {
-    case 1: hipLaunchKernelGGL((prefill_mfma_kernel<D, NW, 1, 2, KT, OT>), dim3(grid), dim3(NW * 64), 0, stream, a); break;
-    case 2: hipLaunchKernelGGL((prefill_mfma_kernel<D, NW, 2, 1, KT, OT>), dim3(grid), dim3(NW * 64), 0, stream, a); break;
-    case 4: hipLaunchKernelGGL((prefill_mfma_kernel<D, NW, 4, 1, KT, OT>), dim3(grid), dim3(NW * 64), 0, stream, a); break;
+    case 1: hipLaunchKernelGGL((prefill_mfma_kernel<D, NW, 1, prefill_min_waves<1>(), KT, OT>), dim3(grid), dim3(NW * 64), 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((prefill_mfma_kernel<D, NW, 2, prefill_min_waves<2>(), KT, OT>), dim3(grid), dim3(NW * 64), 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((prefill_mfma_kernel<D, NW, 4, prefill_min_waves<4>(), KT, OT>), dim3(grid), dim3(NW * 64), 0, stream, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

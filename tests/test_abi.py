@@ -78,8 +78,9 @@ BF16, F16, F32 = 0, 1, 2
 
 
 def _attn(lib, q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, MB=8, lens=FAKE, B=2, Hq=32, Hkv=8, D=128,
-          bs=16, NB=64, out=FAKE, ws=None, wsb=0, part=-1, kernel=0, kvt=BF16, ot=F32):
-    return lib.paged_decode_attention_ex(q, kc, vc, bt, MB, lens, B, Hq, Hkv, D, bs, NB, 0.1,
+          bs=16, NB=64, out=FAKE, ws=None, wsb=0, part=-1, kernel=0, kvt=BF16, ot=F32,
+          scale=0.1):
+    return lib.paged_decode_attention_ex(q, kc, vc, bt, MB, lens, B, Hq, Hkv, D, bs, NB, scale,
                                          kvt, out, ot, ws, wsb, part, kernel, None, None, None)
 
 
@@ -115,9 +116,10 @@ def test_format_pairs(lib):
 
 
 def _prefill(lib, q=FAKE, cu=FAKE, T=8, maxq=4, kc=FAKE, vc=FAKE, bt=FAKE, MB=8, lens=FAKE,
-             B=2, Hq=32, Hkv=8, D=128, bs=16, NB=64, out=FAKE, rb=0, kvt=BF16, ot=F32):
+             B=2, Hq=32, Hkv=8, D=128, bs=16, NB=64, out=FAKE, rb=0, kvt=BF16, ot=F32,
+             scale=0.1):
     return lib.paged_prefill_attention_ex(q, cu, T, maxq, kc, vc, bt, MB, lens, B, Hq, Hkv, D,
-                                          bs, NB, 0.1, kvt, out, ot, rb, None)
+                                          bs, NB, scale, kvt, out, ot, rb, None)
 
 
 def test_prefill_argument_errors(lib):

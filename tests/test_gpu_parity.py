@@ -416,6 +416,21 @@ def test_prefill_parity(dev, name, row_blocks):
     assert err <= ATOL, err
 
 
+@pytest.mark.parametrize("row_blocks", [1, 2, 4])
+def test_prefill_first_position_returns_value_row_exactly(dev, row_blocks):
+    """In a full prefill the row at position 0 sees only key 0, so its output is that value row
+    exactly (one weight of exactly 1), for every query head of the group."""
+    _, d = prefill_case("p3", dev)
+    w = wl.PREFILL_WORKLOADS["p3"]
+    out = run_prefill(d, row_blocks)
+    G = w.num_q_heads // w.num_kv_heads
+    cu = d["cu_seqlens_q"].tolist()
+    for b in range(w.batch):
+        blk0 = int(d["block_tables"][b, 0])
+        v0 = d["v_cache"][blk0, 0].float().repeat_interleave(G, dim=0)  # [Hq, D]
+        assert torch.equal(out[cu[b]], v0), (b, row_blocks)
+
+
 def test_prefill_chunked_sampled(dev):
     w = wl.PREFILL_WORKLOADS["p1"]
     rng = np.random.default_rng(17)
