@@ -49,6 +49,9 @@ def parse_args():
                    help="attention output format: f32 or the input format")
     p.add_argument("--row-blocks", type=int, default=0, choices=[0, 1, 2, 4],
                    help="multi-query workloads: 16-row query blocks per wave (0 = library's choice)")
+    p.add_argument("--separate", action="store_true",
+                   help="decode workloads: KV write and attention as two calls instead of the "
+                        "fused decode step")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-read-probe", action="store_true",
                    help="skip the plain streaming-read reference after the timed steps")
@@ -319,6 +322,15 @@ def main():
         if flush is not None:
             torch.sum(flush)
         for i, d in enumerate(subs):
+            ev = events[i] if events is not None else None
+            if not args.rope and not args.separate:
+                # one launch stores the new rows and attends (plus the merge when split)
+                pk.paged_decode_step(d["q"], d["k_new"], d["v_new"], d["slot_mapping"],
+                                     d["k_cache"], d["v_cache"], d["block_tables"],
+                                     d["context_lens"], d["scale"], d["out"],
+                                     partition_tokens=args.partition, kernel=args.kernel,
+                                     workspace=d["ws"], events=ev)
+                continue
             if args.rope:
                 pk.paged_kv_write_rope(d["q"], d["k_new"], d["v_new"], d["pos"], d["inv_freq"],
                                        d["slot_mapping"], d["k_cache"], d["v_cache"],
@@ -330,8 +342,7 @@ def main():
                                       d["v_cache"], d["block_tables"],
                                       d["context_lens"], d["scale"], d["out"],
                                       partition_tokens=args.partition, kernel=args.kernel,
-                                      workspace=d["ws"],
-                                      events=events[i] if events is not None else None)
+                                      workspace=d["ws"], events=ev)
 
     if args.copy_calibration_mib > 0:
         n = args.copy_calibration_mib << 20
@@ -440,8 +451,10 @@ def main():
             "us_per_call": {p["workload"]: p["attn_kernel_us_mean"] for p in per},
             "pct_of_peak": {p["workload"]: p["pct_of_peak"] for p in per},
             "kernels": {p["workload"]: p["kernel"] for p in per},
-            "step": ("RoPE + KV write" if args.rope else "KV write") +
-                    " + decode attention per sub-workload",
+            "step": ("RoPE + KV write, then decode attention" if args.rope else
+                     "KV write, then decode attention (two calls)" if args.separate else
+                     "fused decode step: KV write + decode attention in one launch") +
+                    " per sub-workload",
         },
         "roofline": {
             "bound": "hbm",

@@ -230,6 +230,36 @@ int paged_decode_attention_ex(const uint16_t* q, const uint16_t* k_cache,
                               hipEvent_t ev_end, hipStream_t stream);
 
 /*
+ * paged_decode_step -- the whole decode step in one call: the KV write of paged_kv_write for
+ * one new token per sequence, then paged_decode_attention_ex over the updated pools ("vLLM-Style
+ * Llama Inference Engine with Tensor Parallelism", How it works, steps 3-4: each rank writes
+ * its paged KV cache, then one-token decode attends over it).
+ *
+ *   k_new, v_new   [batch][num_kv_heads][head_dim], kv_dtype: sequence b's new K and V rows
+ *   slot_mapping   int64 [batch]: slot for row b (< 0 or outside the pool: not stored)
+ *   k_cache, v_cache  as in paged_decode_attention, modified in place at those slots
+ *   everything else as in paged_decode_attention_ex (kernel, events around the main kernel)
+ *
+ * The result equals paged_kv_write(k_new, v_new, slot_mapping, batch, ...) followed by
+ * paged_decode_attention_ex(...) on the same stream, provided the decode-step layout holds:
+ * slot_mapping[b] is the slot that block_tables[b] gives for position context_lens[b] - 1
+ * (the new token is the last position), or negative. The matrix-core kernels then store the
+ * rows and read that position from k_new / v_new within one launch, with no separate write
+ * launch; a slot that addresses some other position this call reads gives an undefined
+ * result. The vector-ALU family (kernel = PAGEDKV_KERNEL_VALU) issues the write as its own
+ * launch before the attention.
+ */
+int paged_decode_step(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
+                      const int64_t* slot_mapping, uint16_t* k_cache, uint16_t* v_cache,
+                      const int32_t* block_tables, int32_t max_blocks_per_seq,
+                      const int32_t* context_lens, int32_t batch, int32_t num_q_heads,
+                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                      int64_t num_blocks, float scale, int32_t kv_dtype, void* out,
+                      int32_t out_dtype, void* workspace, size_t workspace_bytes,
+                      int32_t partition_tokens, int32_t kernel, hipEvent_t ev_begin,
+                      hipEvent_t ev_end, hipStream_t stream);
+
+/*
  * paged_decode_plan -- the launch paged_decode_attention_ex would make for these sizes on
  * the current device, without launching: number of sequence partitions, tokens per
  * partition, and the kernel family (a pagedkv_kernel value, never AUTO). partition_tokens

@@ -73,6 +73,9 @@ def load_library() -> ctypes.CDLL:
         lib.paged_decode_attention_typed.argtypes = typed + [P]
         lib.paged_decode_attention_ex.restype = ctypes.c_int
         lib.paged_decode_attention_ex.argtypes = typed + [I32, P, P, P]
+        lib.paged_decode_step.restype = ctypes.c_int
+        lib.paged_decode_step.argtypes = [P, P, P, P, P, P, P, I32, P, I32, I32, I32, I32, I32,
+                                          I64, F32, I32, P, I32, P, SZ, I32, I32, P, P, P]
         lib.paged_kv_write_rope.restype = ctypes.c_int
         lib.paged_kv_write_rope.argtypes = [P, P, P, P, P, I32, P, I64, P, P, P, I64, I32, I32,
                                             I32, I32, P]
@@ -237,6 +240,56 @@ def paged_decode_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
             context_lens.data_ptr(), B, Hq, Hkv, D, bs, NB, float(scale), DTYPES[dt],
             out.data_ptr(), DTYPES[out.dtype], workspace.data_ptr() if need else None,
             ws_bytes if need else 0, partition_tokens, KERNELS[kernel], ev_b, ev_e,
+            _stream_handle(dev)))
+    return out
+
+
+def paged_decode_step(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                      slot_mapping: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                      block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
+                      out: torch.Tensor, *, partition_tokens: int = 0, kernel: str = "auto",
+                      workspace: Optional[torch.Tensor] = None,
+                      events: Optional[tuple] = None) -> torch.Tensor:
+    """The decode step in one call: store k_new[b] / v_new[b] ([B, Hkv, D]) at slot
+    slot_mapping[b] ([B] int64) of the pools, then attend as paged_decode_attention does.
+    Equals paged_kv_write followed by paged_decode_attention when slot_mapping[b] is the slot
+    of position context_lens[b] - 1 of sequence b (or negative); the matrix-core kernels do both
+    in one launch."""
+    _require(k_cache, "k_cache", INPUT_TYPES, 4)
+    dev, dt = k_cache.device, k_cache.dtype
+    _require(v_cache, "v_cache", dt, 4, dev)
+    _require(q, "q", dt, 3, dev)
+    _require(k_new, "k_new", dt, 3, dev)
+    _require(v_new, "v_new", dt, 3, dev)
+    _require(slot_mapping, "slot_mapping", torch.int64, 1, dev)
+    _require(block_tables, "block_tables", torch.int32, 2, dev)
+    _require(context_lens, "context_lens", torch.int32, 1, dev)
+    _require(out, "out", (torch.float32, dt), 3, dev)
+    NB, bs, Hkv, D = k_cache.shape
+    B, Hq, Dq = q.shape
+    if v_cache.shape != k_cache.shape or Dq != D or out.shape != (B, Hq, D):
+        raise ValueError("shape mismatch between q, out and the caches")
+    if k_new.shape != (B, Hkv, D) or v_new.shape != (B, Hkv, D) or slot_mapping.shape != (B,):
+        raise ValueError(f"k_new/v_new must be [{B}, {Hkv}, {D}] and slot_mapping [{B}]")
+    MB = block_tables.shape[1]
+    if block_tables.shape[0] != B or context_lens.shape != (B,):
+        raise ValueError("block_tables must be [B, MB] and context_lens [B]")
+    if kernel not in KERNELS:
+        raise ValueError(f"kernel must be one of {sorted(KERNELS)}")
+    lib = load_library()
+    need = int(lib.paged_decode_workspace_bytes(B, Hq, D, MB, bs, partition_tokens))
+    if workspace is None:
+        workspace = _cached_workspace(dev, need)
+    elif workspace.device != dev or workspace.dtype != torch.uint8:
+        raise ValueError("workspace must be a uint8 tensor on the cache's device")
+    ev_b, ev_e = events if events is not None else (None, None)
+    with torch.cuda.device(dev):
+        _check(lib.paged_decode_step(
+            q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), slot_mapping.data_ptr(),
+            k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(), MB,
+            context_lens.data_ptr(), B, Hq, Hkv, D, bs, NB, float(scale), DTYPES[dt],
+            out.data_ptr(), DTYPES[out.dtype], workspace.data_ptr() if need else None,
+            workspace.numel() if need else 0, partition_tokens, KERNELS[kernel], ev_b, ev_e,
             _stream_handle(dev)))
     return out
 

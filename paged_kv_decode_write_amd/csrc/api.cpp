@@ -195,6 +195,117 @@ int check_decode_sizes(int32_t max_blocks, int32_t batch, int32_t num_q_heads,
   return PAGEDKV_OK;
 }
 
+// The KV write of a fused decode step: token b's rows go to slot_mapping[b] of the pools.
+struct StepWrite {
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  const int64_t* slot_mapping;
+  uint16_t* k_cache;
+  uint16_t* v_cache;
+};
+
+// Decode attention, optionally fused with the step's KV write (sw non-null).
+int decode_impl(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache,
+                const int32_t* block_tables, int32_t max_blocks_per_seq,
+                const int32_t* context_lens, int32_t batch, int32_t num_q_heads,
+                int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                float scale, int32_t kv_dtype, void* out, int32_t out_dtype, void* workspace,
+                size_t workspace_bytes, int32_t partition_tokens, int32_t kernel,
+                hipEvent_t ev_begin, hipEvent_t ev_end, hipStream_t stream,
+                const StepWrite* sw) {
+  g_last_error.clear();
+  int st = check_formats(kv_dtype, out_dtype);
+  if (st) return st;
+  st = check_decode_sizes(max_blocks_per_seq, batch, num_q_heads, num_kv_heads, head_dim,
+                          block_size, num_blocks);
+  if (st) return st;
+  const int G = num_q_heads / num_kv_heads;
+  int chosen = 0;
+  st = select_kernel(kernel, head_dim, G, block_size, (int64_t)max_blocks_per_seq * block_size,
+                     &chosen);
+  if (st) return st;
+  if (batch == 0) return PAGEDKV_OK;
+  if (!q || !k_cache || !v_cache || !context_lens || !out ||
+      (max_blocks_per_seq > 0 && !block_tables))
+    return fail(PAGEDKV_ERR_NULL,
+                "q, k_cache, v_cache, block_tables, context_lens and out must be non-NULL");
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
+      !aligned(block_tables, 4) || !aligned(context_lens, 4))
+    return fail(PAGEDKV_ERR_ALIGN, "q, k_cache, v_cache and out need 16-byte alignment");
+  if (sw) {
+    if (!sw->k_new || !sw->v_new || !sw->slot_mapping)
+      return fail(PAGEDKV_ERR_NULL, "k_new, v_new and slot_mapping must be non-NULL");
+    if (!aligned(sw->k_new, 16) || !aligned(sw->v_new, 16) || !aligned(sw->slot_mapping, 8))
+      return fail(PAGEDKV_ERR_ALIGN, "k_new and v_new need 16-byte alignment");
+  }
+  int cus = 0;
+  st = cu_count(&cus);
+  if (st) return st;
+  Plan plan{};
+  st = make_plan(batch, num_kv_heads, max_blocks_per_seq, block_size, partition_tokens, cus,
+                 chosen, plan_granule(chosen, block_size), &plan);
+  if (st) return st;
+
+  DecodeArgs a{};
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.out = out;
+  a.max_blocks = max_blocks_per_seq;
+  a.batch = batch;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.block_size = block_size;
+  a.num_blocks = num_blocks;
+  a.scale_log2 = scale * kLog2eHost;
+  a.nparts = plan.nparts;
+  a.part_tokens = plan.part_tokens;
+  a.kv_dtype = kv_dtype;
+  a.out_dtype = out_dtype;
+  if (plan.nparts > 1) {
+    const size_t need = split_workspace_bytes(batch, num_q_heads, head_dim, plan.nparts);
+    if (!workspace || workspace_bytes < need)
+      return fail(PAGEDKV_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                  workspace ? workspace_bytes : (size_t)0);
+    if (!aligned(workspace, 16)) return fail(PAGEDKV_ERR_ALIGN, "workspace needs 16-byte alignment");
+    char* base = static_cast<char*>(workspace);
+    a.ws_acc = reinterpret_cast<float*>(base);
+    a.ws_ml = reinterpret_cast<float*>(base + acc_bytes(batch, num_q_heads, head_dim, plan.nparts));
+  }
+
+  hipError_t e;
+  if (sw && chosen == PAGEDKV_KERNEL_VALU) {
+    // The vector-ALU kernel has no fused write: store first, then attend over the pools.
+    e = launch_kv_write(sw->k_new, sw->v_new, sw->slot_mapping, batch, sw->k_cache,
+                        sw->v_cache, num_blocks * block_size, num_kv_heads * head_dim, stream);
+    if (e != hipSuccess) return hip_fail(e, "kv_write launch");
+  } else if (sw) {
+    a.k_new = sw->k_new;
+    a.v_new = sw->v_new;
+    a.slot_mapping = sw->slot_mapping;
+    a.k_cache_w = sw->k_cache;
+    a.v_cache_w = sw->v_cache;
+  }
+  if (ev_begin && (e = hipEventRecord(ev_begin, stream)) != hipSuccess)
+    return hip_fail(e, "hipEventRecord(begin)");
+  switch (chosen) {
+    case PAGEDKV_KERNEL_MFMA: e = launch_decode_mfma(a, stream); break;
+    case PAGEDKV_KERNEL_MFMA_HEADWAVE: e = launch_decode_mfma_hw(a, stream); break;
+    default: e = launch_decode_valu(a, stream); break;
+  }
+  if (e != hipSuccess) return hip_fail(e, "decode attention launch");
+  if (ev_end && (e = hipEventRecord(ev_end, stream)) != hipSuccess)
+    return hip_fail(e, "hipEventRecord(end)");
+  if (plan.nparts > 1) {
+    e = launch_decode_reduce(a, stream);
+    if (e != hipSuccess) return hip_fail(e, "partition merge launch");
+  }
+  return PAGEDKV_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -340,79 +451,26 @@ int paged_decode_attention_ex(const uint16_t* q, const uint16_t* k_cache,
                               void* workspace, size_t workspace_bytes,
                               int32_t partition_tokens, int32_t kernel, hipEvent_t ev_begin,
                               hipEvent_t ev_end, hipStream_t stream) {
-  g_last_error.clear();
-  int st = check_formats(kv_dtype, out_dtype);
-  if (st) return st;
-  st = check_decode_sizes(max_blocks_per_seq, batch, num_q_heads, num_kv_heads, head_dim,
-                          block_size, num_blocks);
-  if (st) return st;
-  const int G = num_q_heads / num_kv_heads;
-  int chosen = 0;
-  st = select_kernel(kernel, head_dim, G, block_size, (int64_t)max_blocks_per_seq * block_size,
-                     &chosen);
-  if (st) return st;
-  if (batch == 0) return PAGEDKV_OK;
-  if (!q || !k_cache || !v_cache || !context_lens || !out ||
-      (max_blocks_per_seq > 0 && !block_tables))
-    return fail(PAGEDKV_ERR_NULL,
-                "q, k_cache, v_cache, block_tables, context_lens and out must be non-NULL");
-  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
-      !aligned(block_tables, 4) || !aligned(context_lens, 4))
-    return fail(PAGEDKV_ERR_ALIGN, "q, k_cache, v_cache and out need 16-byte alignment");
-  int cus = 0;
-  st = cu_count(&cus);
-  if (st) return st;
-  Plan plan{};
-  st = make_plan(batch, num_kv_heads, max_blocks_per_seq, block_size, partition_tokens, cus,
-                 chosen, plan_granule(chosen, block_size), &plan);
-  if (st) return st;
+  return decode_impl(q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, batch,
+                     num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale,
+                     kv_dtype, out, out_dtype, workspace, workspace_bytes, partition_tokens,
+                     kernel, ev_begin, ev_end, stream, nullptr);
+}
 
-  DecodeArgs a{};
-  a.q = q;
-  a.k_cache = k_cache;
-  a.v_cache = v_cache;
-  a.block_tables = block_tables;
-  a.context_lens = context_lens;
-  a.out = out;
-  a.max_blocks = max_blocks_per_seq;
-  a.batch = batch;
-  a.num_q_heads = num_q_heads;
-  a.num_kv_heads = num_kv_heads;
-  a.head_dim = head_dim;
-  a.block_size = block_size;
-  a.num_blocks = num_blocks;
-  a.scale_log2 = scale * kLog2eHost;
-  a.nparts = plan.nparts;
-  a.part_tokens = plan.part_tokens;
-  a.kv_dtype = kv_dtype;
-  a.out_dtype = out_dtype;
-  if (plan.nparts > 1) {
-    const size_t need = split_workspace_bytes(batch, num_q_heads, head_dim, plan.nparts);
-    if (!workspace || workspace_bytes < need)
-      return fail(PAGEDKV_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
-                  workspace ? workspace_bytes : (size_t)0);
-    if (!aligned(workspace, 16)) return fail(PAGEDKV_ERR_ALIGN, "workspace needs 16-byte alignment");
-    char* base = static_cast<char*>(workspace);
-    a.ws_acc = reinterpret_cast<float*>(base);
-    a.ws_ml = reinterpret_cast<float*>(base + acc_bytes(batch, num_q_heads, head_dim, plan.nparts));
-  }
-
-  hipError_t e;
-  if (ev_begin && (e = hipEventRecord(ev_begin, stream)) != hipSuccess)
-    return hip_fail(e, "hipEventRecord(begin)");
-  switch (chosen) {
-    case PAGEDKV_KERNEL_MFMA: e = launch_decode_mfma(a, stream); break;
-    case PAGEDKV_KERNEL_MFMA_HEADWAVE: e = launch_decode_mfma_hw(a, stream); break;
-    default: e = launch_decode_valu(a, stream); break;
-  }
-  if (e != hipSuccess) return hip_fail(e, "decode attention launch");
-  if (ev_end && (e = hipEventRecord(ev_end, stream)) != hipSuccess)
-    return hip_fail(e, "hipEventRecord(end)");
-  if (plan.nparts > 1) {
-    e = launch_decode_reduce(a, stream);
-    if (e != hipSuccess) return hip_fail(e, "partition merge launch");
-  }
-  return PAGEDKV_OK;
+int paged_decode_step(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
+                      const int64_t* slot_mapping, uint16_t* k_cache, uint16_t* v_cache,
+                      const int32_t* block_tables, int32_t max_blocks_per_seq,
+                      const int32_t* context_lens, int32_t batch, int32_t num_q_heads,
+                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                      int64_t num_blocks, float scale, int32_t kv_dtype, void* out,
+                      int32_t out_dtype, void* workspace, size_t workspace_bytes,
+                      int32_t partition_tokens, int32_t kernel, hipEvent_t ev_begin,
+                      hipEvent_t ev_end, hipStream_t stream) {
+  const StepWrite sw{k_new, v_new, slot_mapping, k_cache, v_cache};
+  return decode_impl(q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, batch,
+                     num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale,
+                     kv_dtype, out, out_dtype, workspace, workspace_bytes, partition_tokens,
+                     kernel, ev_begin, ev_end, stream, &sw);
 }
 
 int paged_decode_attention(const uint16_t* q, const uint16_t* k_cache,

@@ -41,6 +41,37 @@
 
 namespace pagedkv {
 
+// Fused decode step (a.k_new set): the position whose K / V come from the step's new rows
+// instead of the cache, or -1. That is position L - 1 when the slot the step writes for
+// sequence b is the one its block table gives for that position (the decode-step layout);
+// otherwise the cache is read as it stands.
+__device__ __forceinline__ int step_sub_pos(const DecodeArgs& a, const int32_t* table, int b,
+                                            int L) {
+  if (!a.k_new || L <= 0) return -1;
+  const int64_t slot = a.slot_mapping[b];
+  const int64_t want = (int64_t)table[(L - 1) / 16] * 16 + (L - 1) % 16;
+  return slot >= 0 && slot == want && slot < a.num_blocks * 16 ? L - 1 : -1;
+}
+
+// Fused decode step: store KV head g's slice of sequence b's new K and V rows at
+// slot_mapping[b] (negative or outside the pool: nothing), 16 bytes per lane, K from lanes
+// 0..D/8-1 and V from lanes 32..32+D/8-1 of one wave. Only the launch unit that reads
+// position L - 1 (or partition 0 when L = 0) calls it, so every slice is written once and no
+// unit of the launch reads it back (the owner takes that position from the new rows).
+template <int D>
+__device__ __forceinline__ void step_store(const DecodeArgs& a, int b, int g, int lane) {
+  const int64_t slot = a.slot_mapping[b];
+  if (slot < 0 || slot >= a.num_blocks * 16) return;
+  const size_t src = ((size_t)b * a.num_kv_heads + g) * D;
+  const size_t dst = ((size_t)slot * a.num_kv_heads + g) * D;
+  const int i = lane & 31;
+  if (i < D / 8) {
+    const uint4* from = reinterpret_cast<const uint4*>((lane < 32 ? a.k_new : a.v_new) + src);
+    uint4* to = reinterpret_cast<uint4*>((lane < 32 ? a.k_cache_w : a.v_cache_w) + dst);
+    to[i] = from[i];
+  }
+}
+
 template <int D, int NW, int KT, int OT>
 __global__ void __launch_bounds__(NW * 64)
 decode_mfma_kernel(const DecodeArgs a) {
@@ -71,6 +102,7 @@ decode_mfma_kernel(const DecodeArgs a) {
   const int tok1 = min(tok0 + a.part_tokens, L);
   const int blk0 = tok0 / BS;
   const int blk1 = (tok1 + BS - 1) / BS;
+  const int32_t* table = a.block_tables + (size_t)b * a.max_blocks;
 
   // Q^T operand: lane (n16, kg) holds q[head n16][32c + 8kg .. +7] for chunk c (0 if n16>=G).
   uint4 qb[NCH];
@@ -93,7 +125,7 @@ decode_mfma_kernel(const DecodeArgs a) {
   PairCtx<D> ctx;
   ctx.k_cache = a.k_cache;
   ctx.v_cache = a.v_cache;
-  ctx.table = a.block_tables + (size_t)b * a.max_blocks;
+  ctx.table = table;
   ctx.row_stride = (size_t)Hkv * D;
   ctx.head_off = (size_t)g * D;
   ctx.num_blocks = a.num_blocks;
@@ -103,6 +135,12 @@ decode_mfma_kernel(const DecodeArgs a) {
   ctx.wave = wave;
   ctx.n16 = n16;
   ctx.kg = kg;
+  // Fused step: the new row of this head, loaded unconditionally (from the cache when there is
+  // no step write, then never used) so no memory operation waits behind a branch.
+  const int sub_pos = step_sub_pos(a, table, b, L);
+  NewRow<NCH, EPL> nrow;
+  load_new_row(nrow, (a.k_new ? a.k_new : a.k_cache) + ((size_t)b * Hkv + g) * D,
+               (a.v_new ? a.v_new : a.v_cache) + ((size_t)b * Hkv + g) * D, n16, kg);
   const float sl2 = a.scale_log2;
 
   // This wave's block pairs are (blk0 + 2*(wave + NW*k), +1), k = 0 .. np-1. Two pairs are
@@ -121,12 +159,20 @@ decode_mfma_kernel(const DecodeArgs a) {
       const int k1 = min(k + 1, np - 1), k2 = min(k + 2, np - 1), k3 = min(k + 3, np - 1);
       pair_load<D, NW>(t1, ctx, i1, k1);
       i0 = pair_ids<D, NW>(ctx, k2);
+      use_new_row(t0, nrow, sub_pos, n16, kg);
       pair_compute<KT>(t0, st, qb, sl2, kg);
       pair_load<D, NW>(t0, ctx, i0, k2);
       i1 = pair_ids<D, NW>(ctx, k3);
-      if (k + 1 < np) pair_compute<KT>(t1, st, qb, sl2, kg);
+      if (k + 1 < np) {
+        use_new_row(t1, nrow, sub_pos, n16, kg);
+        pair_compute<KT>(t1, st, qb, sl2, kg);
+      }
     }
   }
+
+  // The step's store comes after every block-table read, so the compiler can keep those reads
+  // on the scalar path (no earlier store may have changed the table).
+  if (a.k_new && wave == 0 && (L > 0 ? L - 1 < tok1 : part == 0)) step_store<D>(a, b, g, lane);
 
   // Sum of the running sums over the four lanes of a head.
   float l_run = st.l_run;
@@ -247,6 +293,12 @@ decode_mfma_hw_kernel(const DecodeArgs a) {
   ctx.wave = 0;
   ctx.n16 = n16;
   ctx.kg = kg;
+  // Fused step: the new row of this head, loaded unconditionally (from the cache when there is
+  // no step write, then never used) so no memory operation waits behind a branch.
+  const int sub_pos = step_sub_pos(a, table, b, L);
+  NewRow<NCH, EPL> nrow;
+  load_new_row(nrow, (a.k_new ? a.k_new : a.k_cache) + ((size_t)b * Hkv + g) * D,
+               (a.v_new ? a.v_new : a.v_cache) + ((size_t)b * Hkv + g) * D, n16, kg);
   const float sl2 = a.scale_log2;
 
   // Pairs (blk0 + 2k, blk0 + 2k + 1), k = 0 .. np-1, NBUF pairs in flight. Pair j lives in
@@ -272,10 +324,16 @@ decode_mfma_hw_kernel(const DecodeArgs a) {
         const int ub = (u + NBUF - 1) % NBUF;
         pair_load<D, 1>(t[ub], ctx, ids[ub], jl);
         ids[u] = pair_ids<D, 1>(ctx, min(jl + 1, np - 1));
-        if (j < np) pair_compute<KT>(t[u], st, qb, sl2, kg);
+        if (j < np) {
+          use_new_row(t[u], nrow, sub_pos, n16, kg);
+          pair_compute<KT>(t[u], st, qb, sl2, kg);
+        }
       }
     }
   }
+
+  // The step's store comes after every block-table read (see the split-wave kernel).
+  if (a.k_new && (L > 0 ? L - 1 < tok1 : part == 0)) step_store<D>(a, b, g, lane);
 
   float l_run = st.l_run;
   l_run = row4_sum(l_run);

@@ -27,6 +27,14 @@ struct DecodeArgs {
   int32_t part_tokens;  // tokens per partition, a multiple of block_size
   int32_t kv_dtype;     // format of q and the caches: kDtBf16 or kDtF16
   int32_t out_dtype;    // kDtF32 or kv_dtype
+  // Fused decode step (k_new != nullptr): sequence b's new K / V rows k_new[b], v_new[b]
+  // ([B][Hkv][D]) are stored at slot_mapping[b] of the writable pools and used for position
+  // context_lens[b] - 1 when that slot is the one the block table gives for it.
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  const int64_t* slot_mapping;
+  uint16_t* k_cache_w;
+  uint16_t* v_cache_w;
 };
 
 // Arguments of one multi-query causal (prefill) launch, already validated.

@@ -37,6 +37,12 @@ __device__ __forceinline__ floatx4 mfma16x16x32(const uint4& a, const uint4& b,
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+// c ? a : b for 16-byte values, component by component (a select of the whole struct would
+// go through memory).
+__device__ __forceinline__ uint4 select4(bool c, const uint4& a, const uint4& b) {
+  return make_uint4(c ? a.x : b.x, c ? a.y : b.y, c ? a.z : b.z, c ? a.w : b.w);
+}
+
 // Low / high bf16 halves of two words packed into one word (x's half first).
 __device__ __forceinline__ uint32_t pack_lo(uint32_t x, uint32_t y) {
   return __builtin_amdgcn_perm(y, x, 0x05040100u);
@@ -53,6 +59,9 @@ template <> struct VRow<8> {
   __device__ __forceinline__ void keep_if(bool v) {
     w.x = v ? w.x : 0u; w.y = v ? w.y : 0u; w.z = v ? w.z : 0u; w.w = v ? w.w : 0u;
   }
+  __device__ __forceinline__ void take_if(bool c, const VRow& o) {
+    w.x = c ? o.w.x : w.x; w.y = c ? o.w.y : w.y; w.z = c ? o.w.z : w.z; w.w = c ? o.w.w : w.w;
+  }
   __device__ __forceinline__ uint32_t word(int i) const {
     return i == 0 ? w.x : i == 1 ? w.y : i == 2 ? w.z : w.w;
   }
@@ -61,6 +70,9 @@ template <> struct VRow<4> {
   uint2 w;
   __device__ __forceinline__ void load(const uint16_t* p) { w = *reinterpret_cast<const uint2*>(p); }
   __device__ __forceinline__ void keep_if(bool v) { w.x = v ? w.x : 0u; w.y = v ? w.y : 0u; }
+  __device__ __forceinline__ void take_if(bool c, const VRow& o) {
+    w.x = c ? o.w.x : w.x; w.y = c ? o.w.y : w.y;
+  }
   __device__ __forceinline__ uint32_t word(int i) const { return i == 0 ? w.x : w.y; }
 };
 
@@ -112,7 +124,43 @@ template <int NCH, int EPL> struct PairTile {
   uint4 ka[NCH], kb[NCH];
   VRow<EPL> vr[8];
   int lastA, lastB;  // valid rows in each block (0: block absent or invalid)
+  int tA;            // position of the first row of the pair
 };
+
+// Fused decode step: one lane's pieces of the step's new K and V rows of its head (K columns
+// 32ch + 8kg .. +7, V columns EPL*n16 .. +EPL-1), loaded once before the key loop.
+template <int NCH, int EPL> struct NewRow {
+  uint4 k[NCH];
+  VRow<EPL> v;
+};
+
+template <int NCH, int EPL>
+__device__ __forceinline__ void load_new_row(NewRow<NCH, EPL>& r, const uint16_t* k_row,
+                                             const uint16_t* v_row, int n16, int kg) {
+#pragma unroll
+  for (int ch = 0; ch < NCH; ++ch)
+    r.k[ch] = *reinterpret_cast<const uint4*>(k_row + 8 * kg + 32 * ch);
+  r.v.load(v_row + EPL * n16);
+}
+
+// Put the new row in place of position sub_pos (-1: none) of a loaded pair, by selects on data
+// that has already arrived: the cache slot of that position is being written by the same
+// launch, so what its load returned is discarded.
+template <int NCH, int EPL>
+__device__ __forceinline__ void use_new_row(PairTile<NCH, EPL>& t, const NewRow<NCH, EPL>& r,
+                                            int sub_pos, int n16, int kg) {
+  constexpr int BS = 16;
+  const int rel = sub_pos - t.tA;  // the new token's row in the pair, if 0 <= rel < 32
+  if (rel >= 0 && rel < 2 * BS) {  // uniform
+#pragma unroll
+    for (int ch = 0; ch < NCH; ++ch) {
+      t.ka[ch] = select4(rel == n16, r.k[ch], t.ka[ch]);
+      t.kb[ch] = select4(rel == BS + n16, r.k[ch], t.kb[ch]);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) t.vr[j].take_if(rel == (j / 4) * BS + 4 * kg + (j % 4), r.v);
+  }
+}
 
 template <int D> struct PairCtx {
   const uint16_t* k_cache;
@@ -159,6 +207,7 @@ __device__ __forceinline__ void pair_load(PairTile<NCH, EPL>& t, const PairCtx<D
     t.vr[j].load(c.v_cache + bA + voff + (size_t)j * c.row_stride);
     t.vr[4 + j].load(c.v_cache + bB + voff + (size_t)j * c.row_stride);
   }
+  t.tA = tA;
 }
 
 // V^T operand of output column set e: 8 token slots of column EPL*n16 + e, gathered from the

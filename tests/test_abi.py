@@ -32,7 +32,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for want in ("paged_kv_write", "paged_decode_attention", "paged_decode_attention_ex",
                  "paged_decode_attention_typed", "paged_prefill_attention",
-                 "paged_prefill_attention_ex", "paged_kv_write_rope",
+                 "paged_prefill_attention_ex", "paged_kv_write_rope", "paged_decode_step",
                  "paged_decode_workspace_bytes", "paged_kv_status_string", "paged_kv_abi_version",
                  "paged_kv_last_error", "paged_decode_plan"):
         assert want in names
@@ -113,6 +113,21 @@ def test_format_pairs(lib):
     st = lib.paged_decode_attention_typed(FAKE, FAKE, FAKE, FAKE, 8, FAKE, 2, 32, 8, 128, 16, 64,
                                           0.1, F16, FAKE, BF16, None, 0, 0, None)
     assert st == ERR_UNSUPPORTED
+
+
+def _step(lib, q=FAKE, kn=FAKE, vn=FAKE, sl=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, MB=8, lens=FAKE,
+          B=2, Hq=32, Hkv=8, D=128, bs=16, NB=64, out=FAKE):
+    return lib.paged_decode_step(q, kn, vn, sl, kc, vc, bt, MB, lens, B, Hq, Hkv, D, bs, NB, 0.1,
+                                 BF16, out, F32, None, 0, -1, 0, None, None, None)
+
+
+def test_decode_step_argument_errors(lib):
+    assert _step(lib, kn=None) == ERR_NULL
+    assert _step(lib, sl=None) == ERR_NULL
+    assert _step(lib, vn=FAKE + 8) == ERR_ALIGN
+    assert _step(lib, sl=FAKE + 4) == ERR_ALIGN
+    assert _step(lib, D=96) == ERR_UNSUPPORTED
+    assert _step(lib, B=0, q=None, kn=None, out=None) == OK  # empty batch: no-op
 
 
 def _prefill(lib, q=FAKE, cu=FAKE, T=8, maxq=4, kc=FAKE, vc=FAKE, bt=FAKE, MB=8, lens=FAKE,

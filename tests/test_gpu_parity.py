@@ -264,6 +264,66 @@ def test_length_one_returns_value_row_exactly(dev):
             assert torch.equal(out, vrow), (kernel, partition)
 
 
+# ------------------------------------------------------- fused decode step (write + attend)
+def run_step(d, kernel="auto", partition=0):
+    w = d["workload"]
+    out = torch.full((w.batch, w.num_q_heads, w.head_dim), float("nan"), dtype=torch.float32,
+                     device=d["q"].device)
+    pk.paged_decode_step(d["q"], d["k_new"], d["v_new"], d["slot_mapping"], d["k_cache"],
+                         d["v_cache"], d["block_tables"], d["context_lens"], d["scale"], out,
+                         partition_tokens=partition, kernel=kernel)
+    return out
+
+
+@pytest.mark.parametrize("name", SMALL)
+def test_decode_step_fused_matches_oracle_and_separate_calls(dev, name):
+    """One call stores the new rows and attends with them: the pools equal the oracle's bit for
+    bit, the output is within the bound, and it is bit-identical to the separate write and
+    attention calls, for every kernel family and split."""
+    host, ref, kc_ref, vc_ref, _ = case(name, dev, poison=True)
+    w = wl.WORKLOADS[name]
+    d = to_dev(wl.make_inputs(w, poison=True), dev)  # pools before the write
+    first = True
+    for kernel in ["auto"] + kernels_for(w):
+        for partition in (-1, 0, 256):
+            out = run_step(d, kernel, partition)
+            torch.cuda.synchronize()
+            if first:
+                assert np.array_equal(wl.to_bits(d["k_cache"]), kc_ref)
+                assert np.array_equal(wl.to_bits(d["v_cache"]), vc_ref)
+                first = False
+            err = np.abs(out.cpu().double().numpy() - ref).max()
+            record(f"{name}/step/{kernel}/p{partition}", err)
+            assert np.isfinite(err) and err <= ATOL, (kernel, partition, err)
+            assert torch.equal(out, run_attention(d, kernel, partition)), (kernel, partition)
+
+
+def test_decode_step_negative_slots_and_full_size(dev):
+    """Sequences whose slot is -1 store nothing and read their last position from the cache;
+    c5b at full size matches the separate calls bit for bit."""
+    w = wl.WORKLOADS["c3"]
+    inp = wl.make_inputs(w, poison=True)
+    inp["slot_mapping"][[0, 5, 11]] = -1
+    host = wl.to_host_numpy(inp)
+    ref, kc_ref, vc_ref = oracle.decode_step(host)
+    d = to_dev(inp, dev)
+    for kernel in ["auto"] + kernels_for(w):
+        out = run_step(d, kernel, 0)
+        torch.cuda.synchronize()
+        assert np.array_equal(wl.to_bits(d["k_cache"]), kc_ref)
+        assert np.array_equal(wl.to_bits(d["v_cache"]), vc_ref)
+        assert np.abs(out.cpu().double().numpy() - ref).max() <= ATOL, kernel
+    w = wl.WORKLOADS["c5b"]
+    a = wl.make_inputs(w, device="cuda")
+    b = {k: (v.clone() if isinstance(v, torch.Tensor) else v) for k, v in a.items()}
+    fused = run_step(a)
+    run_write(b)
+    sep = run_attention(b)
+    torch.cuda.synchronize()
+    assert torch.equal(fused, sep)
+    assert torch.equal(a["k_cache"], b["k_cache"]) and torch.equal(a["v_cache"], b["v_cache"])
+
+
 def test_split_agrees_with_unsplit_and_is_deterministic(dev):
     w = wl.WORKLOADS["c4"]
     d = case("c4", dev)[4]
