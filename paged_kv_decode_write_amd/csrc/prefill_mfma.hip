@@ -17,9 +17,9 @@
 // The four waves read the same keys. Each 32-key pair (both 16-token blocks, K and V) is
 // brought from memory once per workgroup: every thread loads 16-byte pieces into registers,
 // which are written to one of two LDS buffers while the waves compute on the other; one
-// barrier per pair. Each wave then takes its MFMA operands from LDS (K rows, and V rows for the
-// in-register transpose) and runs the tiles of mfma_tiles.h on its NB blocks, with a per-lane
-// causal mask on the pairs that reach past its first row. Key slots at or past the
+// barrier per pair. Each wave then takes its MFMA operands from LDS (K rows as they are, V^T
+// through gfx950's transposing LDS read) and runs the tiles of mfma_tiles.h on its NB blocks,
+// with a per-lane causal mask on the pairs that reach past its first row. Key slots at or past the
 // workgroup's last position are stored as zeros, so stale cache contents (NaN included) never
 // reach p.V; every such key is after every row's position, so the causal mask gives it
 // weight 0. Rows are written normalised.
@@ -34,9 +34,13 @@ namespace {
 
 constexpr int kPairRows = 32;  // keys per staged pair
 
-// LDS row pitch in bytes: a token row of D 16-bit values plus 16 bytes, so the 16 rows that
-// one ds_read_b128 wave access touches start in different banks.
-template <int D> constexpr int lds_pitch() { return D * 2 + 16; }
+// LDS row pitch in bytes: a token row of D 16-bit values plus 32 bytes. The pad staggers the
+// rows one wave reads together across the banks; 32 bytes measured half the bank conflicts of
+// 16 or 48 (and no more than 64 or 96), no pad four times as many.
+#ifndef PAGEDKV_LDS_PAD
+#define PAGEDKV_LDS_PAD 32
+#endif
+template <int D> constexpr int lds_pitch() { return D * 2 + PAGEDKV_LDS_PAD; }
 
 template <int D> struct LdsPair {
   alignas(16) unsigned char k[kPairRows * lds_pitch<D>()];
@@ -69,8 +73,12 @@ template <int D> struct Stager {
     }
   }
 
-  // Load pair `pair`. A block id outside the pool, and rows at or past tok1 (only in the last
-  // pair), give zeros; their loads read block 0 instead.
+  // Load pair `pair`. The loads are only issued here; the data is first used by commit(),
+  // after the current pair's compute, so their latency hides behind it. A block id outside the
+  // pool reads block 0 instead, and such a block, and rows at or past tok1 (only in the last
+  // pair), are stored as zeros by commit().
+  int zero_a, zero_b;   // uniform: block A / B of the staged pair is absent or invalid
+  int tail_from;        // rows r >= tail_from of the staged pair are zero (32: none)
   __device__ __forceinline__ void load(const PrefillArgs& a, const int32_t* table, int nblk,
                                        int tok1, size_t row_stride, int pair) {
     const int jA = 2 * pair;
@@ -78,23 +86,30 @@ template <int D> struct Stager {
     const int idB = jA + 1 < nblk ? table[jA + 1] : -1;
     const bool okA = idA >= 0 && (int64_t)idA < a.num_blocks;
     const bool okB = idB >= 0 && (int64_t)idB < a.num_blocks;
+    zero_a = !okA;
+    zero_b = !okB;
+    tail_from = min(tok1 - 32 * pair, 32);
     const size_t bbytes = (size_t)16 * row_stride * 2;  // bytes of one block
     const char* kc = reinterpret_cast<const char*>(a.k_cache);
     const char* vc = reinterpret_cast<const char*>(a.v_cache);
-    const bool tail = 32 * pair + 32 > tok1;  // uniform
 #pragma unroll
     for (int x = 0; x < kPieces; ++x) {
       const bool okb = blk[x] ? okB : okA;
       const size_t base = (size_t)(okb ? (blk[x] ? idB : idA) : 0) * bbytes;
-      const uint4 kw = *reinterpret_cast<const uint4*>(kc + base + goff[x]);
-      const uint4 vw = *reinterpret_cast<const uint4*>(vc + base + goff[x]);
-      const bool ok = okb && (!tail || 32 * pair + row[x] < tok1);
-      k[x] = ok ? kw : make_uint4(0, 0, 0, 0);
-      v[x] = ok ? vw : make_uint4(0, 0, 0, 0);
+      k[x] = *reinterpret_cast<const uint4*>(kc + base + goff[x]);
+      v[x] = *reinterpret_cast<const uint4*>(vc + base + goff[x]);
     }
   }
 
-  __device__ __forceinline__ void commit(LdsPair<D>& p) const {
+  __device__ __forceinline__ void commit(LdsPair<D>& p) {
+    if (zero_a || zero_b || tail_from < 32) {  // uniform: only an edge pair
+#pragma unroll
+      for (int x = 0; x < kPieces; ++x) {
+        const bool ok = !(blk[x] ? zero_b : zero_a) && row[x] < tail_from;
+        k[x] = select4(ok, k[x], make_uint4(0, 0, 0, 0));
+        v[x] = select4(ok, v[x], make_uint4(0, 0, 0, 0));
+      }
+    }
 #pragma unroll
     for (int x = 0; x < kPieces; ++x) {
       *reinterpret_cast<uint4*>(p.k + loff[x]) = k[x];
@@ -103,27 +118,38 @@ template <int D> struct Stager {
   }
 };
 
-// A wave's MFMA operands of a staged pair, in the register tile the shared tiles expect:
-// K rows n16 (first block) and 16 + n16 (second), columns 32ch + 8kg .. +7; V rows 4kg + j
-// and 16 + 4kg + j, columns EPL*n16 .. +EPL-1. Both blocks count as full (lastA = lastB = 16):
-// the zeros and the causal mask take care of positions past the end.
+// 4 x 16-bit elements of LDS through the transposing read ds_read_b64_tr_b16. Within each
+// group of 16 lanes, lane i receives element i % 4 of the 8 bytes that lanes 4j + i / 4
+// address, for j = 0..3.
+typedef short short4v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint2 lds_read_tr16(const unsigned char* p) {
+  const short4v r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) short4v*)(__attribute__((address_space(3))) const unsigned char*)p);
+  return __builtin_bit_cast(uint2, r);
+}
+
+// A wave's MFMA operands of a staged pair:
+//   ka / kb: K rows n16 (first block) and 16 + n16 (second), columns 32ch + 8kg .. +7;
+//   vt[e]:   V^T of output columns 16e .. 16e+15: lane (n16, kg) holds column 16e + n16 of the
+//            keys in its slots 8kg .. 8kg+7, i.e. rows 4kg .. 4kg+3 of the first block and of
+//            the second. Each half is one transposing read in which lane (n16, kg) addresses
+//            row 4kg + n16/4 (of the block) at column 16e + 4*(n16 % 4).
 template <int D, int NCH, int EPL>
-__device__ __forceinline__ void read_pair(PairTile<NCH, EPL>& t, const LdsPair<D>& p, int n16,
-                                          int kg) {
+__device__ __forceinline__ void read_pair(uint4 (&ka)[NCH], uint4 (&kb)[NCH], uint4 (&vt)[EPL],
+                                          const LdsPair<D>& p, int n16, int kg) {
   constexpr int P = lds_pitch<D>();
 #pragma unroll
   for (int ch = 0; ch < NCH; ++ch) {
-    t.ka[ch] = *reinterpret_cast<const uint4*>(p.k + n16 * P + 2 * (32 * ch + 8 * kg));
-    t.kb[ch] = *reinterpret_cast<const uint4*>(p.k + (16 + n16) * P + 2 * (32 * ch + 8 * kg));
+    ka[ch] = *reinterpret_cast<const uint4*>(p.k + n16 * P + 2 * (32 * ch + 8 * kg));
+    kb[ch] = *reinterpret_cast<const uint4*>(p.k + (16 + n16) * P + 2 * (32 * ch + 8 * kg));
   }
+  const unsigned char* va = p.v + (4 * kg + n16 / 4) * P + 8 * (n16 % 4);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    t.vr[j].load(reinterpret_cast<const uint16_t*>(p.v + (4 * kg + j) * P + 2 * EPL * n16));
-    t.vr[4 + j].load(
-        reinterpret_cast<const uint16_t*>(p.v + (16 + 4 * kg + j) * P + 2 * EPL * n16));
+  for (int e = 0; e < EPL; ++e) {
+    const uint2 lo = lds_read_tr16(va + 32 * e);
+    const uint2 hi = lds_read_tr16(va + 16 * P + 32 * e);
+    vt[e] = make_uint4(lo.x, lo.y, hi.x, hi.y);
   }
-  t.lastA = 16;
-  t.lastB = 16;
 }
 
 }  // namespace
@@ -220,9 +246,9 @@ prefill_mfma_kernel(const PrefillArgs a) {
       if (more) s.load(a, table, nblk, tok1, row_stride, k + 1);
       const int key0 = 32 * k;
       if (wave_rows && key0 <= p_max) {
-        PairTile<NCH, EPL> t;
-        read_pair<D>(t, buf[k & 1], n16, kg);
-        pair_compute_nb<KT>(t, st, qb, sl2, kg, row_pos, key0, key0 + 31 > p_min);
+        uint4 ka[NCH], kb[NCH], vt[EPL];
+        read_pair<D>(ka, kb, vt, buf[k & 1], n16, kg);
+        pair_compute_rows<KT>(ka, kb, vt, st, qb, sl2, kg, row_pos, key0, key0 + 31 > p_min);
       }
       if (more) s.commit(buf[(k + 1) & 1]);
       __syncthreads();
@@ -236,13 +262,12 @@ prefill_mfma_kernel(const PrefillArgs a) {
     if (row_ok[nb]) {
       const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
       const size_t o = ((size_t)(q0 + tok[nb]) * Hq + (size_t)g * G + head) * D;
+      // acc[e][i] is output column 16e + 4kg + i
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int e = 0; e < EPL; e += 4)
-          store_out4<OT>(a.out, o + EPL * (4 * kg + i) + e, st[nb].acc[e][i] * inv,
-                         st[nb].acc[e + 1][i] * inv, st[nb].acc[e + 2][i] * inv,
-                         st[nb].acc[e + 3][i] * inv);
+      for (int e = 0; e < EPL; ++e)
+        store_out4<OT>(a.out, o + 16 * e + 4 * kg, st[nb].acc[e][0] * inv,
+                       st[nb].acc[e][1] * inv, st[nb].acc[e][2] * inv,
+                       st[nb].acc[e][3] * inv);
     }
   }
 }
