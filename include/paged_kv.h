@@ -264,7 +264,9 @@ int paged_decode_step(const uint16_t* q, const uint16_t* k_new, const uint16_t* 
  * the current device, without launching: number of sequence partitions, tokens per
  * partition, and the kernel family (a pagedkv_kernel value, never AUTO). partition_tokens
  * and kernel as in paged_decode_attention_ex. Returns a status; the outputs are written on
- * PAGEDKV_OK (chosen_kernel may be NULL).
+ * PAGEDKV_OK (chosen_kernel may be NULL). The plan depends on the device only through its
+ * compute-unit count; if the environment variable PAGEDKV_CU_COUNT holds a positive integer,
+ * every call of the library uses that count instead (meant for planning without a device).
  */
 int paged_decode_plan(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                       int32_t head_dim, int32_t max_blocks_per_seq, int32_t block_size,

@@ -6,6 +6,7 @@
 
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <mutex>
 #include <string>
 
@@ -33,8 +34,17 @@ int hip_fail(hipError_t e, const char* what) {
 
 bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
 
-// Compute-unit count of the current device, queried once per device.
+// Compute-unit count of the current device, queried once per device. PAGEDKV_CU_COUNT (a
+// positive integer) replaces the query, so the host-side planning can be exercised without a
+// device.
 int cu_count(int* out) {
+  if (const char* env = std::getenv("PAGEDKV_CU_COUNT")) {
+    const long n = std::strtol(env, nullptr, 10);
+    if (n > 0 && n < (1L << 20)) {
+      *out = (int)n;
+      return PAGEDKV_OK;
+    }
+  }
   static std::mutex mu;
   static int counts[256] = {0};
   int dev = 0;

@@ -1,0 +1,69 @@
+"""The host-side launch plan (kernel family, partitions per sequence, tokens per partition),
+without a device: PAGEDKV_CU_COUNT stands in for the device's compute-unit count (256 on
+MI355X). Expected values are worked out by hand from the planning rule documented in the
+library (comments of make_plan and select_kernel in csrc/api.cpp):
+  * contexts over 1024 tokens (max_blocks * block_size) use the one-wave-per-KV-head MFMA
+    kernel, shorter ones the split-wave MFMA kernel;
+  * target work: 4 workgroups per CU (split-wave), 8 waves per CU (head-wave), or 4 when the
+    batch * kv_heads units are at most a quarter of the CUs;
+  * n = min(ceil(target / units), ceil(max_len / 256)), tokens per partition rounded up to the
+    kernel's granule (128 split-wave, 32 head-wave), n recomputed from it.
+"""
+import pytest
+
+from paged_kv_decode_write_amd import _binding
+from paged_kv_decode_write_amd import workloads as wl
+
+import os
+
+
+@pytest.fixture()
+def plan(monkeypatch):
+    if not os.path.exists(_binding.library_path()):
+        pytest.skip("libpagedkv.so not built")
+    monkeypatch.setenv("PAGEDKV_CU_COUNT", "256")
+
+    def f(w, partition=0, kernel="auto"):
+        return _binding.decode_plan(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim,
+                                    w.max_blocks, w.block_size, partition, kernel,
+                                    with_kernel=True)
+    return f
+
+
+# (workload, partitions, tokens per partition, kernel), derived per the module docstring:
+#  c1: 128 tokens -> mfma; n = min(ceil(1024/8), ceil(128/256)=1) = 1, P = 128
+#  c2: 512 -> mfma; n = min(32, 2) = 2, P = roundup(256, 128) = 256
+#  c3: 2048 -> mfma_hw; units 128 (x4 > 256): n = min(ceil(2048/128)=16, 8) = 8, P = 256
+#  c4: 4096 -> mfma_hw; units 384: n = min(ceil(2048/384)=6, 16) = 6, P = roundup(683, 32) = 704
+#  c5a: 8192 -> mfma_hw; units 512: n = min(4, 32) = 4, P = 2048
+#  c5b: 32768 -> mfma_hw; units 16 (x4 <= 256): n = min(ceil(1024/16)=64, 128) = 64, P = 512
+EXPECTED = {"c1": (1, 128, "mfma"), "c2": (2, 256, "mfma"), "c3": (8, 256, "mfma_hw"),
+            "c4": (6, 704, "mfma_hw"), "c5a": (4, 2048, "mfma_hw"), "c5b": (64, 512, "mfma_hw")}
+
+
+@pytest.mark.parametrize("name", sorted(EXPECTED))
+def test_automatic_plan_of_each_workload(plan, name):
+    assert plan(wl.WORKLOADS[name]) == EXPECTED[name]
+
+
+def test_forced_partitions_and_kernels(plan):
+    w = wl.WORKLOADS["c5b"]
+    assert plan(w, -1) == (1, 32768, "mfma_hw")               # never split
+    assert plan(w, 1024) == (32, 1024, "mfma_hw")             # forced size
+    # split-wave: target 4 * 256 = 1024 groups over 16 units -> n = 64, P = roundup(512, 128)
+    assert plan(w, 0, "mfma") == (64, 512, "mfma")
+    assert plan(w, 0, "valu")[2] == "valu"
+    with pytest.raises(_binding.PagedKVError):
+        plan(w, 24)                                           # not a multiple of block_size
+    g5 = wl.Workload("g5", batch=2, num_q_heads=40, num_kv_heads=8, head_dim=128, block_size=16,
+                     num_blocks=64, max_blocks=8, seed=1, context_len=128)
+    assert plan(g5)[2] == "mfma"                              # the matrix-core kernel takes G = 5
+    with pytest.raises(_binding.PagedKVError):
+        plan(g5, 0, "valu")                                   # the vector-ALU kernel does not
+
+
+def test_plan_scales_with_the_compute_units(plan, monkeypatch):
+    w = wl.WORKLOADS["c5a"]
+    monkeypatch.setenv("PAGEDKV_CU_COUNT", "128")
+    # units 512 (x4 > 128): target 8 * 128 = 1024 waves -> n = 2, P = 4096
+    assert plan(w) == (2, 4096, "mfma_hw")
