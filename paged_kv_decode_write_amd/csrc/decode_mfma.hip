@@ -247,10 +247,10 @@ decode_mfma_hw_kernel(const DecodeArgs a) {
   const int g = hg * HPW + wave;
   if (g >= Hkv) return;  // no barriers below: waves are independent
 
-  // Loads that do not depend on the context length are issued before it arrives, so a
-  // wave's start costs two dependent round trips (length and ids together, then K/V)
-  // instead of three: q, and the first pair's block ids (every entry of the table row is in
-  // bounds to read; entries past the context are ignored below).
+  // Loads that do not depend on the context length are issued before it arrives: q, the first
+  // pair's block ids (every entry of the table row is in bounds to read; entries past the
+  // context are ignored below) and, below, that pair's K / V. The wave's start then costs the
+  // ids' round trip and the K / V round trip, with the length arriving alongside.
   const int32_t* table = a.block_tables + (size_t)b * a.max_blocks;
   const int tok0 = part * a.part_tokens;
   const int blk0 = tok0 / BS;
@@ -267,19 +267,6 @@ decode_mfma_hw_kernel(const DecodeArgs a) {
     }
   }
 
-  int L = a.context_lens[b];
-  const int Lmax = a.max_blocks * BS;
-  L = L < 0 ? 0 : (L > Lmax ? Lmax : L);
-  if (tok0 >= L && !(L == 0 && part == 0)) return;
-  const int tok1 = min(tok0 + a.part_tokens, L);
-  const int blk1 = (tok1 + BS - 1) / BS;
-
-  WaveState<EPL> st;
-  st.m_run = kNegInf;
-  st.l_run = 0.f;
-#pragma unroll
-  for (int e = 0; e < EPL; ++e) st.acc[e] = floatx4{0.f, 0.f, 0.f, 0.f};
-
   PairCtx<D> ctx;
   ctx.k_cache = a.k_cache;
   ctx.v_cache = a.v_cache;
@@ -288,11 +275,29 @@ decode_mfma_hw_kernel(const DecodeArgs a) {
   ctx.head_off = (size_t)g * D;
   ctx.num_blocks = a.num_blocks;
   ctx.blk0 = blk0;
-  ctx.blk1 = blk1;
-  ctx.tok1 = tok1;
   ctx.wave = 0;
   ctx.n16 = n16;
   ctx.kg = kg;
+  // The first pair's K / V loads go out with q's, before the context length arrives: a
+  // partition that then turns out empty discards them; every other one saves a round trip.
+  PairTile<NCH, EPL> t[NBUF];
+  pair_issue(t[0], ctx, make_int2(idA0, idB0), blk0);
+
+  int L = a.context_lens[b];
+  const int Lmax = a.max_blocks * BS;
+  L = L < 0 ? 0 : (L > Lmax ? Lmax : L);
+  if (tok0 >= L && !(L == 0 && part == 0)) return;
+  const int tok1 = min(tok0 + a.part_tokens, L);
+  const int blk1 = (tok1 + BS - 1) / BS;
+  ctx.blk1 = blk1;
+  ctx.tok1 = tok1;
+
+  WaveState<EPL> st;
+  st.m_run = kNegInf;
+  st.l_run = 0.f;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) st.acc[e] = floatx4{0.f, 0.f, 0.f, 0.f};
+
   // Fused step: the new row of this head, loaded unconditionally (from the cache when there is
   // no step write, then never used) so no memory operation waits behind a branch.
   const int sub_pos = step_sub_pos(a, table, b, L);
@@ -309,13 +314,13 @@ decode_mfma_hw_kernel(const DecodeArgs a) {
   // behind a branch and the wait counts stay exact.
   const int np = (blk1 - blk0 + 1) / 2;
   if (np > 0) {
-    PairTile<NCH, EPL> t[NBUF];
     int2 ids[NBUF];
     ids[0] = make_int2(idA0, blk0 + 1 < blk1 ? idB0 : -1);
+    pair_valid(t[0], ctx, ids[0], blk0);  // issued above
 #pragma unroll
     for (int u = 1; u < NBUF; ++u) ids[u] = pair_ids<D, 1>(ctx, min(u, np - 1));
 #pragma unroll
-    for (int u = 0; u < NBUF - 1; ++u) pair_load<D, 1>(t[u], ctx, ids[u], min(u, np - 1));
+    for (int u = 1; u < NBUF - 1; ++u) pair_load<D, 1>(t[u], ctx, ids[u], min(u, np - 1));
     for (int k = 0; k < np; k += NBUF) {
 #pragma unroll
       for (int u = 0; u < NBUF; ++u) {

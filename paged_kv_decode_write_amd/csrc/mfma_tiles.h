@@ -181,18 +181,16 @@ __device__ __forceinline__ int2 pair_ids(const PairCtx<D>& c, int k) {
   return make_int2(pA, pB);
 }
 
-// Issue the loads of pair k. An invalid or absent block is replaced by block 0 (always in
-// the pool) with no valid rows, so its contents never reach the result.
-template <int D, int NW, int NCH, int EPL>
-__device__ __forceinline__ void pair_load(PairTile<NCH, EPL>& t, const PairCtx<D>& c, int2 ids,
-                                          int k) {
+// Issue the loads of the pair whose first block is block jA of the sequence. An invalid
+// block id is replaced by block 0 (always in the pool); pair_valid then gives it no valid
+// rows, so its contents never reach the result. Only the ids and the constant parts of the
+// context are used, so a kernel may issue a pair before it knows the context length.
+template <int D, int NCH, int EPL>
+__device__ __forceinline__ void pair_issue(PairTile<NCH, EPL>& t, const PairCtx<D>& c, int2 ids,
+                                           int jA) {
   constexpr int BS = 16;
-  const int jA = c.blk0 + 2 * (c.wave + NW * k);
   const bool okA = ids.x >= 0 && (int64_t)ids.x < c.num_blocks;
   const bool okB = ids.y >= 0 && (int64_t)ids.y < c.num_blocks;
-  const int tA = jA * BS;
-  t.lastA = okA ? min(c.tok1 - tA, BS) : 0;
-  t.lastB = okB ? min(c.tok1 - tA - BS, BS) : 0;
   const size_t bA = (size_t)(okA ? ids.x : 0) * BS * c.row_stride + c.head_off;
   const size_t bB = (size_t)(okB ? ids.y : 0) * BS * c.row_stride + c.head_off;
   const size_t koff = (size_t)c.n16 * c.row_stride + 8 * c.kg;
@@ -207,7 +205,29 @@ __device__ __forceinline__ void pair_load(PairTile<NCH, EPL>& t, const PairCtx<D
     t.vr[j].load(c.v_cache + bA + voff + (size_t)j * c.row_stride);
     t.vr[4 + j].load(c.v_cache + bB + voff + (size_t)j * c.row_stride);
   }
-  t.tA = tA;
+  t.tA = jA * BS;
+}
+
+// Valid rows of each block of a pair issued with these ids (0 for an invalid id; <= 0 for a
+// block at or past tok1).
+template <int D, int NCH, int EPL>
+__device__ __forceinline__ void pair_valid(PairTile<NCH, EPL>& t, const PairCtx<D>& c, int2 ids,
+                                           int jA) {
+  constexpr int BS = 16;
+  const bool okA = ids.x >= 0 && (int64_t)ids.x < c.num_blocks;
+  const bool okB = ids.y >= 0 && (int64_t)ids.y < c.num_blocks;
+  const int tA = jA * BS;
+  t.lastA = okA ? min(c.tok1 - tA, BS) : 0;
+  t.lastB = okB ? min(c.tok1 - tA - BS, BS) : 0;
+}
+
+// Issue the loads of this wave's pair k (see pair_issue) and set its valid rows.
+template <int D, int NW, int NCH, int EPL>
+__device__ __forceinline__ void pair_load(PairTile<NCH, EPL>& t, const PairCtx<D>& c, int2 ids,
+                                          int k) {
+  const int jA = c.blk0 + 2 * (c.wave + NW * k);
+  pair_issue(t, c, ids, jA);
+  pair_valid(t, c, ids, jA);
 }
 
 // V^T operand of output column set e: 8 token slots of column EPL*n16 + e, gathered from the
