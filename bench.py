@@ -59,8 +59,9 @@ def parse_args():
                    help="CPU work budget of the oracle baseline sample")
     p.add_argument("--json-out", default=None)
     p.add_argument("--rope", action="store_true",
-                   help="write with the fused rotary embedding (positions L-1, Llama 3 base "
-                        "500000 frequencies) and attend with the rotated q")
+                   help="rotate q and the new keys first (positions L-1, Llama 3 base 500000 "
+                        "frequencies) and attend with the rotated q: one fused launch, or "
+                        "with --separate the rotation + write call, then attention")
     p.add_argument("--graph", action="store_true",
                    help="also capture one step in a HIP graph and time K replays "
                         "(reported as graph_ms_per_step)")
@@ -281,6 +282,9 @@ def main():
         print(f"output format {args.out_dtype} is not built for {args.in_dtype} inputs "
               "(fp32 or the input format)", file=sys.stderr)
         sys.exit(2)
+    if args.rope and args.in_dtype != "bf16":
+        print("the rotary embedding takes bf16 inputs only", file=sys.stderr)
+        sys.exit(2)
     if args.workload in wl.PREFILL_WORKLOADS:
         line = bench_prefill(args, torch, pk, wl)
         out = json.dumps(line)
@@ -310,6 +314,7 @@ def main():
                                                           dtype=torch.float64) / w.head_dim)
                              ).to(torch.float32)
             d["q_rot"] = torch.empty_like(d["q"])
+            d["bytes"]["write"] += d["q"].numel() * 2  # the rotated q is written out
         subs.append(d)
     torch.cuda.synchronize()
 
@@ -323,6 +328,15 @@ def main():
             torch.sum(flush)
         for i, d in enumerate(subs):
             ev = events[i] if events is not None else None
+            if args.rope and not args.separate:
+                # one launch rotates q and the new key, stores the rows and attends
+                pk.paged_decode_step_rope(d["q"], d["k_new"], d["v_new"], d["pos"],
+                                          d["inv_freq"], d["slot_mapping"], d["q_rot"],
+                                          d["k_cache"], d["v_cache"], d["block_tables"],
+                                          d["context_lens"], d["scale"], d["out"],
+                                          partition_tokens=args.partition, kernel=args.kernel,
+                                          workspace=d["ws"], events=ev)
+                continue
             if not args.rope and not args.separate:
                 # one launch stores the new rows and attends (plus the merge when split)
                 pk.paged_decode_step(d["q"], d["k_new"], d["v_new"], d["slot_mapping"],
@@ -451,7 +465,10 @@ def main():
             "us_per_call": {p["workload"]: p["attn_kernel_us_mean"] for p in per},
             "pct_of_peak": {p["workload"]: p["pct_of_peak"] for p in per},
             "kernels": {p["workload"]: p["kernel"] for p in per},
-            "step": ("RoPE + KV write, then decode attention" if args.rope else
+            "step": ("RoPE + KV write, then decode attention (two calls)"
+                     if args.rope and args.separate else
+                     "fused decode step with RoPE: rotation + KV write + decode attention in "
+                     "one launch" if args.rope else
                      "KV write, then decode attention (two calls)" if args.separate else
                      "fused decode step: KV write + decode attention in one launch") +
                     " per sub-workload",

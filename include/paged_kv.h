@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define PAGED_KV_ABI_VERSION 2
+#define PAGED_KV_ABI_VERSION 3
 
 typedef enum {
   PAGEDKV_OK = 0,
@@ -258,6 +258,40 @@ int paged_decode_step(const uint16_t* q, const uint16_t* k_new, const uint16_t* 
                       int32_t out_dtype, void* workspace, size_t workspace_bytes,
                       int32_t partition_tokens, int32_t kernel, hipEvent_t ev_begin,
                       hipEvent_t ev_end, hipStream_t stream);
+
+/*
+ * paged_decode_step_rope -- paged_decode_step with the rotary embedding of paged_kv_write_rope
+ * in front: q and k_new are rotated at positions[b] before they are used ("tiny-vLLM" blog,
+ * CUDA Kernel Engineering: RoPE; llm-stack, Serving engine / KV cache bullet: keys enter the
+ * cache rotated at their absolute positions).
+ *
+ *   q              [batch][num_q_heads][head_dim] bf16, not rotated; left unchanged
+ *   k_new, v_new   as in paged_decode_step (k_new not rotated)
+ *   positions      int32 [batch]: the absolute position of sequence b's new token
+ *   inv_freq, interleaved  as in paged_kv_write_rope (inv_freq 16-byte aligned)
+ *   q_out          [batch][num_q_heads][head_dim] bf16: receives the rotated q; must not
+ *                  overlap q (the attention reads q while q_out is written)
+ *   everything else as in paged_decode_step
+ *
+ * The result (q_out, the pools, out) equals, bit for bit, paged_kv_write_rope(q, k_new, v_new,
+ * positions, inv_freq, interleaved, slot_mapping, batch, q_out, ...) followed by
+ * paged_decode_attention_ex(q_out, ...), under the decode-step layout of paged_decode_step.
+ * The matrix-core kernels do all of it in one launch: the rotation happens in registers on the
+ * pieces of q and of the new key each lane already holds for its matrix tiles. The vector-ALU
+ * family issues paged_kv_write_rope as its own launch. bf16 inputs only
+ * (PAGEDKV_ERR_UNSUPPORTED otherwise); head_dim 64 or 128 as for the attention.
+ */
+int paged_decode_step_rope(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
+                           const int32_t* positions, const float* inv_freq, int32_t interleaved,
+                           const int64_t* slot_mapping, uint16_t* q_out, uint16_t* k_cache,
+                           uint16_t* v_cache, const int32_t* block_tables,
+                           int32_t max_blocks_per_seq, const int32_t* context_lens,
+                           int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                           int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                           float scale, int32_t kv_dtype, void* out, int32_t out_dtype,
+                           void* workspace, size_t workspace_bytes, int32_t partition_tokens,
+                           int32_t kernel, hipEvent_t ev_begin, hipEvent_t ev_end,
+                           hipStream_t stream);
 
 /*
  * paged_decode_plan -- the launch paged_decode_attention_ex would make for these sizes on

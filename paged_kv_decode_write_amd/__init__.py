@@ -6,13 +6,13 @@ tensors into pointers and the current stream, and nothing else. The library is l
 first use; if it is missing the call raises, there is no fallback.
 """
 from ._binding import (paged_kv_write, paged_decode_attention, paged_decode_step,
-                       paged_prefill_attention,
+                       paged_decode_step_rope, paged_prefill_attention,
                        paged_kv_write_rope,
                        decode_workspace_bytes, decode_plan,
                        library_path, load_library, abi_version, PagedKVError)
 
 __all__ = ["paged_kv_write", "paged_decode_attention", "paged_decode_step",
-           "paged_prefill_attention",
+           "paged_decode_step_rope", "paged_prefill_attention",
            "paged_kv_write_rope",
            "decode_workspace_bytes", "decode_plan",
            "library_path", "load_library", "abi_version", "PagedKVError"]

@@ -76,6 +76,10 @@ def load_library() -> ctypes.CDLL:
         lib.paged_decode_step.restype = ctypes.c_int
         lib.paged_decode_step.argtypes = [P, P, P, P, P, P, P, I32, P, I32, I32, I32, I32, I32,
                                           I64, F32, I32, P, I32, P, SZ, I32, I32, P, P, P]
+        lib.paged_decode_step_rope.restype = ctypes.c_int
+        lib.paged_decode_step_rope.argtypes = [P, P, P, P, P, I32, P, P, P, P, P, I32, P, I32,
+                                               I32, I32, I32, I32, I64, F32, I32, P, I32, P, SZ,
+                                               I32, I32, P, P, P]
         lib.paged_kv_write_rope.restype = ctypes.c_int
         lib.paged_kv_write_rope.argtypes = [P, P, P, P, P, I32, P, I64, P, P, P, I64, I32, I32,
                                             I32, I32, P]
@@ -244,17 +248,9 @@ def paged_decode_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
     return out
 
 
-def paged_decode_step(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
-                      slot_mapping: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
-                      block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
-                      out: torch.Tensor, *, partition_tokens: int = 0, kernel: str = "auto",
-                      workspace: Optional[torch.Tensor] = None,
-                      events: Optional[tuple] = None) -> torch.Tensor:
-    """The decode step in one call: store k_new[b] / v_new[b] ([B, Hkv, D]) at slot
-    slot_mapping[b] ([B] int64) of the pools, then attend as paged_decode_attention does.
-    Equals paged_kv_write followed by paged_decode_attention when slot_mapping[b] is the slot
-    of position context_lens[b] - 1 of sequence b (or negative); the matrix-core kernels do both
-    in one launch."""
+def _check_step(q, k_new, v_new, slot_mapping, k_cache, v_cache, block_tables, context_lens,
+                out, kernel):
+    """Validate the tensors of a decode step; returns (dev, dtype, NB, bs, Hkv, D, B, Hq, MB)."""
     _require(k_cache, "k_cache", INPUT_TYPES, 4)
     dev, dt = k_cache.device, k_cache.dtype
     _require(v_cache, "v_cache", dt, 4, dev)
@@ -276,21 +272,75 @@ def paged_decode_step(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
         raise ValueError("block_tables must be [B, MB] and context_lens [B]")
     if kernel not in KERNELS:
         raise ValueError(f"kernel must be one of {sorted(KERNELS)}")
-    lib = load_library()
+    return dev, dt, NB, bs, Hkv, D, B, Hq, MB
+
+
+def _step_workspace(lib, dev, B, Hq, D, MB, bs, partition_tokens, workspace):
     need = int(lib.paged_decode_workspace_bytes(B, Hq, D, MB, bs, partition_tokens))
     if workspace is None:
         workspace = _cached_workspace(dev, need)
     elif workspace.device != dev or workspace.dtype != torch.uint8:
         raise ValueError("workspace must be a uint8 tensor on the cache's device")
+    return (workspace.data_ptr(), workspace.numel()) if need else (None, 0)
+
+
+def paged_decode_step(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                      slot_mapping: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                      block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
+                      out: torch.Tensor, *, partition_tokens: int = 0, kernel: str = "auto",
+                      workspace: Optional[torch.Tensor] = None,
+                      events: Optional[tuple] = None) -> torch.Tensor:
+    """The decode step in one call: store k_new[b] / v_new[b] ([B, Hkv, D]) at slot
+    slot_mapping[b] ([B] int64) of the pools, then attend as paged_decode_attention does.
+    Equals paged_kv_write followed by paged_decode_attention when slot_mapping[b] is the slot
+    of position context_lens[b] - 1 of sequence b (or negative); the matrix-core kernels do both
+    in one launch."""
+    dev, dt, NB, bs, Hkv, D, B, Hq, MB = _check_step(
+        q, k_new, v_new, slot_mapping, k_cache, v_cache, block_tables, context_lens, out, kernel)
+    lib = load_library()
+    ws, wsb = _step_workspace(lib, dev, B, Hq, D, MB, bs, partition_tokens, workspace)
     ev_b, ev_e = events if events is not None else (None, None)
     with torch.cuda.device(dev):
         _check(lib.paged_decode_step(
             q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), slot_mapping.data_ptr(),
             k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(), MB,
             context_lens.data_ptr(), B, Hq, Hkv, D, bs, NB, float(scale), DTYPES[dt],
-            out.data_ptr(), DTYPES[out.dtype], workspace.data_ptr() if need else None,
-            workspace.numel() if need else 0, partition_tokens, KERNELS[kernel], ev_b, ev_e,
-            _stream_handle(dev)))
+            out.data_ptr(), DTYPES[out.dtype], ws, wsb, partition_tokens, KERNELS[kernel], ev_b,
+            ev_e, _stream_handle(dev)))
+    return out
+
+
+def paged_decode_step_rope(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                           positions: torch.Tensor, inv_freq: torch.Tensor,
+                           slot_mapping: torch.Tensor, q_out: torch.Tensor,
+                           k_cache: torch.Tensor, v_cache: torch.Tensor,
+                           block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
+                           out: torch.Tensor, *, interleaved: bool = False,
+                           partition_tokens: int = 0, kernel: str = "auto",
+                           workspace: Optional[torch.Tensor] = None,
+                           events: Optional[tuple] = None) -> torch.Tensor:
+    """paged_decode_step with rotary embedding in front: q and k_new (bf16, not rotated) are
+    rotated at positions[b] ([B] int32) by inv_freq ([D/2] fp32); the rotated q goes to q_out
+    ([B, Hq, D], separate from q), the rotated key into the cache, and attention uses both.
+    Equals paged_kv_write_rope followed by paged_decode_attention(q_out, ...) bit for bit."""
+    dev, dt, NB, bs, Hkv, D, B, Hq, MB = _check_step(
+        q, k_new, v_new, slot_mapping, k_cache, v_cache, block_tables, context_lens, out, kernel)
+    _require(positions, "positions", torch.int32, 1, dev)
+    _require(inv_freq, "inv_freq", torch.float32, 1, dev)
+    _require(q_out, "q_out", dt, 3, dev)
+    if positions.shape != (B,) or inv_freq.shape != (D // 2,) or q_out.shape != q.shape:
+        raise ValueError(f"positions must be [{B}], inv_freq [{D // 2}] and q_out like q")
+    lib = load_library()
+    ws, wsb = _step_workspace(lib, dev, B, Hq, D, MB, bs, partition_tokens, workspace)
+    ev_b, ev_e = events if events is not None else (None, None)
+    with torch.cuda.device(dev):
+        _check(lib.paged_decode_step_rope(
+            q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), positions.data_ptr(),
+            inv_freq.data_ptr(), int(bool(interleaved)), slot_mapping.data_ptr(),
+            q_out.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(), MB,
+            context_lens.data_ptr(), B, Hq, Hkv, D, bs, NB, float(scale), DTYPES[dt],
+            out.data_ptr(), DTYPES[out.dtype], ws, wsb, partition_tokens, KERNELS[kernel], ev_b,
+            ev_e, _stream_handle(dev)))
     return out
 
 

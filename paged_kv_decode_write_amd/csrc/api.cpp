@@ -205,14 +205,24 @@ int check_decode_sizes(int32_t max_blocks, int32_t batch, int32_t num_q_heads,
   return PAGEDKV_OK;
 }
 
-// The KV write of a fused decode step: token b's rows go to slot_mapping[b] of the pools.
+// The KV write of a fused decode step: token b's rows go to slot_mapping[b] of the pools;
+// with positions non-null, q and k_new are first rotated at positions[b] (rotated q to q_out).
 struct StepWrite {
   const uint16_t* k_new;
   const uint16_t* v_new;
   const int64_t* slot_mapping;
   uint16_t* k_cache;
   uint16_t* v_cache;
+  const int32_t* positions;
+  const float* inv_freq;
+  int32_t interleaved;
+  uint16_t* q_out;
 };
+
+bool ranges_overlap(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
 
 // Decode attention, optionally fused with the step's KV write (sw non-null).
 int decode_impl(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache,
@@ -247,6 +257,19 @@ int decode_impl(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_ca
       return fail(PAGEDKV_ERR_NULL, "k_new, v_new and slot_mapping must be non-NULL");
     if (!aligned(sw->k_new, 16) || !aligned(sw->v_new, 16) || !aligned(sw->slot_mapping, 8))
       return fail(PAGEDKV_ERR_ALIGN, "k_new and v_new need 16-byte alignment");
+    if (sw->positions) {
+      if (kv_dtype != PAGEDKV_DTYPE_BF16)
+        return fail(PAGEDKV_ERR_UNSUPPORTED, "the rotary decode step takes bf16 inputs only");
+      if (sw->interleaved != 0 && sw->interleaved != 1)
+        return fail(PAGEDKV_ERR_SHAPE, "interleaved must be 0 or 1");
+      if (!sw->inv_freq || !sw->q_out)
+        return fail(PAGEDKV_ERR_NULL, "positions, inv_freq and q_out must be non-NULL");
+      if (!aligned(sw->inv_freq, 16) || !aligned(sw->q_out, 16) || !aligned(sw->positions, 4))
+        return fail(PAGEDKV_ERR_ALIGN, "inv_freq and q_out need 16-byte alignment");
+      const size_t qbytes = (size_t)batch * num_q_heads * head_dim * 2;
+      if (ranges_overlap(q, qbytes, sw->q_out, qbytes))
+        return fail(PAGEDKV_ERR_SHAPE, "q_out must not overlap q");
+    }
   }
   int cus = 0;
   st = cu_count(&cus);
@@ -287,7 +310,29 @@ int decode_impl(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_ca
   }
 
   hipError_t e;
-  if (sw && chosen == PAGEDKV_KERNEL_VALU) {
+  if (sw && chosen == PAGEDKV_KERNEL_VALU && sw->positions) {
+    // The vector-ALU kernel has no fused write: rotate and store first, then attend over the
+    // pools with the rotated q.
+    RopeArgs r{};
+    r.q = q;
+    r.k = sw->k_new;
+    r.v = sw->v_new;
+    r.positions = sw->positions;
+    r.inv_freq = sw->inv_freq;
+    r.slot_mapping = sw->slot_mapping;
+    r.q_out = sw->q_out;
+    r.k_cache = sw->k_cache;
+    r.v_cache = sw->v_cache;
+    r.num_tokens = batch;
+    r.num_slots = num_blocks * block_size;
+    r.num_q_heads = num_q_heads;
+    r.num_kv_heads = num_kv_heads;
+    r.head_dim = head_dim;
+    r.interleaved = sw->interleaved;
+    e = launch_kv_write_rope(r, stream);
+    if (e != hipSuccess) return hip_fail(e, "rope + kv_write launch");
+    a.q = sw->q_out;
+  } else if (sw && chosen == PAGEDKV_KERNEL_VALU) {
     // The vector-ALU kernel has no fused write: store first, then attend over the pools.
     e = launch_kv_write(sw->k_new, sw->v_new, sw->slot_mapping, batch, sw->k_cache,
                         sw->v_cache, num_blocks * block_size, num_kv_heads * head_dim, stream);
@@ -298,6 +343,10 @@ int decode_impl(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_ca
     a.slot_mapping = sw->slot_mapping;
     a.k_cache_w = sw->k_cache;
     a.v_cache_w = sw->v_cache;
+    a.positions = sw->positions;
+    a.inv_freq = sw->inv_freq;
+    a.interleaved = sw->interleaved;
+    a.q_out = sw->q_out;
   }
   if (ev_begin && (e = hipEventRecord(ev_begin, stream)) != hipSuccess)
     return hip_fail(e, "hipEventRecord(begin)");
@@ -476,7 +525,30 @@ int paged_decode_step(const uint16_t* q, const uint16_t* k_new, const uint16_t* 
                       int32_t out_dtype, void* workspace, size_t workspace_bytes,
                       int32_t partition_tokens, int32_t kernel, hipEvent_t ev_begin,
                       hipEvent_t ev_end, hipStream_t stream) {
-  const StepWrite sw{k_new, v_new, slot_mapping, k_cache, v_cache};
+  const StepWrite sw{k_new, v_new, slot_mapping, k_cache, v_cache, nullptr, nullptr, 0, nullptr};
+  return decode_impl(q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, batch,
+                     num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale,
+                     kv_dtype, out, out_dtype, workspace, workspace_bytes, partition_tokens,
+                     kernel, ev_begin, ev_end, stream, &sw);
+}
+
+int paged_decode_step_rope(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
+                           const int32_t* positions, const float* inv_freq, int32_t interleaved,
+                           const int64_t* slot_mapping, uint16_t* q_out, uint16_t* k_cache,
+                           uint16_t* v_cache, const int32_t* block_tables,
+                           int32_t max_blocks_per_seq, const int32_t* context_lens,
+                           int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                           int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                           float scale, int32_t kv_dtype, void* out, int32_t out_dtype,
+                           void* workspace, size_t workspace_bytes, int32_t partition_tokens,
+                           int32_t kernel, hipEvent_t ev_begin, hipEvent_t ev_end,
+                           hipStream_t stream) {
+  if (!positions) {
+    g_last_error.clear();
+    return fail(PAGEDKV_ERR_NULL, "positions must be non-NULL");
+  }
+  const StepWrite sw{k_new,     v_new,    slot_mapping, k_cache, v_cache,
+                     positions, inv_freq, interleaved,  q_out};
   return decode_impl(q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, batch,
                      num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale,
                      kv_dtype, out, out_dtype, workspace, workspace_bytes, partition_tokens,

@@ -72,7 +72,36 @@ __device__ __forceinline__ void step_store(const DecodeArgs& a, int b, int g, in
   }
 }
 
-template <int D, int NW, int KT, int OT>
+// The same store from a wave's registers (the rotated key row of a RoPE step): the lanes with
+// n16 == 0 hold the whole K row (chunks 32ch + 8kg), the lanes with kg == 0 the whole V row
+// (EPL columns at EPL * n16).
+template <int D, int NCH, int EPL>
+__device__ __forceinline__ void step_store_regs(const DecodeArgs& a, int b, int g,
+                                                const NewRow<NCH, EPL>& r, int n16, int kg) {
+  const int64_t slot = a.slot_mapping[b];
+  if (slot < 0 || slot >= a.num_blocks * 16) return;
+  const size_t dst = ((size_t)slot * a.num_kv_heads + g) * D;
+  if (n16 == 0) {
+#pragma unroll
+    for (int ch = 0; ch < NCH; ++ch)
+      *reinterpret_cast<uint4*>(a.k_cache_w + dst + 32 * ch + 8 * kg) = r.k[ch];
+  }
+  if (kg == 0) r.v.store(a.v_cache_w + dst + EPL * n16);
+}
+
+// RoPE step, part 2 (part 1 is rope_pieces on the loaded q and new-key pieces): the rotated q
+// rows of this wave's heads, from registers. Issued after the block loop, as the step store
+// is, so that no store precedes the loop's block-table reads.
+template <int D, int NCH>
+__device__ __forceinline__ void store_q_out(const DecodeArgs& a, const uint4 (&qb)[NCH], int b,
+                                            int g, int G, int n16, int kg) {
+  if (n16 >= G) return;
+  uint16_t* o = a.q_out + ((size_t)b * a.num_q_heads + (size_t)g * G + n16) * D + 8 * kg;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) *reinterpret_cast<uint4*>(o + 32 * c) = qb[c];
+}
+
+template <int D, int NW, int KT, int OT, bool ROPE>
 __global__ void __launch_bounds__(NW * 64)
 decode_mfma_kernel(const DecodeArgs a) {
   constexpr int BS = 16;
@@ -141,6 +170,9 @@ decode_mfma_kernel(const DecodeArgs a) {
   NewRow<NCH, EPL> nrow;
   load_new_row(nrow, (a.k_new ? a.k_new : a.k_cache) + ((size_t)b * Hkv + g) * D,
                (a.v_new ? a.v_new : a.v_cache) + ((size_t)b * Hkv + g) * D, n16, kg);
+  if constexpr (ROPE)
+    rope_pieces<KT>(qb, nrow.k, (float)a.positions[b], a.inv_freq, a.interleaved != 0, kg,
+                    lane);
   const float sl2 = a.scale_log2;
 
   // This wave's block pairs are (blk0 + 2*(wave + NW*k), +1), k = 0 .. np-1. Two pairs are
@@ -172,7 +204,12 @@ decode_mfma_kernel(const DecodeArgs a) {
 
   // The step's store comes after every block-table read, so the compiler can keep those reads
   // on the scalar path (no earlier store may have changed the table).
-  if (a.k_new && wave == 0 && (L > 0 ? L - 1 < tok1 : part == 0)) step_store<D>(a, b, g, lane);
+  if (a.k_new && wave == 0 && (L > 0 ? L - 1 < tok1 : part == 0)) {
+    if constexpr (ROPE) step_store_regs<D>(a, b, g, nrow, n16, kg);
+    else step_store<D>(a, b, g, lane);
+  }
+  if constexpr (ROPE)
+    if (wave == 0 && part == 0) store_q_out<D>(a, qb, b, g, G, n16, kg);
 
   // Sum of the running sums over the four lanes of a head.
   float l_run = st.l_run;
@@ -223,7 +260,7 @@ decode_mfma_kernel(const DecodeArgs a) {
 // token row of a block instead of D*2, and every wave walks the whole partition on its own
 // (no cross-wave merge). Each wave writes its heads' output, or its partition partial for
 // the merge kernel.
-template <int D, int HPW, int NBUF, int MINW, int KT, int OT>
+template <int D, int HPW, int NBUF, int MINW, int KT, int OT, bool ROPE>
 __global__ void __launch_bounds__(HPW * 64, MINW)
 decode_mfma_hw_kernel(const DecodeArgs a) {
   constexpr int BS = 16;
@@ -278,6 +315,12 @@ decode_mfma_hw_kernel(const DecodeArgs a) {
   ctx.wave = 0;
   ctx.n16 = n16;
   ctx.kg = kg;
+  // Fused step: the new row of this head, loaded unconditionally (from the cache when there is
+  // no step write, then never used) so no memory operation waits behind a branch; issued
+  // before the first pair so that waiting for it never waits for the pair.
+  NewRow<NCH, EPL> nrow;
+  load_new_row(nrow, (a.k_new ? a.k_new : a.k_cache) + ((size_t)b * Hkv + g) * D,
+               (a.v_new ? a.v_new : a.v_cache) + ((size_t)b * Hkv + g) * D, n16, kg);
   // The first pair's K / V loads go out with q's, before the context length arrives: a
   // partition that then turns out empty discards them; every other one saves a round trip.
   PairTile<NCH, EPL> t[NBUF];
@@ -298,12 +341,10 @@ decode_mfma_hw_kernel(const DecodeArgs a) {
 #pragma unroll
   for (int e = 0; e < EPL; ++e) st.acc[e] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  // Fused step: the new row of this head, loaded unconditionally (from the cache when there is
-  // no step write, then never used) so no memory operation waits behind a branch.
   const int sub_pos = step_sub_pos(a, table, b, L);
-  NewRow<NCH, EPL> nrow;
-  load_new_row(nrow, (a.k_new ? a.k_new : a.k_cache) + ((size_t)b * Hkv + g) * D,
-               (a.v_new ? a.v_new : a.v_cache) + ((size_t)b * Hkv + g) * D, n16, kg);
+  if constexpr (ROPE)
+    rope_pieces<KT>(qb, nrow.k, (float)a.positions[b], a.inv_freq, a.interleaved != 0, kg,
+                    lane);
   const float sl2 = a.scale_log2;
 
   // Pairs (blk0 + 2k, blk0 + 2k + 1), k = 0 .. np-1, NBUF pairs in flight. Pair j lives in
@@ -338,7 +379,12 @@ decode_mfma_hw_kernel(const DecodeArgs a) {
   }
 
   // The step's store comes after every block-table read (see the split-wave kernel).
-  if (a.k_new && (L > 0 ? L - 1 < tok1 : part == 0)) step_store<D>(a, b, g, lane);
+  if (a.k_new && (L > 0 ? L - 1 < tok1 : part == 0)) {
+    if constexpr (ROPE) step_store_regs<D>(a, b, g, nrow, n16, kg);
+    else step_store<D>(a, b, g, lane);
+  }
+  if constexpr (ROPE)
+    if (part == 0) store_q_out<D>(a, qb, b, g, G, n16, kg);
 
   float l_run = st.l_run;
   l_run = row4_sum(l_run);
@@ -384,12 +430,19 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream) {
   const unsigned units = (unsigned)((long long)a.batch * a.num_kv_heads * a.nparts);
   return with_formats(a.kv_dtype, a.out_dtype, [&](auto kt, auto ot) {
     constexpr int KT = decltype(kt)::value, OT = decltype(ot)::value;
-    if (a.head_dim == 128)
-      hipLaunchKernelGGL((decode_mfma_kernel<128, NW, KT, OT>), dim3(units), dim3(NW * 64), 0,
-                         stream, a);
+    const bool rope = a.positions != nullptr;
+    if (a.head_dim == 128 && rope)
+      hipLaunchKernelGGL((decode_mfma_kernel<128, NW, KT, OT, true>), dim3(units), dim3(NW * 64),
+                         0, stream, a);
+    else if (a.head_dim == 128)
+      hipLaunchKernelGGL((decode_mfma_kernel<128, NW, KT, OT, false>), dim3(units),
+                         dim3(NW * 64), 0, stream, a);
+    else if (a.head_dim == 64 && rope)
+      hipLaunchKernelGGL((decode_mfma_kernel<64, NW, KT, OT, true>), dim3(units), dim3(NW * 64),
+                         0, stream, a);
     else if (a.head_dim == 64)
-      hipLaunchKernelGGL((decode_mfma_kernel<64, NW, KT, OT>), dim3(units), dim3(NW * 64), 0,
-                         stream, a);
+      hipLaunchKernelGGL((decode_mfma_kernel<64, NW, KT, OT, false>), dim3(units), dim3(NW * 64),
+                         0, stream, a);
     else
       return hipErrorInvalidValue;
     return hipGetLastError();
@@ -405,11 +458,18 @@ hipError_t launch_decode_mfma_hw(const DecodeArgs& a, hipStream_t stream) {
   const unsigned units = (unsigned)((long long)a.batch * ngrp * a.nparts);
   return with_formats(a.kv_dtype, a.out_dtype, [&](auto kt, auto ot) {
     constexpr int KT = decltype(kt)::value, OT = decltype(ot)::value;
-    if (a.head_dim == 128)
-      hipLaunchKernelGGL((decode_mfma_hw_kernel<128, HPW, NBUF, 2, KT, OT>), dim3(units),
+    const bool rope = a.positions != nullptr;
+    if (a.head_dim == 128 && rope)
+      hipLaunchKernelGGL((decode_mfma_hw_kernel<128, HPW, NBUF, 2, KT, OT, true>), dim3(units),
+                         dim3(HPW * 64), 0, stream, a);
+    else if (a.head_dim == 128)
+      hipLaunchKernelGGL((decode_mfma_hw_kernel<128, HPW, NBUF, 2, KT, OT, false>), dim3(units),
+                         dim3(HPW * 64), 0, stream, a);
+    else if (a.head_dim == 64 && rope)
+      hipLaunchKernelGGL((decode_mfma_hw_kernel<64, HPW, NBUF, 2, KT, OT, true>), dim3(units),
                          dim3(HPW * 64), 0, stream, a);
     else if (a.head_dim == 64)
-      hipLaunchKernelGGL((decode_mfma_hw_kernel<64, HPW, NBUF, 2, KT, OT>), dim3(units),
+      hipLaunchKernelGGL((decode_mfma_hw_kernel<64, HPW, NBUF, 2, KT, OT, false>), dim3(units),
                          dim3(HPW * 64), 0, stream, a);
     else
       return hipErrorInvalidValue;

@@ -33,9 +33,11 @@ template <int KT> __device__ __forceinline__ void unpack8(const uint4& w, float 
 // Makes an fp32 value opaque to the optimiser, so the operation that produced it is rounded
 // to fp32 first. Without it, a product feeding an fp16 conversion may be contracted into one
 // v_fma_mix*_f16 (a single rounding of the exact product): close, but not the fp32 result
-// rounded, which is what a 16-bit output is defined to hold.
+// rounded, which is what a 16-bit output is defined to hold. Not volatile: a volatile asm
+// counts as a possible memory write, and one ahead of a loop would stop the compiler from
+// reading the block table through the scalar cache inside it.
 __device__ __forceinline__ float materialize_f32(float f) {
-  asm volatile("" : "+v"(f));
+  asm("" : "+v"(f));
   return f;
 }
 
@@ -46,6 +48,15 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 // fp32 -> fp16 with v_cvt_f16_f32 (round to nearest even; overflow gives infinity).
 __device__ __forceinline__ uint16_t f32_to_f16_rne(float f) {
   return __builtin_bit_cast(uint16_t, (_Float16)materialize_f32(f));
+}
+
+// Rotary embedding of one pair (x0, x1) by an angle with cosine c and sine s, written with
+// explicit fused multiply-adds so every kernel that rotates produces the same bits:
+// y0 = x0 c - x1 s, y1 = x1 c + x0 s, each the fma of one product with the other one rounded.
+__device__ __forceinline__ void rope_rotate(float x0, float x1, float c, float s, float& y0,
+                                            float& y1) {
+  y0 = __builtin_fmaf(x0, c, -(x1 * s));
+  y1 = __builtin_fmaf(x1, c, x0 * s);
 }
 
 // Output stores: one value, or four consecutive values (index a multiple of 4), in the

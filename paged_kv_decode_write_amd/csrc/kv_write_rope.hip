@@ -8,19 +8,12 @@
 // rotated into q_out; k is rotated and stored, v copied, at slot slot_mapping[t] (as the
 // plain write does; a negative slot stores nothing). One launch does what would otherwise be
 // a rotation kernel, a write kernel and a second pass over k.
+#include "device_common.h"
 #include "launch.h"
 
 namespace pagedkv {
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
-
-// fp32 -> bf16, round to nearest even (finite values; NaN stays a quiet NaN).
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  const uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-  const uint32_t rounded = u + 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(rounded >> 16);
-}
 
 // One workgroup per token. Thread (pair i, slice j) forms the angle of pair i and its sine
 // and cosine once, then rotates pair i of heads j, j + NS, j + 2*NS, ... of q and of k
@@ -28,9 +21,10 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 // head, while every thread still has only a few heads to rotate.
 __device__ __forceinline__ void rotate_pair(const uint16_t* src, uint16_t* dst, int i0, int i1,
                                             float cs, float sn) {
-  const float x0 = bf16_to_f32(src[i0]), x1 = bf16_to_f32(src[i1]);
-  dst[i0] = f32_to_bf16(x0 * cs - x1 * sn);
-  dst[i1] = f32_to_bf16(x1 * cs + x0 * sn);
+  float y0, y1;
+  rope_rotate(bf16_to_f32(src[i0]), bf16_to_f32(src[i1]), cs, sn, y0, y1);
+  dst[i0] = f32_to_bf16_rne(y0);
+  dst[i1] = f32_to_bf16_rne(y1);
 }
 
 __global__ void __launch_bounds__(256)

@@ -35,6 +35,13 @@ struct DecodeArgs {
   const int64_t* slot_mapping;
   uint16_t* k_cache_w;
   uint16_t* v_cache_w;
+  // Fused decode step with rotary embedding (positions != nullptr): q and the new keys are
+  // rotated at positions[b] with inv_freq ([D/2], half or interleaved pairing) before use; the
+  // rotated q goes to q_out, the rotated key to the cache.
+  const int32_t* positions;
+  const float* inv_freq;
+  int32_t interleaved;
+  uint16_t* q_out;
 };
 
 // Arguments of one multi-query causal (prefill) launch, already validated.

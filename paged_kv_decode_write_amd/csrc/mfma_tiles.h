@@ -62,6 +62,7 @@ template <> struct VRow<8> {
   __device__ __forceinline__ void take_if(bool c, const VRow& o) {
     w.x = c ? o.w.x : w.x; w.y = c ? o.w.y : w.y; w.z = c ? o.w.z : w.z; w.w = c ? o.w.w : w.w;
   }
+  __device__ __forceinline__ void store(uint16_t* p) const { *reinterpret_cast<uint4*>(p) = w; }
   __device__ __forceinline__ uint32_t word(int i) const {
     return i == 0 ? w.x : i == 1 ? w.y : i == 2 ? w.z : w.w;
   }
@@ -73,6 +74,7 @@ template <> struct VRow<4> {
   __device__ __forceinline__ void take_if(bool c, const VRow& o) {
     w.x = c ? o.w.x : w.x; w.y = c ? o.w.y : w.y;
   }
+  __device__ __forceinline__ void store(uint16_t* p) const { *reinterpret_cast<uint2*>(p) = w; }
   __device__ __forceinline__ uint32_t word(int i) const { return i == 0 ? w.x : w.y; }
 };
 
@@ -141,6 +143,77 @@ __device__ __forceinline__ void load_new_row(NewRow<NCH, EPL>& r, const uint16_t
   for (int ch = 0; ch < NCH; ++ch)
     r.k[ch] = *reinterpret_cast<const uint4*>(k_row + 8 * kg + 32 * ch);
   r.v.load(v_row + EPL * n16);
+}
+
+// 16-bit element t (0..7) of an 8-element piece, and its replacement.
+__device__ __forceinline__ uint32_t piece_word(const uint4& v, int w) {
+  return w == 0 ? v.x : w == 1 ? v.y : w == 2 ? v.z : v.w;
+}
+__device__ __forceinline__ uint32_t piece_elem(const uint4& v, int t) {
+  return (piece_word(v, t / 2) >> (16 * (t % 2))) & 0xffffu;
+}
+__device__ __forceinline__ void piece_set(uint4& v, int t, uint32_t h) {
+  const uint32_t keep = t % 2 ? 0x0000ffffu : 0xffff0000u;
+  const uint32_t put = t % 2 ? h << 16 : h;
+  switch (t / 2) {
+    case 0: v.x = (v.x & keep) | put; break;
+    case 1: v.y = (v.y & keep) | put; break;
+    case 2: v.z = (v.z & keep) | put; break;
+    default: v.w = (v.w & keep) | put; break;
+  }
+}
+
+template <int KT> __device__ __forceinline__ float elem_to_f32(uint32_t h) {
+  return in_lo<KT>(h);
+}
+template <int KT> __device__ __forceinline__ uint32_t f32_to_elem(float f) {
+  if constexpr (KT == kDtF16) return f32_to_f16_rne(f);
+  else return f32_to_bf16_rne(f);
+}
+
+// Rotary embedding, in registers, of one lane's pieces of a query row and of a key row: the
+// lane holds columns 32c + 8kg .. +7 of each (c < NCH). Pair i turns by pos * inv_freq[i]
+// (fp32 product, then sincosf, then rope_rotate, then rounding to the 16-bit format, as the
+// standalone RoPE kernel does). A wave needs only D/2 = 16 NCH angles, so lane l evaluates the
+// sine and cosine of pair l mod D/2 once and the lanes fetch the ones they need from each
+// other (ds_bpermute moves bits, so the values are those of the standalone kernel). Half
+// pairing (i, i + D/2) pairs chunk c with chunk c + NCH/2 at the same offset (pair
+// 32c + 8kg + t); interleaved pairing (2i, 2i+1) pairs neighbours inside a piece (pair
+// 16c + 4kg + u).
+template <int KT, int NCH>
+__device__ __forceinline__ void rope_pieces(uint4 (&q)[NCH], uint4 (&k)[NCH], float pos,
+                                            const float* inv_freq, bool interleaved, int kg,
+                                            int lane) {
+  constexpr int kPairs = 16 * NCH;  // D/2: 64 or 32, never more than a wave
+  float sn_own, cs_own;
+  sincosf(pos * inv_freq[lane % kPairs], &sn_own, &cs_own);
+  const auto turn = [&](uint4& a, int ta, uint4& b, int tb, int pair) {
+    const float sn = __shfl(sn_own, pair), cs = __shfl(cs_own, pair);
+    float y0, y1;
+    rope_rotate(elem_to_f32<KT>(piece_elem(a, ta)), elem_to_f32<KT>(piece_elem(b, tb)), cs, sn,
+                y0, y1);
+    piece_set(a, ta, f32_to_elem<KT>(y0));
+    piece_set(b, tb, f32_to_elem<KT>(y1));
+  };
+  if (!interleaved) {
+#pragma unroll
+    for (int c = 0; c < NCH / 2; ++c)
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const int pair = 32 * c + 8 * kg + t;
+        turn(q[c], t, q[c + NCH / 2], t, pair);
+        turn(k[c], t, k[c + NCH / 2], t, pair);
+      }
+  } else {
+#pragma unroll
+    for (int c = 0; c < NCH; ++c)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int pair = 16 * c + 4 * kg + u;
+        turn(q[c], 2 * u, q[c], 2 * u + 1, pair);
+        turn(k[c], 2 * u, k[c], 2 * u + 1, pair);
+      }
+  }
 }
 
 // Put the new row in place of position sub_pos (-1: none) of a loaded pair, by selects on data

@@ -32,7 +32,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for want in ("paged_kv_write", "paged_decode_attention", "paged_decode_attention_ex",
                  "paged_decode_attention_typed", "paged_prefill_attention",
-                 "paged_prefill_attention_ex", "paged_kv_write_rope", "paged_decode_step",
+                 "paged_prefill_attention_ex", "paged_kv_write_rope", "paged_decode_step", "paged_decode_step_rope",
                  "paged_decode_workspace_bytes", "paged_kv_status_string", "paged_kv_abi_version",
                  "paged_kv_last_error", "paged_decode_plan"):
         assert want in names
@@ -48,7 +48,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.paged_kv_abi_version() == 2
+    assert lib.paged_kv_abi_version() == 3
     assert lib.paged_kv_status_string(OK) == b"PAGEDKV_OK"
     assert lib.paged_kv_status_string(ERR_WORKSPACE) == b"PAGEDKV_ERR_WORKSPACE"
     assert lib.paged_kv_status_string(99) == b"PAGEDKV_UNKNOWN_STATUS"
@@ -173,3 +173,29 @@ def test_binding_rejects_cpu_tensors():
         _binding.paged_kv_write(k, k, torch.zeros(2, dtype=torch.int64),
                                 torch.zeros(4, 16, 8, 128, dtype=torch.bfloat16),
                                 torch.zeros(4, 16, 8, 128, dtype=torch.bfloat16))
+
+
+def _step_rope(lib, q=FAKE, kn=FAKE, vn=FAKE, pos=FAKE, freq=FAKE, il=0, sl=FAKE, qo=FAKE + 4096,
+               kc=FAKE, vc=FAKE, bt=FAKE, MB=8, lens=FAKE, B=2, Hq=32, Hkv=8, D=128, bs=16,
+               NB=64, out=FAKE, kvt=BF16, kernel=0):
+    return lib.paged_decode_step_rope(q, kn, vn, pos, freq, il, sl, qo, kc, vc, bt, MB, lens, B,
+                                      Hq, Hkv, D, bs, NB, 0.1, kvt, out, F32, None, 0, -1,
+                                      kernel, None, None, None)
+
+
+def test_decode_step_rope_argument_errors(lib):
+    # q is 2 x 32 x 128 bf16 = 16 KiB from FAKE: q_out at FAKE + 4096 overlaps it
+    assert _step_rope(lib, pos=None) == ERR_NULL
+    assert _step_rope(lib, freq=None) == ERR_NULL
+    assert _step_rope(lib, qo=None) == ERR_NULL
+    assert _step_rope(lib, kn=None) == ERR_NULL
+    assert _step_rope(lib, il=2, qo=FAKE + 16384) == ERR_SHAPE
+    assert b"interleaved" in lib.paged_kv_last_error()
+    assert _step_rope(lib, kvt=F16) == ERR_UNSUPPORTED
+    assert _step_rope(lib, freq=FAKE + 8) == ERR_ALIGN
+    assert _step_rope(lib, qo=FAKE + 4104) == ERR_ALIGN
+    assert _step_rope(lib, pos=FAKE + 2) == ERR_ALIGN
+    assert _step_rope(lib) == ERR_SHAPE  # q_out overlaps q
+    assert b"overlap" in lib.paged_kv_last_error()
+    assert _step_rope(lib, D=96) == ERR_UNSUPPORTED
+    assert _step_rope(lib, B=0, q=None, kn=None, out=None, qo=None) == OK  # empty batch: no-op

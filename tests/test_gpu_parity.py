@@ -640,3 +640,103 @@ def test_rope_in_place_and_large_positions(dev):
     assert q_out.data_ptr() == d["q"].data_ptr()
     assert bf16_ulp_diff(wl.to_bits(q_out), q_ref).max() <= 1.0
     assert bf16_ulp_diff(wl.to_bits(d["k_cache"]), kc_ref).max() <= 1.0
+
+
+# ------------------------------------------------------- decode step with rotary embedding
+def run_step_rope(d, pos, inv, interleaved, kernel="auto", partition=0):
+    """paged_decode_step_rope into NaN-poisoned q_out and out."""
+    w = d["workload"]
+    out = torch.full((w.batch, w.num_q_heads, w.head_dim), float("nan"), dtype=torch.float32,
+                     device=d["q"].device)
+    q_out = torch.full_like(d["q"], float("nan"))
+    pk.paged_decode_step_rope(d["q"], d["k_new"], d["v_new"], pos, inv, d["slot_mapping"], q_out,
+                              d["k_cache"], d["v_cache"], d["block_tables"], d["context_lens"],
+                              d["scale"], out, interleaved=interleaved,
+                              partition_tokens=partition, kernel=kernel)
+    return q_out, out
+
+
+def run_rope_separate(d, pos, inv, interleaved, kernel="auto", partition=0):
+    """The same step as two calls: the standalone rotation + write, then attention with the
+    rotated q. Modifies d's pools."""
+    q_rot = pk.paged_kv_write_rope(d["q"], d["k_new"], d["v_new"], pos, inv, d["slot_mapping"],
+                                   d["k_cache"], d["v_cache"], interleaved=interleaved)
+    return q_rot, run_attention(dict(d, q=q_rot), kernel, partition)
+
+
+@pytest.mark.parametrize("interleaved", [False, True])
+@pytest.mark.parametrize("name", SMALL)
+def test_decode_step_rope_fused_matches_separate_calls_and_oracle(dev, name, interleaved):
+    """One launch rotates q and the new key at position L-1, stores the rotated key and the
+    value, and attends: q_out, the pools and the output equal the two separate calls bit for
+    bit (every kernel family and split), and the output is within the bound of the oracle's
+    rotation + write + attention."""
+    w = wl.WORKLOADS[name]
+    inp = wl.make_inputs(w, poison=True)
+    host = wl.to_host_numpy(inp)
+    pos_np = (host["context_lens"] - 1).astype(np.int32)
+    inv_np = llama_inv_freq(w.head_dim)
+    q_ref, kc_ref, vc_ref = oracle.kv_write_rope(host["q"], host["k_new"], host["v_new"], pos_np,
+                                                 inv_np, interleaved, host["slot_mapping"],
+                                                 host["k_cache"], host["v_cache"])
+    ref = oracle.decode_attention(q_ref, kc_ref, vc_ref, host["block_tables"],
+                                  host["context_lens"], host["scale"])
+    pos = torch.from_numpy(pos_np).to(dev)
+    inv = torch.from_numpy(inv_np).to(dev)
+    fused = to_dev(inp, dev)
+    sep = to_dev(inp, dev)
+    for kernel in ["auto"] + kernels_for(w):
+        for partition in (-1, 0, 256):
+            q_f, out_f = run_step_rope(fused, pos, inv, interleaved, kernel, partition)
+            q_s, out_s = run_rope_separate(sep, pos, inv, interleaved, kernel, partition)
+            torch.cuda.synchronize()
+            key = (kernel, partition)
+            assert torch.equal(q_f.view(torch.int16), q_s.view(torch.int16)), key
+            assert torch.equal(fused["k_cache"].view(torch.int16),
+                               sep["k_cache"].view(torch.int16)), key
+            assert torch.equal(fused["v_cache"].view(torch.int16),
+                               sep["v_cache"].view(torch.int16)), key
+            assert torch.equal(out_f, out_s), key
+            err = np.abs(out_f.cpu().double().numpy() - ref).max()
+            record(f"{name}/step_rope/il{int(interleaved)}/{kernel}/p{partition}", err)
+            assert np.isfinite(err) and err <= ATOL, (key, err)
+    assert bf16_ulp_diff(wl.to_bits(q_f), q_ref).max() <= 1.0
+    kc = wl.to_bits(fused["k_cache"])
+    same = kc == kc_ref  # the poisoned (NaN) slots nobody writes compare by their bits
+    zero = np.uint16(0)
+    diff = bf16_ulp_diff(np.where(same, zero, kc), np.where(same, zero, kc_ref))
+    assert (same | (diff <= 1.0)).all()
+    assert np.array_equal(wl.to_bits(fused["v_cache"]), vc_ref)
+
+
+def test_decode_step_rope_large_positions_negative_slots_and_full_size(dev):
+    """Positions far beyond the context (the sine and cosine of large angles), sequences with
+    no slot (nothing stored, their last position read from the cache), and c5b at full size:
+    the fused step equals the separate calls bit for bit."""
+    w = wl.WORKLOADS["c3"]
+    inp = wl.make_inputs(w, poison=True)
+    inp["slot_mapping"][[0, 5, 11]] = -1
+    pos = torch.tensor([0, 1, 2, 1000, 8191, 32767, 131071, 65535, 7, 9, 300, 4095, 12, 77,
+                        500000, 3], dtype=torch.int32, device=dev)
+    for interleaved in (False, True):
+        inv = torch.from_numpy(llama_inv_freq(w.head_dim, 10000.0)).to(dev)
+        fused, sep = to_dev(inp, dev), to_dev(inp, dev)
+        for kernel in ["auto"] + kernels_for(w):
+            q_f, out_f = run_step_rope(fused, pos, inv, interleaved, kernel, 0)
+            q_s, out_s = run_rope_separate(sep, pos, inv, interleaved, kernel, 0)
+            torch.cuda.synchronize()
+            assert torch.equal(q_f.view(torch.int16), q_s.view(torch.int16)), kernel
+            assert torch.equal(fused["k_cache"].view(torch.int16),
+                               sep["k_cache"].view(torch.int16)), kernel
+            assert torch.equal(out_f, out_s), kernel
+    w = wl.WORKLOADS["c5b"]
+    a = wl.make_inputs(w, device="cuda")
+    b = {k: (v.clone() if isinstance(v, torch.Tensor) else v) for k, v in a.items()}
+    pos = (a["context_lens"] - 1).to(torch.int32)
+    inv = torch.from_numpy(llama_inv_freq(w.head_dim)).to(dev)
+    q_f, out_f = run_step_rope(a, pos, inv, False)
+    q_s, out_s = run_rope_separate(b, pos, inv, False)
+    torch.cuda.synchronize()
+    assert torch.equal(q_f.view(torch.int16), q_s.view(torch.int16))
+    assert torch.equal(out_f, out_s)
+    assert torch.equal(a["k_cache"], b["k_cache"]) and torch.equal(a["v_cache"], b["v_cache"])
