@@ -9,102 +9,175 @@
 // that motivates the split lists a split-K kernel as out of its scope ("vLLM-Style Llama
 // Inference Engine with Tensor Parallelism", Out of scope); this is the merge it would need.
 //
-// One workgroup of 256 threads per (sequence, query head). The partition statistics are
-// reduced across the whole workgroup; the weighted sum of the partial outputs splits the
-// partitions over 256/D thread groups (thread = (column d, group)), whose loads of a_p are
-// coalesced along d and independent across p. The partials are fp32 whatever the formats;
-// the result is stored in the output format.
+// Many partitions: one workgroup of 512 threads per (sequence, query head), one barrier. Every memory read is
+// issued before any of them is needed, and none waits for another: the merge does not read the
+// context length, because a partition past the context marks its rows with m = -inf (no keys)
+// and its partial outputs are then never used. Each thread folds what it read with the rule
+// above, keeping its own reference max, so nothing waits for the global M either:
+//   (m1, x1) + (m2, x2) = (m, 2^(m1 - m) x1 + 2^(m2 - m) x2),  m = max(m1, m2).
+// Statistics: thread t folds (m_p, l_p) of partitions t, t + 512, ...; the waves combine them
+// by shuffles, the workgroup through LDS. Outputs: thread (column d, group g) folds (m_p,
+// a_p[d]) of partitions g, g + 512/D, ... (loads coalesced along d, independent across p);
+// the groups combine through LDS. The partials are fp32 whatever the formats; the result is
+// stored in the output format.
 #include "device_common.h"
 #include "launch.h"
 
 namespace pagedkv {
 
-constexpr int kReduceThreads = 256;
+constexpr int kReduceThreads = 512;
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int x = 1; x < 64; x <<= 1) v = fmaxf(v, shfl_xor(v, x));
-  return v;
-}
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int x = 1; x < 64; x <<= 1) v += shfl_xor(v, x);
-  return v;
+// (m, x) += (m2, x2) under the rule above. m == -inf means no keys (x is then 0, and an x2
+// that comes with m2 == -inf is not read: it may be stale workspace).
+__device__ __forceinline__ void fold(float& m, float& x, float m2, float x2) {
+  const float mn = fmaxf(m, m2);
+  const float ref = mn == kNegInf ? 0.f : mn;
+  const float y2 = m2 == kNegInf ? 0.f : x2;
+  x = fmaf(x, fast_exp2(m - ref), y2 * fast_exp2(m2 - ref));
+  m = mn;
 }
 
-template <int OT>
+// PER: partitions per column group read in the first pass (a power of two, at most 16; the
+// launch picks the smallest that covers nparts when it can). Used for more than 8 partitions.
+template <int OT, int PER>
 __global__ void __launch_bounds__(kReduceThreads)
 decode_reduce_kernel(const DecodeArgs a) {
   constexpr int NWV = kReduceThreads / 64;
-  __shared__ float red[NWV];
-  __shared__ float part[kReduceThreads];
+  __shared__ float red_m[NWV], red_l[NWV];
+  __shared__ float part_m[kReduceThreads], part_x[kReduceThreads];
 
   const int row = blockIdx.x;  // b * Hq + h
-  const int b = row / a.num_q_heads;
   const int D = a.head_dim;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  int L = a.context_lens[b];
-  const int Lmax = a.max_blocks * a.block_size;
-  L = L < 0 ? 0 : (L > Lmax ? Lmax : L);
-  const size_t o = (size_t)row * D;
-  if (L == 0) {
-    for (int d = tid; d < D; d += kReduceThreads) store_out<OT>(a.out, o + d, 0.f);
-    return;
-  }
-  const int np = (L + a.part_tokens - 1) / a.part_tokens;  // partitions holding keys
-  const float* ml = a.ws_ml + (size_t)row * a.nparts * 2;
-  const float* acc = a.ws_acc + (size_t)row * a.nparts * D;
+  const int nparts = a.nparts;
+  const float* ml = a.ws_ml + (size_t)row * nparts * 2;
+  const float* acc = a.ws_acc + (size_t)row * nparts * D;
 
-  // M = max_p m_p over the workgroup.
-  float M = kNegInf;
-  for (int p = tid; p < np; p += kReduceThreads) M = fmaxf(M, ml[2 * p]);
-  M = wave_max(M);
-  if (lane == 0) red[wave] = M;
-  __syncthreads();
-  M = red[0];
-#pragma unroll
-  for (int w = 1; w < NWV; ++w) M = fmaxf(M, red[w]);
-  __syncthreads();
-
-  // den = sum_p 2^(m_p - M) l_p.
-  float den = 0.f;
-  if (M != kNegInf)
-    for (int p = tid; p < np; p += kReduceThreads)
-      den = fmaf(fast_exp2(ml[2 * p] - M), ml[2 * p + 1], den);
-  den = wave_sum(den);
-  if (lane == 0) red[wave] = den;
-  __syncthreads();
-  den = 0.f;
-#pragma unroll
-  for (int w = 0; w < NWV; ++w) den += red[w];
-
-  // num[d] = sum_p 2^(m_p - M) a_p[d], partitions split over `groups` thread groups.
-  const int groups = kReduceThreads / D;  // D in {64, 128}: 4 or 2
+  const int groups = kReduceThreads / D;  // D in {64, 128}: 8 or 4
   const int d = tid % D, grp = tid / D;
-  float num = 0.f;
-  if (M != kNegInf) {
-#pragma unroll 4
-    for (int p = grp; p < np; p += groups)
-      num = fmaf(fast_exp2(ml[2 * p] - M), acc[(size_t)p * D + d], num);
+
+  // First pass, all loads issued together: the statistics of partition tid and (m_p, a_p[d])
+  // of partitions grp + u * groups, u < PER. Indices past the end are clamped so that every
+  // load is unconditional; their values are masked afterwards.
+  const int last = nparts - 1;
+  const int ps = tid < nparts ? tid : last;
+  const float m_s = ml[2 * ps], l_s = ml[2 * ps + 1];
+  float mp[PER], ap[PER];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int p = grp + u * groups;
+    const int pc = p < nparts ? p : last;
+    mp[u] = ml[2 * pc];
+    ap[u] = acc[(size_t)pc * D + d];
   }
-  part[tid] = num;
+  __builtin_amdgcn_sched_barrier(0);  // keep the loads above ahead of every use
+  float m = tid < nparts ? m_s : kNegInf, l = tid < nparts ? l_s : 0.f;
+  float mx = kNegInf, x = 0.f;
+#pragma unroll
+  for (int u = 0; u < PER; ++u)
+    fold(mx, x, grp + u * groups < nparts ? mp[u] : kNegInf, ap[u]);
+  // The rest, for more than 512 partitions or more than PER per column group.
+  for (int p = tid + kReduceThreads; p < nparts; p += kReduceThreads)
+    fold(m, l, ml[2 * p], ml[2 * p + 1]);
+  for (int p = grp + PER * groups; p < nparts; p += groups)
+    fold(mx, x, ml[2 * p], acc[(size_t)p * D + d]);
+
+#pragma unroll
+  for (int s = 1; s < 64; s <<= 1) {
+    const float m2 = shfl_xor(m, s), l2 = shfl_xor(l, s);
+    fold(m, l, m2, l2);
+  }
+  if (lane == 0) {
+    red_m[wave] = m;
+    red_l[wave] = l;
+  }
+  part_m[tid] = mx;
+  part_x[tid] = x;
   __syncthreads();
-  if (grp == 0) {
-    for (int q = 1; q < groups; ++q) num += part[q * D + d];
-    store_out<OT>(a.out, o + d, den > 0.f ? num / den : 0.f);
+  if (grp != 0) return;
+  float M = red_m[0], den = red_l[0];
+#pragma unroll
+  for (int w = 1; w < NWV; ++w) fold(M, den, red_m[w], red_l[w]);
+  float mo = part_m[d], num = part_x[d];
+  for (int q = 1; q < groups; ++q) fold(mo, num, part_m[q * D + d], part_x[q * D + d]);
+  // num and den end on the same reference: mo and M are maxima of the same set of m_p.
+  store_out<OT>(a.out, (size_t)row * D + d, den > 0.f ? num / den : 0.f);
+}
+
+// Few partitions (nparts <= NP <= 8): one thread per output element reads the statistics and
+// its column of every partition at once and folds them in partition order; no LDS, no barrier.
+// The statistics are the same few addresses for the D threads of a row.
+constexpr int kNarrowThreads = 256;
+
+template <int OT, int NP>
+__global__ void __launch_bounds__(kNarrowThreads)
+decode_reduce_narrow_kernel(const DecodeArgs a) {
+  const int D = a.head_dim;  // 64 or 128: a workgroup covers kNarrowThreads / D whole rows
+  const size_t row = (size_t)blockIdx.x * (kNarrowThreads / D) + threadIdx.x / D;
+  const int d = threadIdx.x % D;
+  if (row >= (size_t)a.batch * a.num_q_heads) return;
+  const size_t e = row * D + d;
+  const int nparts = a.nparts, last = nparts - 1;
+  const float* ml = a.ws_ml + row * nparts * 2;
+  const float* acc = a.ws_acc + row * nparts * D;
+  float mp[NP], lp[NP], ap[NP];
+#pragma unroll
+  for (int u = 0; u < NP; ++u) {
+    const int pc = u < nparts ? u : last;
+    mp[u] = ml[2 * pc];
+    lp[u] = ml[2 * pc + 1];
+    ap[u] = acc[(size_t)pc * D + d];
   }
+  __builtin_amdgcn_sched_barrier(0);  // keep the loads above ahead of every use
+  float m = kNegInf, l = 0.f, mo = kNegInf, x = 0.f;
+#pragma unroll
+  for (int u = 0; u < NP; ++u) {
+    const float mu = u < nparts ? mp[u] : kNegInf;
+    fold(m, l, mu, lp[u]);
+    fold(mo, x, mu, ap[u]);
+  }
+  store_out<OT>(a.out, e, l > 0.f ? x / l : 0.f);
+}
+
+template <int OT>
+hipError_t launch_reduce_per(const DecodeArgs& a, unsigned rows, hipStream_t stream) {
+  if (a.nparts <= 8) {
+    const unsigned grid =
+        (unsigned)(((size_t)rows * a.head_dim + kNarrowThreads - 1) / kNarrowThreads);
+    const dim3 block(kNarrowThreads);
+    if (a.nparts <= 2)
+      hipLaunchKernelGGL((decode_reduce_narrow_kernel<OT, 2>), dim3(grid), block, 0, stream, a);
+    else if (a.nparts <= 4)
+      hipLaunchKernelGGL((decode_reduce_narrow_kernel<OT, 4>), dim3(grid), block, 0, stream, a);
+    else
+      hipLaunchKernelGGL((decode_reduce_narrow_kernel<OT, 8>), dim3(grid), block, 0, stream, a);
+    return hipGetLastError();
+  }
+  const int groups = kReduceThreads / a.head_dim;
+  const int need = (a.nparts + groups - 1) / groups;
+  const dim3 grid(rows), block(kReduceThreads);
+  if (need <= 1)
+    hipLaunchKernelGGL((decode_reduce_kernel<OT, 1>), grid, block, 0, stream, a);
+  else if (need <= 2)
+    hipLaunchKernelGGL((decode_reduce_kernel<OT, 2>), grid, block, 0, stream, a);
+  else if (need <= 4)
+    hipLaunchKernelGGL((decode_reduce_kernel<OT, 4>), grid, block, 0, stream, a);
+  else if (need <= 8)
+    hipLaunchKernelGGL((decode_reduce_kernel<OT, 8>), grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL((decode_reduce_kernel<OT, 16>), grid, block, 0, stream, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_decode_reduce(const DecodeArgs& a, hipStream_t stream) {
   const unsigned rows = (unsigned)((long long)a.batch * a.num_q_heads);
   switch (a.out_dtype) {
-    case kDtF32: hipLaunchKernelGGL(decode_reduce_kernel<kDtF32>, dim3(rows), dim3(kReduceThreads), 0, stream, a); break;
-    case kDtBf16: hipLaunchKernelGGL(decode_reduce_kernel<kDtBf16>, dim3(rows), dim3(kReduceThreads), 0, stream, a); break;
-    case kDtF16: hipLaunchKernelGGL(decode_reduce_kernel<kDtF16>, dim3(rows), dim3(kReduceThreads), 0, stream, a); break;
+    case kDtF32: return launch_reduce_per<kDtF32>(a, rows, stream);
+    case kDtBf16: return launch_reduce_per<kDtBf16>(a, rows, stream);
+    case kDtF16: return launch_reduce_per<kDtF16>(a, rows, stream);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 }  // namespace pagedkv

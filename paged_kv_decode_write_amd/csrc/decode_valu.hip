@@ -52,7 +52,10 @@ decode_valu_kernel(const DecodeArgs a) {
   const int Lmax = a.max_blocks * BS;
   L = L < 0 ? 0 : (L > Lmax ? Lmax : L);
   const int tok0 = part * a.part_tokens;
-  if (tok0 >= L && !(L == 0 && part == 0)) return;  // partition past the end: nothing to do
+  if (tok0 >= L && !(L == 0 && part == 0)) {  // partition past the end: nothing to do
+    if (wave == 0) mark_empty_partition(a, b, g, part, lane);
+    return;
+  }
   const int tok1 = min(tok0 + a.part_tokens, L);
   const int blk0 = tok0 / BS;
   const int blk1 = (tok1 + BS - 1) / BS;

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "launch.h"
+
 namespace pagedkv {
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -137,6 +139,18 @@ __device__ __forceinline__ float row4_sum(float v) {
   const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
                                                   false);
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// A partition that starts past its sequence's context (only in a split launch: partition 0
+// never exits early) marks its G query rows as holding no keys, max -inf and sum 0, which is
+// all the merge reads of it. Thread i < G of the exiting unit marks row i of KV head g.
+__device__ __forceinline__ void mark_empty_partition(const DecodeArgs& a, int b, int g,
+                                                     int part, int i) {
+  const int G = a.num_q_heads / a.num_kv_heads;
+  if (i >= G) return;
+  const size_t pr = ((size_t)b * a.num_q_heads + (size_t)g * G + i) * a.nparts + part;
+  a.ws_ml[pr * 2 + 0] = kNegInf;
+  a.ws_ml[pr * 2 + 1] = 0.f;
 }
 
 }  // namespace pagedkv
