@@ -232,24 +232,44 @@ def test_attention_full_size_sampled(dev, name):
 EDGE_LENGTHS = [1, 15, 16, 17, 256, 257, 4095, 4096, 0, 33]
 
 
-@pytest.mark.parametrize("D,Hq,Hkv", [(128, 32, 8), (64, 24, 8), (128, 8, 8), (64, 16, 2)])
+@pytest.mark.parametrize("D,Hq,Hkv", [(128, 32, 8), (64, 24, 8), (128, 8, 8), (64, 16, 2),
+                                      (128, 32, 2), (64, 48, 8), (128, 16, 8)])
 def test_attention_edge_lengths(dev, D, Hq, Hkv):
+    """Lengths at block and pair boundaries, an empty context and a long one, for group sizes
+    1 to 16 (16 fills the matrix-core tile): the separate write + attention against the
+    oracle, and the fused decode step and the fused RoPE step bit-identical to their separate
+    calls (the new row lands at every position of a pair)."""
     w = wl.Workload("edge", batch=len(EDGE_LENGTHS), num_q_heads=Hq, num_kv_heads=Hkv,
                     head_dim=D, block_size=16, num_blocks=1200, max_blocks=260, seed=4242,
                     q_std=3.0)
     inp = wl.make_inputs(w, poison=True, lengths=EDGE_LENGTHS)
     host = wl.to_host_numpy(inp)
     ref, _, _ = oracle.decode_step(host)
+    pos = (inp["context_lens"].clamp(min=1) - 1).to(dev, torch.int32)
+    inv = torch.from_numpy(llama_inv_freq(D)).to(dev)
     for kernel in kernels_for(w):
         for partition in (0, -1, 16, 256, 272):
             d = to_dev(inp, dev)
             run_write(d)
-            out = run_attention(d, kernel, partition).cpu().double().numpy()
+            out_t = run_attention(d, kernel, partition)
+            out = out_t.cpu().double().numpy()
             err = np.abs(out - ref).max()
             record(f"edge/D{D}/G{Hq // Hkv}/{kernel}/p{partition}", err)
             assert np.isfinite(out).all()
             assert err <= ATOL, (kernel, partition, err)
             assert not out[EDGE_LENGTHS.index(0)].any()  # empty context -> zeros
+            fused = to_dev(inp, dev)
+            step_out = run_step(fused, kernel, partition)
+            assert torch.equal(step_out, out_t), ("step", kernel, partition)
+            for pool in ("k_cache", "v_cache"):
+                assert torch.equal(fused[pool].view(torch.int16), d[pool].view(torch.int16))
+            fr, sr = to_dev(inp, dev), to_dev(inp, dev)
+            q_f, o_f = run_step_rope(fr, pos, inv, False, kernel, partition)
+            q_s, o_s = run_rope_separate(sr, pos, inv, False, kernel, partition)
+            assert torch.equal(q_f.view(torch.int16), q_s.view(torch.int16)), ("rope", kernel)
+            assert torch.equal(o_f, o_s), ("rope", kernel, partition)
+            for pool in ("k_cache", "v_cache"):
+                assert torch.equal(fr[pool].view(torch.int16), sr[pool].view(torch.int16))
 
 
 def test_length_one_returns_value_row_exactly(dev):
