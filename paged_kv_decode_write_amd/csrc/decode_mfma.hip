@@ -290,7 +290,9 @@ decode_mfma_hw_kernel(const DecodeArgs a) {
   // Loads that do not depend on the context length are issued before it arrives: q, the first
   // pair's block ids (every entry of the table row is in bounds to read; entries past the
   // context are ignored below) and, below, that pair's K / V. The wave's start then costs the
-  // ids' round trip and the K / V round trip, with the length arriving alongside.
+  // ids' round trip and the K / V round trip, with the length arriving alongside. The length
+  // is read after the pair is issued: a wait for any scalar load waits for all of them, so an
+  // earlier read would hold the pair back.
   const int32_t* table = a.block_tables + (size_t)b * a.max_blocks;
   const int tok0 = part * a.part_tokens;
   const int blk0 = tok0 / BS;
@@ -333,7 +335,12 @@ decode_mfma_hw_kernel(const DecodeArgs a) {
   const int Lmax = a.max_blocks * BS;
   L = L < 0 ? 0 : (L > Lmax ? Lmax : L);
   if (tok0 >= L && !(L == 0 && part == 0)) {
-    mark_empty_partition(a, b, g, part, lane);
+    // The speculative loads count as used here too, so the compiler keeps them ahead of this
+    // branch (and of the wait for the length) instead of sinking them into the main path.
+    float neg_inf = kNegInf;
+    keep_issued(t[0], neg_inf);
+    keep_issued(nrow, neg_inf);
+    mark_empty_partition(a, b, g, part, lane, neg_inf);
     return;
   }
   const int tok1 = min(tok0 + a.part_tokens, L);
@@ -436,15 +443,17 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream) {
   const unsigned units = (unsigned)((long long)a.batch * a.num_kv_heads * a.nparts);
   return with_formats(a.kv_dtype, a.out_dtype, [&](auto kt, auto ot) {
     constexpr int KT = decltype(kt)::value, OT = decltype(ot)::value;
+    constexpr bool kRope = KT == kDtBf16;  // bf16 inputs only, as in the head-per-wave launch
     const bool rope = a.positions != nullptr;
+    if (rope && !kRope) return hipErrorInvalidValue;
     if (a.head_dim == 128 && rope)
-      hipLaunchKernelGGL((decode_mfma_kernel<128, NW, KT, OT, true>), dim3(units), dim3(NW * 64),
+      hipLaunchKernelGGL((decode_mfma_kernel<128, NW, KT, OT, kRope>), dim3(units), dim3(NW * 64),
                          0, stream, a);
     else if (a.head_dim == 128)
       hipLaunchKernelGGL((decode_mfma_kernel<128, NW, KT, OT, false>), dim3(units),
                          dim3(NW * 64), 0, stream, a);
     else if (a.head_dim == 64 && rope)
-      hipLaunchKernelGGL((decode_mfma_kernel<64, NW, KT, OT, true>), dim3(units), dim3(NW * 64),
+      hipLaunchKernelGGL((decode_mfma_kernel<64, NW, KT, OT, kRope>), dim3(units), dim3(NW * 64),
                          0, stream, a);
     else if (a.head_dim == 64)
       hipLaunchKernelGGL((decode_mfma_kernel<64, NW, KT, OT, false>), dim3(units), dim3(NW * 64),
@@ -464,15 +473,18 @@ hipError_t launch_decode_mfma_hw(const DecodeArgs& a, hipStream_t stream) {
   const unsigned units = (unsigned)((long long)a.batch * ngrp * a.nparts);
   return with_formats(a.kv_dtype, a.out_dtype, [&](auto kt, auto ot) {
     constexpr int KT = decltype(kt)::value, OT = decltype(ot)::value;
+    // The rotary step takes bf16 inputs only (the host layer checks): no fp16 instance.
+    constexpr bool kRope = KT == kDtBf16;
     const bool rope = a.positions != nullptr;
+    if (rope && !kRope) return hipErrorInvalidValue;
     if (a.head_dim == 128 && rope)
-      hipLaunchKernelGGL((decode_mfma_hw_kernel<128, HPW, NBUF, 2, KT, OT, true>), dim3(units),
+      hipLaunchKernelGGL((decode_mfma_hw_kernel<128, HPW, NBUF, 2, KT, OT, kRope>), dim3(units),
                          dim3(HPW * 64), 0, stream, a);
     else if (a.head_dim == 128)
       hipLaunchKernelGGL((decode_mfma_hw_kernel<128, HPW, NBUF, 2, KT, OT, false>), dim3(units),
                          dim3(HPW * 64), 0, stream, a);
     else if (a.head_dim == 64 && rope)
-      hipLaunchKernelGGL((decode_mfma_hw_kernel<64, HPW, NBUF, 2, KT, OT, true>), dim3(units),
+      hipLaunchKernelGGL((decode_mfma_hw_kernel<64, HPW, NBUF, 2, KT, OT, kRope>), dim3(units),
                          dim3(HPW * 64), 0, stream, a);
     else if (a.head_dim == 64)
       hipLaunchKernelGGL((decode_mfma_hw_kernel<64, HPW, NBUF, 2, KT, OT, false>), dim3(units),

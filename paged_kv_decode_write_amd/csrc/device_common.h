@@ -144,12 +144,14 @@ __device__ __forceinline__ float row4_sum(float v) {
 // A partition that starts past its sequence's context (only in a split launch: partition 0
 // never exits early) marks its G query rows as holding no keys, max -inf and sum 0, which is
 // all the merge reads of it. Thread i < G of the exiting unit marks row i of KV head g.
+// neg_inf is -inf (a kernel may pass it through an empty asm first, see keep_issued).
 __device__ __forceinline__ void mark_empty_partition(const DecodeArgs& a, int b, int g,
-                                                     int part, int i) {
+                                                     int part, int i,
+                                                     float neg_inf = kNegInf) {
   const int G = a.num_q_heads / a.num_kv_heads;
   if (i >= G) return;
   const size_t pr = ((size_t)b * a.num_q_heads + (size_t)g * G + i) * a.nparts + part;
-  a.ws_ml[pr * 2 + 0] = kNegInf;
+  a.ws_ml[pr * 2 + 0] = neg_inf;
   a.ws_ml[pr * 2 + 1] = 0.f;
 }
 

@@ -129,12 +129,39 @@ template <int NCH, int EPL> struct PairTile {
   int tA;            // position of the first row of the pair
 };
 
+// Marks the loads of a tile as used by `tie`, a value the caller then stores. A kernel that
+// issues loads before a branch that may exit passes the value it stores on the exit path: a
+// load whose value is used on both sides of the branch cannot be moved below it, so it stays
+// ahead of the wait the branch needs, and only the exit path waits for it. The asm is empty
+// (tie keeps its value) and not volatile, so the compiler sees no memory access in it; one
+// word of each load is enough, since a load is a single instruction.
+__device__ __forceinline__ void keep_issued(uint32_t w, float& tie) {
+  asm("" : "+v"(tie) : "v"(w));
+}
+template <int NCH, int EPL>
+__device__ __forceinline__ void keep_issued(const PairTile<NCH, EPL>& t, float& tie) {
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    keep_issued(t.ka[c].x, tie);
+    keep_issued(t.kb[c].x, tie);
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) keep_issued(t.vr[j].word(0), tie);
+}
+
 // Fused decode step: one lane's pieces of the step's new K and V rows of its head (K columns
 // 32ch + 8kg .. +7, V columns EPL*n16 .. +EPL-1), loaded once before the key loop.
 template <int NCH, int EPL> struct NewRow {
   uint4 k[NCH];
   VRow<EPL> v;
 };
+
+template <int NCH, int EPL>
+__device__ __forceinline__ void keep_issued(const NewRow<NCH, EPL>& r, float& tie) {
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) keep_issued(r.k[c].x, tie);
+  keep_issued(r.v.word(0), tie);
+}
 
 template <int NCH, int EPL>
 __device__ __forceinline__ void load_new_row(NewRow<NCH, EPL>& r, const uint16_t* k_row,
