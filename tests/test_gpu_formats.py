@@ -225,3 +225,35 @@ def test_binding_rejects_mixed_formats(dev):
         pk.paged_decode_attention(d["q"].to(torch.bfloat16), d["k_cache"], d["v_cache"],
                                   d["block_tables"], d["context_lens"], d["scale"],
                                   out.float())
+
+
+@pytest.mark.parametrize("kvt,ot", PAIRS)
+@pytest.mark.parametrize("name", ["c2", "c4"])
+def test_decode_step_formats_match_separate_calls(dev, name, kvt, ot):
+    """The fused decode step (write + attention in one launch) with fp16 inputs or a 16-bit
+    output equals the separate write and attention calls bit for bit, pools included, for
+    every kernel family and split."""
+    w = wl.WORKLOADS[name]
+    inp = wl.make_inputs(w, dtype=kvt, poison=True)
+    for kernel in ("auto", "valu", "mfma", "mfma_hw"):
+        if kernel == "valu" and w.gqa not in (1, 2, 3, 4, 8):
+            continue
+        for part in (-1, 0, 256):
+            fused, sep = to_dev(inp, dev), to_dev(inp, dev)
+            out_f = torch.full((w.batch, w.num_q_heads, w.head_dim), float("nan"),
+                               dtype=TORCH[ot], device=dev)
+            pk.paged_decode_step(fused["q"], fused["k_new"], fused["v_new"],
+                                 fused["slot_mapping"], fused["k_cache"], fused["v_cache"],
+                                 fused["block_tables"], fused["context_lens"], fused["scale"],
+                                 out_f, partition_tokens=part, kernel=kernel)
+            pk.paged_kv_write(sep["k_new"], sep["v_new"], sep["slot_mapping"], sep["k_cache"],
+                              sep["v_cache"])
+            out_s = run_decode(sep, ot, kernel, part)
+            torch.cuda.synchronize()
+            key = (name, kvt, ot, kernel, part)
+            if ot == "f32":
+                assert torch.equal(out_f, out_s), key
+            else:
+                assert torch.equal(out_f.view(torch.int16), out_s.view(torch.int16)), key
+            for pool in ("k_cache", "v_cache"):
+                assert torch.equal(fused[pool].view(torch.int16), sep[pool].view(torch.int16))
