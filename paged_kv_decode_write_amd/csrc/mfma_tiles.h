@@ -88,11 +88,20 @@ constexpr float kRescaleSlack = 8.f;
 template <int KT> constexpr float kWeightLift = KT == kDtF16 ? 7.f : 0.f;
 
 // Weights p[0..7] (token slots of the P^T operand) as hi + lo in the input format, with
-// p = hi + lo + O(2^-16 p): bf16 hi is p truncated (exact), lo the rounded remainder; fp16
-// hi is p rounded toward zero (v_cvt_pkrtz_f16_f32), lo the remainder likewise.
+// p = hi + lo + O(2^-16 p). bf16: hi is p rounded to nearest even, two per v_cvt_pk; the
+// remainders p - hi come from v_dot2c_f32_bf16 against (-1, 0) and (0, -1), one instruction
+// each (p - hi is exact in fp32, and the other product is 0), and lo is them rounded. fp16: hi
+// is p rounded toward zero (v_cvt_pkrtz_f16_f32), lo the remainder likewise.
 template <int KT>
 __device__ __forceinline__ void split_weights(const float (&p)[8], uint4& hi, uint4& lo) {
   uint32_t hw[4], lw[4];
+  // (-1, 0) and (0, -1) as packed bf16, held in scalar registers: written as constants, the
+  // first one became the inline constant -1.0, which the instruction reads as (0, -1).
+  uint32_t neg_first = 0x0000bf80u, neg_second = 0xbf800000u;
+  if constexpr (KT == kDtBf16) {
+    asm("" : "+s"(neg_first));
+    asm("" : "+s"(neg_second));
+  }
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     if constexpr (KT == kDtF16) {
@@ -102,11 +111,14 @@ __device__ __forceinline__ void split_weights(const float (&p)[8], uint4& hi, ui
       hw[q] = __builtin_bit_cast(uint32_t, h);
       lw[q] = __builtin_bit_cast(uint32_t, l);
     } else {
-      const uint32_t u0 = __float_as_uint(p[2 * q]), u1 = __float_as_uint(p[2 * q + 1]);
-      hw[q] = __builtin_amdgcn_perm(u1, u0, 0x07060302u);
-      const floatx2 r = {p[2 * q] - __uint_as_float(u0 & 0xffff0000u),
-                         p[2 * q + 1] - __uint_as_float(u1 & 0xffff0000u)};
-      lw[q] = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2));  // one cvt_pk
+      const floatx2 v = {p[2 * q], p[2 * q + 1]};
+      const bf16x2 h = __builtin_convertvector(v, bf16x2);
+      const floatx2 r = {
+          __builtin_amdgcn_fdot2_f32_bf16(h, __builtin_bit_cast(bf16x2, neg_first), v[0], false),
+          __builtin_amdgcn_fdot2_f32_bf16(h, __builtin_bit_cast(bf16x2, neg_second), v[1],
+                                          false)};
+      hw[q] = __builtin_bit_cast(uint32_t, h);
+      lw[q] = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2));
     }
   }
   hi = make_uint4(hw[0], hw[1], hw[2], hw[3]);
@@ -410,12 +422,11 @@ __device__ __forceinline__ void softmax_step(WaveState<EPL>& st, const float (&s
   }
   const float mu = (st.m_run == kNegInf ? 0.f : st.m_run) - kWeightLift<KT>;
   float p[8];
-  float psum = 0.f;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    p[i] = fast_exp2(s[i] - mu);
-    psum += p[i];
-  }
+  for (int i = 0; i < 8; ++i) p[i] = fast_exp2(s[i] - mu);
+  float psum = p[0];  // the same bits as 0 + p[0] (weights are >= 0), one add fewer
+#pragma unroll
+  for (int i = 1; i < 8; ++i) psum += p[i];
   st.l_run += psum;
   split_weights<KT>(p, phi, plo);
 }
