@@ -409,29 +409,49 @@ def test_one_workspace_across_shapes(dev):
                     assert diff <= 1e-4, (kernel, partition, diff)
 
 
+@pytest.mark.parametrize("mode", ["separate", "fused", "rope"])
 @pytest.mark.parametrize("name,partition", [("c2", 0), ("c4", 64)])
-def test_graph_capture_replays_match_eager(dev, name, partition):
-    """The write + attention step captured in a HIP graph (no allocation, no memset inside the
-    library calls) replays to the eager result, replay after replay, with eager work and
-    synchronisations in between."""
+def test_graph_capture_replays_match_eager(dev, name, partition, mode):
+    """The decode step captured in a HIP graph (no allocation, no memset inside the library
+    calls) replays to the eager result, replay after replay, with eager work and
+    synchronisations in between: as a write call then an attention call, as the fused step,
+    and as the fused step with rotary embedding."""
     w = wl.WORKLOADS[name]
     inp = wl.make_inputs(w)
     d = to_dev(inp, dev)
     out = torch.empty(w.batch, w.num_q_heads, w.head_dim, dtype=torch.float32, device=dev)
+    q_out = torch.empty_like(d["q"])
+    pos = (d["context_lens"] - 1).to(torch.int32)
+    inv = torch.from_numpy(llama_inv_freq(w.head_dim)).to(dev)
     ws = pk.new_workspace(pk.decode_workspace_bytes(w.batch, w.num_q_heads, w.head_dim,
                                                     w.max_blocks, w.block_size, partition), dev)
 
     def step():
-        pk.paged_kv_write(d["k_new"], d["v_new"], d["slot_mapping"], d["k_cache"], d["v_cache"])
-        pk.paged_decode_attention(d["q"], d["k_cache"], d["v_cache"], d["block_tables"],
-                                  d["context_lens"], d["scale"], out,
-                                  partition_tokens=partition, workspace=ws)
+        if mode == "separate":
+            pk.paged_kv_write(d["k_new"], d["v_new"], d["slot_mapping"], d["k_cache"],
+                              d["v_cache"])
+            pk.paged_decode_attention(d["q"], d["k_cache"], d["v_cache"], d["block_tables"],
+                                      d["context_lens"], d["scale"], out,
+                                      partition_tokens=partition, workspace=ws)
+        elif mode == "fused":
+            pk.paged_decode_step(d["q"], d["k_new"], d["v_new"], d["slot_mapping"],
+                                 d["k_cache"], d["v_cache"], d["block_tables"],
+                                 d["context_lens"], d["scale"], out,
+                                 partition_tokens=partition, workspace=ws)
+        else:
+            pk.paged_decode_step_rope(d["q"], d["k_new"], d["v_new"], pos, inv,
+                                      d["slot_mapping"], q_out, d["k_cache"], d["v_cache"],
+                                      d["block_tables"], d["context_lens"], d["scale"], out,
+                                      partition_tokens=partition, workspace=ws)
 
     step()
     torch.cuda.synchronize()
-    eager = out.clone()
-    _, ref, kc_ref, vc_ref, _ = case(name, dev)
-    assert np.abs(eager.cpu().double().numpy() - ref).max() <= ATOL
+    eager, eager_q = out.clone(), q_out.clone()
+    eager_kc, eager_vc = wl.to_bits(d["k_cache"]), wl.to_bits(d["v_cache"])
+    if mode != "rope":
+        _, ref, kc_ref, vc_ref, _ = case(name, dev)
+        assert np.abs(eager.cpu().double().numpy() - ref).max() <= ATOL
+        assert np.array_equal(eager_kc, kc_ref) and np.array_equal(eager_vc, vc_ref)
 
     side = torch.cuda.Stream(device=dev)
     side.wait_stream(torch.cuda.current_stream(dev))
@@ -444,13 +464,16 @@ def test_graph_capture_replays_match_eager(dev, name, partition):
         step()
     for r in range(4):
         out.fill_(float("nan"))
+        q_out.fill_(float("nan"))
         d["k_cache"].view(torch.int16)[0, 0, 0, 0] += 0  # eager work between replays
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(out, eager), f"replay {r}"
-    assert np.array_equal(wl.to_bits(d["k_cache"]), kc_ref)
-    assert np.array_equal(wl.to_bits(d["v_cache"]), vc_ref)
+        if mode == "rope":
+            assert torch.equal(q_out.view(torch.int16), eager_q.view(torch.int16)), f"replay {r}"
+    assert np.array_equal(wl.to_bits(d["k_cache"]), eager_kc)
+    assert np.array_equal(wl.to_bits(d["v_cache"]), eager_vc)
 
 
 # ------------------------------------------------------- multi-query causal (prefill)
