@@ -783,3 +783,84 @@ def test_decode_step_rope_large_positions_negative_slots_and_full_size(dev):
     assert torch.equal(q_f.view(torch.int16), q_s.view(torch.int16))
     assert torch.equal(out_f, out_s)
     assert torch.equal(a["k_cache"], b["k_cache"]) and torch.equal(a["v_cache"], b["v_cache"])
+
+
+# ------------------------------------------------------- addressing past 4 GiB
+def _move_to_big_pool(d, first_block, nb_big, dev):
+    """Device copy of input dict d whose pools are [nb_big] blocks, with d's blocks placed
+    from block `first_block` on (the rest uninitialised) and the tables and slots shifted to
+    match."""
+    big = dict(d)
+    for pool in ("k_cache", "v_cache"):
+        src = d[pool]
+        dst = torch.empty((nb_big,) + tuple(src.shape[1:]), dtype=src.dtype, device=dev)
+        dst[first_block:first_block + src.shape[0]] = src.to(dev)
+        big[pool] = dst
+    bt = d["block_tables"].to(dev)
+    big["block_tables"] = torch.where(bt >= 0, bt + first_block, bt)
+    bs = d["k_cache"].shape[1]
+    sm = d["slot_mapping"].to(dev)
+    big["slot_mapping"] = torch.where(sm >= 0, sm + first_block * bs, sm)
+    for key in ("q", "k_new", "v_new", "context_lens", "cu_seqlens_q"):
+        if key in d:
+            big[key] = d[key].to(dev)
+    return big
+
+
+def test_pools_past_4gib_every_path(dev):
+    """Block ids whose byte offsets lie past 2^32 (blocks from 140000 on, 32 KiB each, in a
+    4.6 GiB pool pair): the write, every decode kernel family and split, the fused step, the
+    fused RoPE step and prefill give the oracle's results, so no kernel forms a block
+    address in 32 bits. The oracle runs on the compact copy of the same data."""
+    first, nb_big = 140_000, 150_000
+    w = wl.WORKLOADS["c2"]
+    inp = wl.make_inputs(w, poison=True)
+    host = wl.to_host_numpy(inp)
+    ref, kc_ref, vc_ref = oracle.decode_step(host)
+    nb = inp["k_cache"].shape[0]
+    d = _move_to_big_pool(inp, first, nb_big, dev)
+    assert (d["k_cache"].element_size() * d["k_cache"][0].numel() * first) > 2 ** 32
+    run_write(d)
+    torch.cuda.synchronize()
+    assert np.array_equal(wl.to_bits(d["k_cache"][first:first + nb]), kc_ref)
+    assert np.array_equal(wl.to_bits(d["v_cache"][first:first + nb]), vc_ref)
+    for kernel in kernels_for(w):
+        for partition in (-1, 0, 128):
+            err = np.abs(run_attention(d, kernel, partition).cpu().double().numpy() - ref).max()
+            record(f"big/{kernel}/p{partition}", err)
+            assert err <= ATOL, (kernel, partition, err)
+    f = _move_to_big_pool(inp, first, nb_big, dev)
+    out = run_step(f, "auto", 0)
+    torch.cuda.synchronize()
+    assert np.abs(out.cpu().double().numpy() - ref).max() <= ATOL
+    assert np.array_equal(wl.to_bits(f["k_cache"][first:first + nb]), kc_ref)
+    del f
+    pos = (inp["context_lens"] - 1).to(dev, torch.int32)
+    inv = torch.from_numpy(llama_inv_freq(w.head_dim)).to(dev)
+    fr = _move_to_big_pool(inp, first, nb_big, dev)
+    q_f, o_f = run_step_rope(fr, pos, inv, False)
+    small = to_dev(inp, dev)
+    q_s, o_s = run_rope_separate(small, pos, inv, False)
+    torch.cuda.synchronize()
+    assert torch.equal(q_f.view(torch.int16), q_s.view(torch.int16))
+    assert torch.equal(o_f, o_s)
+    assert torch.equal(fr["k_cache"][first:first + nb].view(torch.int16),
+                       small["k_cache"].view(torch.int16))
+    del fr, d
+    pw = wl.PREFILL_WORKLOADS["p2"]
+    pinp = wl.make_prefill_inputs(pw)
+    phost = wl.to_host_numpy(pinp)
+    kc, vc = oracle.kv_write(phost["k_new"], phost["v_new"], phost["slot_mapping"],
+                             phost["k_cache"], phost["v_cache"])
+    pref = oracle.prefill_attention(phost["q"], phost["cu_seqlens_q"], kc, vc,
+                                    phost["block_tables"], phost["context_lens"], phost["scale"])
+    p = _move_to_big_pool(pinp, first, nb_big, dev)
+    run_write(p)
+    T, Hq, D = p["q"].shape
+    pout = torch.full((T, Hq, D), float("nan"), device=dev)
+    pk.paged_prefill_attention(p["q"], p["cu_seqlens_q"], p["k_cache"], p["v_cache"],
+                               p["block_tables"], p["context_lens"], p["scale"], pout,
+                               max_q_len=p["max_q_len"])
+    err = np.abs(pout.cpu().double().numpy() - pref).max()
+    record("big/prefill", err)
+    assert err <= ATOL, err
