@@ -233,10 +233,11 @@ EDGE_LENGTHS = [1, 15, 16, 17, 256, 257, 4095, 4096, 0, 33]
 
 
 @pytest.mark.parametrize("D,Hq,Hkv", [(128, 32, 8), (64, 24, 8), (128, 8, 8), (64, 16, 2),
-                                      (128, 32, 2), (64, 48, 8), (128, 16, 8)])
+                                      (128, 32, 2), (64, 48, 8), (128, 16, 8), (128, 16, 1),
+                                      (64, 4, 1)])
 def test_attention_edge_lengths(dev, D, Hq, Hkv):
     """Lengths at block and pair boundaries, an empty context and a long one, for group sizes
-    1 to 16 (16 fills the matrix-core tile): the separate write + attention against the
+    1 to 16 (16 fills the matrix-core tile) and a single KV head: the separate write + attention against the
     oracle, and the fused decode step and the fused RoPE step bit-identical to their separate
     calls (the new row lands at every position of a pair)."""
     w = wl.Workload("edge", batch=len(EDGE_LENGTHS), num_q_heads=Hq, num_kv_heads=Hkv,
@@ -864,3 +865,29 @@ def test_pools_past_4gib_every_path(dev):
     err = np.abs(pout.cpu().double().numpy() - pref).max()
     record("big/prefill", err)
     assert err <= ATOL, err
+
+
+def test_many_short_ragged_sequences(dev):
+    """1024 sequences of 1..160 tokens (a wide continuous-batching step of short contexts),
+    every kernel family and split, against the oracle; the fused step matches the separate
+    calls bit for bit."""
+    B = 1024
+    lengths = [int(x) for x in np.random.default_rng(77).integers(1, 161, size=B)]
+    nblocks = sum((L + 15) // 16 for L in lengths)
+    w = wl.Workload("wide", batch=B, num_q_heads=32, num_kv_heads=8, head_dim=128,
+                    block_size=16, num_blocks=nblocks + 64, max_blocks=10, seed=606,
+                    context_len=1)
+    inp = wl.make_inputs(w, poison=True, lengths=lengths)
+    host = wl.to_host_numpy(inp)
+    ref, kc_ref, _ = oracle.decode_step(host)
+    for kernel in kernels_for(w):
+        for partition in (0, -1, 64):
+            d = to_dev(inp, dev)
+            run_write(d)
+            out = run_attention(d, kernel, partition)
+            err = np.abs(out.cpu().double().numpy() - ref).max()
+            record(f"wide/{kernel}/p{partition}", err)
+            assert err <= ATOL, (kernel, partition, err)
+            f = to_dev(inp, dev)
+            assert torch.equal(run_step(f, kernel, partition), out), (kernel, partition)
+            assert np.array_equal(wl.to_bits(f["k_cache"]), kc_ref)
