@@ -20,6 +20,7 @@ from __future__ import annotations
 import argparse
 import ctypes
 import hashlib
+import re
 import json
 import os
 import sys
@@ -112,12 +113,18 @@ class HipEvents:
 
 
 def kernel_source_hash(kernel: str) -> str:
+    """Hash of the code (comments and blank lines removed) of the sources a decode kernel
+    family is built from: a recorded traffic figure stays valid across comment edits only."""
     csrc = os.path.join(HERE, "paged_kv_decode_write_amd", "csrc")
     files = ["device_common.h", "launch.h", "mfma_tiles.h", "decode_%s.hip" % kernel.split("_")[0]]
     h = hashlib.sha256()
     for f in files:
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(csrc, f), encoding="utf-8") as fh:
+            text = re.sub(r"/\*.*?\*/", "", fh.read(), flags=re.S)
+        for line in text.splitlines():
+            code = line.split("//", 1)[0].rstrip()
+            if code.strip():
+                h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 

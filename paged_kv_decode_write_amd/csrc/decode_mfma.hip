@@ -28,10 +28,10 @@
 //                        row 4kg+j-4). P^T is then built in place with no data movement;
 //                        V^T needs 8 token rows per lane, loaded as EPL contiguous bf16 per
 //                        row and transposed in registers with v_perm_b32.
-//   P is split as p = hi + lo with both parts in the input format (bf16: hi = p truncated,
-//   exact, lo = bf16(p - hi); fp16: both rounded toward zero, weights lifted by 2^7 to stay
-//   clear of fp16's small range), two MFMAs per tile, so the weights keep ~16 bits of
-//   precision.
+//   P is split as p = hi + lo with both parts in the input format (bf16: hi = p rounded to
+//   nearest even, lo = bf16(p - hi), the exact remainder taken with one v_dot2c_f32_bf16;
+//   fp16: both rounded toward zero, weights lifted by 2^7 to stay clear of fp16's small
+//   range), two MFMAs per tile, so the weights keep ~16 bits of precision.
 // The running max is shared by the four lanes of a head (two cross-lane maxima per step);
 // the running sum stays per lane and is reduced once at the end. Waves are merged through
 // LDS with the log-sum-exp rule and the result is written out, or left as a partition
@@ -466,8 +466,9 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream) {
 
 hipError_t launch_decode_mfma_hw(const DecodeArgs& a, hipStream_t stream) {
   constexpr int HPW = kHeadsPerGroup;
-  // Two block pairs in flight per wave: measured as fast as four (which needs occupancy 1)
-  // on every workload, and it keeps two waves per SIMD.
+  // Two block pairs in flight per wave. Three or four (which need occupancy 1) measured
+  // slower on the cold 2 x 32768 case (52-53 us against 49), and no faster elsewhere; two
+  // keep two waves per SIMD.
   constexpr int NBUF = 2;
   const long long ngrp = (a.num_kv_heads + HPW - 1) / HPW;
   const unsigned units = (unsigned)((long long)a.batch * ngrp * a.nparts);
