@@ -891,3 +891,30 @@ def test_many_short_ragged_sequences(dev):
             f = to_dev(inp, dev)
             assert torch.equal(run_step(f, kernel, partition), out), (kernel, partition)
             assert np.array_equal(wl.to_bits(f["k_cache"]), kc_ref)
+
+
+def test_concurrent_calls_on_two_streams(dev):
+    """Two split decode calls of different workloads run at the same time on two streams, each
+    with the workspace the binding keeps for its stream: both equal their results computed
+    alone (the library holds no state a call could share with another)."""
+    names = ("c3", "c4")
+    alone = {}
+    data = {}
+    for name in names:
+        d = case(name, dev)[4]
+        data[name] = d
+        alone[name] = run_attention(d, "auto", 256)
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(device=dev) for _ in names]
+    outs = {}
+    for rep in range(3):
+        for s in streams:
+            s.wait_stream(torch.cuda.current_stream(dev))
+        for name, s in zip(names, streams):
+            with torch.cuda.stream(s):
+                outs[name] = run_attention(data[name], "auto", 256)
+        for s in streams:
+            torch.cuda.current_stream(dev).wait_stream(s)
+        torch.cuda.synchronize()
+        for name in names:
+            assert torch.equal(outs[name], alone[name]), (rep, name)
