@@ -6,6 +6,7 @@ is no fallback: if the library is missing or a call fails, an exception is raise
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 import threading
@@ -108,13 +109,33 @@ def _check(status: int) -> None:
         raise PagedKVError(status, msg)
 
 
+# torch's raw current-stream query (an int handle, no Stream object built); the public
+# torch.cuda.current_stream(...).cuda_stream gives the same value at several times the cost,
+# which matters for the launch-bound small calls.
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream_handle(device: torch.device) -> int:
+    if _raw_stream is not None and device.index is not None:
+        return _raw_stream(device.index)
     return torch.cuda.current_stream(device).cuda_stream
+
+
+def _device(dev: torch.device):
+    """Context making dev the current device for a library call; a no-op when it already is."""
+    if dev.index is not None and torch.cuda.current_device() == dev.index:
+        return contextlib.nullcontext()
+    return torch.cuda.device(dev)
 
 
 def _require(t: torch.Tensor, name: str, dtype, ndim: int,
              device: Optional[torch.device] = None) -> None:
     """dtype: one torch dtype, or a tuple of accepted ones."""
+    # Fast path: every check passes (cheap attribute reads only).
+    if (isinstance(t, torch.Tensor) and t.is_cuda and t.dim() == ndim and
+            (t.dtype in dtype if isinstance(dtype, tuple) else t.dtype == dtype) and
+            (device is None or t.get_device() == device.index) and t.is_contiguous()):
+        return
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     accepted = dtype if isinstance(dtype, tuple) else (dtype,)
@@ -148,7 +169,7 @@ def paged_kv_write(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,
     if k.shape != (T, Hkv, D) or v.shape != (T, Hkv, D) or slot_mapping.shape != (T,):
         raise ValueError(f"k/v must be [T, {Hkv}, {D}] and slot_mapping [T]")
     lib = load_library()
-    with torch.cuda.device(dev):
+    with _device(dev):
         _check(lib.paged_kv_write(k.data_ptr(), v.data_ptr(), slot_mapping.data_ptr(), T,
                                   k_cache.data_ptr(), v_cache.data_ptr(), NB, bs, Hkv, D,
                                   _stream_handle(dev)))
@@ -181,7 +202,7 @@ def decode_plan(batch, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq, 
 
 
 def _cached_workspace(dev: torch.device, nbytes: int) -> torch.Tensor:
-    key = (dev.index, torch.cuda.current_stream(dev).cuda_stream)
+    key = (dev.index, _stream_handle(dev))
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
         ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
@@ -238,7 +259,7 @@ def paged_decode_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
         raise ValueError("workspace must be a uint8 tensor on the cache's device")
     ws_bytes = workspace.numel()
     ev_b, ev_e = events if events is not None else (None, None)
-    with torch.cuda.device(dev):
+    with _device(dev):
         _check(lib.paged_decode_attention_ex(
             q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(), MB,
             context_lens.data_ptr(), B, Hq, Hkv, D, bs, NB, float(scale), DTYPES[dt],
@@ -300,7 +321,7 @@ def paged_decode_step(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
     lib = load_library()
     ws, wsb = _step_workspace(lib, dev, B, Hq, D, MB, bs, partition_tokens, workspace)
     ev_b, ev_e = events if events is not None else (None, None)
-    with torch.cuda.device(dev):
+    with _device(dev):
         _check(lib.paged_decode_step(
             q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), slot_mapping.data_ptr(),
             k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(), MB,
@@ -333,7 +354,7 @@ def paged_decode_step_rope(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Te
     lib = load_library()
     ws, wsb = _step_workspace(lib, dev, B, Hq, D, MB, bs, partition_tokens, workspace)
     ev_b, ev_e = events if events is not None else (None, None)
-    with torch.cuda.device(dev):
+    with _device(dev):
         _check(lib.paged_decode_step_rope(
             q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), positions.data_ptr(),
             inv_freq.data_ptr(), int(bool(interleaved)), slot_mapping.data_ptr(),
@@ -375,7 +396,7 @@ def paged_prefill_attention(q: torch.Tensor, cu_seqlens_q: torch.Tensor, k_cache
     if max_q_len is None:
         max_q_len = int((cu_seqlens_q[1:] - cu_seqlens_q[:-1]).max().item()) if B else 0
     lib = load_library()
-    with torch.cuda.device(dev):
+    with _device(dev):
         _check(lib.paged_prefill_attention_ex(
             q.data_ptr(), cu_seqlens_q.data_ptr(), T, int(max_q_len), k_cache.data_ptr(),
             v_cache.data_ptr(), block_tables.data_ptr(), block_tables.shape[1],
@@ -412,7 +433,7 @@ def paged_kv_write_rope(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     if q_out.shape != q.shape:
         raise ValueError("q_out must have q's shape")
     lib = load_library()
-    with torch.cuda.device(dev):
+    with _device(dev):
         _check(lib.paged_kv_write_rope(q.data_ptr(), k.data_ptr(), v.data_ptr(),
                                        positions.data_ptr(), inv_freq.data_ptr(),
                                        int(bool(interleaved)), slot_mapping.data_ptr(), T,
