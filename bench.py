@@ -136,36 +136,42 @@ def resolved_kernel(pk, w, requested):
 
 
 def read_probe(torch, dev, nbytes, reps=5):
-    """Achievable streaming-read rate at this byte count: a plain grid-stride read kernel
+    """Achievable streaming-read rate at this byte count: a grid-stride read kernel
     (libpagedkv_probe.so) over a buffer of nbytes, cold (a 1 GiB buffer is read in between so
-    neither L2 nor the MALL holds it), timed with events. Returns (median us, GB/s)."""
+    neither L2 nor the MALL holds it), timed with events, once with plain loads and once with
+    the non-temporal hint. Returns the faster as (median us, GB/s), and both rates."""
     import ctypes
     lib = ctypes.CDLL(os.path.join(HERE, "paged_kv_decode_write_amd", "libpagedkv_probe.so"))
-    lib.pagedkv_read_probe.restype = ctypes.c_int
-    lib.pagedkv_read_probe.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
-                                       ctypes.c_int32, ctypes.c_void_p]
+    for fn in (lib.pagedkv_read_probe, lib.pagedkv_read_probe_nt):
+        fn.restype = ctypes.c_int
+        fn.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int32,
+                       ctypes.c_void_p]
     grid = 256 * 16
     nbytes = (nbytes + 15) // 16 * 16
     buf = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
     flush = torch.ones((1 << 30) // 4, dtype=torch.float32, device=dev)
     sink = torch.zeros(grid, dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream(dev).cuda_stream
-    times = []
-    for i in range(reps + 1):
-        if lib.pagedkv_read_probe(flush.data_ptr(), flush.numel() * 4, sink.data_ptr(), grid,
-                                  stream):
-            raise RuntimeError("read probe launch failed")
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        if lib.pagedkv_read_probe(buf.data_ptr(), nbytes, sink.data_ptr(), grid, stream):
-            raise RuntimeError("read probe launch failed")
-        b.record()
-        torch.cuda.synchronize()
-        if i:
-            times.append(a.elapsed_time(b) * 1e3)
+    rates = {}
+    for name, fn in (("plain", lib.pagedkv_read_probe), ("nontemporal", lib.pagedkv_read_probe_nt)):
+        times = []
+        for i in range(reps + 1):
+            if lib.pagedkv_read_probe(flush.data_ptr(), flush.numel() * 4, sink.data_ptr(), grid,
+                                      stream):
+                raise RuntimeError("read probe launch failed")
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            if fn(buf.data_ptr(), nbytes, sink.data_ptr(), grid, stream):
+                raise RuntimeError("read probe launch failed")
+            b.record()
+            torch.cuda.synchronize()
+            if i:
+                times.append(a.elapsed_time(b) * 1e3)
+        rates[name] = sorted(times)[len(times) // 2]
     del buf, flush, sink
-    us = sorted(times)[len(times) // 2]
-    return us, nbytes / (us * 1e-6) / 1e9
+    us = min(rates.values())
+    return us, nbytes / (us * 1e-6) / 1e9, {k: round(nbytes / (v * 1e-6) / 1e9, 1)
+                                              for k, v in rates.items()}
 
 
 def cpu_baseline(d, seconds):
@@ -431,8 +437,9 @@ def main():
     probe = {}
     if not args.no_read_probe:
         for d in subs:
-            us, gbs = read_probe(torch, dev, d["bytes"]["attention"])
-            probe[d["workload"].name] = {"us": round(us, 2), "GBps": round(gbs, 1)}
+            us, gbs, both = read_probe(torch, dev, d["bytes"]["attention"])
+            probe[d["workload"].name] = {"us": round(us, 2), "GBps": round(gbs, 1),
+                                         "GBps_by_load": both}
 
     step_bytes = sum(d["bytes"]["attention"] + d["bytes"]["write"] for d in subs)
     value = step_bytes / (ms_per_step * 1e-3) / 1e9

@@ -8,6 +8,9 @@
  * rare case that a block's XOR of its data equals a fixed sentinel; it exists so the loads
  * cannot be optimised away. Time the launch with events to obtain the achievable streaming-read
  * rate. Returns 0, 1 for a bad argument, or 5 if the launch failed.
+ *
+ * pagedkv_read_probe_nt -- the same read with the non-temporal (streaming) hint on every load,
+ * the hint the attention kernels put on their V loads.
  */
 #ifndef PAGED_KV_PROBE_H
 #define PAGED_KV_PROBE_H
@@ -22,6 +25,8 @@ extern "C" {
 
 int pagedkv_read_probe(const void* buf, size_t bytes, uint32_t* sink, int32_t grid,
                        hipStream_t stream);
+int pagedkv_read_probe_nt(const void* buf, size_t bytes, uint32_t* sink, int32_t grid,
+                          hipStream_t stream);
 
 #ifdef __cplusplus
 }

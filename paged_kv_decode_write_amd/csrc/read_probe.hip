@@ -8,26 +8,41 @@
 
 namespace {
 
-// Grid-stride read of n16 16-byte words. The XOR of everything read is stored only if it hits
-// a sentinel, which keeps the loads live without a write per thread.
-__global__ void __launch_bounds__(256) read_probe_kernel(const uint4* __restrict__ p, size_t n16,
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Grid-stride read of n16 16-byte words, plain or with the non-temporal (streaming) hint. The
+// XOR of everything read is stored only if it hits a sentinel, which keeps the loads live
+// without a write per thread.
+template <bool NT>
+__global__ void __launch_bounds__(256) read_probe_kernel(const u32x4* __restrict__ p, size_t n16,
                                                          uint32_t* sink) {
   uint32_t acc = 0;
   const size_t stride = (size_t)gridDim.x * blockDim.x;
 #pragma unroll 8
   for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n16; i += stride) {
-    const uint4 v = p[i];
-    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+    const u32x4 v = NT ? __builtin_nontemporal_load(p + i) : p[i];
+    acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
   }
   if (acc == 0x9e3779b9u) sink[blockIdx.x] = acc;
+}
+
+template <bool NT>
+int launch_probe(const void* buf, size_t bytes, uint32_t* sink, int32_t grid,
+                 hipStream_t stream) {
+  if (!buf || !sink || grid <= 0 || (reinterpret_cast<uintptr_t>(buf) & 15)) return 1;
+  hipLaunchKernelGGL(read_probe_kernel<NT>, dim3((unsigned)grid), dim3(256), 0, stream,
+                     static_cast<const u32x4*>(buf), bytes / 16, sink);
+  return hipGetLastError() == hipSuccess ? 0 : 5;
 }
 
 }  // namespace
 
 extern "C" int pagedkv_read_probe(const void* buf, size_t bytes, uint32_t* sink, int32_t grid,
                                   hipStream_t stream) {
-  if (!buf || !sink || grid <= 0 || (reinterpret_cast<uintptr_t>(buf) & 15)) return 1;
-  hipLaunchKernelGGL(read_probe_kernel, dim3((unsigned)grid), dim3(256), 0, stream,
-                     static_cast<const uint4*>(buf), bytes / 16, sink);
-  return hipGetLastError() == hipSuccess ? 0 : 5;
+  return launch_probe<false>(buf, bytes, sink, grid, stream);
+}
+
+extern "C" int pagedkv_read_probe_nt(const void* buf, size_t bytes, uint32_t* sink,
+                                     int32_t grid, hipStream_t stream) {
+  return launch_probe<true>(buf, bytes, sink, grid, stream);
 }
