@@ -43,7 +43,8 @@ def parse_args():
     p.add_argument("--workload", default="c5")
     p.add_argument("--kernel", default="auto", choices=["auto", "valu", "mfma", "mfma_hw"])
     p.add_argument("--partition", type=int, default=0,
-                   help="tokens per partition: 0 automatic, -1 never split")
+                   help="tokens per partition (multi-query workloads: keys per partition of a "
+                        "query tile, a multiple of 32): 0 automatic, -1 never split")
     p.add_argument("--in-dtype", default="bf16", choices=["bf16", "f16"],
                    help="format of q and the K/V pools")
     p.add_argument("--out-dtype", default="f32", choices=["f32", "bf16", "f16"],
@@ -228,6 +229,8 @@ def bench_prefill(args, torch, pk, wl):
     out = torch.empty(T, Hq, D, dtype=getattr(torch, OUT_TORCH[args.out_dtype]), device=dev)
     alg = wl.prefill_algorithmic(w)
     write_bytes = T * w.num_kv_heads * w.head_dim * 2 * 2 * 2
+    plan = pk.prefill_plan(T, d["max_q_len"], len(w.context_lens), Hq, w.num_kv_heads, D,
+                           w.max_blocks, w.block_size, args.row_blocks, args.partition)
 
     def step(ev=None):
         pk.paged_kv_write(d["k_new"], d["v_new"], d["slot_mapping"], d["k_cache"], d["v_cache"])
@@ -235,7 +238,8 @@ def bench_prefill(args, torch, pk, wl):
             ev[0].record()
         pk.paged_prefill_attention(d["q"], d["cu_seqlens_q"], d["k_cache"], d["v_cache"],
                                    d["block_tables"], d["context_lens"], d["scale"], out,
-                                   max_q_len=d["max_q_len"], row_blocks=args.row_blocks)
+                                   max_q_len=d["max_q_len"], row_blocks=args.row_blocks,
+                                   partition_tokens=args.partition)
         if ev is not None:
             ev[1].record()
 
@@ -261,11 +265,13 @@ def bench_prefill(args, torch, pk, wl):
         "vs_baseline": None, "dtype": args.in_dtype,
         "data": f"synthetic (seeded N(0,1) {args.in_dtype}), resident in HBM",
         "config": {"workload": w.description, "kernel": "prefill_mfma",
-                   "row_blocks": args.row_blocks,
+                   "row_blocks": plan[0], "key_partitions": plan[1],
+                   "keys_per_partition": plan[2],
                    "formats": f"{args.in_dtype} in, {args.out_dtype} out",
                    "us_per_call": round(mean * 1e3, 2),
                    "GBps": round(alg["bytes"] / (mean * 1e-3) / 1e9, 1),
-                   "step": "KV write of the chunk + multi-query causal attention"},
+                   "step": "KV write of the chunk + multi-query causal attention"
+                           + (" + partition merge" if plan[1] > 1 else "")},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": None},

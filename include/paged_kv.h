@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define PAGED_KV_ABI_VERSION 3
+#define PAGED_KV_ABI_VERSION 4
 
 typedef enum {
   PAGEDKV_OK = 0,
@@ -358,6 +358,61 @@ int paged_prefill_attention_ex(const uint16_t* q, const int32_t* cu_seqlens_q,
                                int32_t head_dim, int32_t block_size, int64_t num_blocks,
                                float scale, int32_t kv_dtype, void* out, int32_t out_dtype,
                                int32_t row_blocks, hipStream_t stream);
+
+/*
+ * paged_prefill_attention_split -- paged_prefill_attention_ex with the keys of each query
+ * tile optionally cut into partitions, each computed by workgroups of its own and combined by
+ * the log-sum-exp merge of the decode path (the running-max rescaling of the tiled online
+ * softmax, llm-stack, Attention kernel section, applied across partitions; the split-K kernel
+ * the "vLLM-Style Llama Inference Engine with Tensor Parallelism" page lists as out of its
+ * scope). It shortens the serial chain of keys when a batch has few query rows against long
+ * contexts, such as a short chunk appended to a long cached prefix.
+ *
+ *   workspace, workspace_bytes  device memory of at least paged_prefill_workspace_bytes(...)
+ *                  bytes, 16-byte aligned, used only while the call's kernels run; NULL / 0 is
+ *                  allowed when the plan does not split. Contents need no initialisation.
+ *                  Calls that may overlap (other streams) need their own workspace.
+ *   partition_tokens  keys per partition: 0 lets the library choose (it splits only when the
+ *                  query tiles cannot fill the device and contexts may exceed 2048 keys, into
+ *                  at most 4 partitions of at least 512 keys), -1 never splits, > 0 forces
+ *                  that size, which must be a multiple of 32 (else PAGEDKV_ERR_SHAPE).
+ *   Other arguments as in paged_prefill_attention_ex. A split adds a second launch (the
+ *   merge) on `stream`. Results agree with the unsplit call up to fp32 rounding of the same
+ *   sums; a row that sees a single key still returns that value row exactly.
+ */
+int paged_prefill_attention_split(const uint16_t* q, const int32_t* cu_seqlens_q,
+                                  int64_t num_tokens, int32_t max_q_len,
+                                  const uint16_t* k_cache, const uint16_t* v_cache,
+                                  const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                  const int32_t* context_lens, int32_t batch,
+                                  int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                  int32_t block_size, int64_t num_blocks, float scale,
+                                  int32_t kv_dtype, void* out, int32_t out_dtype,
+                                  int32_t row_blocks, void* workspace, size_t workspace_bytes,
+                                  int32_t partition_tokens, hipStream_t stream);
+
+/*
+ * paged_prefill_workspace_bytes -- bytes of workspace paged_prefill_attention_split needs
+ * (0 when it never splits for these sizes). For partition_tokens 0 the bound covers every
+ * plan the automatic choice can make; it does not depend on the device.
+ */
+size_t paged_prefill_workspace_bytes(int64_t num_tokens, int32_t num_q_heads, int32_t head_dim,
+                                     int32_t max_blocks_per_seq, int32_t block_size,
+                                     int32_t partition_tokens);
+
+/*
+ * paged_prefill_plan -- the launch paged_prefill_attention_split would make for these sizes
+ * on the current device, without launching: 16-row blocks per wave, key partitions per query
+ * tile (1: no split) and keys per partition. Arguments as in paged_prefill_attention_split;
+ * outputs are written on PAGEDKV_OK. PAGEDKV_CU_COUNT overrides the compute-unit count as in
+ * paged_decode_plan (the choice of row_blocks = 0 also asks the runtime for the kernels'
+ * occupancy, which needs a device).
+ */
+int paged_prefill_plan(int64_t num_tokens, int32_t max_q_len, int32_t batch,
+                       int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                       int32_t max_blocks_per_seq, int32_t block_size, int32_t row_blocks,
+                       int32_t partition_tokens, int32_t* row_blocks_used,
+                       int32_t* num_partitions, int32_t* keys_per_partition);
 
 #ifdef __cplusplus
 }

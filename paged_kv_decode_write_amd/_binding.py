@@ -95,6 +95,16 @@ def load_library() -> ctypes.CDLL:
         lib.paged_decode_plan.argtypes = [I32, I32, I32, I32, I32, I32, I32, I32,
                                           ctypes.POINTER(I32), ctypes.POINTER(I32),
                                           ctypes.POINTER(I32)]
+        lib.paged_prefill_attention_split.restype = ctypes.c_int
+        lib.paged_prefill_attention_split.argtypes = [P, P, I64, I32, P, P, P, I32, P, I32, I32,
+                                                      I32, I32, I32, I64, F32, I32, P, I32, I32,
+                                                      P, SZ, I32, P]
+        lib.paged_prefill_workspace_bytes.restype = SZ
+        lib.paged_prefill_workspace_bytes.argtypes = [I64, I32, I32, I32, I32, I32]
+        lib.paged_prefill_plan.restype = ctypes.c_int
+        lib.paged_prefill_plan.argtypes = [I64, I32, I32, I32, I32, I32, I32, I32, I32, I32,
+                                           ctypes.POINTER(I32), ctypes.POINTER(I32),
+                                           ctypes.POINTER(I32)]
         _lib = lib
         return lib
 
@@ -183,6 +193,27 @@ def decode_workspace_bytes(batch: int, num_q_heads: int, head_dim: int,
 
 
 KERNEL_NAMES = {v: k for k, v in KERNELS.items()}
+
+
+def prefill_workspace_bytes(num_tokens: int, num_q_heads: int, head_dim: int,
+                            max_blocks_per_seq: int, block_size: int,
+                            partition_tokens: int = 0) -> int:
+    return int(load_library().paged_prefill_workspace_bytes(
+        num_tokens, num_q_heads, head_dim, max_blocks_per_seq, block_size, partition_tokens))
+
+
+def prefill_plan(num_tokens, max_q_len, batch, num_q_heads, num_kv_heads, head_dim,
+                 max_blocks_per_seq, block_size, row_blocks=0, partition_tokens=0):
+    """(row_blocks, num_partitions, keys_per_partition) the multi-query call would use on
+    the current device."""
+    nb = ctypes.c_int32(0)
+    n = ctypes.c_int32(0)
+    p = ctypes.c_int32(0)
+    _check(load_library().paged_prefill_plan(num_tokens, max_q_len, batch, num_q_heads,
+                                             num_kv_heads, head_dim, max_blocks_per_seq,
+                                             block_size, row_blocks, partition_tokens,
+                                             ctypes.byref(nb), ctypes.byref(n), ctypes.byref(p)))
+    return nb.value, n.value, p.value
 
 
 def decode_plan(batch, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq, block_size,
@@ -368,7 +399,9 @@ def paged_decode_step_rope(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Te
 def paged_prefill_attention(q: torch.Tensor, cu_seqlens_q: torch.Tensor, k_cache: torch.Tensor,
                             v_cache: torch.Tensor, block_tables: torch.Tensor,
                             context_lens: torch.Tensor, scale: float, out: torch.Tensor, *,
-                            max_q_len: Optional[int] = None, row_blocks: int = 0) -> torch.Tensor:
+                            max_q_len: Optional[int] = None, row_blocks: int = 0,
+                            partition_tokens: int = 0,
+                            workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Multi-query causal attention over the paged cache (prefill / chunked prefill).
 
     Sequence b's query rows are q[cu_seqlens_q[b]:cu_seqlens_q[b+1]], its last Q_b positions;
@@ -377,6 +410,9 @@ def paged_prefill_attention(q: torch.Tensor, cu_seqlens_q: torch.Tensor, k_cache
     max_q_len (the largest Q_b) sizes the launch; when
     omitted it is read from cu_seqlens_q, which synchronises with the device. row_blocks
     (1, 2 or 4; 0 = chosen by the library) is the number of 16-row query blocks per wave.
+    partition_tokens splits each query tile's keys (0 = the library's choice, -1 = never, > 0
+    = that many keys, a multiple of 32); a split uses `workspace` (uint8, reused per stream
+    when not given).
     """
     _require(k_cache, "k_cache", INPUT_TYPES, 4)
     dev, dt = k_cache.device, k_cache.dtype
@@ -396,12 +432,21 @@ def paged_prefill_attention(q: torch.Tensor, cu_seqlens_q: torch.Tensor, k_cache
     if max_q_len is None:
         max_q_len = int((cu_seqlens_q[1:] - cu_seqlens_q[:-1]).max().item()) if B else 0
     lib = load_library()
+    MB = block_tables.shape[1]
+    need = int(lib.paged_prefill_workspace_bytes(T, Hq, D, MB, bs, int(partition_tokens)))
+    if workspace is None:
+        if need:
+            workspace = _cached_workspace(dev, need)
+    elif workspace.device != dev or workspace.dtype != torch.uint8:
+        raise ValueError("workspace must be a uint8 tensor on the cache's device")
+    ws_ptr, ws_bytes = (workspace.data_ptr(), workspace.numel()) if workspace is not None \
+        else (None, 0)
     with _device(dev):
-        _check(lib.paged_prefill_attention_ex(
+        _check(lib.paged_prefill_attention_split(
             q.data_ptr(), cu_seqlens_q.data_ptr(), T, int(max_q_len), k_cache.data_ptr(),
-            v_cache.data_ptr(), block_tables.data_ptr(), block_tables.shape[1],
-            context_lens.data_ptr(), B, Hq, Hkv, D, bs, NB, float(scale), DTYPES[dt],
-            out.data_ptr(), DTYPES[out.dtype], int(row_blocks), _stream_handle(dev)))
+            v_cache.data_ptr(), block_tables.data_ptr(), MB, context_lens.data_ptr(), B, Hq,
+            Hkv, D, bs, NB, float(scale), DTYPES[dt], out.data_ptr(), DTYPES[out.dtype],
+            int(row_blocks), ws_ptr, ws_bytes, int(partition_tokens), _stream_handle(dev)))
     return out
 
 

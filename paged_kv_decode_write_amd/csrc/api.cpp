@@ -146,6 +146,93 @@ size_t split_workspace_bytes(int64_t B, int64_t Hq, int64_t D, int64_t n) {
   return acc_bytes(B, Hq, D, n) + (size_t)round_up(B * Hq * n * 2 * 4, 256);
 }
 
+// Key split of the multi-query kernel. It pays when the batch's query tiles are too few to
+// fill the device and contexts are long: one tile's keys are then a long serial chain that a
+// few workgroups walk while the rest of the device idles. The automatic choice splits when the
+// workgroups that have rows to compute (counted from num_tokens, a lower bound for ragged
+// batches) fill fewer than two residency rounds and the contexts may exceed
+// kPrefillSplitMinKeys; it cuts them into at most kPrefillMaxAutoParts partitions of at least
+// kPrefillMinPartKeys keys. Partitions are multiples of the 32 keys one staged pair holds.
+constexpr int64_t kPrefillSplitMinKeys = 2048;
+constexpr int64_t kPrefillMaxAutoParts = 4;
+constexpr int64_t kPrefillMinPartKeys = 512;
+constexpr int64_t kPrefillPairKeys = 32;
+// Workgroups of the one- and two-block kernels one CU holds (their registers allow two); a
+// constant so that the split does not depend on an occupancy query.
+constexpr int64_t kPrefillGroupsPerCU = 2;
+
+struct PrefillPlan {
+  int32_t nb;         // 16-row blocks per wave
+  int32_t nparts;     // key partitions per query tile
+  int32_t part_keys;  // keys per partition
+  int64_t ntiles;     // query tiles per sequence
+};
+
+int64_t prefill_auto_part_keys(int64_t max_len) {
+  const int64_t P = round_up(ceil_div(max_len, kPrefillMaxAutoParts), kPrefillPairKeys);
+  return P > kPrefillMinPartKeys ? P : kPrefillMinPartKeys;
+}
+
+// Upper bound of the partition count, device-independent (sizes the workspace).
+int64_t prefill_nparts_bound(int64_t max_len, int32_t partition_tokens) {
+  if (max_len <= 0 || partition_tokens == -1) return 1;
+  if (partition_tokens > 0)
+    return partition_tokens % kPrefillPairKeys ? 1 : ceil_div(max_len, partition_tokens);
+  if (max_len <= kPrefillSplitMinKeys) return 1;
+  return ceil_div(max_len, prefill_auto_part_keys(max_len));
+}
+
+int check_prefill_knobs(int32_t row_blocks, int32_t partition_tokens) {
+  if (row_blocks != 0 && row_blocks != 1 && row_blocks != 2 && row_blocks != 4)
+    return fail(PAGEDKV_ERR_SHAPE, "row_blocks must be 0 (auto), 1, 2 or 4, got %d", row_blocks);
+  if (partition_tokens < -1)
+    return fail(PAGEDKV_ERR_SHAPE, "partition_tokens must be >= -1");
+  if (partition_tokens > 0 && partition_tokens % kPrefillPairKeys)
+    return fail(PAGEDKV_ERR_SHAPE, "partition_tokens %d is not a multiple of %d",
+                partition_tokens, (int)kPrefillPairKeys);
+  return PAGEDKV_OK;
+}
+
+int make_prefill_plan(int64_t num_tokens, int32_t max_q_len, int32_t batch,
+                      int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int G,
+                      int32_t max_blocks, int32_t block_size, int32_t row_blocks,
+                      int32_t partition_tokens, int cus, PrefillPlan* plan) {
+  const int st = check_prefill_knobs(row_blocks, partition_tokens);
+  if (st) return st;
+  const int nb = row_blocks > 0 ? row_blocks
+                                : prefill_rows_per_wave(num_tokens, num_kv_heads, head_dim, G, cus);
+  const int64_t per_group = prefill_tokens_per_group(G, nb);
+  const int64_t ntiles = ceil_div(max_q_len, per_group);
+  const int64_t max_len = (int64_t)max_blocks * block_size;
+  const bool rows_fit = num_tokens * num_q_heads <= INT32_MAX;  // the merge's row count
+  int64_t n = 1, P = 0;
+  if (partition_tokens > 0 && max_len > 0) {
+    P = partition_tokens;
+    n = ceil_div(max_len, P);
+    if (n > 1 && !rows_fit)
+      return fail(PAGEDKV_ERR_SHAPE, "num_tokens * num_q_heads exceeds int32 for a key split");
+  } else if (partition_tokens == 0 && max_len > kPrefillSplitMinKeys && rows_fit) {
+    const int64_t groups = (int64_t)num_kv_heads * ceil_div(num_tokens, per_group);
+    if (groups < 2 * kPrefillGroupsPerCU * cus) {
+      P = prefill_auto_part_keys(max_len);
+      n = ceil_div(max_len, P);
+    }
+  }
+  if (n <= 1) {
+    n = 1;
+    P = round_up(max_len > 0 ? max_len : 1, kPrefillPairKeys);
+  }
+  if (P > INT32_MAX) return fail(PAGEDKV_ERR_SHAPE, "partition plan overflows");
+  if ((int64_t)batch * num_kv_heads * ntiles * n > INT32_MAX)
+    return fail(PAGEDKV_ERR_SHAPE,
+                "too many workgroups (batch * kv heads * query tiles * key partitions)");
+  plan->nb = nb;
+  plan->nparts = (int32_t)n;
+  plan->part_keys = (int32_t)P;
+  plan->ntiles = ntiles;
+  return PAGEDKV_OK;
+}
+
 int select_kernel(int32_t kernel, int D, int G, int bs, int64_t max_len, int* chosen) {
   switch (kernel) {
     case PAGEDKV_KERNEL_AUTO:
@@ -585,19 +672,21 @@ int paged_decode_attention_typed(const uint16_t* q, const uint16_t* k_cache,
                                    PAGEDKV_KERNEL_AUTO, nullptr, nullptr, stream);
 }
 
-int paged_prefill_attention_ex(const uint16_t* q, const int32_t* cu_seqlens_q,
-                               int64_t num_tokens, int32_t max_q_len, const uint16_t* k_cache,
-                               const uint16_t* v_cache, const int32_t* block_tables,
-                               int32_t max_blocks_per_seq, const int32_t* context_lens,
-                               int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
-                               int32_t head_dim, int32_t block_size, int64_t num_blocks,
-                               float scale, int32_t kv_dtype, void* out, int32_t out_dtype,
-                               int32_t row_blocks, hipStream_t stream) {
+int paged_prefill_attention_split(const uint16_t* q, const int32_t* cu_seqlens_q,
+                                  int64_t num_tokens, int32_t max_q_len,
+                                  const uint16_t* k_cache, const uint16_t* v_cache,
+                                  const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                  const int32_t* context_lens, int32_t batch,
+                                  int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                  int32_t block_size, int64_t num_blocks, float scale,
+                                  int32_t kv_dtype, void* out, int32_t out_dtype,
+                                  int32_t row_blocks, void* workspace, size_t workspace_bytes,
+                                  int32_t partition_tokens, hipStream_t stream) {
   g_last_error.clear();
   int st = check_formats(kv_dtype, out_dtype);
   if (st) return st;
-  if (row_blocks != 0 && row_blocks != 1 && row_blocks != 2 && row_blocks != 4)
-    return fail(PAGEDKV_ERR_SHAPE, "row_blocks must be 0 (auto), 1, 2 or 4, got %d", row_blocks);
+  st = check_prefill_knobs(row_blocks, partition_tokens);
+  if (st) return st;
   st = check_decode_sizes(max_blocks_per_seq, batch, num_q_heads, num_kv_heads, head_dim,
                           block_size, num_blocks);
   if (st) return st;
@@ -620,12 +709,11 @@ int paged_prefill_attention_ex(const uint16_t* q, const int32_t* cu_seqlens_q,
   int cus = 0;
   st = cu_count(&cus);
   if (st) return st;
-  const int nb = row_blocks > 0 ? row_blocks
-                               : prefill_rows_per_wave(num_tokens, num_kv_heads, head_dim, G, cus);
-  const int64_t per_group = prefill_tokens_per_group(G, nb);
-  const int64_t ntiles = ceil_div(max_q_len, per_group);
-  if ((int64_t)batch * num_kv_heads * ntiles > INT32_MAX)
-    return fail(PAGEDKV_ERR_SHAPE, "too many workgroups (batch * kv heads * query tiles)");
+  PrefillPlan plan{};
+  st = make_prefill_plan(num_tokens, max_q_len, batch, num_q_heads, num_kv_heads, head_dim, G,
+                         max_blocks_per_seq, block_size, row_blocks, partition_tokens, cus,
+                         &plan);
+  if (st) return st;
   PrefillArgs a{};
   a.q = q;
   a.cu_seqlens_q = cu_seqlens_q;
@@ -642,12 +730,102 @@ int paged_prefill_attention_ex(const uint16_t* q, const int32_t* cu_seqlens_q,
   a.block_size = block_size;
   a.num_blocks = num_blocks;
   a.scale_log2 = scale * kLog2eHost;
-  a.ntiles = (int32_t)ntiles;
-  a.nb = nb;
+  a.ntiles = (int32_t)plan.ntiles;
+  a.nb = plan.nb;
   a.kv_dtype = kv_dtype;
   a.out_dtype = out_dtype;
+  a.nparts = plan.nparts;
+  a.part_keys = plan.part_keys;
+  if (plan.nparts > 1) {
+    const size_t need = split_workspace_bytes(num_tokens, num_q_heads, head_dim, plan.nparts);
+    if (!workspace || workspace_bytes < need)
+      return fail(PAGEDKV_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                  workspace ? workspace_bytes : (size_t)0);
+    if (!aligned(workspace, 16)) return fail(PAGEDKV_ERR_ALIGN, "workspace needs 16-byte alignment");
+    char* base = static_cast<char*>(workspace);
+    a.ws_acc = reinterpret_cast<float*>(base);
+    a.ws_ml = reinterpret_cast<float*>(
+        base + acc_bytes(num_tokens, num_q_heads, head_dim, plan.nparts));
+  }
   hipError_t e = launch_prefill_mfma(a, stream);
   if (e != hipSuccess) return hip_fail(e, "prefill attention launch");
+  if (plan.nparts > 1) {
+    // The merge of the decode path, with the query tokens as the batch (its rows are (token,
+    // query head), the layout of out and of the partials), in the form that skips rows written
+    // out directly and partitions without keys.
+    DecodeArgs m{};
+    m.out = out;
+    m.ws_acc = a.ws_acc;
+    m.ws_ml = a.ws_ml;
+    m.batch = (int32_t)num_tokens;
+    m.num_q_heads = num_q_heads;
+    m.num_kv_heads = num_kv_heads;
+    m.head_dim = head_dim;
+    m.block_size = block_size;
+    m.nparts = plan.nparts;
+    m.kv_dtype = kv_dtype;
+    m.out_dtype = out_dtype;
+    e = launch_prefill_merge(m, stream);
+    if (e != hipSuccess) return hip_fail(e, "partition merge launch");
+  }
+  return PAGEDKV_OK;
+}
+
+int paged_prefill_attention_ex(const uint16_t* q, const int32_t* cu_seqlens_q,
+                               int64_t num_tokens, int32_t max_q_len, const uint16_t* k_cache,
+                               const uint16_t* v_cache, const int32_t* block_tables,
+                               int32_t max_blocks_per_seq, const int32_t* context_lens,
+                               int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                               int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                               float scale, int32_t kv_dtype, void* out, int32_t out_dtype,
+                               int32_t row_blocks, hipStream_t stream) {
+  return paged_prefill_attention_split(q, cu_seqlens_q, num_tokens, max_q_len, k_cache, v_cache,
+                                       block_tables, max_blocks_per_seq, context_lens, batch,
+                                       num_q_heads, num_kv_heads, head_dim, block_size,
+                                       num_blocks, scale, kv_dtype, out, out_dtype, row_blocks,
+                                       nullptr, 0, -1, stream);
+}
+
+size_t paged_prefill_workspace_bytes(int64_t num_tokens, int32_t num_q_heads, int32_t head_dim,
+                                     int32_t max_blocks_per_seq, int32_t block_size,
+                                     int32_t partition_tokens) {
+  if (num_tokens <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_blocks_per_seq <= 0 ||
+      block_size <= 0)
+    return 0;
+  const int64_t n =
+      prefill_nparts_bound((int64_t)max_blocks_per_seq * block_size, partition_tokens);
+  return split_workspace_bytes(num_tokens, num_q_heads, head_dim, n);
+}
+
+int paged_prefill_plan(int64_t num_tokens, int32_t max_q_len, int32_t batch,
+                       int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                       int32_t max_blocks_per_seq, int32_t block_size, int32_t row_blocks,
+                       int32_t partition_tokens, int32_t* row_blocks_used,
+                       int32_t* num_partitions, int32_t* keys_per_partition) {
+  g_last_error.clear();
+  if (!row_blocks_used || !num_partitions || !keys_per_partition)
+    return fail(PAGEDKV_ERR_NULL, "output pointers must be non-NULL");
+  int st = check_decode_sizes(max_blocks_per_seq, batch, num_q_heads, num_kv_heads, head_dim,
+                              block_size, 1);
+  if (st) return st;
+  if (num_tokens < 0 || max_q_len < 0 || num_tokens > INT32_MAX)
+    return fail(PAGEDKV_ERR_SHAPE, "num_tokens and max_q_len must be in [0, 2^31)");
+  const int G = num_q_heads / num_kv_heads;
+  if (!supported_prefill(head_dim, G, block_size))
+    return fail(PAGEDKV_ERR_UNSUPPORTED,
+                "no multi-query kernel for head_dim %d, block_size %d, group size %d", head_dim,
+                block_size, G);
+  int cus = 0;
+  st = cu_count(&cus);
+  if (st) return st;
+  PrefillPlan plan{};
+  st = make_prefill_plan(num_tokens, max_q_len, batch, num_q_heads, num_kv_heads, head_dim, G,
+                         max_blocks_per_seq, block_size, row_blocks, partition_tokens, cus,
+                         &plan);
+  if (st) return st;
+  *row_blocks_used = plan.nb;
+  *num_partitions = plan.nparts;
+  *keys_per_partition = plan.part_keys;
   return PAGEDKV_OK;
 }
 

@@ -37,9 +37,14 @@ __device__ __forceinline__ void fold(float& m, float& x, float m2, float x2) {
   m = mn;
 }
 
+// SPARSE (the key split of the multi-query kernel): a row whose first slot holds the done
+// marker (-inf, -1) was written out directly and is left alone, and partial outputs are read
+// only for partitions that saw keys (m > -inf). That costs a second round trip (statistics,
+// then outputs) and saves the reads of the many empty partitions that split causal tiles have.
+
 // PER: partitions per column group read in the first pass (a power of two, at most 16; the
 // launch picks the smallest that covers nparts when it can). Used for more than 8 partitions.
-template <int OT, int PER>
+template <int OT, int PER, bool SPARSE>
 __global__ void __launch_bounds__(kReduceThreads)
 decode_reduce_kernel(const DecodeArgs a) {
   constexpr int NWV = kReduceThreads / 64;
@@ -56,6 +61,8 @@ decode_reduce_kernel(const DecodeArgs a) {
 
   const int groups = kReduceThreads / D;  // D in {64, 128}: 8 or 4
   const int d = tid % D, grp = tid / D;
+  if constexpr (SPARSE)
+    if (ml[1] < 0.f) return;  // done marker (uniform over the workgroup, before the barrier)
 
   // First pass, all loads issued together: the statistics of partition tid and (m_p, a_p[d])
   // of partitions grp + u * groups, u < PER. Indices past the end are clamped so that every
@@ -69,7 +76,14 @@ decode_reduce_kernel(const DecodeArgs a) {
     const int p = grp + u * groups;
     const int pc = p < nparts ? p : last;
     mp[u] = ml[2 * pc];
-    ap[u] = acc[(size_t)pc * D + d];
+    if constexpr (!SPARSE) ap[u] = acc[(size_t)pc * D + d];
+  }
+  if constexpr (SPARSE) {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int p = grp + u * groups;
+      ap[u] = p < nparts && mp[u] != kNegInf ? acc[(size_t)p * D + d] : 0.f;
+    }
   }
   __builtin_amdgcn_sched_barrier(0);  // keep the loads above ahead of every use
   float m = tid < nparts ? m_s : kNegInf, l = tid < nparts ? l_s : 0.f;
@@ -80,8 +94,10 @@ decode_reduce_kernel(const DecodeArgs a) {
   // The rest, for more than 512 partitions or more than PER per column group.
   for (int p = tid + kReduceThreads; p < nparts; p += kReduceThreads)
     fold(m, l, ml[2 * p], ml[2 * p + 1]);
-  for (int p = grp + PER * groups; p < nparts; p += groups)
-    fold(mx, x, ml[2 * p], acc[(size_t)p * D + d]);
+  for (int p = grp + PER * groups; p < nparts; p += groups) {
+    const float m2 = ml[2 * p];
+    fold(mx, x, m2, !SPARSE || m2 != kNegInf ? acc[(size_t)p * D + d] : 0.f);
+  }
 
 #pragma unroll
   for (int s = 1; s < 64; s <<= 1) {
@@ -110,7 +126,7 @@ decode_reduce_kernel(const DecodeArgs a) {
 // The statistics are the same few addresses for the D threads of a row.
 constexpr int kNarrowThreads = 256;
 
-template <int OT, int NP>
+template <int OT, int NP, bool SPARSE>
 __global__ void __launch_bounds__(kNarrowThreads)
 decode_reduce_narrow_kernel(const DecodeArgs a) {
   const int D = a.head_dim;  // 64 or 128: a workgroup covers kNarrowThreads / D whole rows
@@ -127,7 +143,13 @@ decode_reduce_narrow_kernel(const DecodeArgs a) {
     const int pc = u < nparts ? u : last;
     mp[u] = ml[2 * pc];
     lp[u] = ml[2 * pc + 1];
-    ap[u] = acc[(size_t)pc * D + d];
+    if constexpr (!SPARSE) ap[u] = acc[(size_t)pc * D + d];
+  }
+  if constexpr (SPARSE) {
+    if (lp[0] < 0.f) return;  // done marker: written out directly
+#pragma unroll
+    for (int u = 0; u < NP; ++u)
+      ap[u] = u < nparts && mp[u] != kNegInf ? acc[(size_t)u * D + d] : 0.f;
   }
   __builtin_amdgcn_sched_barrier(0);  // keep the loads above ahead of every use
   float m = kNegInf, l = 0.f, mo = kNegInf, x = 0.f;
@@ -140,44 +162,56 @@ decode_reduce_narrow_kernel(const DecodeArgs a) {
   store_out<OT>(a.out, e, l > 0.f ? x / l : 0.f);
 }
 
-template <int OT>
+template <int OT, bool SPARSE>
 hipError_t launch_reduce_per(const DecodeArgs& a, unsigned rows, hipStream_t stream) {
   if (a.nparts <= 8) {
     const unsigned grid =
         (unsigned)(((size_t)rows * a.head_dim + kNarrowThreads - 1) / kNarrowThreads);
     const dim3 block(kNarrowThreads);
     if (a.nparts <= 2)
-      hipLaunchKernelGGL((decode_reduce_narrow_kernel<OT, 2>), dim3(grid), block, 0, stream, a);
+      hipLaunchKernelGGL((decode_reduce_narrow_kernel<OT, 2, SPARSE>), dim3(grid), block, 0,
+                         stream, a);
     else if (a.nparts <= 4)
-      hipLaunchKernelGGL((decode_reduce_narrow_kernel<OT, 4>), dim3(grid), block, 0, stream, a);
+      hipLaunchKernelGGL((decode_reduce_narrow_kernel<OT, 4, SPARSE>), dim3(grid), block, 0,
+                         stream, a);
     else
-      hipLaunchKernelGGL((decode_reduce_narrow_kernel<OT, 8>), dim3(grid), block, 0, stream, a);
+      hipLaunchKernelGGL((decode_reduce_narrow_kernel<OT, 8, SPARSE>), dim3(grid), block, 0,
+                         stream, a);
     return hipGetLastError();
   }
   const int groups = kReduceThreads / a.head_dim;
   const int need = (a.nparts + groups - 1) / groups;
   const dim3 grid(rows), block(kReduceThreads);
   if (need <= 1)
-    hipLaunchKernelGGL((decode_reduce_kernel<OT, 1>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((decode_reduce_kernel<OT, 1, SPARSE>), grid, block, 0, stream, a);
   else if (need <= 2)
-    hipLaunchKernelGGL((decode_reduce_kernel<OT, 2>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((decode_reduce_kernel<OT, 2, SPARSE>), grid, block, 0, stream, a);
   else if (need <= 4)
-    hipLaunchKernelGGL((decode_reduce_kernel<OT, 4>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((decode_reduce_kernel<OT, 4, SPARSE>), grid, block, 0, stream, a);
   else if (need <= 8)
-    hipLaunchKernelGGL((decode_reduce_kernel<OT, 8>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((decode_reduce_kernel<OT, 8, SPARSE>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL((decode_reduce_kernel<OT, 16>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((decode_reduce_kernel<OT, 16, SPARSE>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 
-hipError_t launch_decode_reduce(const DecodeArgs& a, hipStream_t stream) {
+template <bool SPARSE>
+hipError_t launch_reduce(const DecodeArgs& a, hipStream_t stream) {
   const unsigned rows = (unsigned)((long long)a.batch * a.num_q_heads);
   switch (a.out_dtype) {
-    case kDtF32: return launch_reduce_per<kDtF32>(a, rows, stream);
-    case kDtBf16: return launch_reduce_per<kDtBf16>(a, rows, stream);
-    case kDtF16: return launch_reduce_per<kDtF16>(a, rows, stream);
+    case kDtF32: return launch_reduce_per<kDtF32, SPARSE>(a, rows, stream);
+    case kDtBf16: return launch_reduce_per<kDtBf16, SPARSE>(a, rows, stream);
+    case kDtF16: return launch_reduce_per<kDtF16, SPARSE>(a, rows, stream);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_decode_reduce(const DecodeArgs& a, hipStream_t stream) {
+  return launch_reduce<false>(a, stream);
+}
+
+hipError_t launch_prefill_merge(const DecodeArgs& a, hipStream_t stream) {
+  return launch_reduce<true>(a, stream);
 }
 
 }  // namespace pagedkv

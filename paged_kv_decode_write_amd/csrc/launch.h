@@ -60,6 +60,13 @@ struct PrefillArgs {
   int32_t ntiles;  // query tiles per sequence (ceil(max_q_len / tokens per workgroup))
   int32_t nb;      // 16-row N blocks per wave: 1, 2 or 4
   int32_t kv_dtype, out_dtype;  // as in DecodeArgs
+  // Key split: each query tile's keys are cut into partitions of part_keys (a multiple of 32)
+  // and each (tile, partition) is one workgroup, which leaves per-row partials for the
+  // partition merge (the layout of DecodeArgs with the query tokens as the batch).
+  int32_t nparts;     // partitions per query tile (1 = write out directly)
+  int32_t part_keys;  // keys per partition
+  float* ws_acc;      // [T][Hq][nparts][D] (split only)
+  float* ws_ml;       // [T][Hq][nparts][2] (split only)
 };
 
 // Arguments of one rotary-embedding + KV-write launch, already validated.
@@ -103,6 +110,9 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_mfma_hw(const DecodeArgs& a, hipStream_t stream);
 
 hipError_t launch_decode_reduce(const DecodeArgs& a, hipStream_t stream);
+// The merge of the multi-query key split: rows are (token, query head); rows marked done are
+// skipped and empty partitions' outputs are not read.
+hipError_t launch_prefill_merge(const DecodeArgs& a, hipStream_t stream);
 
 bool supported_prefill(int head_dim, int group, int block_size);
 int prefill_rows_per_wave(int64_t num_tokens, int num_kv_heads, int head_dim, int group, int cus);

@@ -14,6 +14,15 @@
 // (the most keys under the causal mask) is dispatched first: a longest-job-first order for the
 // uneven causal work.
 //
+// Key split: when a batch has too few query tiles to fill the device and some contexts are
+// long (a short chunk appended to a long cached prefix), one tile's keys would be a long serial
+// chain for a few workgroups. The keys are then cut into partitions of part_keys and each
+// (tile, partition) is a workgroup of its own, which leaves each row's partial (unnormalised
+// output, reference max, sum) for the partition merge of the decode path, with the query
+// tokens in place of the batch. A partition past a tile's keys marks its rows as empty; a
+// tile whose keys fit in one partition is written out directly and its rows marked done, so
+// the merge (in the form that skips done rows and empty partitions) does not touch them.
+//
 // The four waves read the same keys. Each 32-key pair (both 16-token blocks, K and V) is
 // brought from memory once per workgroup: every thread loads 16-byte pieces into registers,
 // which are written to one of two LDS buffers while the waves compute on the other; one
@@ -171,10 +180,13 @@ prefill_mfma_kernel(const PrefillArgs a) {
   const int Hkv = a.num_kv_heads;
   const int G = Hq / Hkv;
   const int R = 16 / G;  // query tokens per N block
-  // Tiles counted from the end of each sequence, tile index slowest (see the top of the file).
+  // Tiles counted from the end of each sequence, tile index slowest (see the top of the file),
+  // then the key partition, then (sequence, KV head).
   const int unit = blockIdx.x;
-  const int bg = unit % (a.batch * Hkv);
-  const int tile = unit / (a.batch * Hkv);
+  const int nbg = a.batch * Hkv;
+  const int bg = unit % nbg;
+  const int part = (unit / nbg) % a.nparts;
+  const int tile = unit / (nbg * a.nparts);
   const int g = bg % Hkv;
   const int b = bg / Hkv;
 
@@ -207,6 +219,9 @@ prefill_mfma_kernel(const PrefillArgs a) {
   const int tok1 = wg_p_max + 1 > 0 ? wg_p_max + 1 : 0;
   const int nblk = (tok1 + 15) / 16;
   const int np = (nblk + 1) / 2;
+  // Key split: this workgroup takes pairs [pair_lo, pair_hi) of the tile's np pairs.
+  const int pair_lo = part * (a.part_keys / kPairRows);
+  const int pair_hi = min(pair_lo + a.part_keys / kPairRows, np);
 
   uint4 qb[NB][NCH];
 #pragma unroll
@@ -234,23 +249,41 @@ prefill_mfma_kernel(const PrefillArgs a) {
   const size_t row_stride = (size_t)Hkv * D;
   const size_t head_off = (size_t)g * D;
   const float sl2 = a.scale_log2;
+  const int nparts = a.nparts;
+  // With a key split, a tile whose keys fit in one partition is not split: partition 0 writes
+  // its rows out directly and marks them done for the merge, the other partitions have nothing
+  // to do. A split tile's partitions past its keys mark their rows as having no keys, so the
+  // merge never reads their partial outputs. (Uniform over the workgroup, before any barrier.)
+  const bool tile_split = nparts > 1 && np > a.part_keys / kPairRows;
+  if (nparts > 1 && !tile_split && part != 0) return;
+  if (tile_split && pair_lo >= np) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+      if (row_ok[nb] && kg == 0) {
+        const size_t pr = ((size_t)(q0 + tok[nb]) * Hq + (size_t)g * G + head) * nparts + part;
+        a.ws_ml[pr * 2 + 0] = kNegInf;
+        a.ws_ml[pr * 2 + 1] = 0.f;
+      }
+    return;
+  }
 
-  if (np > 0) {
+  if (pair_lo < pair_hi) {
     Stager<D> s;
     s.init(wave, row_stride, head_off);
-    s.load(a, table, nblk, tok1, row_stride, 0);
+    s.load(a, table, nblk, tok1, row_stride, pair_lo);
     s.commit(buf[0]);
     __syncthreads();
-    for (int k = 0; k < np; ++k) {
-      const bool more = k + 1 < np;  // uniform
+    for (int k = pair_lo; k < pair_hi; ++k) {
+      const bool more = k + 1 < pair_hi;  // uniform
+      const int cur = (k - pair_lo) & 1;
       if (more) s.load(a, table, nblk, tok1, row_stride, k + 1);
       const int key0 = 32 * k;
       if (wave_rows && key0 <= p_max) {
         uint4 ka[NCH], kb[NCH], vt[EPL];
-        read_pair<D>(ka, kb, vt, buf[k & 1], n16, kg);
+        read_pair<D>(ka, kb, vt, buf[cur], n16, kg);
         pair_compute_rows<KT>(ka, kb, vt, st, qb, sl2, kg, row_pos, key0, key0 + 31 > p_min);
       }
-      if (more) s.commit(buf[(k + 1) & 1]);
+      if (more) s.commit(buf[cur ^ 1]);
       __syncthreads();
     }
   }
@@ -259,15 +292,34 @@ prefill_mfma_kernel(const PrefillArgs a) {
   for (int nb = 0; nb < NB; ++nb) {
     float l_run = st[nb].l_run;
     l_run = row4_sum(l_run);
-    if (row_ok[nb]) {
+    if (!row_ok[nb]) continue;
+    const size_t row = (size_t)(q0 + tok[nb]) * Hq + (size_t)g * G + head;
+    if (!tile_split) {
       const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-      const size_t o = ((size_t)(q0 + tok[nb]) * Hq + (size_t)g * G + head) * D;
+      const size_t o = row * D;
       // acc[e][i] is output column 16e + 4kg + i
 #pragma unroll
       for (int e = 0; e < EPL; ++e)
         store_out4<OT>(a.out, o + 16 * e + 4 * kg, st[nb].acc[e][0] * inv,
                        st[nb].acc[e][1] * inv, st[nb].acc[e][2] * inv,
                        st[nb].acc[e][3] * inv);
+      if (nparts > 1 && kg == 0) {  // done: the merge leaves this row alone
+        a.ws_ml[row * nparts * 2 + 0] = kNegInf;
+        a.ws_ml[row * nparts * 2 + 1] = -1.f;
+      }
+    } else {
+      // This partition's partial for the merge: unnormalised output, reference max and sum
+      // (a row whose position lies before the partition saw no keys: -inf and 0).
+      const size_t pr = row * nparts + part;
+      float* o = a.ws_acc + pr * D;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e)
+        *reinterpret_cast<float4*>(o + 16 * e + 4 * kg) =
+            make_float4(st[nb].acc[e][0], st[nb].acc[e][1], st[nb].acc[e][2], st[nb].acc[e][3]);
+      if (kg == 0) {
+        a.ws_ml[pr * 2 + 0] = st[nb].m_run;
+        a.ws_ml[pr * 2 + 1] = l_run;
+      }
     }
   }
 }
@@ -344,7 +396,8 @@ static hipError_t launch_prefill_d(const PrefillArgs& a, unsigned grid, hipStrea
 }
 
 hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t stream) {
-  const unsigned units = (unsigned)((long long)a.batch * a.num_kv_heads * a.ntiles);
+  const unsigned units =
+      (unsigned)((long long)a.batch * a.num_kv_heads * a.ntiles * a.nparts);
   return with_formats(a.kv_dtype, a.out_dtype, [&](auto kt, auto ot) {
     constexpr int KT = decltype(kt)::value, OT = decltype(ot)::value;
     if (a.head_dim == 128) return launch_prefill_d<128, KT, OT>(a, units, stream);

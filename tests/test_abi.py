@@ -34,7 +34,8 @@ def test_header_declares_the_entry_points():
                  "paged_decode_attention_typed", "paged_prefill_attention",
                  "paged_prefill_attention_ex", "paged_kv_write_rope", "paged_decode_step", "paged_decode_step_rope",
                  "paged_decode_workspace_bytes", "paged_kv_status_string", "paged_kv_abi_version",
-                 "paged_kv_last_error", "paged_decode_plan"):
+                 "paged_kv_last_error", "paged_decode_plan", "paged_prefill_attention_split",
+                 "paged_prefill_workspace_bytes", "paged_prefill_plan"):
         assert want in names
 
 
@@ -48,7 +49,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.paged_kv_abi_version() == 3
+    assert lib.paged_kv_abi_version() == 4
     assert lib.paged_kv_status_string(OK) == b"PAGEDKV_OK"
     assert lib.paged_kv_status_string(ERR_WORKSPACE) == b"PAGEDKV_ERR_WORKSPACE"
     assert lib.paged_kv_status_string(99) == b"PAGEDKV_UNKNOWN_STATUS"
@@ -149,6 +150,36 @@ def test_prefill_argument_errors(lib):
     assert _prefill(lib, cu=None) == ERR_NULL
     assert _prefill(lib, out=FAKE + 4) == ERR_ALIGN
     assert _prefill(lib, T=0, q=None, out=None) == OK  # no query rows: no-op
+
+
+def _prefill_split(lib, ws=None, ws_bytes=0, part=0, T=8, maxq=4, MB=8, q=FAKE, rb=0):
+    return lib.paged_prefill_attention_split(q, FAKE, T, maxq, FAKE, FAKE, FAKE, MB, FAKE, 2, 32,
+                                             8, 128, 16, 64, 0.1, BF16, FAKE, F32, rb, ws,
+                                             ws_bytes, part, None)
+
+
+def test_prefill_split_argument_errors(lib):
+    assert _prefill_split(lib, part=-2) == ERR_SHAPE
+    assert _prefill_split(lib, part=48) == ERR_SHAPE       # not a multiple of 32 keys
+    assert _prefill_split(lib, rb=3) == ERR_SHAPE
+    assert _prefill_split(lib, q=None) == ERR_NULL
+    assert _prefill_split(lib, T=0, q=None) == OK           # no query rows: no-op
+
+
+def test_prefill_workspace_bytes(lib):
+    f = lib.paged_prefill_workspace_bytes
+    assert f(100, 24, 128, 256, 16, -1) == 0                # never split
+    assert f(100, 24, 128, 128, 16, 0) == 0                 # 2048 keys: auto never splits
+    # auto over 4096 keys: at most 4 partitions of 1024 keys
+    acc = 100 * 24 * 4 * 128 * 4
+    ml = 100 * 24 * 4 * 2 * 4
+    r = lambda x: (x + 255) // 256 * 256
+    assert f(100, 24, 128, 256, 16, 0) == r(acc) + r(ml)
+    assert f(100, 24, 128, 256, 16, 1024) == r(acc) + r(ml)
+    # forced 512-key partitions: 8 of them
+    assert f(100, 24, 128, 256, 16, 512) == r(2 * acc) + r(2 * ml)
+    assert f(100, 24, 128, 256, 16, 48) == 0                # not a multiple of 32
+    assert f(0, 24, 128, 256, 16, 0) == 0
 
 
 def test_workspace_bytes(lib):

@@ -500,12 +500,13 @@ def prefill_case(name, dev, poison=False, rows=None):
     return _PCASES[key]
 
 
-def run_prefill(d, row_blocks=0):
+def run_prefill(d, row_blocks=0, partition=0, workspace=None):
     T, Hq, D = d["q"].shape
     out = torch.full((T, Hq, D), float("nan"), dtype=torch.float32, device=d["q"].device)
     pk.paged_prefill_attention(d["q"], d["cu_seqlens_q"], d["k_cache"], d["v_cache"],
                                d["block_tables"], d["context_lens"], d["scale"], out,
-                               max_q_len=d["max_q_len"], row_blocks=row_blocks)
+                               max_q_len=d["max_q_len"], row_blocks=row_blocks,
+                               partition_tokens=partition, workspace=workspace)
     return out
 
 
@@ -520,19 +521,68 @@ def test_prefill_parity(dev, name, row_blocks):
     assert err <= ATOL, err
 
 
-@pytest.mark.parametrize("row_blocks", [1, 2, 4])
-def test_prefill_first_position_returns_value_row_exactly(dev, row_blocks):
+@pytest.mark.parametrize("row_blocks,partition", [(1, 0), (2, 0), (4, 0), (1, 32), (2, 512)])
+def test_prefill_first_position_returns_value_row_exactly(dev, row_blocks, partition):
     """In a full prefill the row at position 0 sees only key 0, so its output is that value row
-    exactly (one weight of exactly 1), for every query head of the group."""
+    exactly (one weight of exactly 1), for every query head of the group; with the keys split,
+    the merge of that one partial with empty partitions keeps it exact."""
     _, d = prefill_case("p3", dev)
     w = wl.PREFILL_WORKLOADS["p3"]
-    out = run_prefill(d, row_blocks)
+    out = run_prefill(d, row_blocks, partition)
     G = w.num_q_heads // w.num_kv_heads
     cu = d["cu_seqlens_q"].tolist()
     for b in range(w.batch):
         blk0 = int(d["block_tables"][b, 0])
         v0 = d["v_cache"][blk0, 0].float().repeat_interleave(G, dim=0)  # [Hq, D]
         assert torch.equal(out[cu[b]], v0), (b, row_blocks)
+
+
+@pytest.mark.parametrize("partition", [0, -1, 32, 96, 512, 1024])
+@pytest.mark.parametrize("row_blocks", [1, 2])
+@pytest.mark.parametrize("name", ["p2", "p3"])
+def test_prefill_key_split_parity(dev, name, row_blocks, partition):
+    """Key partitions of 32 keys (one staged pair) up to 1024, the automatic choice and no
+    split: every output against the oracle, and the split within fp32 rounding of the unsplit
+    call."""
+    ref, d = prefill_case(name, dev)
+    out = run_prefill(d, row_blocks, partition)
+    base = run_prefill(d, row_blocks, -1)
+    plan = pk.prefill_plan(d["q"].shape[0], d["max_q_len"], d["context_lens"].shape[0],
+                           d["q"].shape[1], d["k_cache"].shape[2], d["q"].shape[2],
+                           d["block_tables"].shape[1], d["k_cache"].shape[1], row_blocks,
+                           partition)
+    err = np.abs(out.cpu().double().numpy() - ref).max()
+    record(f"{name}/prefill_split/rb{row_blocks}/p{partition}/n{plan[1]}", err)
+    assert torch.isfinite(out).all()
+    assert err <= ATOL, err
+    assert (out - base).abs().max().item() <= 1e-5
+    if partition == -1:
+        assert plan[1] == 1
+    if partition == 32:
+        assert plan[1] > 1
+
+
+def test_prefill_key_split_ignores_workspace_contents(dev):
+    """Every (row, partition) slot the merge reads is written by the call: a workspace full of
+    NaN gives the same result as a fresh one, twice in a row."""
+    _, d = prefill_case("p2", dev)
+    T, Hq, D = d["q"].shape
+    need = pk.prefill_workspace_bytes(T, Hq, D, d["block_tables"].shape[1], d["k_cache"].shape[1],
+                                      64)
+    ws = torch.full((need // 4,), float("nan"), dtype=torch.float32, device=dev).view(torch.uint8)
+    first = run_prefill(d, 1, 64, workspace=ws)
+    second = run_prefill(d, 1, 64, workspace=ws)
+    fresh = run_prefill(d, 1, 64, workspace=torch.zeros(need, dtype=torch.uint8, device=dev))
+    assert torch.equal(first, fresh) and torch.equal(second, fresh)
+
+
+def test_prefill_key_split_rejects_a_small_workspace(dev):
+    _, d = prefill_case("p2", dev)
+    T, Hq, D = d["q"].shape
+    need = pk.prefill_workspace_bytes(T, Hq, D, d["block_tables"].shape[1], d["k_cache"].shape[1],
+                                      512)
+    with pytest.raises(pk.PagedKVError):
+        run_prefill(d, 1, 512, workspace=torch.empty(need - 256, dtype=torch.uint8, device=dev))
 
 
 def test_prefill_chunked_sampled(dev):
@@ -542,11 +592,12 @@ def test_prefill_chunked_sampled(dev):
     rows = sorted({(0, 0), (T - 1, w.num_q_heads - 1)} |
                   {(int(rng.integers(T)), int(rng.integers(w.num_q_heads))) for _ in range(40)})
     ref, d = prefill_case("p1", dev, rows=rows)
-    out = run_prefill(d).cpu().double().numpy()
-    assert np.isfinite(out).all()
-    err = max(np.abs(out[r, h] - ref[r, h]).max() for r, h in rows)
-    record("p1/prefill/sampled", err)
-    assert err <= ATOL, err
+    for partition in (0, 1024):
+        out = run_prefill(d, 0, partition).cpu().double().numpy()
+        assert np.isfinite(out).all()
+        err = max(np.abs(out[r, h] - ref[r, h]).max() for r, h in rows)
+        record(f"p1/prefill/sampled/p{partition}", err)
+        assert err <= ATOL, err
 
 
 def test_prefill_poisoned_pool_matches_clean(dev):
@@ -573,11 +624,12 @@ def test_prefill_single_query_matches_decode(dev, name):
     assert np.abs(out.cpu().double().numpy() - ref).max() <= ATOL
 
 
-@pytest.mark.parametrize("row_blocks", [1, 4])
+@pytest.mark.parametrize("row_blocks,partition", [(1, 0), (4, 0), (1, 32), (4, 64)])
 @pytest.mark.parametrize("Hq,Hkv,D", [(24, 8, 64), (16, 16, 128), (32, 2, 128)])
-def test_prefill_group_sizes_and_edges(dev, Hq, Hkv, D, row_blocks):
+def test_prefill_group_sizes_and_edges(dev, Hq, Hkv, D, row_blocks, partition):
     """G = 3, 1 and 16 (5, 16 and 1 query tokens per wave), lengths at block edges, single
-    tokens, full prefills and chunks, on a poisoned pool."""
+    tokens, full prefills and chunks, on a poisoned pool; unsplit and with the keys split into
+    partitions of 32 or 64 (rows before a partition, partitions past a tile's keys)."""
     w = wl.PrefillWorkload("edge", num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, block_size=16,
                            num_blocks=200, max_blocks=80, seed=77,
                            context_lens=(1, 16, 17, 33, 300, 1000),
@@ -590,9 +642,9 @@ def test_prefill_group_sizes_and_edges(dev, Hq, Hkv, D, row_blocks):
                                    host["context_lens"], host["scale"])
     d = to_dev(inp, dev)
     run_write(d)
-    out = run_prefill(d, row_blocks).cpu().double().numpy()
+    out = run_prefill(d, row_blocks, partition).cpu().double().numpy()
     err = np.abs(out - ref).max()
-    record(f"edge_prefill/D{D}/G{Hq // Hkv}/rb{row_blocks}", err)
+    record(f"edge_prefill/D{D}/G{Hq // Hkv}/rb{row_blocks}/p{partition}", err)
     assert np.isfinite(out).all() and err <= ATOL, err
 
 

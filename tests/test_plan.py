@@ -67,3 +67,37 @@ def test_plan_scales_with_the_compute_units(plan, monkeypatch):
     monkeypatch.setenv("PAGEDKV_CU_COUNT", "128")
     # units 512 (x4 > 128): target 8 * 128 = 1024 waves -> n = 2, P = 4096
     assert plan(w) == (2, 4096, "mfma_hw")
+
+
+# Multi-query (prefill) plans, from the rule documented beside make_prefill_plan: split when
+# kv_heads * ceil(num_tokens / tokens per workgroup) < 2 * 2 * CUs and the contexts may exceed
+# 2048 keys, into ceil(max_len / P) partitions, P = max(512, roundup(ceil(max_len / 4), 32)).
+# row_blocks is passed explicitly (its automatic choice asks the device for occupancy).
+#  p1: 8 kv heads * ceil(4096 / 32) = 1024 workgroups, not < 1024: no split
+#  p2: 8 * ceil(1438 / 20) = 576 < 1024 and 4096 keys: P = 1024, 4 partitions
+#  p3: 2048 keys: never split automatically
+PREFILL_EXPECTED = {"p1": (2, 1, 4096), "p2": (1, 4, 1024), "p3": (1, 1, 2048)}
+
+
+def _prefill_plan(w, row_blocks, partition=0):
+    return _binding.prefill_plan(sum(w.query_lens), max(w.query_lens), len(w.context_lens),
+                                 w.num_q_heads, w.num_kv_heads, w.head_dim, w.max_blocks,
+                                 w.block_size, row_blocks, partition)
+
+
+@pytest.mark.parametrize("name", sorted(PREFILL_EXPECTED))
+def test_prefill_plan_of_each_workload(plan, name):
+    exp = PREFILL_EXPECTED[name]
+    assert _prefill_plan(wl.PREFILL_WORKLOADS[name], exp[0]) == exp
+
+
+def test_prefill_plan_forced_and_scaled(plan, monkeypatch):
+    w = wl.PREFILL_WORKLOADS["p2"]
+    assert _prefill_plan(w, 1, 512) == (1, 8, 512)
+    assert _prefill_plan(w, 1, -1) == (1, 1, 4096)
+    assert _prefill_plan(w, 1, 8192) == (1, 1, 4096 // 32 * 32)   # one partition: no split
+    with pytest.raises(_binding.PagedKVError):
+        _prefill_plan(w, 1, 48)                                    # not a multiple of 32
+    # four times the compute units: p1's 1024 workgroups no longer fill two rounds
+    monkeypatch.setenv("PAGEDKV_CU_COUNT", "1024")
+    assert _prefill_plan(wl.PREFILL_WORKLOADS["p1"], 2) == (2, 4, 1024)
