@@ -119,7 +119,7 @@ decode_mfma_kernel(const DecodeArgs a) {
   const int Hq = a.num_q_heads;
   const int G = Hq / Hkv;
   const int unit = blockIdx.x;
-  const int part = unit % nparts;
+  const int part = xcd_balanced_part(unit, nparts);
   const int g = (unit / nparts) % Hkv;
   const int b = unit / (nparts * Hkv);
 
@@ -281,7 +281,7 @@ decode_mfma_hw_kernel(const DecodeArgs a) {
   const int G = Hq / Hkv;
   const int ngrp = (Hkv + HPW - 1) / HPW;
   const int unit = blockIdx.x;
-  const int part = unit % nparts;
+  const int part = xcd_balanced_part(unit, nparts);
   const int hg = (unit / nparts) % ngrp;
   const int b = unit / (nparts * ngrp);
   const int g = hg * HPW + wave;

@@ -43,7 +43,7 @@ decode_valu_kernel(const DecodeArgs a) {
   const int nparts = a.nparts;
   const int Hkv = a.num_kv_heads;
   const int unit = blockIdx.x;
-  const int part = unit % nparts;
+  const int part = xcd_balanced_part(unit, nparts);
   const int g = (unit / nparts) % Hkv;
   const int b = unit / (nparts * Hkv);
   const int Hq = a.num_q_heads;

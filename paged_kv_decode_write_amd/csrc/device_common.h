@@ -141,6 +141,23 @@ __device__ __forceinline__ float row4_sum(float v) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// Partition index of a decode work unit. Units are numbered row-major with the partition
+// fastest (row = unit / nparts), and the hardware deals workgroups to the 8 XCDs round-robin by
+// block index, so with nparts sharing a factor with 8 the partition index would be tied to the
+// XCD (with nparts = 8, partition p of every row on XCD p). In a ragged batch early partitions
+// carry far more work than late ones, which are empty for short contexts, and the XCDs that
+// drew the early ones would bound the time. Rotating each row's partitions by row / m, with
+// m = 8 / gcd(nparts, 8), lands every partition index on each XCD equally often across rows.
+// A permutation of the partitions within each row.
+constexpr int kXcds = 8;
+__device__ __forceinline__ int xcd_balanced_part(int unit, int nparts) {
+  const int row = unit / nparts;
+  const int slot = unit - row * nparts;
+  const int low = nparts & -nparts;  // the largest power of two dividing nparts
+  const int m = kXcds / (low < kXcds ? low : kXcds);
+  return (slot + row / m) % nparts;
+}
+
 // A partition that starts past its sequence's context (only in a split launch: partition 0
 // never exits early) marks its G query rows as holding no keys, max -inf and sum 0, which is
 // all the merge reads of it. Thread i < G of the exiting unit marks row i of KV head g.
