@@ -470,50 +470,4 @@ __device__ __forceinline__ void pair_compute(PairTile<NCH, EPL>& t, WaveState<EP
   }
 }
 
-// Several N blocks of 16 query rows against one pair of key blocks (multi-query kernels),
-// from operands already in registers: the K rows of both blocks as the A operand of q.K, and
-// vt[e], the V^T operand of output-column group e. Every (pair, block) shares them, so one
-// pass over the keys feeds 16*NB rows. Block nb's rows sit at positions row_pos[nb] (per
-// lane); keys after a row's position get weight 0 when `active` (uniform) says some key of
-// the pair lies after the earliest row. No key of the pair is stale (the caller zeroes those
-// and the causal mask covers them).
-template <int KT, int NCH, int EPL, int NB>
-__device__ __forceinline__ void pair_compute_rows(const uint4 (&ka)[NCH], const uint4 (&kb)[NCH],
-                                                  const uint4 (&vt)[EPL],
-                                                  WaveState<EPL> (&st)[NB],
-                                                  const uint4 (&qb)[NB][NCH], float sl2, int kg,
-                                                  const int (&row_pos)[NB], int key0,
-                                                  bool active) {
-  constexpr int BS = 16;
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    floatx4 sA = {0.f, 0.f, 0.f, 0.f}, sB = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ch = 0; ch < NCH; ++ch) {
-      sA = mfma16x16x32<KT>(ka[ch], qb[nb][ch], sA);
-      sB = mfma16x16x32<KT>(kb[ch], qb[nb][ch], sB);
-    }
-    float s[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      s[i] = sA[i] * sl2;
-      s[4 + i] = sB[i] * sl2;
-    }
-    if (active) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        s[i] = key0 + 4 * kg + i <= row_pos[nb] ? s[i] : kNegInf;
-        s[4 + i] = key0 + BS + 4 * kg + i <= row_pos[nb] ? s[4 + i] : kNegInf;
-      }
-    }
-    uint4 phi, plo;
-    softmax_step<KT>(st[nb], s, phi, plo);
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-      st[nb].acc[e] = mfma16x16x32<KT>(vt[e], phi, st[nb].acc[e]);
-      st[nb].acc[e] = mfma16x16x32<KT>(vt[e], plo, st[nb].acc[e]);
-    }
-  }
-}
-
 }  // namespace pagedkv

@@ -163,6 +163,97 @@ __device__ __forceinline__ void read_pair(uint4 (&ka)[NCH], uint4 (&kb)[NCH], ui
 
 }  // namespace
 
+// Several N blocks of 16 query rows against one pair of key blocks, from operands already in
+// registers: the K rows of both blocks as the A operand of q.K, and vt[e], the V^T operand of
+// output-column group e. Every (pair, block) shares them, so one pass over the keys feeds
+// 16*NB rows. Block nb's rows sit at positions row_pos[nb] (per lane); keys after a row's
+// position get weight 0 when `active` (uniform) says some key of the pair lies after the
+// earliest row. No key of the pair is stale (the caller zeroes those and the causal mask
+// covers them).
+//
+// The online-softmax update is the decode one (softmax_step), regrouped over the blocks: every
+// block's q.K^T first, then the maxima, then one rescaling branch for all blocks (a block whose
+// maximum did not move multiplies by exactly 1, so the results are those of one update per
+// block), then each block's weights and P.V. With no branch between one block's products and
+// the next block's exponentials, the compiler can issue the vector work of block nb + 1 while
+// the matrix products of block nb run.
+template <int KT, int NCH, int EPL, int NB>
+__device__ __forceinline__ void pair_compute_rows(const uint4 (&ka)[NCH], const uint4 (&kb)[NCH],
+                                                  const uint4 (&vt)[EPL],
+                                                  WaveState<EPL> (&st)[NB],
+                                                  const uint4 (&qb)[NB][NCH], float sl2, int kg,
+                                                  const int (&row_pos)[NB], int key0,
+                                                  bool active) {
+  constexpr int BS = 16;
+  floatx4 sA[NB], sB[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    sA[nb] = floatx4{0.f, 0.f, 0.f, 0.f};
+    sB[nb] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ch = 0; ch < NCH; ++ch) {
+      sA[nb] = mfma16x16x32<KT>(ka[ch], qb[nb][ch], sA[nb]);
+      sB[nb] = mfma16x16x32<KT>(kb[ch], qb[nb][ch], sB[nb]);
+    }
+  }
+  float s[NB][8];
+  float mn[NB];
+  bool upd[NB];
+  bool any_upd = false;
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      s[nb][i] = sA[nb][i] * sl2;
+      s[nb][4 + i] = sB[nb][i] * sl2;
+    }
+    if (active) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        s[nb][i] = key0 + 4 * kg + i <= row_pos[nb] ? s[nb][i] : kNegInf;
+        s[nb][4 + i] = key0 + BS + 4 * kg + i <= row_pos[nb] ? s[nb][4 + i] : kNegInf;
+      }
+    }
+    float mx = s[nb][0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) mx = fmaxf(mx, s[nb][i]);
+    mx = row4_max(mx);
+    mn[nb] = fmaxf(st[nb].m_run, mx);
+    upd[nb] = mn[nb] > st[nb].m_run + kRescaleSlack;  // also true while m_run is -inf
+    any_upd = any_upd || upd[nb];
+  }
+  if (__any(any_upd)) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const float m_new = upd[nb] ? mn[nb] : st[nb].m_run;
+      const float alpha =
+          upd[nb] ? fast_exp2(st[nb].m_run - (m_new == kNegInf ? 0.f : m_new)) : 1.f;
+      st[nb].l_run *= alpha;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) st[nb].acc[e] *= alpha;
+      st[nb].m_run = m_new;
+    }
+  }
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const float mu = (st[nb].m_run == kNegInf ? 0.f : st[nb].m_run) - kWeightLift<KT>;
+    float pw[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) pw[i] = fast_exp2(s[nb][i] - mu);
+    float psum = pw[0];  // the same bits as 0 + pw[0] (weights are >= 0), one add fewer
+#pragma unroll
+    for (int i = 1; i < 8; ++i) psum += pw[i];
+    st[nb].l_run += psum;
+    uint4 phi, plo;
+    split_weights<KT>(pw, phi, plo);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      st[nb].acc[e] = mfma16x16x32<KT>(vt[e], phi, st[nb].acc[e]);
+      st[nb].acc[e] = mfma16x16x32<KT>(vt[e], plo, st[nb].acc[e]);
+    }
+  }
+}
+
 template <int D, int NW, int NB, int MINW, int KT, int OT>
 __global__ void __launch_bounds__(NW * 64, MINW)
 prefill_mfma_kernel(const PrefillArgs a) {
