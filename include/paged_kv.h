@@ -133,9 +133,10 @@ int paged_kv_write_rope(const uint16_t* q, const uint16_t* k, const uint16_t* v,
 
 /*
  * paged_decode_workspace_bytes -- bytes of device workspace paged_decode_attention needs
- * for these sizes (0 when the call never splits a sequence). `partition_tokens` has the
- * same meaning as in paged_decode_attention; for 0 (automatic) the bound covers every
- * partition size the automatic choice can make.
+ * for these sizes (0 when the call never splits a sequence and block_size is 16): the split
+ * partials, then, for blocks larger than 16 tokens, the table of 16-token block ids.
+ * `partition_tokens` has the same meaning as in paged_decode_attention; for 0 (automatic)
+ * the bound covers every partition size the automatic choice can make.
  */
 size_t paged_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t head_dim,
                                     int32_t max_blocks_per_seq, int32_t block_size,
@@ -166,8 +167,12 @@ size_t paged_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t 
  *                  split a sequence; > 0: split each sequence into partitions of this many
  *                  tokens (a multiple of block_size) whose partial softmax results are
  *                  merged by a log-sum-exp reduction.
- * Supported: head_dim in {64, 128}; block_size 16; num_q_heads / num_kv_heads in
- * {1, 2, 3, 4, 8} (other ratios up to 16 with the matrix-core kernel).
+ * Supported: head_dim in {64, 128}; block_size a multiple of 16 up to 1024 (other sizes:
+ * PAGEDKV_ERR_UNSUPPORTED); num_q_heads / num_kv_heads in {1, 2, 3, 4, 8} (other ratios up
+ * to 16 with the matrix-core kernel). The kernels read 16-token blocks: a pool of larger
+ * blocks is read as the same memory cut into 16-token blocks, through a table of their ids
+ * (batch x max_blocks_per_seq x block_size/16 int32) that one small extra launch writes into
+ * the workspace, after the split partials. num_blocks * block_size / 16 must fit in int32.
  * Accuracy: scores, softmax statistics and sums in fp32; the attention weights enter the
  * matrix product with V as a bf16 hi + lo pair (about 16 significant bits). Measured
  * |out - exact| stays below 5e-5 on the test workloads (logits of std up to 3); the tests

@@ -146,6 +146,27 @@ size_t split_workspace_bytes(int64_t B, int64_t Hq, int64_t D, int64_t n) {
   return acc_bytes(B, Hq, D, n) + (size_t)round_up(B * Hq * n * 2 * 4, 256);
 }
 
+// Blocks larger than 16 tokens. The decode kernels are built for 16-token blocks; a pool of
+// blocks of 16 * sub tokens is the same memory as a pool of 16-token blocks (block p is
+// 16-token blocks sub * p .. sub * p + sub - 1, and slot numbers name the same rows), so a
+// call with larger blocks attends over that view, through a table of 16-token block ids that
+// one small launch writes into the workspace, after the split region.
+constexpr int32_t kKernelBlock = 16;
+constexpr int32_t kMaxDecodeBlock = 1024;
+
+int decode_block_view(int32_t block_size, int32_t* sub) {
+  if (block_size % kKernelBlock || block_size > kMaxDecodeBlock)
+    return fail(PAGEDKV_ERR_UNSUPPORTED,
+                "block_size %d: decode attention takes a multiple of 16 up to %d", block_size,
+                (int)kMaxDecodeBlock);
+  *sub = block_size / kKernelBlock;
+  return PAGEDKV_OK;
+}
+
+size_t view_table_bytes(int64_t batch, int64_t max_blocks, int32_t sub) {
+  return sub > 1 ? (size_t)round_up(batch * max_blocks * sub * 4, 256) : 0;
+}
+
 // Key split of the multi-query kernel. It pays when the batch's query tiles are too few to
 // fill the device and contexts are long: one tile's keys are then a long serial chain that a
 // few workgroups walk while the rest of the device idles. The automatic choice splits when the
@@ -326,10 +347,20 @@ int decode_impl(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_ca
   st = check_decode_sizes(max_blocks_per_seq, batch, num_q_heads, num_kv_heads, head_dim,
                           block_size, num_blocks);
   if (st) return st;
+  int32_t sub = 1;
+  st = decode_block_view(block_size, &sub);
+  if (st) return st;
+  if (sub > 1 && partition_tokens > 0 && partition_tokens % block_size)
+    return fail(PAGEDKV_ERR_SHAPE, "partition_tokens %d is not a multiple of block_size %d",
+                partition_tokens, block_size);
+  if (num_blocks > (int64_t)INT32_MAX / sub)
+    return fail(PAGEDKV_ERR_SHAPE, "num_blocks * block_size / 16 exceeds int32");
+  // From here on, sizes are those of the 16-token view.
+  const int32_t mb16 = max_blocks_per_seq * sub;
+  const int64_t nb16 = num_blocks * sub;
   const int G = num_q_heads / num_kv_heads;
   int chosen = 0;
-  st = select_kernel(kernel, head_dim, G, block_size, (int64_t)max_blocks_per_seq * block_size,
-                     &chosen);
+  st = select_kernel(kernel, head_dim, G, kKernelBlock, (int64_t)mb16 * kKernelBlock, &chosen);
   if (st) return st;
   if (batch == 0) return PAGEDKV_OK;
   if (!q || !k_cache || !v_cache || !context_lens || !out ||
@@ -362,8 +393,8 @@ int decode_impl(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_ca
   st = cu_count(&cus);
   if (st) return st;
   Plan plan{};
-  st = make_plan(batch, num_kv_heads, max_blocks_per_seq, block_size, partition_tokens, cus,
-                 chosen, plan_granule(chosen, block_size), &plan);
+  st = make_plan(batch, num_kv_heads, mb16, kKernelBlock, partition_tokens, cus, chosen,
+                 plan_granule(chosen, kKernelBlock), &plan);
   if (st) return st;
 
   DecodeArgs a{};
@@ -373,25 +404,29 @@ int decode_impl(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_ca
   a.block_tables = block_tables;
   a.context_lens = context_lens;
   a.out = out;
-  a.max_blocks = max_blocks_per_seq;
+  a.max_blocks = mb16;
   a.batch = batch;
   a.num_q_heads = num_q_heads;
   a.num_kv_heads = num_kv_heads;
   a.head_dim = head_dim;
-  a.block_size = block_size;
-  a.num_blocks = num_blocks;
+  a.block_size = kKernelBlock;
+  a.num_blocks = nb16;
   a.scale_log2 = scale * kLog2eHost;
   a.nparts = plan.nparts;
   a.part_tokens = plan.part_tokens;
   a.kv_dtype = kv_dtype;
   a.out_dtype = out_dtype;
-  if (plan.nparts > 1) {
-    const size_t need = split_workspace_bytes(batch, num_q_heads, head_dim, plan.nparts);
+  const size_t split_need = split_workspace_bytes(batch, num_q_heads, head_dim, plan.nparts);
+  const size_t table_need = view_table_bytes(batch, max_blocks_per_seq, sub);
+  if (split_need + table_need > 0) {
+    const size_t need = split_need + table_need;
     if (!workspace || workspace_bytes < need)
       return fail(PAGEDKV_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
                   workspace ? workspace_bytes : (size_t)0);
     if (!aligned(workspace, 16)) return fail(PAGEDKV_ERR_ALIGN, "workspace needs 16-byte alignment");
-    char* base = static_cast<char*>(workspace);
+  }
+  char* base = static_cast<char*>(workspace);
+  if (plan.nparts > 1) {
     a.ws_acc = reinterpret_cast<float*>(base);
     a.ws_ml = reinterpret_cast<float*>(base + acc_bytes(batch, num_q_heads, head_dim, plan.nparts));
   }
@@ -434,6 +469,13 @@ int decode_impl(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_ca
     a.inv_freq = sw->inv_freq;
     a.interleaved = sw->interleaved;
     a.q_out = sw->q_out;
+  }
+  if (sub > 1) {
+    int32_t* view = reinterpret_cast<int32_t*>(base + split_need);
+    e = launch_expand_table(block_tables, batch, max_blocks_per_seq, sub, num_blocks, view,
+                            stream);
+    if (e != hipSuccess) return hip_fail(e, "block table view launch");
+    a.block_tables = view;
   }
   if (ev_begin && (e = hipEventRecord(ev_begin, stream)) != hipSuccess)
     return hip_fail(e, "hipEventRecord(begin)");
@@ -556,9 +598,11 @@ size_t paged_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t 
   if (batch <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_blocks_per_seq <= 0 ||
       block_size <= 0)
     return 0;
-  const int64_t n = nparts_bound((int64_t)max_blocks_per_seq * block_size, block_size,
+  const int32_t sub = block_size % kKernelBlock == 0 ? block_size / kKernelBlock : 1;
+  const int64_t n = nparts_bound((int64_t)max_blocks_per_seq * block_size, kKernelBlock,
                                  partition_tokens);
-  return split_workspace_bytes(batch, num_q_heads, head_dim, n);
+  return split_workspace_bytes(batch, num_q_heads, head_dim, n) +
+         view_table_bytes(batch, max_blocks_per_seq, sub);
 }
 
 int paged_decode_plan(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
@@ -571,16 +615,23 @@ int paged_decode_plan(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
   if (st) return st;
   if (!num_partitions || !tokens_per_partition)
     return fail(PAGEDKV_ERR_NULL, "output pointers must be non-NULL");
+  int32_t sub = 1;
+  st = decode_block_view(block_size, &sub);
+  if (st) return st;
+  if (sub > 1 && partition_tokens > 0 && partition_tokens % block_size)
+    return fail(PAGEDKV_ERR_SHAPE, "partition_tokens %d is not a multiple of block_size %d",
+                partition_tokens, block_size);
+  const int32_t mb16 = max_blocks_per_seq * sub;
   int chosen = 0;
-  st = select_kernel(kernel, head_dim, num_q_heads / num_kv_heads, block_size,
-                     (int64_t)max_blocks_per_seq * block_size, &chosen);
+  st = select_kernel(kernel, head_dim, num_q_heads / num_kv_heads, kKernelBlock,
+                     (int64_t)mb16 * kKernelBlock, &chosen);
   if (st) return st;
   int cus = 0;
   st = cu_count(&cus);
   if (st) return st;
   Plan plan{};
-  st = make_plan(batch, num_kv_heads, max_blocks_per_seq, block_size, partition_tokens, cus,
-                 chosen, plan_granule(chosen, block_size), &plan);
+  st = make_plan(batch, num_kv_heads, mb16, kKernelBlock, partition_tokens, cus, chosen,
+                 plan_granule(chosen, kKernelBlock), &plan);
   if (st) return st;
   *num_partitions = plan.nparts;
   *tokens_per_partition = plan.part_tokens;

@@ -121,6 +121,12 @@ hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t stream);
 
 hipError_t launch_kv_write_rope(const RopeArgs& a, hipStream_t stream);
 
+// Writes the 16-token-block view of a table of blocks of 16 * sub tokens: out is
+// [batch][max_blocks * sub]; ids outside [0, num_blocks) become -1.
+hipError_t launch_expand_table(const int32_t* table, int32_t batch, int32_t max_blocks,
+                               int32_t sub, int64_t num_blocks, int32_t* out,
+                               hipStream_t stream);
+
 hipError_t launch_kv_write(const uint16_t* k, const uint16_t* v, const int64_t* slots,
                            int64_t num_tokens, uint16_t* k_cache, uint16_t* v_cache,
                            int64_t num_slots, int32_t row_elems, hipStream_t stream);

@@ -91,6 +91,9 @@ def test_attention_argument_errors(lib):
     assert _attn(lib, NB=0) == ERR_SHAPE
     assert _attn(lib, D=96) == ERR_UNSUPPORTED
     assert _attn(lib, bs=8) == ERR_UNSUPPORTED
+    assert _attn(lib, bs=24) == ERR_UNSUPPORTED      # blocks: multiples of 16 only
+    assert _attn(lib, bs=2048, MB=2) == ERR_UNSUPPORTED
+    assert _attn(lib, bs=32, part=48) == ERR_SHAPE   # partitions: multiples of block_size
     assert _attn(lib, kernel=7) == ERR_UNSUPPORTED
     assert _attn(lib, kernel=1, Hq=40) == ERR_UNSUPPORTED  # G=5 has no VALU build
     assert _attn(lib, q=None) == ERR_NULL
@@ -195,6 +198,11 @@ def test_workspace_bytes(lib):
     assert f(2, 32, 128, 2048, 16, 0) == acc + ml
     assert f(2, 32, 128, 2048, 16, 24) == 0               # not a multiple of block_size
     assert f(0, 32, 128, 2048, 16, 0) == 0
+    # blocks of 32 or 64 tokens: the same split region, then the table of 16-token block ids
+    # (batch x max_blocks x block_size/16 int32, rounded up to 256 bytes)
+    assert f(2, 32, 128, 1024, 32, 256) == acc + ml + 2 * 1024 * 2 * 4
+    assert f(2, 32, 128, 512, 64, 0) == acc + ml + 2 * 512 * 4 * 4
+    assert f(3, 8, 64, 5, 32, -1) == 256                 # 3 x 10 ids, one 256-byte granule
 
 
 def test_binding_rejects_cpu_tensors():
@@ -230,3 +238,13 @@ def test_decode_step_rope_argument_errors(lib):
     assert b"overlap" in lib.paged_kv_last_error()
     assert _step_rope(lib, D=96) == ERR_UNSUPPORTED
     assert _step_rope(lib, B=0, q=None, kn=None, out=None, qo=None) == OK  # empty batch: no-op
+
+
+def test_larger_blocks_need_the_table_workspace(lib, monkeypatch):
+    """A call with blocks of 32 tokens writes its table of 16-token block ids into the
+    workspace, so it needs one even when it does not split; the check comes before any
+    launch."""
+    monkeypatch.setenv("PAGEDKV_CU_COUNT", "256")
+    assert _attn(lib, bs=32, part=-1) == ERR_WORKSPACE
+    assert b"workspace" in lib.paged_kv_last_error()
+

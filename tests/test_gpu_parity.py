@@ -319,6 +319,36 @@ def test_decode_step_fused_matches_oracle_and_separate_calls(dev, name):
             assert torch.equal(out, run_attention(d, kernel, partition)), (kernel, partition)
 
 
+@pytest.mark.parametrize("block_size", [32, 64])
+@pytest.mark.parametrize("name", ["c2", "c4"])
+def test_larger_blocks_match_oracle(dev, name, block_size):
+    """Blocks of 32 and 64 tokens (read as 16-token blocks through a table the call writes
+    into its workspace): on a poisoned pool, the fused step's pools equal the oracle's bit for
+    bit, the output is within the bound for every kernel family and split, and equals the
+    separate attention call on the written pools."""
+    import dataclasses
+    k = block_size // 16
+    base = wl.WORKLOADS[name]
+    w = dataclasses.replace(base, name=f"{name}_bs{block_size}", block_size=block_size,
+                            max_blocks=base.max_blocks // k, num_blocks=base.num_blocks // k)
+    inp = wl.make_inputs(w, poison=True)
+    ref, kc_ref, vc_ref = oracle.decode_step(wl.to_host_numpy(inp))
+    d = to_dev(inp, dev)
+    first = True
+    for kernel in ["auto"] + kernels_for(w):
+        for partition in (-1, 0, 4 * block_size):
+            out = run_step(d, kernel, partition)
+            torch.cuda.synchronize()
+            if first:
+                assert np.array_equal(wl.to_bits(d["k_cache"]), kc_ref)
+                assert np.array_equal(wl.to_bits(d["v_cache"]), vc_ref)
+                first = False
+            err = np.abs(out.cpu().double().numpy() - ref).max()
+            record(f"{w.name}/step/{kernel}/p{partition}", err)
+            assert np.isfinite(err) and err <= ATOL, (kernel, partition, err)
+            assert torch.equal(out, run_attention(d, kernel, partition)), (kernel, partition)
+
+
 def test_decode_step_negative_slots_and_full_size(dev):
     """Sequences whose slot is -1 store nothing and read their last position from the cache;
     c5b at full size matches the separate calls bit for bit."""

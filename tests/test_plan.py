@@ -101,3 +101,18 @@ def test_prefill_plan_forced_and_scaled(plan, monkeypatch):
     # four times the compute units: p1's 1024 workgroups no longer fill two rounds
     monkeypatch.setenv("PAGEDKV_CU_COUNT", "1024")
     assert _prefill_plan(wl.PREFILL_WORKLOADS["p1"], 2) == (2, 4, 1024)
+
+
+@pytest.mark.parametrize("name", ["c2", "c4", "c5b"])
+@pytest.mark.parametrize("block_size", [32, 64])
+def test_larger_blocks_plan_as_their_16_token_view(plan, name, block_size):
+    """Blocks of 16k tokens are attended as 16-token blocks: the plan (kernel, partitions,
+    tokens per partition) is that of the same context length in 16-token blocks."""
+    import dataclasses
+    w = wl.WORKLOADS[name]
+    k = block_size // 16
+    big = dataclasses.replace(w, block_size=block_size, max_blocks=w.max_blocks // k,
+                              num_blocks=w.num_blocks // k)
+    assert plan(big) == plan(w)
+    assert plan(big, -1) == plan(w, -1)
+    assert plan(big, 4 * block_size) == plan(w, 4 * block_size)
