@@ -18,6 +18,7 @@ oracle timed on a bounded sample of the same workload on this host.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import ctypes
 import hashlib
 import re
@@ -71,6 +72,10 @@ def parse_args():
                    help="before every step, read a buffer of this many MiB so no input stays "
                         "in the 256 MB last-level cache (cold-cache timing; the read is inside "
                         "the measured step time, the kernel times exclude it)")
+    p.add_argument("--block-size", type=int, default=16,
+                   help="decode workloads: tokens per cache block (a multiple of 16); the "
+                        "table width and pool shrink by the same factor, so the contexts and "
+                        "the bytes read stay those of the workload")
     p.add_argument("--copy-calibration-mib", type=int, default=0,
                    help="run one plain device-to-device copy of this many MiB before the "
                         "steps (reference dispatch for hardware byte counters)")
@@ -316,6 +321,14 @@ def main():
     subs = []
     for name in names:
         w = wl.WORKLOADS[name]
+        if args.block_size != w.block_size:
+            k = args.block_size // w.block_size
+            if k < 1 or args.block_size % w.block_size or w.max_blocks % k or w.num_blocks % k:
+                print(f"--block-size {args.block_size} does not divide {name}'s table",
+                      file=sys.stderr)
+                sys.exit(2)
+            w = dataclasses.replace(w, block_size=args.block_size, max_blocks=w.max_blocks // k,
+                                    num_blocks=w.num_blocks // k)
         d = wl.make_inputs(w, device="cuda", dtype=args.in_dtype)
         d["out"] = torch.empty(w.batch, w.num_q_heads, w.head_dim,
                                dtype=getattr(torch, OUT_TORCH[args.out_dtype]), device=dev)
@@ -481,6 +494,7 @@ def main():
             "workload": "+".join(d["workload"].description for d in subs),
             "kernel": kernel,
             "partition_tokens": args.partition,
+            "block_size": subs[0]["workload"].block_size,
             "formats": f"{args.in_dtype} in, {args.out_dtype} out",
             "us_per_call": {p["workload"]: p["attn_kernel_us_mean"] for p in per},
             "pct_of_peak": {p["workload"]: p["pct_of_peak"] for p in per},
