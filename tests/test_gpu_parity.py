@@ -27,7 +27,7 @@ SUMMARY = {}
 def dev():
     if not torch.cuda.is_available():
         pytest.skip("no GPU visible")
-    pk.load_library()  # a missing library is an error on a GPU machine, not a skip
+    pk.load_library()  # with a GPU present, a missing library is an error, not a skip
     return torch.device("cuda:0")
 
 
