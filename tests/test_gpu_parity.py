@@ -835,6 +835,46 @@ def test_decode_step_rope_fused_matches_separate_calls_and_oracle(dev, name, int
     assert np.array_equal(wl.to_bits(fused["v_cache"]), vc_ref)
 
 
+def test_decode_step_rope_larger_blocks(dev):
+    """The rotary decode step with 32-token blocks (c4 shape, ragged, poisoned pools): q_out,
+    the pools and the output equal the separate rotation + write and attention calls bit for
+    bit, for every kernel family and split, and the output is within the bound of the
+    oracle's."""
+    import dataclasses
+    base = wl.WORKLOADS["c4"]
+    w = dataclasses.replace(base, name="c4_bs32", block_size=32, max_blocks=base.max_blocks // 2,
+                            num_blocks=base.num_blocks // 2)
+    inp = wl.make_inputs(w, poison=True)
+    host = wl.to_host_numpy(inp)
+    pos_np = (host["context_lens"] - 1).astype(np.int32)
+    inv_np = llama_inv_freq(w.head_dim)
+    q_ref, kc_ref, vc_ref = oracle.kv_write_rope(host["q"], host["k_new"], host["v_new"], pos_np,
+                                                 inv_np, False, host["slot_mapping"],
+                                                 host["k_cache"], host["v_cache"])
+    ref = oracle.decode_attention(q_ref, kc_ref, vc_ref, host["block_tables"],
+                                  host["context_lens"], host["scale"])
+    pos = torch.from_numpy(pos_np).to(dev)
+    inv = torch.from_numpy(inv_np).to(dev)
+    fused = to_dev(inp, dev)
+    sep = to_dev(inp, dev)
+    for kernel in ["auto"] + kernels_for(w):
+        for partition in (-1, 0, 128):
+            q_f, out_f = run_step_rope(fused, pos, inv, False, kernel, partition)
+            q_s, out_s = run_rope_separate(sep, pos, inv, False, kernel, partition)
+            torch.cuda.synchronize()
+            key = (kernel, partition)
+            assert torch.equal(q_f.view(torch.int16), q_s.view(torch.int16)), key
+            assert torch.equal(fused["k_cache"].view(torch.int16),
+                               sep["k_cache"].view(torch.int16)), key
+            assert torch.equal(fused["v_cache"].view(torch.int16),
+                               sep["v_cache"].view(torch.int16)), key
+            assert torch.equal(out_f, out_s), key
+            err = np.abs(out_f.cpu().double().numpy() - ref).max()
+            record(f"c4_bs32/step_rope/{kernel}/p{partition}", err)
+            assert np.isfinite(err) and err <= ATOL, (key, err)
+    assert np.array_equal(wl.to_bits(fused["v_cache"]), vc_ref)
+
+
 def test_decode_step_rope_large_positions_negative_slots_and_full_size(dev):
     """Positions far beyond the context (the sine and cosine of large angles), sequences with
     no slot (nothing stored, their last position read from the cache), and c5b at full size:
