@@ -72,6 +72,9 @@ def parse_args():
                    help="before every step, read a buffer of this many MiB so no input stays "
                         "in the 256 MB last-level cache (cold-cache timing; the read is inside "
                         "the measured step time, the kernel times exclude it)")
+    p.add_argument("--prepared", action="store_true",
+                   help="decode workloads: also time the fused step as prepared calls "
+                        "(checks and argument conversion done once; prepared_ms_per_step)")
     p.add_argument("--block-size", type=int, default=16,
                    help="decode workloads: tokens per cache block (a multiple of 16); the "
                         "table width and pool shrink by the same factor, so the contexts and "
@@ -453,6 +456,35 @@ def main():
         torch.cuda.synchronize()
         graph_ms = (time.perf_counter() - g0) * 1e3 / args.steps
 
+    prepared_ms = plain_ms = None
+    if args.prepared and not args.rope and not args.separate:
+        prepared = [pk.prepare_decode_step(d["q"], d["k_new"], d["v_new"], d["slot_mapping"],
+                                           d["k_cache"], d["v_cache"], d["block_tables"],
+                                           d["context_lens"], d["scale"], d["out"],
+                                           partition_tokens=args.partition, kernel=args.kernel,
+                                           workspace=d["ws"])
+                    for d in subs]
+
+        def prepared_step():
+            if flush is not None:
+                torch.sum(flush)
+            for call in prepared:
+                call()
+
+        def per_step_ms(fn):
+            for _ in range(args.warmup):
+                fn()
+            torch.cuda.synchronize()
+            t = time.perf_counter()
+            for _ in range(args.steps):
+                fn()
+            torch.cuda.synchronize()
+            return (time.perf_counter() - t) * 1e3 / args.steps
+
+        # the same calls through the plain binding, with no timing events, for comparison
+        plain_ms = per_step_ms(step)
+        prepared_ms = per_step_ms(prepared_step)
+
     probe = {}
     if not args.no_read_probe:
         for d in subs:
@@ -519,6 +551,9 @@ def main():
     }
     if graph_ms is not None:
         line["graph_ms_per_step"] = round(graph_ms, 4)
+    if prepared_ms is not None:
+        line["prepared_ms_per_step"] = round(prepared_ms, 4)
+        line["plain_ms_per_step_no_events"] = round(plain_ms, 4)
     if probe:
         # plain streaming read (cold) of the attention's algorithmic bytes: the rate HBM
         # delivers to a simple kernel on this part, beside the 8 TB/s vendor peak

@@ -6,14 +6,16 @@ tensors into pointers and the current stream, and nothing else. The library is l
 first use; if it is missing the call raises, there is no fallback.
 """
 from ._binding import (paged_kv_write, paged_decode_attention, paged_decode_step,
-                       paged_decode_step_rope, paged_prefill_attention,
+                       prepare_decode_step, PreparedDecodeStep, paged_decode_step_rope,
+                       paged_prefill_attention,
                        paged_kv_write_rope,
                        decode_workspace_bytes, decode_plan,
                        prefill_workspace_bytes, prefill_plan,
                        library_path, load_library, abi_version, PagedKVError)
 
 __all__ = ["paged_kv_write", "paged_decode_attention", "paged_decode_step",
-           "paged_decode_step_rope", "paged_prefill_attention",
+           "prepare_decode_step", "PreparedDecodeStep", "paged_decode_step_rope",
+           "paged_prefill_attention",
            "paged_kv_write_rope",
            "decode_workspace_bytes", "decode_plan",
            "prefill_workspace_bytes", "prefill_plan",

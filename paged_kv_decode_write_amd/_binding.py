@@ -362,6 +362,66 @@ def paged_decode_step(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
     return out
 
 
+class PreparedDecodeStep:
+    """paged_decode_step bound once to its tensors, for a serving loop that launches the same
+    step again and again while updating the tensors in place (new q, k_new, v_new, slots,
+    tables and lengths written into the same storage). The checks, the workspace and the
+    argument conversion happen once, here; a call reads the current stream and calls the
+    library. The object holds references to every bound tensor and to a workspace of its own
+    (a shared per-stream workspace could be regrown under it). Calls that may run at the same
+    time must not share one prepared step (they share its workspace and output)."""
+
+    __slots__ = ("_fn", "_args", "_dev_index", "_refs", "out")
+
+    def __init__(self, q, k_new, v_new, slot_mapping, k_cache, v_cache, block_tables,
+                 context_lens, scale, out, *, partition_tokens=0, kernel="auto",
+                 workspace=None):
+        dev, dt, NB, bs, Hkv, D, B, Hq, MB = _check_step(
+            q, k_new, v_new, slot_mapping, k_cache, v_cache, block_tables, context_lens, out,
+            kernel)
+        lib = load_library()
+        need = int(lib.paged_decode_workspace_bytes(B, Hq, D, MB, bs, partition_tokens))
+        if workspace is None:
+            workspace = new_workspace(need, dev) if need else None
+        elif (workspace.device != dev or workspace.dtype != torch.uint8 or
+              workspace.numel() < need):
+            raise ValueError(f"workspace must be a uint8 tensor of >= {need} bytes on the "
+                             "cache's device")
+        P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+        ws = P(workspace.data_ptr()) if need else None
+        wsb = ctypes.c_size_t(workspace.numel() if need else 0)
+        self._args = (
+            P(q.data_ptr()), P(k_new.data_ptr()), P(v_new.data_ptr()), P(slot_mapping.data_ptr()),
+            P(k_cache.data_ptr()), P(v_cache.data_ptr()), P(block_tables.data_ptr()), I32(MB),
+            P(context_lens.data_ptr()), I32(B), I32(Hq), I32(Hkv), I32(D), I32(bs), I64(NB),
+            ctypes.c_float(scale), I32(DTYPES[dt]), P(out.data_ptr()), I32(DTYPES[out.dtype]),
+            ws, wsb, I32(partition_tokens), I32(KERNELS[kernel]), None, None)
+        self._refs = (q, k_new, v_new, slot_mapping, k_cache, v_cache, block_tables,
+                      context_lens, out, workspace)
+        self._fn = lib.paged_decode_step
+        self._dev_index = dev.index
+        self.out = out
+
+    def __call__(self) -> torch.Tensor:
+        idx = self._dev_index
+        if torch.cuda.current_device() != idx:
+            with torch.cuda.device(idx):
+                return self()
+        stream = (_raw_stream(idx) if _raw_stream is not None
+                  else torch.cuda.current_stream(idx).cuda_stream)
+        status = self._fn(*self._args, stream)
+        if status:
+            _check(status)
+        return self.out
+
+
+def prepare_decode_step(q, k_new, v_new, slot_mapping, k_cache, v_cache, block_tables,
+                        context_lens, scale, out, **kw) -> PreparedDecodeStep:
+    """A PreparedDecodeStep for these tensors (arguments as in paged_decode_step)."""
+    return PreparedDecodeStep(q, k_new, v_new, slot_mapping, k_cache, v_cache, block_tables,
+                              context_lens, scale, out, **kw)
+
+
 def paged_decode_step_rope(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
                            positions: torch.Tensor, inv_freq: torch.Tensor,
                            slot_mapping: torch.Tensor, q_out: torch.Tensor,

@@ -36,3 +36,17 @@ def test_non_tensors_are_refused():
     with pytest.raises(TypeError):  # the pools are checked first
         pk.paged_kv_write(bf16(2, 8, 128), bf16(2, 8, 128), torch.zeros(2, dtype=torch.int64),
                           [0], bf16(4, 16, 8, 128))
+
+
+def test_prepared_step_checks_at_preparation():
+    """A prepared decode step runs the same checks as paged_decode_step when it is built."""
+    with pytest.raises(ValueError, match="GPU device"):
+        pk.prepare_decode_step(bf16(2, 32, 128), bf16(2, 8, 128), bf16(2, 8, 128),
+                               torch.zeros(2, dtype=torch.int64), bf16(4, 16, 8, 128),
+                               bf16(4, 16, 8, 128), torch.zeros(2, 4, dtype=torch.int32),
+                               torch.ones(2, dtype=torch.int32), 0.1, torch.zeros(2, 32, 128))
+    with pytest.raises(ValueError, match="must be"):
+        pk.prepare_decode_step(bf16(2, 32, 128), bf16(2, 8, 128), bf16(2, 8, 128),
+                               torch.zeros(2, dtype=torch.int32), bf16(4, 16, 8, 128),
+                               bf16(4, 16, 8, 128), torch.zeros(2, 4, dtype=torch.int32),
+                               torch.ones(2, dtype=torch.int32), 0.1, torch.zeros(2, 32, 128))

@@ -349,6 +349,38 @@ def test_larger_blocks_match_oracle(dev, name, block_size):
             assert torch.equal(out, run_attention(d, kernel, partition)), (kernel, partition)
 
 
+@pytest.mark.parametrize("name", ["c2", "c4"])
+def test_prepared_step_matches_the_plain_call(dev, name):
+    """A prepared decode step re-reads its bound tensors at every call: after new q / k_new /
+    v_new values and lengths are written into them in place, its output and pools equal those
+    of paged_decode_step on identical copies, bit for bit, call after call."""
+    w = wl.WORKLOADS[name]
+    inp = wl.make_inputs(w, poison=True)
+    a = to_dev(inp, dev)
+    b = to_dev(inp, dev)
+    out_a = torch.full((w.batch, w.num_q_heads, w.head_dim), float("nan"), device=dev)
+    step = pk.prepare_decode_step(a["q"], a["k_new"], a["v_new"], a["slot_mapping"],
+                                  a["k_cache"], a["v_cache"], a["block_tables"],
+                                  a["context_lens"], a["scale"], out_a)
+    gen = torch.Generator(device="cpu").manual_seed(7)
+    for it in range(3):
+        if it:
+            for key in ("q", "k_new", "v_new"):
+                new = torch.randn(a[key].shape, generator=gen).to(a[key].dtype).to(dev)
+                a[key].copy_(new)
+                b[key].copy_(new)
+            lens = torch.clamp(a["context_lens"] - it, min=1)
+            a["context_lens"].copy_(lens)
+            b["context_lens"].copy_(lens)
+        got = step()
+        want = run_step(b)
+        torch.cuda.synchronize()
+        assert got.data_ptr() == out_a.data_ptr()
+        assert torch.equal(got, want), it
+        assert torch.equal(a["k_cache"].view(torch.int16), b["k_cache"].view(torch.int16)), it
+        assert torch.equal(a["v_cache"].view(torch.int16), b["v_cache"].view(torch.int16)), it
+
+
 def test_decode_step_negative_slots_and_full_size(dev):
     """Sequences whose slot is -1 store nothing and read their last position from the cache;
     c5b at full size matches the separate calls bit for bit."""
