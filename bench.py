@@ -429,6 +429,7 @@ def main():
             "attn_kernel_us_mean": round(mean * 1e3, 2),
             "attn_kernel_us_median": round(durs[len(durs) // 2] * 1e3, 2),
             "attn_kernel_us_min": round(durs[0] * 1e3, 2),
+            "attn_kernel_us_max": round(durs[-1] * 1e3, 2),
             "attn_bytes": d["bytes"]["attention"],
             "attn_kernel_GBps": round(d["bytes"]["attention"] / (mean * 1e-3) / 1e9, 1),
             "pct_of_peak": round(100 * d["bytes"]["attention"] / (mean * 1e-3) / 1e9
