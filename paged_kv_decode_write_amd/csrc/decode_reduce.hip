@@ -121,52 +121,68 @@ decode_reduce_kernel(const DecodeArgs a) {
   store_out<OT>(a.out, (size_t)row * D + d, den > 0.f ? num / den : 0.f);
 }
 
-// Few partitions (nparts <= NP <= 8): one thread per output element reads the statistics and
-// its column of every partition at once and folds them in partition order; no LDS, no barrier.
-// The statistics are the same few addresses for the D threads of a row.
+// Few partitions (nparts <= NP <= 8): one thread per four consecutive output elements reads
+// the statistics and its four columns of every partition at once (16-byte loads) and folds
+// them in partition order; no LDS, no barrier. The statistics are the same few addresses for
+// the D/4 threads of a row. The sum and the four outputs share one reference max, so the
+// weights 2^(m - ref) and 2^(m_p - ref) are computed once per partition for all five.
 constexpr int kNarrowThreads = 256;
 
 template <int OT, int NP, bool SPARSE>
 __global__ void __launch_bounds__(kNarrowThreads)
 decode_reduce_narrow_kernel(const DecodeArgs a) {
-  const int D = a.head_dim;  // 64 or 128: a workgroup covers kNarrowThreads / D whole rows
-  const size_t row = (size_t)blockIdx.x * (kNarrowThreads / D) + threadIdx.x / D;
-  const int d = threadIdx.x % D;
+  const int D = a.head_dim;  // 64 or 128: a workgroup covers 4 * kNarrowThreads / D rows
+  const int tpr = D / 4;     // threads per row
+  const size_t row = (size_t)blockIdx.x * (kNarrowThreads / tpr) + threadIdx.x / tpr;
+  const int d = 4 * (threadIdx.x % tpr);
   if (row >= (size_t)a.batch * a.num_q_heads) return;
-  const size_t e = row * D + d;
   const int nparts = a.nparts, last = nparts - 1;
   const float* ml = a.ws_ml + row * nparts * 2;
-  const float* acc = a.ws_acc + row * nparts * D;
-  float mp[NP], lp[NP], ap[NP];
+  const float* acc = a.ws_acc + row * nparts * D + d;
+  float mp[NP], lp[NP];
+  float4 ap[NP];
 #pragma unroll
   for (int u = 0; u < NP; ++u) {
     const int pc = u < nparts ? u : last;
     mp[u] = ml[2 * pc];
     lp[u] = ml[2 * pc + 1];
-    if constexpr (!SPARSE) ap[u] = acc[(size_t)pc * D + d];
+    if constexpr (!SPARSE) ap[u] = *reinterpret_cast<const float4*>(acc + (size_t)pc * D);
   }
   if constexpr (SPARSE) {
     if (lp[0] < 0.f) return;  // done marker: written out directly
 #pragma unroll
     for (int u = 0; u < NP; ++u)
-      ap[u] = u < nparts && mp[u] != kNegInf ? acc[(size_t)u * D + d] : 0.f;
+      ap[u] = u < nparts && mp[u] != kNegInf
+                  ? *reinterpret_cast<const float4*>(acc + (size_t)u * D)
+                  : make_float4(0.f, 0.f, 0.f, 0.f);
   }
   __builtin_amdgcn_sched_barrier(0);  // keep the loads above ahead of every use
-  float m = kNegInf, l = 0.f, mo = kNegInf, x = 0.f;
+  // fold() of (m, l) and of (m, a[k]) for k < 4, which see the same maxima
+  float m = kNegInf, l = 0.f;
+  float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
   for (int u = 0; u < NP; ++u) {
-    const float mu = u < nparts ? mp[u] : kNegInf;
-    fold(m, l, mu, lp[u]);
-    fold(mo, x, mu, ap[u]);
+    const float m2 = u < nparts ? mp[u] : kNegInf;
+    const float mn = fmaxf(m, m2);
+    const float ref = mn == kNegInf ? 0.f : mn;
+    const bool none = m2 == kNegInf;
+    const float s1 = fast_exp2(m - ref), s2 = fast_exp2(m2 - ref);
+    l = fmaf(l, s1, (none ? 0.f : lp[u]) * s2);
+    x.x = fmaf(x.x, s1, (none ? 0.f : ap[u].x) * s2);
+    x.y = fmaf(x.y, s1, (none ? 0.f : ap[u].y) * s2);
+    x.z = fmaf(x.z, s1, (none ? 0.f : ap[u].z) * s2);
+    x.w = fmaf(x.w, s1, (none ? 0.f : ap[u].w) * s2);
+    m = mn;
   }
-  store_out<OT>(a.out, e, l > 0.f ? x / l : 0.f);
+  store_out4<OT>(a.out, row * D + d, l > 0.f ? x.x / l : 0.f, l > 0.f ? x.y / l : 0.f,
+                 l > 0.f ? x.z / l : 0.f, l > 0.f ? x.w / l : 0.f);
 }
 
 template <int OT, bool SPARSE>
 hipError_t launch_reduce_per(const DecodeArgs& a, unsigned rows, hipStream_t stream) {
   if (a.nparts <= 8) {
     const unsigned grid =
-        (unsigned)(((size_t)rows * a.head_dim + kNarrowThreads - 1) / kNarrowThreads);
+        (unsigned)(((size_t)rows * (a.head_dim / 4) + kNarrowThreads - 1) / kNarrowThreads);
     const dim3 block(kNarrowThreads);
     if (a.nparts <= 2)
       hipLaunchKernelGGL((decode_reduce_narrow_kernel<OT, 2, SPARSE>), dim3(grid), block, 0,
