@@ -273,6 +273,40 @@ def test_attention_edge_lengths(dev, D, Hq, Hkv):
                 assert torch.equal(fr[pool].view(torch.int16), sr[pool].view(torch.int16))
 
 
+@pytest.mark.parametrize("block_size", [32, 64])
+@pytest.mark.parametrize("D,Hq,Hkv", [(128, 32, 8), (64, 24, 8)])
+def test_larger_blocks_edge_lengths(dev, D, Hq, Hkv, block_size):
+    """Lengths at 16-token, pair and large-block boundaries with 32- and 64-token blocks, on a
+    poisoned pool: the write + attention against the oracle for every kernel family and
+    split, an empty context gives zeros, a one-token context gives its value row exactly, and
+    the fused step equals the separate calls."""
+    lengths = EDGE_LENGTHS + [31, 32, 63, 64, 65, 127, 129]
+    w = wl.Workload("edge_big", batch=len(lengths), num_q_heads=Hq, num_kv_heads=Hkv,
+                    head_dim=D, block_size=block_size, num_blocks=1200 * 16 // block_size,
+                    max_blocks=4096 // block_size + 4, seed=4343, q_std=3.0)
+    inp = wl.make_inputs(w, poison=True, lengths=lengths)
+    ref, _, _ = oracle.decode_step(wl.to_host_numpy(inp))
+    G = Hq // Hkv
+    for kernel in kernels_for(w):
+        for partition in (0, -1, block_size, 4 * block_size):
+            d = to_dev(inp, dev)
+            run_write(d)
+            out_t = run_attention(d, kernel, partition)
+            out = out_t.cpu().double().numpy()
+            err = np.abs(out - ref).max()
+            record(f"edge_bs{block_size}/D{D}/G{G}/{kernel}/p{partition}", err)
+            assert np.isfinite(out).all()
+            assert err <= ATOL, (kernel, partition, err)
+            assert not out[lengths.index(0)].any()
+            one = lengths.index(1)
+            vrow = d["v_new"][one].float().repeat_interleave(G, dim=0)
+            assert torch.equal(out_t[one], vrow), (kernel, partition)
+            fused = to_dev(inp, dev)
+            assert torch.equal(run_step(fused, kernel, partition), out_t), (kernel, partition)
+            for pool in ("k_cache", "v_cache"):
+                assert torch.equal(fused[pool].view(torch.int16), d[pool].view(torch.int16))
+
+
 def test_length_one_returns_value_row_exactly(dev):
     w = wl.Workload("one", batch=5, num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
                     num_blocks=10, max_blocks=2, seed=99, context_len=1, q_std=3.0)
