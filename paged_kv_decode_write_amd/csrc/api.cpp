@@ -749,6 +749,8 @@ int paged_prefill_attention_split(const uint16_t* q, const int32_t* cu_seqlens_q
     return fail(PAGEDKV_ERR_UNSUPPORTED,
                 "no multi-query kernel for head_dim %d, block_size %d, group size %d", head_dim,
                 block_size, G);
+  if (num_blocks > (int64_t)INT32_MAX / (block_size / kKernelBlock))
+    return fail(PAGEDKV_ERR_SHAPE, "num_blocks * block_size / 16 exceeds int32");
   if (batch == 0 || num_tokens == 0 || max_q_len == 0) return PAGEDKV_OK;
   if (!q || !cu_seqlens_q || !k_cache || !v_cache || !context_lens || !out ||
       (max_blocks_per_seq > 0 && !block_tables))

@@ -61,6 +61,16 @@ template <int D> struct LdsPair {
 // at column (t + 256x) % (D/8). With 64 threads covering 64/(D/8) whole rows, the block a
 // piece falls in is the same for the whole wave, so block base addresses stay scalar and a
 // load is a scalar base plus a per-thread 32-bit offset fixed for the whole kernel.
+// The kernel reads the pools as 16-token blocks. A cache block of 16 * sub tokens holds the
+// same memory as 16-token blocks sub * p .. sub * p + sub - 1, so 16-token block j of a
+// sequence is that block of table entry j / sub. -1 when the entry is outside the pool.
+__device__ __forceinline__ int sub_block_id(const int32_t* table, int j, int sub,
+                                           int64_t num_blocks) {
+  const int e = j / sub;
+  const int p = table[e];
+  return p >= 0 && (int64_t)p < num_blocks ? p * sub + (j - e * sub) : -1;
+}
+
 template <int D> struct Stager {
   static constexpr int kCPR = D / 8;                           // pieces per row
   static constexpr int kPieces = kPairRows * kCPR / 256;      // per thread: D 64 -> 1, 128 -> 2
@@ -91,10 +101,11 @@ template <int D> struct Stager {
   __device__ __forceinline__ void load(const PrefillArgs& a, const int32_t* table, int nblk,
                                        int tok1, size_t row_stride, int pair) {
     const int jA = 2 * pair;
-    const int idA = table[jA];
-    const int idB = jA + 1 < nblk ? table[jA + 1] : -1;
-    const bool okA = idA >= 0 && (int64_t)idA < a.num_blocks;
-    const bool okB = idB >= 0 && (int64_t)idB < a.num_blocks;
+    const int sub = a.block_size / 16;
+    const int idA = sub_block_id(table, jA, sub, a.num_blocks);
+    const int idB = jA + 1 < nblk ? sub_block_id(table, jA + 1, sub, a.num_blocks) : -1;
+    const bool okA = idA >= 0;
+    const bool okB = idB >= 0;
     zero_a = !okA;
     zero_b = !okB;
     tail_from = min(tok1 - 32 * pair, 32);
@@ -287,7 +298,7 @@ prefill_mfma_kernel(const PrefillArgs a) {
   const int wg_end = Q - tile * NW * NB * R;  // one past the workgroup's last token
   if (wg_end <= 0) return;                    // uniform over the workgroup: before any barrier
   int L = a.context_lens[b];
-  const int Lmax = a.max_blocks * 16;
+  const int Lmax = a.max_blocks * a.block_size;
   L = L < 0 ? 0 : (L > Lmax ? Lmax : L);
 
   // This wave's tokens (possibly none: it still loads and meets every barrier).
@@ -416,7 +427,8 @@ prefill_mfma_kernel(const PrefillArgs a) {
 }
 
 bool supported_prefill(int head_dim, int group, int block_size) {
-  return block_size == 16 && (head_dim == 64 || head_dim == 128) && group >= 1 && group <= 16;
+  return block_size % 16 == 0 && block_size <= 1024 && (head_dim == 64 || head_dim == 128) &&
+         group >= 1 && group <= 16;
 }
 
 int prefill_tokens_per_group(int group, int nb) { return kWavesPerGroup * nb * (16 / group); }

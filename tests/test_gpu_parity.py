@@ -658,6 +658,37 @@ def test_prefill_key_split_parity(dev, name, row_blocks, partition):
         assert plan[1] > 1
 
 
+@pytest.mark.parametrize("block_size", [32, 64])
+@pytest.mark.parametrize("name", ["p2", "p3"])
+def test_prefill_larger_blocks(dev, name, block_size):
+    """Multi-query attention over pools of 32- and 64-token blocks (read as 16-token blocks),
+    on poisoned pools: every output against the oracle for one and two row blocks per wave,
+    unsplit, automatic and with the keys split."""
+    import dataclasses
+    k = block_size // 16
+    base = wl.PREFILL_WORKLOADS[name]
+    w = dataclasses.replace(base, name=f"{name}_bs{block_size}", block_size=block_size,
+                            num_blocks=base.num_blocks // k + 8,
+                            max_blocks=-(-base.max_blocks // k))
+    inp = wl.make_prefill_inputs(w, poison=True)
+    host = wl.to_host_numpy(inp)
+    kc, vc = oracle.kv_write(host["k_new"], host["v_new"], host["slot_mapping"],
+                             host["k_cache"], host["v_cache"])
+    ref = oracle.prefill_attention(host["q"], host["cu_seqlens_q"], kc, vc,
+                                   host["block_tables"], host["context_lens"], host["scale"])
+    d = to_dev(inp, dev)
+    run_write(d)
+    torch.cuda.synchronize()
+    assert np.array_equal(wl.to_bits(d["k_cache"]), kc)
+    for row_blocks in (1, 2):
+        for partition in (-1, 0, 256):
+            out = run_prefill(d, row_blocks, partition).cpu().double().numpy()
+            err = np.abs(out - ref).max()
+            record(f"{w.name}/prefill/rb{row_blocks}/p{partition}", err)
+            assert np.isfinite(out).all()
+            assert err <= ATOL, (row_blocks, partition, err)
+
+
 def test_prefill_key_split_ignores_workspace_contents(dev):
     """Every (row, partition) slot the merge reads is written by the call: a workspace full of
     NaN gives the same result as a fresh one, twice in a row."""
