@@ -334,8 +334,8 @@ int paged_decode_plan(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
  *   k_cache, v_cache, block_tables, context_lens, scale: as in paged_decode_attention;
  *                  Q_b <= context_lens[b] (rows whose position would be negative get 0)
  *   out            fp32 [num_tokens][num_q_heads][head_dim] (written)
- * Supported: head_dim in {64, 128}; block_size a multiple of 16 up to 1024 (blocks larger than
- * 16 tokens are read as the same memory cut into 16-token blocks; num_blocks * block_size / 16
+ * Supported: head_dim in {64, 128}; block_size 16, 32, 64, ... 1024 (blocks larger than 16
+ * tokens are read as the same memory cut into 16-token blocks; num_blocks * block_size / 16
  * must fit in int32); num_q_heads / num_kv_heads in 1..16.
  * Needs no workspace. Asynchronous on `stream`; status codes as above.
  */

@@ -61,14 +61,15 @@ template <int D> struct LdsPair {
 // at column (t + 256x) % (D/8). With 64 threads covering 64/(D/8) whole rows, the block a
 // piece falls in is the same for the whole wave, so block base addresses stay scalar and a
 // load is a scalar base plus a per-thread 32-bit offset fixed for the whole kernel.
-// The kernel reads the pools as 16-token blocks. A cache block of 16 * sub tokens holds the
-// same memory as 16-token blocks sub * p .. sub * p + sub - 1, so 16-token block j of a
-// sequence is that block of table entry j / sub. -1 when the entry is outside the pool.
-__device__ __forceinline__ int sub_block_id(const int32_t* table, int j, int sub,
+// The kernel reads the pools as 16-token blocks. A cache block of 16 << sh tokens holds the
+// same memory as 16-token blocks p << sh .. (p << sh) + (1 << sh) - 1, so 16-token block j of
+// a sequence is that block of table entry j >> sh (sh = 0 for 16-token blocks: the plain
+// table entry, at the cost of two scalar operations and no branch). -1 when the entry is
+// outside the pool.
+__device__ __forceinline__ int sub_block_id(const int32_t* table, int j, int sh,
                                            int64_t num_blocks) {
-  const int e = j / sub;
-  const int p = table[e];
-  return p >= 0 && (int64_t)p < num_blocks ? p * sub + (j - e * sub) : -1;
+  const int p = table[j >> sh];
+  return p >= 0 && (int64_t)p < num_blocks ? (p << sh) | (j & ((1 << sh) - 1)) : -1;
 }
 
 template <int D> struct Stager {
@@ -101,9 +102,9 @@ template <int D> struct Stager {
   __device__ __forceinline__ void load(const PrefillArgs& a, const int32_t* table, int nblk,
                                        int tok1, size_t row_stride, int pair) {
     const int jA = 2 * pair;
-    const int sub = a.block_size / 16;
-    const int idA = sub_block_id(table, jA, sub, a.num_blocks);
-    const int idB = jA + 1 < nblk ? sub_block_id(table, jA + 1, sub, a.num_blocks) : -1;
+    const int sh = __builtin_ctz((unsigned)a.block_size) - 4;  // block_size = 16 << sh
+    const int idA = sub_block_id(table, jA, sh, a.num_blocks);
+    const int idB = jA + 1 < nblk ? sub_block_id(table, jA + 1, sh, a.num_blocks) : -1;
     const bool okA = idA >= 0;
     const bool okB = idB >= 0;
     zero_a = !okA;
@@ -427,8 +428,9 @@ prefill_mfma_kernel(const PrefillArgs a) {
 }
 
 bool supported_prefill(int head_dim, int group, int block_size) {
-  return block_size % 16 == 0 && block_size <= 1024 && (head_dim == 64 || head_dim == 128) &&
-         group >= 1 && group <= 16;
+  // 16-token blocks or larger powers of two up to 1024 (the loader shifts block indices)
+  return block_size >= 16 && block_size <= 1024 && (block_size & (block_size - 1)) == 0 &&
+         (head_dim == 64 || head_dim == 128) && group >= 1 && group <= 16;
 }
 
 int prefill_tokens_per_group(int group, int nb) { return kWavesPerGroup * nb * (16 / group); }

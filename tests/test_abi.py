@@ -149,6 +149,10 @@ def test_prefill_argument_errors(lib):
     assert _prefill(lib, Hq=30) == ERR_SHAPE
     assert _prefill(lib, D=96) == ERR_UNSUPPORTED
     assert _prefill(lib, Hq=34, Hkv=2) == ERR_UNSUPPORTED  # group of 17 query heads
+    assert _prefill(lib, bs=8) == ERR_UNSUPPORTED     # blocks: 16 << k tokens only
+    assert _prefill(lib, bs=48) == ERR_UNSUPPORTED
+    assert _prefill(lib, bs=2048, MB=2) == ERR_UNSUPPORTED
+    assert _prefill(lib, bs=64, T=0, q=None, out=None) == OK  # 64-token blocks are taken
     assert _prefill(lib, q=None) == ERR_NULL
     assert _prefill(lib, cu=None) == ERR_NULL
     assert _prefill(lib, out=FAKE + 4) == ERR_ALIGN
