@@ -120,6 +120,29 @@ def test_decode_formats_all_kernels_and_splits(dev, name, kvt, ot):
 
 
 @pytest.mark.parametrize("kvt,ot", PAIRS)
+def test_decode_formats_with_32_token_blocks(dev, kvt, ot):
+    """The formats with 32-token blocks (the ragged c4 shape): every kernel family and split
+    against the oracle, and the 16-bit output the launch's fp32 result rounded."""
+    import dataclasses
+    base = wl.WORKLOADS["c4"]
+    w = dataclasses.replace(base, name="c4_bs32", block_size=32, max_blocks=base.max_blocks // 2,
+                            num_blocks=base.num_blocks // 2)
+    inp = wl.make_inputs(w, dtype=kvt)
+    host = wl.to_host_numpy(inp)
+    kc, vc = oracle.kv_write(host["k_new"], host["v_new"], host["slot_mapping"],
+                             host["k_cache"], host["v_cache"])
+    ref = oracle.decode_attention(host["q"], kc, vc, host["block_tables"],
+                                  host["context_lens"], host["scale"], dtype=kvt)
+    d = to_dev(inp, dev)
+    pk.paged_kv_write(d["k_new"], d["v_new"], d["slot_mapping"], d["k_cache"], d["v_cache"])
+    for kernel in ("valu", "mfma", "mfma_hw"):
+        for part in (-1, 0, 256):
+            out = run_decode(d, ot, kernel, part)
+            full = run_decode(d, "f32", kernel, part) if ot != "f32" else None
+            check_output(out, ref, ot, f"c4_bs32/{kvt}->{ot}/{kernel}/p{part}", full)
+
+
+@pytest.mark.parametrize("kvt,ot", PAIRS)
 def test_decode_formats_full_size_sampled(dev, kvt, ot):
     """c5b (2 x 32768 tokens, logits std 3) in the launch the benchmark times, on sampled
     rows."""
