@@ -183,9 +183,9 @@ def read_probe(torch, dev, nbytes, reps=5):
                                               for k, v in rates.items()}
 
 
-def cpu_baseline(d, seconds):
-    """The float64 oracle, as it stands, on the first sequences of the workload (write +
-    attention, all heads) until `seconds` of CPU time are spent, on one thread."""
+def cpu_baseline(subs, seconds):
+    """The float64 oracle, as it stands, on the sequences of the step's sub-workloads in order
+    (write + attention, all heads) until `seconds` of CPU time are spent, on one thread."""
     import numpy as np
     import torch
     from threadpoolctl import threadpool_limits
@@ -193,36 +193,40 @@ def cpu_baseline(d, seconds):
     import oracle
     from paged_kv_decode_write_amd import workloads as wl
 
-    w = d["workload"]
-    bs = w.block_size
-    tables = d["block_tables"].cpu().numpy()
-    lens = d["context_lens"].cpu().numpy()
-    q = wl.to_bits(d["q"])
-    kn, vn = wl.to_bits(d["k_new"]), wl.to_bits(d["v_new"])
-    spent, nbytes, done = 0.0, 0, 0
+    spent, nbytes, parts = 0.0, 0, []
     with threadpool_limits(limits=1):
-        for b in range(w.batch):
-            L = int(lens[b])
-            n = (L + bs - 1) // bs
-            ids = torch.from_numpy(tables[b, :n].astype(np.int64)).to(d["k_cache"].device)
-            kc = wl.to_bits(d["k_cache"].index_select(0, ids))
-            vc = wl.to_bits(d["v_cache"].index_select(0, ids))
-            local = np.arange(n, dtype=np.int32)[None]
-            slot = np.array([(n - 1) * bs + (L - 1) % bs], dtype=np.int64)
-            t0 = time.perf_counter()
-            kc2, vc2 = oracle.kv_write(kn[b:b + 1], vn[b:b + 1], slot, kc, vc)
-            oracle.decode_attention(q[b:b + 1], kc2, vc2, local, lens[b:b + 1], d["scale"])
-            spent += time.perf_counter() - t0
-            ab = wl.algorithmic_bytes(w, [L])
-            nbytes += ab["kv"] + (ab["q"] + ab["out"] + ab["write"]) // w.batch
-            done += 1
-            if spent >= seconds:
-                break
+        for d in subs:
+            w = d["workload"]
+            bs = w.block_size
+            tables = d["block_tables"].cpu().numpy()
+            lens = d["context_lens"].cpu().numpy()
+            q = wl.to_bits(d["q"])
+            kn, vn = wl.to_bits(d["k_new"]), wl.to_bits(d["v_new"])
+            done = 0
+            for b in range(w.batch):
+                if spent >= seconds:
+                    break
+                L = int(lens[b])
+                n = (L + bs - 1) // bs
+                ids = torch.from_numpy(tables[b, :n].astype(np.int64)).to(d["k_cache"].device)
+                kc = wl.to_bits(d["k_cache"].index_select(0, ids))
+                vc = wl.to_bits(d["v_cache"].index_select(0, ids))
+                local = np.arange(n, dtype=np.int32)[None]
+                slot = np.array([(n - 1) * bs + (L - 1) % bs], dtype=np.int64)
+                t0 = time.perf_counter()
+                kc2, vc2 = oracle.kv_write(kn[b:b + 1], vn[b:b + 1], slot, kc, vc)
+                oracle.decode_attention(q[b:b + 1], kc2, vc2, local, lens[b:b + 1],
+                                        d["scale"])
+                spent += time.perf_counter() - t0
+                ab = wl.algorithmic_bytes(w, [L])
+                nbytes += ab["kv"] + (ab["q"] + ab["out"] + ab["write"]) // w.batch
+                done += 1
+            if done:
+                parts.append(f"{w.name}: sequences 0..{done - 1} of {w.batch}")
     return {"value": round(nbytes / spent / 1e9, 4), "unit": "GB/s", "cores": 1,
             "kind": "oracle",
-            "sample": f"{w.name}: sequences 0..{done - 1} of {w.batch} (KV write + attention, "
-                      f"all {w.num_q_heads} heads), float64 numpy, one BLAS thread, "
-                      f"{spent:.1f} s"}
+            "sample": "; ".join(parts) + f" (KV write + attention, all query heads), float64 "
+                      f"numpy, one BLAS thread, {spent:.1f} s"}
 
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix throughput, vendor figure
@@ -560,7 +564,7 @@ def main():
         # delivers to a simple kernel on this part, beside the 8 TB/s vendor peak
         line["read_probe"] = probe
     if not args.no_cpu_baseline and (args.in_dtype, args.out_dtype) == ("bf16", "f32"):
-        line["cpu_baseline"] = cpu_baseline(subs[0], args.cpu_seconds)
+        line["cpu_baseline"] = cpu_baseline(subs, args.cpu_seconds)
     out = json.dumps(line)
     print(out, flush=True)
     if args.json_out:
