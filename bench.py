@@ -82,7 +82,10 @@ def parse_args():
     p.add_argument("--copy-calibration-mib", type=int, default=0,
                    help="run one plain device-to-device copy of this many MiB before the "
                         "steps (reference dispatch for hardware byte counters)")
-    return p.parse_args()
+    args = p.parse_args()
+    if args.block_size < 16 or args.block_size % 16:
+        p.error(f"--block-size {args.block_size}: a multiple of 16 tokens")
+    return args
 
 
 class HipEvents:

@@ -24,3 +24,12 @@ def test_help_lists_the_contract_flags():
     assert res.returncode == 0
     for flag in ("--gpus", "--steps", "--warmup", "--workload", "--kernel", "--partition"):
         assert flag in res.stdout
+
+
+def test_block_size_must_be_a_multiple_of_16():
+    for bs in ("8", "24"):
+        res = run_bench("--block-size", bs)
+        assert res.returncode == 2, res
+        assert "multiple of 16" in res.stderr, res.stderr
+        assert res.stdout == ""
+
