@@ -226,14 +226,32 @@ def prefill_attention(q_bits: np.ndarray, cu_seqlens_q: np.ndarray, k_cache_bits
         K = gather_dense(k_cache_bits, block_tables[b], L, dtype)
         V = gather_dense(v_cache_bits, block_tables[b], L, dtype)
         qd = decode_bits(q_bits[cu[b]:cu[b + 1]], dtype)
-        for i in range(Q):
-            p = L - Q + i
-            heads = range(Hq) if wanted is None else wanted.get(int(cu[b]) + i, [])
-            for h in heads:
-                g = kv_head_for(h, Hq, Hkv)
-                out[cu[b] + i, h] = attend_one(qd[i, h], K[:p + 1, g, :], V[:p + 1, g, :],
-                                               scale_eff)
+        positions = L - Q + np.arange(Q)  # row i sits at position L - Q + i
+        for h in range(Hq):
+            if wanted is None:
+                idx = np.arange(Q)
+            else:
+                idx = np.array([i for i in range(Q) if h in wanted.get(int(cu[b]) + i, [])],
+                               dtype=np.int64)
+                if idx.size == 0:
+                    continue
+            g = kv_head_for(h, Hq, Hkv)
+            out[cu[b] + idx, h] = attend_causal(qd[idx, h], np.ascontiguousarray(K[:, g, :]),
+                                                np.ascontiguousarray(V[:, g, :]),
+                                                positions[idx], scale_eff)
     return out
+
+
+def attend_causal(Qh: np.ndarray, K: np.ndarray, V: np.ndarray, positions: np.ndarray,
+                  scale_eff: float) -> np.ndarray:
+    """Row i: softmax(K[:positions[i]+1] Qh[i] * scale) V[:positions[i]+1], for a block of
+    query rows of one head at once. Keys after a row's position get score -inf (the causal
+    mask), so each row is the one-query definition of attend_one over its own prefix."""
+    s = (Qh @ K.T) * scale_eff                       # [rows, L]
+    s[np.arange(K.shape[0])[None, :] > positions[:, None]] = -np.inf
+    m = s.max(axis=1, keepdims=True)
+    p = np.exp(s - m)
+    return (p @ V) / p.sum(axis=1, keepdims=True)
 
 
 def decode_step(inp: dict, rows=None) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:

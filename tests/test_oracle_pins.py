@@ -572,7 +572,7 @@ def test_P14_full_prefill_equals_is_causal():
 def test_P15_single_query_prefill_equals_decode():
     c = prefill_case(321, [70, 5, 128], [1, 1, 1], 8, 2, 16, 16)
     dec = oracle.decode_attention(c["q"], c["kc"], c["vc"], c["tables"], c["lens"], c["scale"])
-    assert np.array_equal(run_prefill(c), dec)
+    np.testing.assert_allclose(run_prefill(c), dec, rtol=0, atol=1e-13)
 
 
 def brute_force_prefill(c):
@@ -685,6 +685,38 @@ def test_rope_known_values_and_identity():
                                        np.zeros((2, 4, 2, 16), np.uint16),
                                        np.zeros((2, 4, 2, 16), np.uint16))
     assert np.array_equal(q_rot, qb)  # position 0 rotates nothing
+
+
+def test_rope_frequency_of_each_pair_by_hand():
+    """Pair i turns by position * inv_freq[i], for each pair separately. D = 8 with frequencies
+    1, 1/2, 1/4, 1/8 (exact in fp32) at position 1: unit vector e_j must come out as the
+    cosine / sine of its own pair's angle 2^-i at its own pair's two indices, for half pairing
+    (i, i + 4) and interleaved pairing (2i, 2i + 1). A frequency list applied in another order
+    (e.g. reversed) gives other angles and fails."""
+    inv = np.array([1.0, 0.5, 0.25, 0.125], dtype=np.float32)
+    eye = np.eye(8)
+    for inter in (False, True):
+        for i in range(4):
+            a, b = (2 * i, 2 * i + 1) if inter else (i, i + 4)
+            th = 2.0 ** -i
+            want_a = np.zeros(8)
+            want_a[a], want_a[b] = math.cos(th), math.sin(th)
+            want_b = np.zeros(8)
+            want_b[a], want_b[b] = -math.sin(th), math.cos(th)
+            np.testing.assert_allclose(oracle.rope_rotate(eye[a], 1, inv, inter), want_a,
+                                       rtol=0, atol=1e-15)
+            np.testing.assert_allclose(oracle.rope_rotate(eye[b], 1, inv, inter), want_b,
+                                       rtol=0, atol=1e-15)
+
+
+def test_rope_angle_is_formed_in_fp32():
+    """The angle is fp32(position) * inv_freq rounded to fp32, as a GPU forms it. Two cases
+    worked by hand: position 2^24 + 1 becomes 2^24 in fp32; 3 * (1 + 2^-23) = 3 + 1.5 units in
+    the last place of [2, 4), a tie that rounds to the even neighbour 3 + 2^-21."""
+    x = np.array([1.0, 0.0])
+    for pos, f, th in ((2 ** 24 + 1, 1.0, 2.0 ** 24), (3, 1.0 + 2.0 ** -23, 3.0 + 2.0 ** -21)):
+        y = oracle.rope_rotate(x, pos, np.array([f], dtype=np.float32), False)
+        np.testing.assert_allclose(y, [math.cos(th), math.sin(th)], rtol=0, atol=1e-15)
 
 
 def test_rope_preserves_pair_norms_and_relative_positions():
