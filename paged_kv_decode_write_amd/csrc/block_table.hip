@@ -2,9 +2,9 @@
 //
 // A pool of blocks of block_size = 16*k token slots ([NB][16k][Hkv][D]) holds the same bytes
 // as a pool of 16-token blocks ([k*NB][16][Hkv][D]): slots of physical block p are 16-token
-// blocks k*p .. k*p + k - 1, and a slot number (block * block_size + offset, the per-sequence
-// block table of "Building a High-Performance LLM Inference Engine from Scratch with
-// tiny-vLLM" and the mini-vLLM README's block pool) names the same row in both views. The
+// blocks k*p .. k*p + k - 1, and a slot number (block * block_size + offset; the pool of
+// physical blocks of block_size token slots and the per-sequence block table are those of the
+// mini-vLLM README's paged KV-cache paragraph) names the same row in both views. The
 // decode kernels are built for 16-token blocks; for larger blocks they read the 16-token view
 // through the table this launch writes: entry j of a row is k * T[j / k] + j % k, where T is
 // the caller's row. Entries whose id is outside [0, NB) (unused tail entries, which may hold

@@ -53,6 +53,16 @@ __device__ __forceinline__ int step_sub_pos(const DecodeArgs& a, const int32_t* 
   return slot >= 0 && slot == want && slot < a.num_blocks * 16 ? L - 1 : -1;
 }
 
+// Rows the fused step's new-row loads read for KV head g of sequence b: the step's new K / V
+// rows when the call has them; otherwise slot 0 of head g in the pools, which exists for any
+// batch (the pool holds at least one block) and whose values are then never used.
+__device__ __forceinline__ const uint16_t* new_k_row(const DecodeArgs& a, int b, int g, int D) {
+  return a.k_new ? a.k_new + ((size_t)b * a.num_kv_heads + g) * D : a.k_cache + (size_t)g * D;
+}
+__device__ __forceinline__ const uint16_t* new_v_row(const DecodeArgs& a, int b, int g, int D) {
+  return a.v_new ? a.v_new + ((size_t)b * a.num_kv_heads + g) * D : a.v_cache + (size_t)g * D;
+}
+
 // Fused decode step: store KV head g's slice of sequence b's new K and V rows at
 // slot_mapping[b] (negative or outside the pool: nothing), 16 bytes per lane, K from lanes
 // 0..D/8-1 and V from lanes 32..32+D/8-1 of one wave. Only the launch unit that reads
@@ -167,12 +177,11 @@ decode_mfma_kernel(const DecodeArgs a) {
   ctx.wave = wave;
   ctx.n16 = n16;
   ctx.kg = kg;
-  // Fused step: the new row of this head, loaded unconditionally (from the cache when there is
-  // no step write, then never used) so no memory operation waits behind a branch.
+  // Fused step: the new row of this head, loaded unconditionally (from pool slot 0 when there
+  // is no step write, then never used) so no memory operation waits behind a branch.
   const int sub_pos = step_sub_pos(a, table, b, L);
   NewRow<NCH, EPL> nrow;
-  load_new_row(nrow, (a.k_new ? a.k_new : a.k_cache) + ((size_t)b * Hkv + g) * D,
-               (a.v_new ? a.v_new : a.v_cache) + ((size_t)b * Hkv + g) * D, n16, kg);
+  load_new_row(nrow, new_k_row(a, b, g, D), new_v_row(a, b, g, D), n16, kg);
   if constexpr (ROPE)
     rope_pieces<KT>(qb, nrow.k, (float)a.positions[b], a.inv_freq, a.interleaved != 0, kg,
                     lane);
@@ -320,12 +329,11 @@ decode_mfma_hw_kernel(const DecodeArgs a) {
   ctx.wave = 0;
   ctx.n16 = n16;
   ctx.kg = kg;
-  // Fused step: the new row of this head, loaded unconditionally (from the cache when there is
-  // no step write, then never used) so no memory operation waits behind a branch; issued
+  // Fused step: the new row of this head, loaded unconditionally (from pool slot 0 when there
+  // is no step write, then never used) so no memory operation waits behind a branch; issued
   // before the first pair so that waiting for it never waits for the pair.
   NewRow<NCH, EPL> nrow;
-  load_new_row(nrow, (a.k_new ? a.k_new : a.k_cache) + ((size_t)b * Hkv + g) * D,
-               (a.v_new ? a.v_new : a.v_cache) + ((size_t)b * Hkv + g) * D, n16, kg);
+  load_new_row(nrow, new_k_row(a, b, g, D), new_v_row(a, b, g, D), n16, kg);
   // The first pair's K / V loads go out with q's, before the context length arrives: a
   // partition that then turns out empty discards them; every other one saves a round trip.
   PairTile<NCH, EPL> t[NBUF];
