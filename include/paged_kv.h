@@ -18,7 +18,8 @@
  *     aligned. bf16 values are passed as their uint16_t bit patterns.
  *   - The caller owns every buffer (inputs, outputs, workspace). The library allocates and
  *     frees nothing during a call and keeps no pointer after it returns. Its only state is
- *     a per-device cache of device properties (compute-unit count), filled on first use.
+ *     a per-device cache of device properties (compute-unit count), filled on first use, and
+ *     the static scratch array of paged_decode_step_noalloc (one per device).
  *   - Calls are asynchronous: kernels are enqueued on `stream` (NULL = the null stream) and
  *     the call returns without synchronising. Ordering between a write and a later
  *     attention call is the caller's stream order.
@@ -46,7 +47,7 @@
 extern "C" {
 #endif
 
-#define PAGED_KV_ABI_VERSION 4
+#define PAGED_KV_ABI_VERSION 5
 
 typedef enum {
   PAGEDKV_OK = 0,
@@ -267,6 +268,40 @@ int paged_decode_step(const uint16_t* q, const uint16_t* k_new, const uint16_t* 
                       int32_t out_dtype, void* workspace, size_t workspace_bytes,
                       int32_t partition_tokens, int32_t kernel, hipEvent_t ev_begin,
                       hipEvent_t ev_end, hipStream_t stream);
+
+/* Size of the device scratch array paged_decode_step_noalloc uses (per device). */
+#define PAGEDKV_STATIC_SCRATCH_BYTES (16u << 20)
+
+/*
+ * paged_decode_step_noalloc -- paged_decode_step for callers that cannot allocate device
+ * memory: code recorded under HIP graph capture, tight serving loops, and harnesses that forbid
+ * hipMalloc. It takes no workspace. The split partials and, for blocks larger than 16 tokens,
+ * the table of 16-token block ids live in a file-scope device array of
+ * PAGEDKV_STATIC_SCRATCH_BYTES bytes inside the library, one per device, held until the
+ * process ends; the call allocates and frees nothing (no hipMalloc / hipFree, no allocating
+ * library routine).
+ *
+ *   Arguments as in paged_decode_step, without workspace and workspace_bytes. The result
+ *   equals paged_decode_step with a workspace of its own.
+ *   Scratch bound: a call whose plan needs more than PAGEDKV_STATIC_SCRATCH_BYTES (for 16-token
+ *   blocks: batch * num_q_heads * partitions * (head_dim + 2) * 4 bytes when it splits, 0 when
+ *   it does not; paged_decode_plan gives the partition count) returns PAGEDKV_ERR_WORKSPACE
+ *   before anything is enqueued, with the sizes in paged_kv_last_error().
+ *   Sharing: every call on one device uses that device's one array, which keeps the last
+ *   call's contents; no part of it needs to start at zero (every value a call reads was
+ *   written by the same call). Calls that may overlap on one device (other streams, other
+ *   threads) race on the array and must be serialised by the caller.
+ *   Set-up: the first call on a device looks up the array's device address (with that device
+ *   current) and keeps it; a failure there returns PAGEDKV_ERR_HIP.
+ */
+int paged_decode_step_noalloc(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
+                              const int64_t* slot_mapping, uint16_t* k_cache, uint16_t* v_cache,
+                              const int32_t* block_tables, int32_t max_blocks_per_seq,
+                              const int32_t* context_lens, int32_t batch, int32_t num_q_heads,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                              int64_t num_blocks, float scale, int32_t kv_dtype, void* out,
+                              int32_t out_dtype, int32_t partition_tokens, int32_t kernel,
+                              hipEvent_t ev_begin, hipEvent_t ev_end, hipStream_t stream);
 
 /*
  * paged_decode_step_rope -- paged_decode_step with the rotary embedding of paged_kv_write_rope

@@ -6,7 +6,7 @@ tensors into pointers and the current stream, and nothing else. The library is l
 first use; if it is missing the call raises, there is no fallback.
 """
 from ._binding import (paged_kv_write, paged_decode_attention, paged_decode_step,
-                       prepare_decode_step, PreparedDecodeStep, paged_decode_step_rope,
+                       paged_decode_step_noalloc, prepare_decode_step, PreparedDecodeStep, paged_decode_step_rope,
                        paged_prefill_attention,
                        paged_kv_write_rope,
                        decode_workspace_bytes, decode_plan,
@@ -14,7 +14,7 @@ from ._binding import (paged_kv_write, paged_decode_attention, paged_decode_step
                        library_path, load_library, abi_version, PagedKVError)
 
 __all__ = ["paged_kv_write", "paged_decode_attention", "paged_decode_step",
-           "prepare_decode_step", "PreparedDecodeStep", "paged_decode_step_rope",
+           "paged_decode_step_noalloc", "prepare_decode_step", "PreparedDecodeStep", "paged_decode_step_rope",
            "paged_prefill_attention",
            "paged_kv_write_rope",
            "decode_workspace_bytes", "decode_plan",

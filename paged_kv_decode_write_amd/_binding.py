@@ -77,6 +77,10 @@ def load_library() -> ctypes.CDLL:
         lib.paged_decode_step.restype = ctypes.c_int
         lib.paged_decode_step.argtypes = [P, P, P, P, P, P, P, I32, P, I32, I32, I32, I32, I32,
                                           I64, F32, I32, P, I32, P, SZ, I32, I32, P, P, P]
+        lib.paged_decode_step_noalloc.restype = ctypes.c_int
+        lib.paged_decode_step_noalloc.argtypes = [P, P, P, P, P, P, P, I32, P, I32, I32, I32,
+                                                  I32, I32, I64, F32, I32, P, I32, I32, I32, P,
+                                                  P, P]
         lib.paged_decode_step_rope.restype = ctypes.c_int
         lib.paged_decode_step_rope.argtypes = [P, P, P, P, P, I32, P, P, P, P, P, I32, P, I32,
                                                I32, I32, I32, I32, I64, F32, I32, P, I32, P, SZ,
@@ -359,6 +363,29 @@ def paged_decode_step(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
             context_lens.data_ptr(), B, Hq, Hkv, D, bs, NB, float(scale), DTYPES[dt],
             out.data_ptr(), DTYPES[out.dtype], ws, wsb, partition_tokens, KERNELS[kernel], ev_b,
             ev_e, _stream_handle(dev)))
+    return out
+
+
+def paged_decode_step_noalloc(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                              slot_mapping: torch.Tensor, k_cache: torch.Tensor,
+                              v_cache: torch.Tensor, block_tables: torch.Tensor,
+                              context_lens: torch.Tensor, scale: float, out: torch.Tensor, *,
+                              partition_tokens: int = 0, kernel: str = "auto",
+                              events: Optional[tuple] = None) -> torch.Tensor:
+    """paged_decode_step with no workspace: the library keeps the split partials in a static
+    device array of its own (PAGEDKV_STATIC_SCRATCH_BYTES per device), so the call allocates
+    nothing. Calls that may overlap on one device race on that array."""
+    dev, dt, NB, bs, Hkv, D, B, Hq, MB = _check_step(
+        q, k_new, v_new, slot_mapping, k_cache, v_cache, block_tables, context_lens, out, kernel)
+    lib = load_library()
+    ev_b, ev_e = events if events is not None else (None, None)
+    with _device(dev):
+        _check(lib.paged_decode_step_noalloc(
+            q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), slot_mapping.data_ptr(),
+            k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(), MB,
+            context_lens.data_ptr(), B, Hq, Hkv, D, bs, NB, float(scale), DTYPES[dt],
+            out.data_ptr(), DTYPES[out.dtype], partition_tokens, KERNELS[kernel], ev_b, ev_e,
+            _stream_handle(dev)))
     return out
 
 

@@ -332,6 +332,33 @@ bool ranges_overlap(const void* a, size_t na, const void* b, size_t nb) {
   return x < y + nb && y < x + na;
 }
 
+// Scratch of paged_decode_step_noalloc: the split partials and the block-table view of a decode
+// call, in a file-scope device array instead of a caller's workspace. Each device holds its own
+// copy for the life of the process; calls on one device share it (see the header).
+static __device__ __align__(256) unsigned char scratch[PAGEDKV_STATIC_SCRATCH_BYTES];
+
+// Device address of `scratch` on the current device, looked up once per device with that device
+// current and kept; host code uses this address, never the array's name (which in host code
+// is a stand-in, not a device address).
+int scratch_address(void** out) {
+  static std::mutex mu;
+  static void* ptrs[256] = {nullptr};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= 256) return fail(PAGEDKV_ERR_HIP, "device ordinal %d out of range", dev);
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptrs[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(PAGEDKV_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    ptrs[dev] = p;
+  }
+  *out = ptrs[dev];
+  return PAGEDKV_OK;
+}
+
 // Decode attention, optionally fused with the step's KV write (sw non-null).
 int decode_impl(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache,
                 const int32_t* block_tables, int32_t max_blocks_per_seq,
@@ -340,7 +367,7 @@ int decode_impl(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_ca
                 float scale, int32_t kv_dtype, void* out, int32_t out_dtype, void* workspace,
                 size_t workspace_bytes, int32_t partition_tokens, int32_t kernel,
                 hipEvent_t ev_begin, hipEvent_t ev_end, hipStream_t stream,
-                const StepWrite* sw) {
+                const StepWrite* sw, bool static_scratch = false) {
   g_last_error.clear();
   int st = check_formats(kv_dtype, out_dtype);
   if (st) return st;
@@ -418,6 +445,17 @@ int decode_impl(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_ca
   a.out_dtype = out_dtype;
   const size_t split_need = split_workspace_bytes(batch, num_q_heads, head_dim, plan.nparts);
   const size_t table_need = view_table_bytes(batch, max_blocks_per_seq, sub);
+  if (static_scratch) {
+    const size_t need = split_need + table_need;
+    if (need > PAGEDKV_STATIC_SCRATCH_BYTES)
+      return fail(PAGEDKV_ERR_WORKSPACE,
+                  "this call needs %zu bytes of scratch (%d partitions of %d tokens); the "
+                  "static scratch holds %zu (PAGEDKV_STATIC_SCRATCH_BYTES)",
+                  need, plan.nparts, plan.part_tokens, (size_t)PAGEDKV_STATIC_SCRATCH_BYTES);
+    st = scratch_address(&workspace);
+    if (st) return st;
+    workspace_bytes = PAGEDKV_STATIC_SCRATCH_BYTES;
+  }
   if (split_need + table_need > 0) {
     const size_t need = split_need + table_need;
     if (!workspace || workspace_bytes < need)
@@ -668,6 +706,21 @@ int paged_decode_step(const uint16_t* q, const uint16_t* k_new, const uint16_t* 
                      num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale,
                      kv_dtype, out, out_dtype, workspace, workspace_bytes, partition_tokens,
                      kernel, ev_begin, ev_end, stream, &sw);
+}
+
+int paged_decode_step_noalloc(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
+                              const int64_t* slot_mapping, uint16_t* k_cache, uint16_t* v_cache,
+                              const int32_t* block_tables, int32_t max_blocks_per_seq,
+                              const int32_t* context_lens, int32_t batch, int32_t num_q_heads,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                              int64_t num_blocks, float scale, int32_t kv_dtype, void* out,
+                              int32_t out_dtype, int32_t partition_tokens, int32_t kernel,
+                              hipEvent_t ev_begin, hipEvent_t ev_end, hipStream_t stream) {
+  const StepWrite sw{k_new, v_new, slot_mapping, k_cache, v_cache, nullptr, nullptr, 0, nullptr};
+  return decode_impl(q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, batch,
+                     num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale,
+                     kv_dtype, out, out_dtype, nullptr, 0, partition_tokens, kernel, ev_begin,
+                     ev_end, stream, &sw, /*static_scratch=*/true);
 }
 
 int paged_decode_step_rope(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,

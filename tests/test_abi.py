@@ -49,7 +49,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.paged_kv_abi_version() == 4
+    assert lib.paged_kv_abi_version() == 5
     assert lib.paged_kv_status_string(OK) == b"PAGEDKV_OK"
     assert lib.paged_kv_status_string(ERR_WORKSPACE) == b"PAGEDKV_ERR_WORKSPACE"
     assert lib.paged_kv_status_string(99) == b"PAGEDKV_UNKNOWN_STATUS"
@@ -252,3 +252,23 @@ def test_larger_blocks_need_the_table_workspace(lib, monkeypatch):
     assert _attn(lib, bs=32, part=-1) == ERR_WORKSPACE
     assert b"workspace" in lib.paged_kv_last_error()
 
+
+
+def _step_noalloc(lib, q=FAKE, kn=FAKE, vn=FAKE, sl=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, MB=8,
+                  lens=FAKE, B=2, Hq=32, Hkv=8, D=128, bs=16, NB=64, out=FAKE, part=-1):
+    return lib.paged_decode_step_noalloc(q, kn, vn, sl, kc, vc, bt, MB, lens, B, Hq, Hkv, D, bs,
+                                         NB, 0.1, BF16, out, F32, part, 0, None, None, None)
+
+
+def test_decode_step_noalloc_host_checks(lib, monkeypatch):
+    """The no-workspace step validates like paged_decode_step, and refuses on the host, before
+    any device call, a plan whose partials exceed its static scratch: 64 x 8192 tokens in
+    16-token partitions need 64*32*512*130*4 bytes."""
+    monkeypatch.setenv("PAGEDKV_CU_COUNT", "256")
+    assert _step_noalloc(lib, kn=None) == ERR_NULL
+    assert _step_noalloc(lib, vn=FAKE + 8) == ERR_ALIGN
+    assert _step_noalloc(lib, D=96) == ERR_UNSUPPORTED
+    assert _step_noalloc(lib, B=0, q=None, kn=None, out=None) == OK
+    assert _step_noalloc(lib, B=64, MB=512, NB=32768, part=16) == ERR_WORKSPACE
+    msg = lib.paged_kv_last_error()
+    assert b"static scratch" in msg and str(64 * 32 * 512 * 130 * 4).encode() in msg
