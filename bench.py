@@ -9,9 +9,12 @@ sequence and then attends over all cached tokens of every sequence.
 
 Prints ONE JSON line. `value` is the whole step's algorithmic HBM throughput (GB/s):
 K and V of every context token (bf16), q (bf16), out (fp32) and the written K/V rows, over
-the measured step time. `roofline` reports the main attention kernel alone, timed with HIP
-events recorded on its own stream around each launch; `cpu_baseline` is the float64 CPU
-oracle timed on a bounded sample of the same workload on this host.
+the measured step time. `config.us_per_call` / `pct_of_peak` time each sub-workload's whole
+attention call (the fused write, the attention kernel and the split-K merge) with HIP events
+around the call; `roofline` reports the main attention kernel alone, timed with HIP events
+the library records on its stream around each launch (even timed steps carry those, odd ones
+the call events); `cpu_baseline` is the float64 CPU oracle timed on a bounded sample of the
+same workload on this host, on all its cores and on one.
 
     python bench.py [--steps K] [--warmup W] [--workload c5|c5a|c5b|c1..c4]
 """
@@ -59,8 +62,12 @@ def parse_args():
     p.add_argument("--no-read-probe", action="store_true",
                    help="skip the plain streaming-read reference after the timed steps")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
-                   help="CPU work budget of the oracle baseline sample")
+                   help="wall-time budget of each of the two oracle baseline passes")
     p.add_argument("--json-out", default=None)
+    p.add_argument("--jsonl", default=None,
+                   help="after the timed steps, also write one JSON row per (decode workload, "
+                        "cold / hot) to this file: call and kernel times, GB/s, read probe, "
+                        "max |out - oracle|, oracle times, seeds, input hashes, versions")
     p.add_argument("--rope", action="store_true",
                    help="rotate q and the new keys first (positions L-1, Llama 3 base 500000 "
                         "frequencies) and attend with the rotated q: one fused launch, or "
@@ -103,6 +110,7 @@ class HipEvents:
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
                                                  ctypes.c_void_p, ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
         self.events = []
 
     def create(self):
@@ -111,6 +119,10 @@ class HipEvents:
             raise RuntimeError("hipEventCreateWithFlags failed")
         self.events.append(ev.value)
         return ev.value
+
+    def record(self, ev, stream):
+        if self.hip.hipEventRecord(ev, stream) != 0:
+            raise RuntimeError("hipEventRecord failed")
 
     def elapsed_ms(self, a, b):
         ms = ctypes.c_float()
@@ -186,50 +198,255 @@ def read_probe(torch, dev, nbytes, reps=5):
                                               for k, v in rates.items()}
 
 
-def cpu_baseline(subs, seconds):
+def _oracle_pass(subs, seconds):
     """The float64 oracle, as it stands, on the sequences of the step's sub-workloads in order
-    (write + attention, all heads) until `seconds` of CPU time are spent, on one thread."""
+    (KV write + attention, all heads) until `seconds` of wall time are spent. Returns
+    (algorithmic bytes covered, seconds, sample description)."""
     import numpy as np
     import torch
-    from threadpoolctl import threadpool_limits
 
     import oracle
     from paged_kv_decode_write_amd import workloads as wl
 
     spent, nbytes, parts = 0.0, 0, []
+    for d in subs:
+        w = d["workload"]
+        bs = w.block_size
+        tables = d["block_tables"].cpu().numpy()
+        lens = d["context_lens"].cpu().numpy()
+        q = wl.to_bits(d["q"])
+        kn, vn = wl.to_bits(d["k_new"]), wl.to_bits(d["v_new"])
+        done = 0
+        for b in range(w.batch):
+            if spent >= seconds:
+                break
+            L = int(lens[b])
+            n = (L + bs - 1) // bs
+            ids = torch.from_numpy(tables[b, :n].astype(np.int64)).to(d["k_cache"].device)
+            kc = wl.to_bits(d["k_cache"].index_select(0, ids))
+            vc = wl.to_bits(d["v_cache"].index_select(0, ids))
+            local = np.arange(n, dtype=np.int32)[None]
+            slot = np.array([(n - 1) * bs + (L - 1) % bs], dtype=np.int64)
+            t0 = time.perf_counter()
+            kc2, vc2 = oracle.kv_write(kn[b:b + 1], vn[b:b + 1], slot, kc, vc)
+            oracle.decode_attention(q[b:b + 1], kc2, vc2, local, lens[b:b + 1], d["scale"])
+            spent += time.perf_counter() - t0
+            ab = wl.algorithmic_bytes(w, [L])
+            nbytes += ab["kv"] + (ab["q"] + ab["out"] + ab["write"]) // w.batch
+            done += 1
+        if done:
+            parts.append(f"{w.name}: sequences 0..{done - 1} of {w.batch}")
+    return nbytes, spent, "; ".join(parts)
+
+
+def cpu_baseline(subs, seconds):
+    """The oracle timed on this host: once with numpy's BLAS on every core this process may
+    run on (its default), once on one thread. Each pass gets `seconds` of wall time at most."""
+    import numpy  # noqa: F401  (loads the BLAS whose thread pool is read below)
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    host_cores = len(os.sched_getaffinity(0))
+    blas = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+    threads = max((p.get("num_threads", 1) for p in blas), default=1)
+    nb_all, t_all, sample_all = _oracle_pass(subs, seconds)
     with threadpool_limits(limits=1):
-        for d in subs:
-            w = d["workload"]
-            bs = w.block_size
-            tables = d["block_tables"].cpu().numpy()
-            lens = d["context_lens"].cpu().numpy()
-            q = wl.to_bits(d["q"])
-            kn, vn = wl.to_bits(d["k_new"]), wl.to_bits(d["v_new"])
-            done = 0
-            for b in range(w.batch):
-                if spent >= seconds:
-                    break
-                L = int(lens[b])
-                n = (L + bs - 1) // bs
-                ids = torch.from_numpy(tables[b, :n].astype(np.int64)).to(d["k_cache"].device)
-                kc = wl.to_bits(d["k_cache"].index_select(0, ids))
-                vc = wl.to_bits(d["v_cache"].index_select(0, ids))
-                local = np.arange(n, dtype=np.int32)[None]
-                slot = np.array([(n - 1) * bs + (L - 1) % bs], dtype=np.int64)
-                t0 = time.perf_counter()
-                kc2, vc2 = oracle.kv_write(kn[b:b + 1], vn[b:b + 1], slot, kc, vc)
-                oracle.decode_attention(q[b:b + 1], kc2, vc2, local, lens[b:b + 1],
-                                        d["scale"])
-                spent += time.perf_counter() - t0
-                ab = wl.algorithmic_bytes(w, [L])
-                nbytes += ab["kv"] + (ab["q"] + ab["out"] + ab["write"]) // w.batch
-                done += 1
-            if done:
-                parts.append(f"{w.name}: sequences 0..{done - 1} of {w.batch}")
-    return {"value": round(nbytes / spent / 1e9, 4), "unit": "GB/s", "cores": 1,
+        nb_one, t_one, sample_one = _oracle_pass(subs, seconds)
+    what = " (KV write + attention, all query heads), float64 numpy"
+    return {"value": round(nb_all / t_all / 1e9, 4), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
-            "sample": "; ".join(parts) + f" (KV write + attention, all query heads), float64 "
-                      f"numpy, one BLAS thread, {spent:.1f} s"}
+            "sample": f"{sample_all}{what}, {threads} BLAS threads on {host_cores} host "
+                      f"cores, {t_all:.1f} s",
+            "host_cores": host_cores,
+            "single_thread": {"value": round(nb_one / t_one / 1e9, 4), "unit": "GB/s",
+                              "cores": 1,
+                              "sample": f"{sample_one}{what}, one BLAS thread, "
+                                        f"{t_one:.1f} s"}}
+
+
+RECORD_WORKLOADS = ["c1", "c2", "c3", "c4", "c5a", "c5b"]
+
+
+def _gather_sequences(d):
+    """Each sequence's blocks as host bit patterns, local table, slot of its new row."""
+    import numpy as np
+    import torch
+    from paged_kv_decode_write_amd import workloads as wl
+
+    w = d["workload"]
+    bs = w.block_size
+    tables = d["block_tables"].cpu().numpy()
+    lens = d["context_lens"].cpu().numpy()
+    seqs = []
+    for b in range(w.batch):
+        L = int(lens[b])
+        n = (L + bs - 1) // bs
+        ids = torch.from_numpy(tables[b, :n].astype(np.int64)).to(d["k_cache"].device)
+        kc = wl.to_bits(d["k_cache"].index_select(0, ids))
+        vc = wl.to_bits(d["v_cache"].index_select(0, ids))
+        slot = np.array([(n - 1) * bs + (L - 1) % bs if L else -1], dtype=np.int64)
+        seqs.append((kc, vc, np.arange(n, dtype=np.int32)[None], slot, lens[b:b + 1]))
+    return seqs
+
+
+def _oracle_step(d, seqs):
+    """The oracle's decode step (write + attention, all heads), sequence by sequence; returns
+    (float64 output [B, Hq, D], seconds spent in the oracle)."""
+    import numpy as np
+
+    import oracle
+    from paged_kv_decode_write_amd import workloads as wl
+
+    q = wl.to_bits(d["q"])
+    kn, vn = wl.to_bits(d["k_new"]), wl.to_bits(d["v_new"])
+    out = np.zeros(q.shape, dtype=np.float64)
+    spent = 0.0
+    for b, (kc, vc, local, slot, L) in enumerate(seqs):
+        t0 = time.perf_counter()
+        kc2, vc2 = oracle.kv_write(kn[b:b + 1], vn[b:b + 1], slot, kc, vc)
+        out[b:b + 1] = oracle.decode_attention(q[b:b + 1], kc2, vc2, local, L, d["scale"])
+        spent += time.perf_counter() - t0
+    return out, spent
+
+
+def _environment(torch):
+    props = torch.cuda.get_device_properties(0)
+    rocm = None
+    for path in ("/opt/rocm/.info/version", "/opt/rocm/.info/version-dev"):
+        if os.path.exists(path):
+            with open(path) as f:
+                rocm = f.read().strip()
+            break
+    return {"gpu": props.name, "gcn_arch": getattr(props, "gcnArchName", None),
+            "compute_units": props.multi_processor_count, "rocm": rocm,
+            "hip": torch.version.hip, "torch": torch.__version__,
+            "host_cores": len(os.sched_getaffinity(0)),
+            "kernel_source": kernel_source_hash("mfma_hw")}
+
+
+def _input_sha256(d):
+    from paged_kv_decode_write_amd import workloads as wl
+    h = hashlib.sha256()
+    for key in ("q", "k_cache", "v_cache", "k_new", "v_new"):
+        h.update(wl.to_bits(d[key]).tobytes())
+    for key in ("block_tables", "context_lens", "slot_mapping"):
+        h.update(d[key].cpu().numpy().tobytes())
+    return h.hexdigest()
+
+
+def measurement_record(args, torch, pk, wl, path):
+    """One JSON row per (workload, cold / hot) for every decode workload, written to `path`:
+    the fused decode step (write + attention + merge) timed with HIP events around the call
+    on its stream, 3 warm-up calls and the median of 10 samples. Cold: a 512 MiB buffer is
+    read before each sample (no input left in L2 or the 256 MB last-level cache); hot: 100
+    back-to-back calls per sample, enqueued behind a GPU-side delay so that the host's launch
+    rate does not set the pace. Each cold row also carries the attention kernel alone, a
+    cold streaming read of the same bytes, the max |out - oracle| over every output row, and
+    the float64 oracle's time for the same step on all host cores and on one (median of 3
+    for the three smallest workloads, one run otherwise)."""
+    import numpy as np
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    dev = torch.device("cuda:0")
+    env = _environment(torch)
+    hip = HipEvents()
+    flush = torch.zeros((512 << 20) // 4, dtype=torch.float32, device=dev)
+    blas = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+    threads = max((p.get("num_threads", 1) for p in blas), default=1)
+    rows = []
+    for name in RECORD_WORKLOADS:
+        w = wl.WORKLOADS[name]
+        big = name.startswith("c5")
+        inp = wl.make_inputs(w, device="cuda" if big else "cpu")
+        d = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+        del inp
+        sha = _input_sha256(d)
+        out = torch.empty(w.batch, w.num_q_heads, w.head_dim, dtype=torch.float32, device=dev)
+        ws = pk.new_workspace(pk.decode_workspace_bytes(w.batch, w.num_q_heads, w.head_dim,
+                                                        w.max_blocks, w.block_size, 0), dev)
+        plan = pk.decode_plan(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.max_blocks,
+                              w.block_size, 0, "auto", with_kernel=True)
+        ab = wl.algorithmic_bytes(w, d["context_lens"].cpu().tolist())
+        stream = torch.cuda.current_stream(dev).cuda_stream
+
+        def call(events=None):
+            pk.paged_decode_step(d["q"], d["k_new"], d["v_new"], d["slot_mapping"],
+                                 d["k_cache"], d["v_cache"], d["block_tables"],
+                                 d["context_lens"], d["scale"], out, workspace=ws,
+                                 events=events)
+
+        def sample(cold, reps=1, kernel_only=False):
+            if cold:
+                torch.sum(flush)
+            else:
+                # keep the GPU busy (a bounded spin, no memory traffic) while the host enqueues
+                # the burst, so back-to-back calls are timed, not the host's launch rate
+                torch.cuda._sleep(4_000_000)
+            a, b = hip.create(), hip.create()
+            if kernel_only:
+                call((a, b))
+            else:
+                hip.record(a, stream)
+                for _ in range(reps):
+                    call()
+                hip.record(b, stream)
+            torch.cuda.synchronize()
+            return hip.elapsed_ms(a, b) * 1e3 / reps
+
+        for _ in range(3):
+            sample(True)
+        cold = sorted(sample(True) for _ in range(10))
+        kern = sorted(sample(True, kernel_only=True) for _ in range(10))
+        for _ in range(3):
+            sample(False)
+        hot = sorted(sample(False, reps=100) for _ in range(10))
+        probe_us, probe_gbs, _ = read_probe(torch, dev, ab["attention"])
+        hip.close()
+
+        seqs = _gather_sequences(d)
+        runs = 1 if name in ("c4", "c5a", "c5b") else 3
+        ref, t_all = None, []
+        for _ in range(runs):
+            ref, t = _oracle_step(d, seqs)
+            t_all.append(t)
+        t_one = []
+        with threadpool_limits(limits=1):
+            for _ in range(runs):
+                t_one.append(_oracle_step(d, seqs)[1])
+        del seqs
+        err = float(np.abs(out.cpu().double().numpy() - ref).max())
+        base = {"workload": name, "description": w.description, "seed": w.seed,
+                "input_sha256": sha, "batch": w.batch, "num_q_heads": w.num_q_heads,
+                "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
+                "block_size": w.block_size, "num_blocks": w.num_blocks,
+                "kernel": plan[2], "partitions": plan[0], "tokens_per_partition": plan[1],
+                "call": "paged_decode_step (write + attention + merge), bf16 in, f32 out",
+                "algorithmic_bytes": ab["attention"], "env": env}
+        for mode, us in (("cold", cold), ("hot", hot)):
+            med = us[len(us) // 2]
+            row = dict(base, mode=mode,
+                       us={"median": round(med, 2), "min": round(us[0], 2),
+                           "max": round(us[-1], 2), "samples": len(us)},
+                       GBps=round(ab["attention"] / (med * 1e-6) / 1e9, 1),
+                       pct_of_peak=round(100 * ab["attention"] / (med * 1e-6) / 1e9
+                                         / PEAK_HBM_GBS, 2),
+                       max_abs_err=err)
+            if mode == "cold":
+                row["attn_kernel_us_median"] = round(kern[len(kern) // 2], 2)
+                row["read_probe"] = {"us": round(probe_us, 2), "GBps": round(probe_gbs, 1)}
+                row["oracle"] = {"seconds_median": round(sorted(t_all)[len(t_all) // 2], 4),
+                                 "blas_threads": threads,
+                                 "seconds_one_thread_median": round(
+                                     sorted(t_one)[len(t_one) // 2], 4),
+                                 "runs": runs}
+            rows.append(row)
+        print(f"[record] {name}: cold {cold[len(cold) // 2]:.2f} us, hot "
+              f"{hot[len(hot) // 2]:.2f} us, max|err| {err:.2e}", file=sys.stderr, flush=True)
+        del d, out, ws
+        torch.cuda.empty_cache()
+    with open(path, "w") as f:
+        for row in rows:
+            f.write(json.dumps(row) + "\n")
+    return rows
 
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix throughput, vendor figure
@@ -365,40 +582,56 @@ def main():
     flush = (torch.zeros((args.flush_mib << 20) // 4, dtype=torch.float32, device=dev)
              if args.flush_mib > 0 else None)
 
-    def step(events=None):
-        if flush is not None:
-            torch.sum(flush)
-        for i, d in enumerate(subs):
-            ev = events[i] if events is not None else None
-            if args.rope and not args.separate:
-                # one launch rotates q and the new key, stores the rows and attends
-                pk.paged_decode_step_rope(d["q"], d["k_new"], d["v_new"], d["pos"],
-                                          d["inv_freq"], d["slot_mapping"], d["q_rot"],
-                                          d["k_cache"], d["v_cache"], d["block_tables"],
-                                          d["context_lens"], d["scale"], d["out"],
-                                          partition_tokens=args.partition, kernel=args.kernel,
-                                          workspace=d["ws"], events=ev)
-                continue
-            if not args.rope and not args.separate:
-                # one launch stores the new rows and attends (plus the merge when split)
-                pk.paged_decode_step(d["q"], d["k_new"], d["v_new"], d["slot_mapping"],
-                                     d["k_cache"], d["v_cache"], d["block_tables"],
-                                     d["context_lens"], d["scale"], d["out"],
-                                     partition_tokens=args.partition, kernel=args.kernel,
-                                     workspace=d["ws"], events=ev)
-                continue
-            if args.rope:
-                pk.paged_kv_write_rope(d["q"], d["k_new"], d["v_new"], d["pos"], d["inv_freq"],
-                                       d["slot_mapping"], d["k_cache"], d["v_cache"],
-                                       q_out=d["q_rot"])
-            else:
-                pk.paged_kv_write(d["k_new"], d["v_new"], d["slot_mapping"], d["k_cache"],
-                                  d["v_cache"])
+    hip = HipEvents()
+
+    def attend(d, ev):
+        """The sub-workload's attention call (the fused step, or with --separate the write
+        call and then the attention call); ev = (kernel begin, kernel end) or None."""
+        if args.rope and not args.separate:
+            # one launch rotates q and the new key, stores the rows and attends
+            pk.paged_decode_step_rope(d["q"], d["k_new"], d["v_new"], d["pos"],
+                                      d["inv_freq"], d["slot_mapping"], d["q_rot"],
+                                      d["k_cache"], d["v_cache"], d["block_tables"],
+                                      d["context_lens"], d["scale"], d["out"],
+                                      partition_tokens=args.partition, kernel=args.kernel,
+                                      workspace=d["ws"], events=ev)
+        elif not args.separate:
+            # one launch stores the new rows and attends (plus the merge when split)
+            pk.paged_decode_step(d["q"], d["k_new"], d["v_new"], d["slot_mapping"],
+                                 d["k_cache"], d["v_cache"], d["block_tables"],
+                                 d["context_lens"], d["scale"], d["out"],
+                                 partition_tokens=args.partition, kernel=args.kernel,
+                                 workspace=d["ws"], events=ev)
+        else:
             pk.paged_decode_attention(d["q_rot"] if args.rope else d["q"], d["k_cache"],
                                       d["v_cache"], d["block_tables"],
                                       d["context_lens"], d["scale"], d["out"],
                                       partition_tokens=args.partition, kernel=args.kernel,
                                       workspace=d["ws"], events=ev)
+
+    def step(events=None, kernel_events=False):
+        """One decode step over every sub-workload. events[i] = (begin, end) of sub-workload
+        i. With kernel_events the library records them around the attention kernel alone;
+        otherwise they bracket the whole attention call on its stream (the fused write, the
+        attention kernel and the partition merge), with no event between its launches."""
+        if flush is not None:
+            torch.sum(flush)
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        for i, d in enumerate(subs):
+            ev = events[i] if events is not None else None
+            if args.separate:
+                if args.rope:
+                    pk.paged_kv_write_rope(d["q"], d["k_new"], d["v_new"], d["pos"],
+                                           d["inv_freq"], d["slot_mapping"], d["k_cache"],
+                                           d["v_cache"], q_out=d["q_rot"])
+                else:
+                    pk.paged_kv_write(d["k_new"], d["v_new"], d["slot_mapping"], d["k_cache"],
+                                      d["v_cache"])
+            if ev is not None and not kernel_events:
+                hip.record(ev[0], stream)
+            attend(d, ev if kernel_events else None)
+            if ev is not None and not kernel_events:
+                hip.record(ev[1], stream)
 
     if args.copy_calibration_mib > 0:
         n = args.copy_calibration_mib << 20
@@ -414,33 +647,43 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    hip = HipEvents()
+    # Even steps time the attention kernel (events recorded by the library around it), odd
+    # steps the whole call (events around the call only); both kinds are in the timed region.
     evs = [[(hip.create(), hip.create()) for _ in subs] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(evs[i])
+        step(evs[i], kernel_events=(i % 2 == 0) or args.steps == 1)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
 
     per = []
     for j, d in enumerate(subs):
-        durs = sorted(hip.elapsed_ms(*evs[i][j]) for i in range(args.steps))
-        mean = sum(durs) / len(durs)
+        kern = sorted(hip.elapsed_ms(*evs[i][j]) for i in range(0, args.steps, 2))
+        call = sorted(hip.elapsed_ms(*evs[i][j]) for i in range(1, args.steps, 2)) or kern
+        kmean = sum(kern) / len(kern)
+        cmean = sum(call) / len(call)
         w = d["workload"]
+        ab = d["bytes"]["attention"]
         per.append({
             "workload": w.name, "description": w.description,
             "kernel": d["plan"][2],
             "partitions": d["plan"][0], "tokens_per_partition": d["plan"][1],
-            "attn_kernel_us_mean": round(mean * 1e3, 2),
-            "attn_kernel_us_median": round(durs[len(durs) // 2] * 1e3, 2),
-            "attn_kernel_us_min": round(durs[0] * 1e3, 2),
-            "attn_kernel_us_max": round(durs[-1] * 1e3, 2),
-            "attn_bytes": d["bytes"]["attention"],
-            "attn_kernel_GBps": round(d["bytes"]["attention"] / (mean * 1e-3) / 1e9, 1),
-            "pct_of_peak": round(100 * d["bytes"]["attention"] / (mean * 1e-3) / 1e9
-                                 / PEAK_HBM_GBS, 2),
+            "call_us_mean": round(cmean * 1e3, 2),
+            "call_us_median": round(call[len(call) // 2] * 1e3, 2),
+            "call_us_min": round(call[0] * 1e3, 2),
+            "call_us_max": round(call[-1] * 1e3, 2),
+            "attn_bytes": ab,
+            "call_GBps": round(ab / (cmean * 1e-3) / 1e9, 1),
+            "pct_of_peak": round(100 * ab / (cmean * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
+            "attn_kernel_us_mean": round(kmean * 1e3, 2),
+            "attn_kernel_us_median": round(kern[len(kern) // 2] * 1e3, 2),
+            "attn_kernel_us_min": round(kern[0] * 1e3, 2),
+            "attn_kernel_us_max": round(kern[-1] * 1e3, 2),
+            "attn_kernel_GBps": round(ab / (kmean * 1e-3) / 1e9, 1),
+            "attn_kernel_pct_of_peak": round(100 * ab / (kmean * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                                             2),
         })
     hip.close()
 
@@ -536,8 +779,9 @@ def main():
             "partition_tokens": args.partition,
             "block_size": subs[0]["workload"].block_size,
             "formats": f"{args.in_dtype} in, {args.out_dtype} out",
-            "us_per_call": {p["workload"]: p["attn_kernel_us_mean"] for p in per},
+            "us_per_call": {p["workload"]: p["call_us_mean"] for p in per},
             "pct_of_peak": {p["workload"]: p["pct_of_peak"] for p in per},
+            "attn_kernel_us": {p["workload"]: p["attn_kernel_us_mean"] for p in per},
             "kernels": {p["workload"]: p["kernel"] for p in per},
             "step": ("RoPE + KV write, then decode attention (two calls)"
                      if args.rope and args.separate else
@@ -568,6 +812,10 @@ def main():
         line["read_probe"] = probe
     if not args.no_cpu_baseline and (args.in_dtype, args.out_dtype) == ("bf16", "f32"):
         line["cpu_baseline"] = cpu_baseline(subs, args.cpu_seconds)
+    if args.jsonl:
+        del subs
+        torch.cuda.empty_cache()
+        measurement_record(args, torch, pk, wl, args.jsonl)
     out = json.dumps(line)
     print(out, flush=True)
     if args.json_out:

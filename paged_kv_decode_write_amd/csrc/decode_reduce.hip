@@ -9,7 +9,8 @@
 // that motivates the split lists a split-K kernel as out of its scope ("vLLM-Style Llama
 // Inference Engine with Tensor Parallelism", Out of scope); this is the merge it would need.
 //
-// Many partitions: one workgroup of 512 threads per (sequence, query head), one barrier. Every memory read is
+// More than 128 partitions (and the multi-query key split): one workgroup of 512 threads per
+// (sequence, query head), one barrier. Every memory read is
 // issued before any of them is needed, and none waits for another: the merge does not read the
 // context length, because a partition past the context marks its rows with m = -inf (no keys)
 // and its partial outputs are then never used. Each thread folds what it read with the rule
@@ -178,6 +179,81 @@ decode_reduce_narrow_kernel(const DecodeArgs a) {
                  l > 0.f ? x.z / l : 0.f, l > 0.f ? x.w / l : 0.f);
 }
 
+// Up to 128 partitions: SPLIT consecutive lanes share four consecutive output columns of a row
+// and split its partitions between them, lane j reading partitions j, j + SPLIT, ... (NP of
+// them, clamped and masked past the end). Every lane issues all its loads at once (16-byte
+// partial outputs, 8-byte statistics), folds them in partition order as the narrow form does,
+// and the SPLIT lanes then combine their (max, sum, four outputs) by shuffles. No LDS and no
+// barrier: the whole merge is one round trip to memory plus log2(SPLIT) shuffle steps.
+template <int OT, int NP, int SPLIT>
+__global__ void __launch_bounds__(256)
+decode_reduce_split_kernel(const DecodeArgs a) {
+  const int D = a.head_dim;
+  const int tpr = (D / 4) * SPLIT;  // threads per row
+  const size_t row = (size_t)blockIdx.x * (blockDim.x / tpr) + threadIdx.x / tpr;
+  const int j = threadIdx.x % SPLIT;
+  const int d = 4 * ((threadIdx.x % tpr) / SPLIT);
+  const bool live = row < (size_t)a.batch * a.num_q_heads;
+  const size_t r = live ? row : 0;  // dead lanes load row 0 and store nothing
+  const int nparts = a.nparts, last = nparts - 1;
+  const float2* ml = reinterpret_cast<const float2*>(a.ws_ml) + r * nparts;
+  const float* acc = a.ws_acc + r * nparts * D + d;
+  float2 st[NP];
+  float4 ap[NP];
+#pragma unroll
+  for (int u = 0; u < NP; ++u) {
+    const int p = j + u * SPLIT;
+    const int pc = p < nparts ? p : last;
+    st[u] = ml[pc];
+    ap[u] = *reinterpret_cast<const float4*>(acc + (size_t)pc * D);
+  }
+  __builtin_amdgcn_sched_barrier(0);  // keep the loads above ahead of every use
+  float m = kNegInf, l = 0.f;
+  float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int u = 0; u < NP; ++u) {
+    const float m2 = j + u * SPLIT < nparts ? st[u].x : kNegInf;
+    const float mn = fmaxf(m, m2);
+    const float ref = mn == kNegInf ? 0.f : mn;
+    const bool none = m2 == kNegInf;
+    const float s1 = fast_exp2(m - ref), s2 = fast_exp2(m2 - ref);
+    l = fmaf(l, s1, (none ? 0.f : st[u].y) * s2);
+    x.x = fmaf(x.x, s1, (none ? 0.f : ap[u].x) * s2);
+    x.y = fmaf(x.y, s1, (none ? 0.f : ap[u].y) * s2);
+    x.z = fmaf(x.z, s1, (none ? 0.f : ap[u].z) * s2);
+    x.w = fmaf(x.w, s1, (none ? 0.f : ap[u].w) * s2);
+    m = mn;
+  }
+#pragma unroll
+  for (int s = 1; s < SPLIT; s <<= 1) {
+    const float m2 = shfl_xor(m, s), l2 = shfl_xor(l, s);
+    const float x0 = shfl_xor(x.x, s), x1 = shfl_xor(x.y, s), x2 = shfl_xor(x.z, s),
+                x3 = shfl_xor(x.w, s);
+    const float mn = fmaxf(m, m2);
+    const float ref = mn == kNegInf ? 0.f : mn;
+    const float s1 = fast_exp2(m - ref), s2 = fast_exp2(m2 - ref);
+    l = fmaf(l, s1, l2 * s2);
+    x.x = fmaf(x.x, s1, x0 * s2);
+    x.y = fmaf(x.y, s1, x1 * s2);
+    x.z = fmaf(x.z, s1, x2 * s2);
+    x.w = fmaf(x.w, s1, x3 * s2);
+    m = mn;
+  }
+  if (live && j == 0)
+    store_out4<OT>(a.out, row * D + d, l > 0.f ? x.x / l : 0.f, l > 0.f ? x.y / l : 0.f,
+                   l > 0.f ? x.z / l : 0.f, l > 0.f ? x.w / l : 0.f);
+}
+
+template <int OT, int NP, int SPLIT>
+hipError_t launch_split_merge(const DecodeArgs& a, unsigned rows, hipStream_t stream) {
+  const int tpr = (a.head_dim / 4) * SPLIT;
+  const int block = tpr >= 128 ? tpr : 128;
+  const unsigned per = (unsigned)(block / tpr);
+  hipLaunchKernelGGL((decode_reduce_split_kernel<OT, NP, SPLIT>), dim3((rows + per - 1) / per),
+                     dim3(block), 0, stream, a);
+  return hipGetLastError();
+}
+
 template <int OT, bool SPARSE>
 hipError_t launch_reduce_per(const DecodeArgs& a, unsigned rows, hipStream_t stream) {
   if (a.nparts <= 8) {
@@ -194,6 +270,12 @@ hipError_t launch_reduce_per(const DecodeArgs& a, unsigned rows, hipStream_t str
       hipLaunchKernelGGL((decode_reduce_narrow_kernel<OT, 8, SPARSE>), dim3(grid), block, 0,
                          stream, a);
     return hipGetLastError();
+  }
+  if constexpr (!SPARSE) {
+    if (a.nparts <= 16) return launch_split_merge<OT, 4, 4>(a, rows, stream);
+    if (a.nparts <= 32) return launch_split_merge<OT, 8, 4>(a, rows, stream);
+    if (a.nparts <= 64) return launch_split_merge<OT, 16, 4>(a, rows, stream);
+    if (a.nparts <= 128) return launch_split_merge<OT, 16, 8>(a, rows, stream);
   }
   const int groups = kReduceThreads / a.head_dim;
   const int need = (a.nparts + groups - 1) / groups;
