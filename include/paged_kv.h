@@ -210,14 +210,27 @@ int paged_decode_attention_typed(const uint16_t* q, const uint16_t* k_cache,
 
 /* Kernel families for paged_decode_attention_ex. */
 typedef enum {
-  PAGEDKV_KERNEL_AUTO = 0,  /* the library's choice for the shape (the default path):
-                               MFMA_HEADWAVE for contexts over 1024 tokens, else MFMA */
+  PAGEDKV_KERNEL_AUTO = 0,  /* the library's choice for the shape (the default path): for
+                               contexts over 1024 tokens MFMA_HEADWAVE, or MFMA_STREAM when
+                               batch * num_kv_heads exceeds a quarter of the compute units and
+                               the head-per-wave plan would leave a partial last round of
+                               workgroups; for shorter contexts MFMA */
   PAGEDKV_KERNEL_VALU = 1,  /* fp32 vector-ALU dot products and accumulation; a workgroup's
                                4 waves split one (sequence, KV head) partition */
   PAGEDKV_KERNEL_MFMA = 2,  /* bf16 matrix-core (MFMA) tiles, fp32 accumulation; a
                                workgroup's 4 waves split one (sequence, KV head) partition */
-  PAGEDKV_KERNEL_MFMA_HEADWAVE = 3  /* MFMA tiles; a workgroup's 4 waves take 4 KV heads of
+  PAGEDKV_KERNEL_MFMA_HEADWAVE = 3, /* MFMA tiles; a workgroup's 4 waves take 4 KV heads of
                                one (sequence, partition), one wave per head */
+  PAGEDKV_KERNEL_MFMA_STREAM = 4  /* MFMA tiles, one wave per KV head as in MFMA_HEADWAVE; a
+                               persistent grid (two workgroups per compute unit) counts the
+                               batch's work on the device from context_lens and gives every
+                               workgroup an equal contiguous slice of it (32-token pairs of
+                               (sequence, 4 KV heads)), so ragged batches stay balanced; a
+                               slice that spans sequences leaves one partial per sequence for
+                               the partition merge. Contexts over 1024 tokens only. It always
+                               splits: partition_tokens 0 lets the library bound the partials
+                               (at most 16 per sequence), > 0 sets the least tokens per
+                               workgroup, -1 returns PAGEDKV_ERR_UNSUPPORTED */
 } pagedkv_kernel;
 
 /*
@@ -270,7 +283,7 @@ int paged_decode_step(const uint16_t* q, const uint16_t* k_new, const uint16_t* 
                       hipEvent_t ev_end, hipStream_t stream);
 
 /* Size of the device scratch array paged_decode_step_noalloc uses (per device). */
-#define PAGEDKV_STATIC_SCRATCH_BYTES (16u << 20)
+#define PAGEDKV_STATIC_SCRATCH_BYTES (32u << 20)
 
 /*
  * paged_decode_step_noalloc -- paged_decode_step for callers that cannot allocate device
@@ -340,7 +353,8 @@ int paged_decode_step_rope(const uint16_t* q, const uint16_t* k_new, const uint1
 /*
  * paged_decode_plan -- the launch paged_decode_attention_ex would make for these sizes on
  * the current device, without launching: number of sequence partitions, tokens per
- * partition, and the kernel family (a pagedkv_kernel value, never AUTO). partition_tokens
+ * partition, and the kernel family (a pagedkv_kernel value, never AUTO). For the stream
+ * family: partial slots per (sequence, KV head) and the least tokens per workgroup. partition_tokens
  * and kernel as in paged_decode_attention_ex. Returns a status; the outputs are written on
  * PAGEDKV_OK (chosen_kernel may be NULL). The plan depends on the device only through its
  * compute-unit count; if the environment variable PAGEDKV_CU_COUNT holds a positive integer,

@@ -20,7 +20,7 @@ LIB_NAME = "libpagedkv.so"
 STATUS_NAMES = {0: "PAGEDKV_OK", 1: "PAGEDKV_ERR_NULL", 2: "PAGEDKV_ERR_SHAPE",
                 3: "PAGEDKV_ERR_UNSUPPORTED", 4: "PAGEDKV_ERR_WORKSPACE", 5: "PAGEDKV_ERR_HIP",
                 6: "PAGEDKV_ERR_ALIGN"}
-KERNELS = {"auto": 0, "valu": 1, "mfma": 2, "mfma_hw": 3}
+KERNELS = {"auto": 0, "valu": 1, "mfma": 2, "mfma_hw": 3, "mfma_sk": 4}
 # pagedkv_dtype values of the tensor element types the library takes.
 DTYPES = {torch.bfloat16: 0, torch.float16: 1, torch.float32: 2}
 INPUT_TYPES = (torch.bfloat16, torch.float16)

@@ -23,7 +23,7 @@ OUT = os.path.join(HERE, "libpagedkv.so")
 PROBE_OUT = os.path.join(HERE, "libpagedkv_probe.so")
 PROBE_SOURCES = ["read_probe.hip"]  # measurement utility, a library of its own
 
-SOURCES = ["api.cpp", "kv_write.hip", "decode_valu.hip", "decode_mfma.hip", "decode_reduce.hip",
+SOURCES = ["api.cpp", "kv_write.hip", "decode_valu.hip", "decode_mfma.hip", "decode_sk.hip", "decode_reduce.hip",
            "prefill_mfma.hip", "kv_write_rope.hip", "block_table.hip"]
 ARCH = os.environ.get("PAGEDKV_ARCH", "gfx950")
 

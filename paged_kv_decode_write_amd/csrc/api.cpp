@@ -126,14 +126,48 @@ int make_plan(int32_t batch, int32_t num_kv_heads, int32_t max_blocks, int32_t b
   return PAGEDKV_OK;
 }
 
+// Evenly divided (stream-K) decode. A workgroup takes at least `min_pairs` 32-token pairs of
+// the batch's work, so a (sequence, KV head) whose pairs_max pairs at most fall to workgroups
+// in slices of q >= min_pairs items touches at most (pairs_max - 1) / min_pairs + 2 of them:
+// that many partial slots. Automatically the slots are at most kStreamSlots (min_pairs from the
+// table width alone, so the workspace bound needs no device; and never below 256 tokens, below
+// which a slice costs more in start-up than it gains in balance); partition_tokens > 0 sets
+// min_pairs to that many tokens instead. The grid is two workgroups per compute unit (the
+// kernel's registers allow two), kStreamGroupsPerCU.
+constexpr int64_t kStreamSlots = 16;
+constexpr int64_t kStreamPairTokens = 32;
+constexpr int kStreamGroupsPerCU = 2;
+
+struct StreamPlan {
+  int32_t min_pairs;
+  int32_t slots;
+};
+
+StreamPlan stream_plan(int64_t max_len, int32_t partition_tokens) {
+  const int64_t pairs_max = ceil_div(max_len, kStreamPairTokens);
+  int64_t q = 1;
+  if (partition_tokens > 0) {
+    q = ceil_div(partition_tokens, kStreamPairTokens);
+  } else {
+    q = kMinAutoPartition / kStreamPairTokens;  // automatic slices stay >= 256 tokens
+    if (pairs_max > 1 && ceil_div(pairs_max - 1, kStreamSlots - 2) > q)
+      q = ceil_div(pairs_max - 1, kStreamSlots - 2);
+  }
+  if (q < 1) q = 1;
+  const int64_t slots = pairs_max > 0 ? (pairs_max - 1) / q + 2 : 2;
+  return StreamPlan{(int32_t)q, (int32_t)slots};
+}
+
 // Upper bound of the partition count for a partition_tokens setting, device-independent.
+// (The stream family serves contexts over kHeadWaveMinContext tokens only, so its slots count
+// only there.)
 int64_t nparts_bound(int64_t max_len, int32_t block_size, int32_t partition_tokens) {
   if (max_len <= 0 || partition_tokens == -1) return 1;
-  if (partition_tokens > 0) {
-    if (partition_tokens % block_size) return 1;
-    return ceil_div(max_len, partition_tokens);
-  }
-  return ceil_div(max_len, kMinAutoPartition);
+  if (partition_tokens > 0 && partition_tokens % block_size) return 1;
+  const int64_t n = ceil_div(max_len, partition_tokens > 0 ? partition_tokens : kMinAutoPartition);
+  if (max_len <= kHeadWaveMinContext) return n;
+  const int64_t s = stream_plan(max_len, partition_tokens).slots;
+  return n > s ? n : s;
 }
 
 // Workspace layout of a split call: [partial outputs | partial (max, sum)].
@@ -268,6 +302,7 @@ int select_kernel(int32_t kernel, int D, int G, int bs, int64_t max_len, int* ch
       break;
     case PAGEDKV_KERNEL_MFMA:
     case PAGEDKV_KERNEL_MFMA_HEADWAVE:
+    case PAGEDKV_KERNEL_MFMA_STREAM:
       if (supported_mfma(D, G, bs)) { *chosen = kernel; return PAGEDKV_OK; }
       break;
     default:
@@ -277,6 +312,73 @@ int select_kernel(int32_t kernel, int D, int G, int bs, int64_t max_len, int* ch
               "no %s kernel for head_dim %d, block_size %d, group size %d",
               kernel == PAGEDKV_KERNEL_MFMA ? "MFMA" : kernel == PAGEDKV_KERNEL_VALU ? "VALU" : "",
               D, bs, G);
+}
+
+// The launch of a decode call: the kernel family, its partitions (for the stream family:
+// partial slots and minimum tokens per workgroup) and, for the stream family, the grid.
+// An automatic choice of the head-per-wave kernel becomes the stream family when the caller
+// left the split to the library, the (sequence, KV head) units exceed a quarter of the compute
+// units, and the head-per-wave plan would not fill the device in whole rounds of workgroups
+// (more workgroups than resident slots, two per compute unit, and not a multiple of them): its
+// last, partial round then runs as a tail while most of the device idles, and the stream family,
+// which always makes exactly one round of equal slices, is faster (ragged or not). A plan in
+// whole rounds keeps the head-per-wave kernel: on uniform batches of full-width tables it is
+// about 1% faster (the stream family spends one more memory round trip reading the lengths
+// before it can read the block ids), and the host cannot see whether the batch is ragged
+// without reading context_lens, which would need a synchronisation.
+struct DecodePlan {
+  int kernel;
+  Plan plan;
+  int32_t min_pairs;  // stream family only
+  int32_t grid;       // stream family only
+};
+
+int plan_granule(int kernel, int32_t block_size);
+
+int plan_decode(int32_t requested, int chosen, int32_t batch, int32_t num_q_heads,
+                int32_t num_kv_heads, int32_t mb16, int32_t partition_tokens, int cus,
+                DecodePlan* out) {
+  const int64_t units = (int64_t)batch * num_kv_heads;
+  if (requested == PAGEDKV_KERNEL_AUTO && chosen == PAGEDKV_KERNEL_MFMA_HEADWAVE &&
+      partition_tokens == 0 && units * 4 > cus) {
+    Plan hw{};
+    const int st = make_plan(batch, num_kv_heads, mb16, kKernelBlock, 0, cus, chosen,
+                             plan_granule(chosen, kKernelBlock), &hw);
+    if (st) return st;
+    const int64_t groups = (int64_t)batch * ceil_div(num_kv_heads, kHeadsPerGroup) * hw.nparts;
+    const int64_t slots = (int64_t)kStreamGroupsPerCU * cus;
+    if (groups > slots && groups % slots) chosen = PAGEDKV_KERNEL_MFMA_STREAM;
+  }
+  out->kernel = chosen;
+  out->min_pairs = 0;
+  out->grid = 0;
+  if (chosen != PAGEDKV_KERNEL_MFMA_STREAM)
+    return make_plan(batch, num_kv_heads, mb16, kKernelBlock, partition_tokens, cus, chosen,
+                     plan_granule(chosen, kKernelBlock), &out->plan);
+  if ((int64_t)mb16 * kKernelBlock <= kHeadWaveMinContext)
+    return fail(PAGEDKV_ERR_UNSUPPORTED,
+                "the stream kernel family takes contexts over %d tokens (max_blocks_per_seq * "
+                "block_size)", (int)kHeadWaveMinContext);
+  if (partition_tokens == -1)
+    return fail(PAGEDKV_ERR_UNSUPPORTED,
+                "the stream kernel family always leaves partials (partition_tokens -1)");
+  if (partition_tokens < -1) return fail(PAGEDKV_ERR_SHAPE, "partition_tokens must be >= -1");
+  if (partition_tokens > 0 && partition_tokens % kKernelBlock)
+    return fail(PAGEDKV_ERR_SHAPE, "partition_tokens %d is not a multiple of 16",
+                partition_tokens);
+  const int64_t max_len = (int64_t)mb16 * kKernelBlock;
+  const StreamPlan sp = stream_plan(max_len, partition_tokens);
+  const int64_t ngrp = ceil_div(num_kv_heads, kHeadsPerGroup);
+  const int64_t work = (int64_t)batch * ngrp * ceil_div(max_len, kStreamPairTokens);
+  const int64_t grid = (int64_t)kStreamGroupsPerCU * cus;
+  if (work + grid > INT32_MAX / 2 || grid > INT32_MAX / 2 ||
+      (int64_t)batch * num_q_heads * sp.slots > INT32_MAX)
+    return fail(PAGEDKV_ERR_SHAPE, "stream plan overflows (batch * heads * context too large)");
+  out->plan.nparts = sp.slots;
+  out->plan.part_tokens = (int32_t)(sp.min_pairs * kStreamPairTokens);
+  out->min_pairs = sp.min_pairs;
+  out->grid = (int32_t)grid;
+  return PAGEDKV_OK;
 }
 
 int plan_granule(int kernel, int32_t block_size) {
@@ -419,10 +521,12 @@ int decode_impl(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_ca
   int cus = 0;
   st = cu_count(&cus);
   if (st) return st;
-  Plan plan{};
-  st = make_plan(batch, num_kv_heads, mb16, kKernelBlock, partition_tokens, cus, chosen,
-                 plan_granule(chosen, kKernelBlock), &plan);
+  DecodePlan dp{};
+  st = plan_decode(kernel, chosen, batch, num_q_heads, num_kv_heads, mb16, partition_tokens, cus,
+                   &dp);
   if (st) return st;
+  chosen = dp.kernel;
+  const Plan plan = dp.plan;
 
   DecodeArgs a{};
   a.q = q;
@@ -443,6 +547,7 @@ int decode_impl(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_ca
   a.part_tokens = plan.part_tokens;
   a.kv_dtype = kv_dtype;
   a.out_dtype = out_dtype;
+  a.sk_min_pairs = dp.min_pairs;
   const size_t split_need = split_workspace_bytes(batch, num_q_heads, head_dim, plan.nparts);
   const size_t table_need = view_table_bytes(batch, max_blocks_per_seq, sub);
   if (static_scratch) {
@@ -520,6 +625,7 @@ int decode_impl(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_ca
   switch (chosen) {
     case PAGEDKV_KERNEL_MFMA: e = launch_decode_mfma(a, stream); break;
     case PAGEDKV_KERNEL_MFMA_HEADWAVE: e = launch_decode_mfma_hw(a, stream); break;
+    case PAGEDKV_KERNEL_MFMA_STREAM: e = launch_decode_mfma_sk(a, dp.grid, stream); break;
     default: e = launch_decode_valu(a, stream); break;
   }
   if (e != hipSuccess) return hip_fail(e, "decode attention launch");
@@ -667,13 +773,13 @@ int paged_decode_plan(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
   int cus = 0;
   st = cu_count(&cus);
   if (st) return st;
-  Plan plan{};
-  st = make_plan(batch, num_kv_heads, mb16, kKernelBlock, partition_tokens, cus, chosen,
-                 plan_granule(chosen, kKernelBlock), &plan);
+  DecodePlan dp{};
+  st = plan_decode(kernel, chosen, batch, num_q_heads, num_kv_heads, mb16, partition_tokens, cus,
+                   &dp);
   if (st) return st;
-  *num_partitions = plan.nparts;
-  *tokens_per_partition = plan.part_tokens;
-  if (chosen_kernel) *chosen_kernel = chosen;
+  *num_partitions = dp.plan.nparts;
+  *tokens_per_partition = dp.plan.part_tokens;
+  if (chosen_kernel) *chosen_kernel = dp.kernel;
   return PAGEDKV_OK;
 }
 

@@ -185,7 +185,10 @@ decode_reduce_narrow_kernel(const DecodeArgs a) {
 // partial outputs, 8-byte statistics), folds them in partition order as the narrow form does,
 // and the SPLIT lanes then combine their (max, sum, four outputs) by shuffles. No LDS and no
 // barrier: the whole merge is one round trip to memory plus log2(SPLIT) shuffle steps.
-template <int OT, int NP, int SPLIT>
+// LIVE: read a slot's partial output only when its statistics say it saw keys (m > -inf): a
+// second round trip, worth it when most slots are empty (the stream family's, whose slot count
+// bounds the segments a sequence can need while a uniform batch uses a few of them).
+template <int OT, int NP, int SPLIT, bool LIVE>
 __global__ void __launch_bounds__(256)
 decode_reduce_split_kernel(const DecodeArgs a) {
   const int D = a.head_dim;
@@ -205,7 +208,20 @@ decode_reduce_split_kernel(const DecodeArgs a) {
     const int p = j + u * SPLIT;
     const int pc = p < nparts ? p : last;
     st[u] = ml[pc];
-    ap[u] = *reinterpret_cast<const float4*>(acc + (size_t)pc * D);
+    if constexpr (!LIVE) ap[u] = *reinterpret_cast<const float4*>(acc + (size_t)pc * D);
+  }
+  if constexpr (LIVE)  // with the statistics: slot j (see below)
+    ap[0] = *reinterpret_cast<const float4*>(acc + (size_t)(j < nparts ? j : last) * D);
+  if constexpr (LIVE) {
+    // The first SPLIT slots were read with the statistics (a sequence's first segments fill the
+    // lowest slots, so on a uniform batch these are all its live ones); the rest only if live.
+#pragma unroll
+    for (int u = 1; u < NP; ++u) {
+      const int p = j + u * SPLIT;
+      ap[u] = p < nparts && st[u].x != kNegInf
+                  ? *reinterpret_cast<const float4*>(acc + (size_t)p * D)
+                  : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
   }
   __builtin_amdgcn_sched_barrier(0);  // keep the loads above ahead of every use
   float m = kNegInf, l = 0.f;
@@ -249,8 +265,12 @@ hipError_t launch_split_merge(const DecodeArgs& a, unsigned rows, hipStream_t st
   const int tpr = (a.head_dim / 4) * SPLIT;
   const int block = tpr >= 128 ? tpr : 128;
   const unsigned per = (unsigned)(block / tpr);
-  hipLaunchKernelGGL((decode_reduce_split_kernel<OT, NP, SPLIT>), dim3((rows + per - 1) / per),
-                     dim3(block), 0, stream, a);
+  if (a.sk_min_pairs > 0)  // the stream family's slots: mostly empty on uniform batches
+    hipLaunchKernelGGL((decode_reduce_split_kernel<OT, NP, SPLIT, true>),
+                       dim3((rows + per - 1) / per), dim3(block), 0, stream, a);
+  else
+    hipLaunchKernelGGL((decode_reduce_split_kernel<OT, NP, SPLIT, false>),
+                       dim3((rows + per - 1) / per), dim3(block), 0, stream, a);
   return hipGetLastError();
 }
 

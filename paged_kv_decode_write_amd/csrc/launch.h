@@ -42,6 +42,9 @@ struct DecodeArgs {
   const float* inv_freq;
   int32_t interleaved;
   uint16_t* q_out;
+  // Evenly divided (stream-K) launch: a workgroup takes at least this many 32-token pairs of
+  // the batch's work; nparts is then the number of partial slots per (sequence, KV head).
+  int32_t sk_min_pairs;
 };
 
 // Arguments of one multi-query causal (prefill) launch, already validated.
@@ -108,6 +111,9 @@ bool supported_mfma(int head_dim, int group, int block_size);
 hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream);
 // One wave per KV head, kHeadsPerGroup heads of a (sequence, partition) per workgroup.
 hipError_t launch_decode_mfma_hw(const DecodeArgs& a, hipStream_t stream);
+// The batch's work counted on the device and cut into equal slices, one per workgroup of
+// `workgroups` (kHeadsPerGroup KV heads, one wave each); leaves partials for the merge.
+hipError_t launch_decode_mfma_sk(const DecodeArgs& a, int workgroups, hipStream_t stream);
 
 hipError_t launch_decode_reduce(const DecodeArgs& a, hipStream_t stream);
 // The merge of the multi-query key split: rows are (token, query head); rows marked done are

@@ -449,13 +449,11 @@ __device__ __forceinline__ void softmax_step(WaveState<EPL>& st, const float (&s
   split_weights<KT>(p, phi, plo);
 }
 
-// q.K, online softmax and p.V for one loaded pair and one 16-row N block (decode).
+// Online softmax and p.V for one loaded pair whose scores s are computed (decode).
 template <int KT, int NCH, int EPL>
-__device__ __forceinline__ void pair_compute(PairTile<NCH, EPL>& t, WaveState<EPL>& st,
-                                             const uint4 (&qb)[NCH], float sl2, int kg) {
+__device__ __forceinline__ void pair_finish(PairTile<NCH, EPL>& t, WaveState<EPL>& st,
+                                            float (&s)[8], int kg) {
   constexpr int BS = 16;
-  float s[8];
-  pair_scores<KT>(t, qb, sl2, s);
   if (t.lastA < BS || t.lastB < BS) {  // a block holds positions at or past the end
     mask_stale_scores(t, kg, s);
     clear_stale_rows(t, kg);
@@ -468,6 +466,15 @@ __device__ __forceinline__ void pair_compute(PairTile<NCH, EPL>& t, WaveState<EP
     st.acc[e] = mfma16x16x32<KT>(vt, phi, st.acc[e]);
     st.acc[e] = mfma16x16x32<KT>(vt, plo, st.acc[e]);
   }
+}
+
+// q.K, online softmax and p.V for one loaded pair and one 16-row N block (decode).
+template <int KT, int NCH, int EPL>
+__device__ __forceinline__ void pair_compute(PairTile<NCH, EPL>& t, WaveState<EPL>& st,
+                                             const uint4 (&qb)[NCH], float sl2, int kg) {
+  float s[8];
+  pair_scores<KT>(t, qb, sl2, s);
+  pair_finish<KT>(t, st, s, kg);
 }
 
 }  // namespace pagedkv

@@ -193,19 +193,21 @@ def test_workspace_bytes(lib):
     f = lib.paged_decode_workspace_bytes
     assert f(64, 32, 128, 512, 16, -1) == 0              # never split
     assert f(1, 32, 64, 8, 16, 0) == 0                   # 128 tokens: auto never splits
-    # forced 256-token partitions over 32768 tokens: 128 partitions of D+2 floats per head
-    n = 128
-    acc = 2 * 32 * n * 128 * 4
-    ml = 2 * 32 * n * 2 * 4
-    assert f(2, 32, 128, 2048, 16, 256) == acc + ml
-    # auto bound: partitions of at least 256 tokens
-    assert f(2, 32, 128, 2048, 16, 0) == acc + ml
+    def split(n):  # n partial slots of D + 2 floats per (sequence, query head)
+        return 2 * 32 * n * 128 * 4 + 2 * 32 * n * 2 * 4
+    # forced 256-token partitions over 32768 tokens: 128 partitions; the stream family, with
+    # at least 8 pairs of 32 tokens per workgroup, can need (1024 - 1) // 8 + 2 = 129 slots
+    assert f(2, 32, 128, 2048, 16, 256) == split(129)
+    # auto bound: partitions of at least 256 tokens (128), or the stream family's 16 at most
+    assert f(2, 32, 128, 2048, 16, 0) == split(128)
     assert f(2, 32, 128, 2048, 16, 24) == 0               # not a multiple of block_size
     assert f(0, 32, 128, 2048, 16, 0) == 0
+    # 2048 tokens: 8 partitions of 256, or the stream family's (64 - 1) // 8 + 2 = 9 slots
+    assert f(2, 32, 128, 128, 16, 0) == split(9)
     # blocks of 32 or 64 tokens: the same split region, then the table of 16-token block ids
     # (batch x max_blocks x block_size/16 int32, rounded up to 256 bytes)
-    assert f(2, 32, 128, 1024, 32, 256) == acc + ml + 2 * 1024 * 2 * 4
-    assert f(2, 32, 128, 512, 64, 0) == acc + ml + 2 * 512 * 4 * 4
+    assert f(2, 32, 128, 1024, 32, 256) == split(129) + 2 * 1024 * 2 * 4
+    assert f(2, 32, 128, 512, 64, 0) == split(128) + 2 * 512 * 4 * 4
     assert f(3, 8, 64, 5, 32, -1) == 256                 # 3 x 10 ids, one 256-byte granule
 
 

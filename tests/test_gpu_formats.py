@@ -31,6 +31,26 @@ def dev():
     return torch.device("cuda:0")
 
 
+def families(w):
+    """The kernel families built for workload w's shape (the stream family takes contexts over
+    1024 tokens only, the vector-ALU family group sizes 1, 2, 3, 4 and 8)."""
+    out = []
+    for k in ("valu", "mfma", "mfma_hw", "mfma_sk"):
+        try:
+            pk.decode_plan(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.max_blocks,
+                           w.block_size, 0, k)
+            out.append(k)
+        except pk.PagedKVError:
+            pass
+    return out
+
+
+def part_for(kernel, partition):
+    """partition_tokens for a kernel family: the stream family always leaves partials, so
+    where a test asks for no split (-1) it runs with the family's own automatic slices."""
+    return 0 if kernel == "mfma_sk" and partition == -1 else partition
+
+
 def to_dev(inp, dev):
     return {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
 
@@ -100,7 +120,8 @@ def run_decode(d, ot, kernel="auto", partition=0):
     out = torch.full((w.batch, w.num_q_heads, w.head_dim), float("nan"), dtype=TORCH[ot],
                      device=d["q"].device)
     pk.paged_decode_attention(d["q"], d["k_cache"], d["v_cache"], d["block_tables"],
-                              d["context_lens"], d["scale"], out, partition_tokens=partition,
+                              d["context_lens"], d["scale"], out,
+                              partition_tokens=part_for(kernel, partition),
                               kernel=kernel)
     return out
 
@@ -110,10 +131,8 @@ def run_decode(d, ot, kernel="auto", partition=0):
 def test_decode_formats_all_kernels_and_splits(dev, name, kvt, ot):
     ref, d = decode_case(name, kvt, dev)
     w = wl.WORKLOADS[name]
-    for kernel in ("valu", "mfma", "mfma_hw"):
+    for kernel in families(w):
         for part in (-1, 0, 256):
-            if kernel == "valu" and w.gqa not in (1, 2, 3, 4, 8):
-                continue
             out = run_decode(d, ot, kernel, part)
             full = run_decode(d, "f32", kernel, part) if ot != "f32" else None
             check_output(out, ref, ot, f"{name}/{kvt}->{ot}/{kernel}/p{part}", full)
@@ -135,7 +154,7 @@ def test_decode_formats_with_32_token_blocks(dev, kvt, ot):
                                   host["context_lens"], host["scale"], dtype=kvt)
     d = to_dev(inp, dev)
     pk.paged_kv_write(d["k_new"], d["v_new"], d["slot_mapping"], d["k_cache"], d["v_cache"])
-    for kernel in ("valu", "mfma", "mfma_hw"):
+    for kernel in families(w):
         for part in (-1, 0, 256):
             out = run_decode(d, ot, kernel, part)
             full = run_decode(d, "f32", kernel, part) if ot != "f32" else None
@@ -189,11 +208,11 @@ def test_f16_small_weights_still_count(dev):
     ref = oracle.decode_attention(wl.to_bits(q), wl.to_bits(kc), wl.to_bits(vc), tables.numpy(),
                                   lens.numpy(), scale, dtype="f16")
     dq, dkc, dvc = q.to(dev), kc.to(dev), vc.to(dev)
-    for kernel in ("mfma", "mfma_hw", "valu"):
+    for kernel in ("mfma", "mfma_hw", "mfma_sk", "valu"):
         for part in (-1, 0):
             out = torch.empty(1, Hq, D, dtype=torch.float32, device=dev)
             pk.paged_decode_attention(dq, dkc, dvc, tables.to(dev), lens.to(dev), scale, out,
-                                      partition_tokens=part, kernel=kernel)
+                                      partition_tokens=part_for(kernel, part), kernel=kernel)
             err = np.abs(out.cpu().double().numpy() - ref).max()
             print(f"[formats] f16 small weights {kernel}/p{part}: {err:.3e}", flush=True)
             assert err <= 1e-4, (kernel, part, err)
@@ -258,9 +277,7 @@ def test_decode_step_formats_match_separate_calls(dev, name, kvt, ot):
     every kernel family and split."""
     w = wl.WORKLOADS[name]
     inp = wl.make_inputs(w, dtype=kvt, poison=True)
-    for kernel in ("auto", "valu", "mfma", "mfma_hw"):
-        if kernel == "valu" and w.gqa not in (1, 2, 3, 4, 8):
-            continue
+    for kernel in ["auto"] + families(w):
         for part in (-1, 0, 256):
             fused, sep = to_dev(inp, dev), to_dev(inp, dev)
             out_f = torch.full((w.batch, w.num_q_heads, w.head_dim), float("nan"),
@@ -268,7 +285,7 @@ def test_decode_step_formats_match_separate_calls(dev, name, kvt, ot):
             pk.paged_decode_step(fused["q"], fused["k_new"], fused["v_new"],
                                  fused["slot_mapping"], fused["k_cache"], fused["v_cache"],
                                  fused["block_tables"], fused["context_lens"], fused["scale"],
-                                 out_f, partition_tokens=part, kernel=kernel)
+                                 out_f, partition_tokens=part_for(kernel, part), kernel=kernel)
             pk.paged_kv_write(sep["k_new"], sep["v_new"], sep["slot_mapping"], sep["k_cache"],
                               sep["v_cache"])
             out_s = run_decode(sep, ot, kernel, part)

@@ -44,7 +44,7 @@ def _write_summary():
 
 def kernels_for(w):
     out = []
-    for k in ("valu", "mfma", "mfma_hw"):
+    for k in ("valu", "mfma", "mfma_hw", "mfma_sk"):
         try:
             pk.decode_plan(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.max_blocks,
                            w.block_size, 0, k)
@@ -53,6 +53,12 @@ def kernels_for(w):
             pass
     assert out, f"no kernel for {w}"
     return out
+
+
+def part_for(kernel, partition):
+    """partition_tokens for a kernel family: the stream family always leaves partials, so
+    where a test asks for no split (-1) it runs with the family's own automatic slices."""
+    return 0 if kernel == "mfma_sk" and partition == -1 else partition
 
 
 def to_dev(inp, dev):
@@ -68,7 +74,8 @@ def run_attention(d, kernel="auto", partition=0):
     out = torch.full((w.batch, w.num_q_heads, w.head_dim), float("nan"), dtype=torch.float32,
                      device=d["q"].device)
     pk.paged_decode_attention(d["q"], d["k_cache"], d["v_cache"], d["block_tables"],
-                              d["context_lens"], d["scale"], out, partition_tokens=partition,
+                              d["context_lens"], d["scale"], out,
+                              partition_tokens=part_for(kernel, partition),
                               kernel=kernel)
     return out
 
@@ -355,7 +362,7 @@ def run_step(d, kernel="auto", partition=0):
                      device=d["q"].device)
     pk.paged_decode_step(d["q"], d["k_new"], d["v_new"], d["slot_mapping"], d["k_cache"],
                          d["v_cache"], d["block_tables"], d["context_lens"], d["scale"], out,
-                         partition_tokens=partition, kernel=kernel)
+                         partition_tokens=part_for(kernel, partition), kernel=kernel)
     return out
 
 
@@ -524,8 +531,8 @@ def test_one_workspace_across_shapes(dev):
                 out = torch.full((w.batch, w.num_q_heads, w.head_dim), float("nan"), device=dev)
                 pk.paged_decode_attention(d["q"], d["k_cache"], d["v_cache"], d["block_tables"],
                                           d["context_lens"], d["scale"], out,
-                                          partition_tokens=partition, kernel=kernel,
-                                          workspace=ws)
+                                          partition_tokens=part_for(kernel, partition),
+                                          kernel=kernel, workspace=ws)
                 if ref is not None:
                     err = np.abs(out.cpu().double().numpy() - ref).max()
                     assert err <= ATOL, (kernel, partition, err)
@@ -901,7 +908,7 @@ def run_step_rope(d, pos, inv, interleaved, kernel="auto", partition=0):
     pk.paged_decode_step_rope(d["q"], d["k_new"], d["v_new"], pos, inv, d["slot_mapping"], q_out,
                               d["k_cache"], d["v_cache"], d["block_tables"], d["context_lens"],
                               d["scale"], out, interleaved=interleaved,
-                              partition_tokens=partition, kernel=kernel)
+                              partition_tokens=part_for(kernel, partition), kernel=kernel)
     return q_out, out
 
 

@@ -3,7 +3,8 @@ without a device: PAGEDKV_CU_COUNT stands in for the device's compute-unit count
 MI355X). Expected values are worked out by hand from the planning rule documented in the
 library (comments of make_plan and select_kernel in csrc/api.cpp):
   * contexts over 1024 tokens (max_blocks * block_size) use the one-wave-per-KV-head MFMA
-    kernel, shorter ones the split-wave MFMA kernel;
+    kernel, or the stream family when batch * kv_heads exceeds a quarter of the CUs and the
+    split is left automatic; shorter ones the split-wave MFMA kernel;
   * target work: 4 workgroups per CU (split-wave), 8 waves per CU (head-wave), or 4 when the
     batch * kv_heads units are at most a quarter of the CUs;
   * n = min(ceil(target / units), ceil(max_len / 256)), tokens per partition rounded up to the
@@ -33,12 +34,17 @@ def plan(monkeypatch):
 # (workload, partitions, tokens per partition, kernel), derived per the module docstring:
 #  c1: 128 tokens -> mfma; n = min(ceil(1024/8), ceil(128/256)=1) = 1, P = 128
 #  c2: 512 -> mfma; n = min(32, 2) = 2, P = roundup(256, 128) = 256
-#  c3: 2048 -> mfma_hw; units 128 (x4 > 256): n = min(ceil(2048/128)=16, 8) = 8, P = 256
-#  c4: 4096 -> mfma_hw; units 384: n = min(ceil(2048/384)=6, 16) = 6, P = roundup(683, 32) = 704
-#  c5a: 8192 -> mfma_hw; units 512: n = min(4, 32) = 4, P = 2048
+#  c3: 2048 -> mfma_hw; units 128 (x4 > 256): n = min(ceil(2048/128)=16, 8) = 8, P = 256;
+#      16 x 2 head groups x 8 = 256 workgroups, within the 512 slots: kept
+#  c4: 4096, units 384: head-per-wave n = min(ceil(2048/384)=6, 16) = 6 gives 48 x 2 x 6 = 576
+#      workgroups, a partial second round over 512 slots: the stream family, whose slots and
+#      least pairs per workgroup come from pairs_max = max_len / 32 alone:
+#      q = max(8, ceil((pairs_max - 1) / 14)) = 10, slots (128 - 1) // 10 + 2 = 14, 320 tokens
+#  c5a: 8192 -> mfma_hw; units 512: n = min(4, 32) = 4, P = 2048; 64 x 2 x 4 = 512: one round
 #  c5b: 32768 -> mfma_hw; units 16 (x4 <= 256): n = min(ceil(1024/16)=64, 128) = 64, P = 512
 EXPECTED = {"c1": (1, 128, "mfma"), "c2": (2, 256, "mfma"), "c3": (8, 256, "mfma_hw"),
-            "c4": (6, 704, "mfma_hw"), "c5a": (4, 2048, "mfma_hw"), "c5b": (64, 512, "mfma_hw")}
+            "c4": (14, 320, "mfma_sk"), "c5a": (4, 2048, "mfma_hw"),
+            "c5b": (64, 512, "mfma_hw")}
 
 
 @pytest.mark.parametrize("name", sorted(EXPECTED))
@@ -65,8 +71,31 @@ def test_forced_partitions_and_kernels(plan):
 def test_plan_scales_with_the_compute_units(plan, monkeypatch):
     w = wl.WORKLOADS["c5a"]
     monkeypatch.setenv("PAGEDKV_CU_COUNT", "128")
-    # units 512 (x4 > 128): target 8 * 128 = 1024 waves -> n = 2, P = 4096
-    assert plan(w) == (2, 4096, "mfma_hw")
+    # head-per-wave, units 512: target 8 * 128 = 1024 waves -> n = 2, P = 4096
+    assert plan(w, 0, "mfma_hw") == (2, 4096, "mfma_hw")
+    # c5b's 16 units (x4 <= 128): head-per-wave, 4 * 128 waves -> n = 32, P = 1024
+    assert plan(wl.WORKLOADS["c5b"]) == (32, 1024, "mfma_hw")
+    # with 24 CUs the 16 units exceed a quarter of them; head-per-wave targets 8 * 24 waves ->
+    # n = 12 (P = 2752 -> n = 12), 2 x 2 x 12 = 48 workgroups, one full round of 48 slots: kept
+    monkeypatch.setenv("PAGEDKV_CU_COUNT", "24")
+    assert plan(wl.WORKLOADS["c5b"]) == (12, 2752, "mfma_hw")
+    # with 20 CUs: n = ceil(160 / 16) = 10 (P = 3296 -> n = 10), 40 workgroups over 40 slots:
+    # kept; with 28: n = 14 (P = 2368 -> 14), 56 over 56: kept; with 36: n = 18 (P = 1824 ->
+    # n = 18), 72 over 72: kept -- c5b's plan always fills whole rounds, so the c4 workload
+    # stands for the switch (test_automatic_plan_of_each_workload)
+
+
+def test_stream_family_forced(plan):
+    w = wl.WORKLOADS["c4"]
+    assert plan(w, 0, "mfma_sk") == (14, 320, "mfma_sk")
+    # partition_tokens > 0: the least tokens per workgroup (2 pairs), slots 127 // 2 + 2 = 65
+    assert plan(w, 64, "mfma_sk") == (65, 64, "mfma_sk")
+    with pytest.raises(_binding.PagedKVError):
+        plan(w, -1, "mfma_sk")                                # always splits
+    with pytest.raises(_binding.PagedKVError):
+        plan(wl.WORKLOADS["c2"], 0, "mfma_sk")                # 512 tokens: too short
+    assert plan(w, -1) == (1, 4096, "mfma_hw")                # auto never picks it for -1
+    assert plan(w, 256) == (16, 256, "mfma_hw")               # nor for a forced size
 
 
 # Multi-query (prefill) plans, from the rule documented beside make_prefill_plan: split when
