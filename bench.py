@@ -73,8 +73,13 @@ def parse_args():
                         "frequencies) and attend with the rotated q: one fused launch, or "
                         "with --separate the rotation + write call, then attention")
     p.add_argument("--graph", action="store_true",
-                   help="also capture one step in a HIP graph and time K replays "
-                        "(reported as graph_ms_per_step)")
+                   help="also capture one step in a graph and time K replays: through torch's "
+                        "graph wrapper (graph_ms_per_step) and through the HIP runtime's own "
+                        "stream capture (hip_graph_ms_per_step), beside K plain steps with no "
+                        "timing events (eager_ms_per_step_no_events)")
+    p.add_argument("--graph-steps", type=int, default=1,
+                   help="with --graph: decode steps captured in one graph (as a model captures "
+                        "all its layers' steps in one graph); the times are per step")
     p.add_argument("--flush-mib", type=int, default=0,
                    help="before every step, read a buffer of this many MiB so no input stays "
                         "in the 256 MB last-level cache (cold-cache timing; the read is inside "
@@ -134,6 +139,51 @@ class HipEvents:
         for ev in self.events:
             self.hip.hipEventDestroy(ev)
         self.events = []
+
+
+def hip_graph_replay_ms(args, torch, dev, step):
+    """args.graph_steps steps captured with the HIP runtime's own stream capture
+    (hipStreamBeginCapture on a side stream the library is called on, no torch graph wrapper)
+    into one graph, instantiated and replayed back to back for about args.steps steps;
+    milliseconds per step."""
+    hip = ctypes.CDLL("libamdhip64.so.7")
+    vp = ctypes.c_void_p
+    hip.hipStreamBeginCapture.argtypes = [vp, ctypes.c_int]
+    hip.hipStreamEndCapture.argtypes = [vp, ctypes.POINTER(vp)]
+    hip.hipGraphInstantiate.argtypes = [ctypes.POINTER(vp), vp, vp, vp, ctypes.c_size_t]
+    hip.hipGraphLaunch.argtypes = [vp, vp]
+    hip.hipGraphExecDestroy.argtypes = [vp]
+    hip.hipGraphDestroy.argtypes = [vp]
+    side = torch.cuda.Stream(device=dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        step()  # first call on this stream outside the capture
+    torch.cuda.synchronize()
+    handle = side.cuda_stream
+    graph, exe = vp(), vp()
+    with torch.cuda.stream(side):
+        if hip.hipStreamBeginCapture(handle, 2):  # hipStreamCaptureModeRelaxed
+            raise RuntimeError("hipStreamBeginCapture failed")
+        for _ in range(args.graph_steps):
+            step()
+        if hip.hipStreamEndCapture(handle, ctypes.byref(graph)):
+            raise RuntimeError("hipStreamEndCapture failed")
+    if hip.hipGraphInstantiate(ctypes.byref(exe), graph, None, None, 0):
+        raise RuntimeError("hipGraphInstantiate failed")
+    try:
+        for _ in range(args.warmup):
+            hip.hipGraphLaunch(exe, handle)
+        torch.cuda.synchronize()
+        reps = max(1, args.steps // args.graph_steps)
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            if hip.hipGraphLaunch(exe, handle):
+                raise RuntimeError("hipGraphLaunch failed")
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / (reps * args.graph_steps)
+    finally:
+        hip.hipGraphExecDestroy(exe)
+        hip.hipGraphDestroy(graph)
 
 
 def kernel_source_hash(kernel: str) -> str:
@@ -687,8 +737,18 @@ def main():
         })
     hip.close()
 
-    graph_ms = None
+    graph_ms = hip_graph_ms = eager_ms = None
     if args.graph:
+        # The same steps, plain, with no timing events: the reference for the replays.
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        e0 = time.perf_counter()
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        eager_ms = (time.perf_counter() - e0) * 1e3 / args.steps
+        hip_graph_ms = hip_graph_replay_ms(args, torch, dev, step)
         side = torch.cuda.Stream(device=dev)
         side.wait_stream(torch.cuda.current_stream(dev))
         with torch.cuda.stream(side):
@@ -697,15 +757,17 @@ def main():
         torch.cuda.synchronize()
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
-            step()
+            for _ in range(args.graph_steps):
+                step()
         for _ in range(args.warmup):
             graph.replay()
         torch.cuda.synchronize()
+        reps = max(1, args.steps // args.graph_steps)
         g0 = time.perf_counter()
-        for _ in range(args.steps):
+        for _ in range(reps):
             graph.replay()
         torch.cuda.synchronize()
-        graph_ms = (time.perf_counter() - g0) * 1e3 / args.steps
+        graph_ms = (time.perf_counter() - g0) * 1e3 / (reps * args.graph_steps)
 
     prepared_ms = plain_ms = None
     if args.prepared and not args.rope and not args.separate:
@@ -803,6 +865,8 @@ def main():
     }
     if graph_ms is not None:
         line["graph_ms_per_step"] = round(graph_ms, 4)
+        line["hip_graph_ms_per_step"] = round(hip_graph_ms, 4)
+        line["eager_ms_per_step_no_events"] = round(eager_ms, 4)
     if prepared_ms is not None:
         line["prepared_ms_per_step"] = round(prepared_ms, 4)
         line["plain_ms_per_step_no_events"] = round(plain_ms, 4)

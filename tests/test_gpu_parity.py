@@ -609,6 +609,66 @@ def test_graph_capture_replays_match_eager(dev, name, partition, mode):
     assert np.array_equal(wl.to_bits(d["v_cache"]), eager_vc)
 
 
+@pytest.mark.parametrize("name", ["c1", "c2", "c4"])
+def test_hip_stream_capture_of_several_steps(dev, name):
+    """Eight fused decode steps (as a model captures every layer's step) recorded with the HIP
+    runtime's own stream capture, no torch graph wrapper, into one graph; three replays, with
+    eager work and synchronisations in between, each leave the output and the pools bit-identical
+    to the eager step (the steps are idempotent: each stores the same new rows)."""
+    import ctypes
+    hip = ctypes.CDLL("libamdhip64.so.7")
+    vp = ctypes.c_void_p
+    hip.hipStreamBeginCapture.argtypes = [vp, ctypes.c_int]
+    hip.hipStreamEndCapture.argtypes = [vp, ctypes.POINTER(vp)]
+    hip.hipGraphInstantiate.argtypes = [ctypes.POINTER(vp), vp, vp, vp, ctypes.c_size_t]
+    hip.hipGraphLaunch.argtypes = [vp, vp]
+    hip.hipGraphExecDestroy.argtypes = [vp]
+    hip.hipGraphDestroy.argtypes = [vp]
+    w = wl.WORKLOADS[name]
+    d = to_dev(wl.make_inputs(w, poison=True), dev)
+    out = torch.empty(w.batch, w.num_q_heads, w.head_dim, dtype=torch.float32, device=dev)
+    ws = pk.new_workspace(pk.decode_workspace_bytes(w.batch, w.num_q_heads, w.head_dim,
+                                                    w.max_blocks, w.block_size, 0), dev)
+
+    def step():
+        pk.paged_decode_step(d["q"], d["k_new"], d["v_new"], d["slot_mapping"], d["k_cache"],
+                             d["v_cache"], d["block_tables"], d["context_lens"], d["scale"], out,
+                             workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    eager = out.clone()
+    eager_kc, eager_vc = wl.to_bits(d["k_cache"]), wl.to_bits(d["v_cache"])
+    _, ref, kc_ref, vc_ref, _ = case(name, dev, poison=True)
+    assert np.abs(eager.cpu().double().numpy() - ref).max() <= ATOL
+    assert np.array_equal(eager_kc, kc_ref) and np.array_equal(eager_vc, vc_ref)
+    side = torch.cuda.Stream(device=dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.synchronize()
+    graph, exe = vp(), vp()
+    with torch.cuda.stream(side):
+        assert hip.hipStreamBeginCapture(side.cuda_stream, 2) == 0  # relaxed mode
+        for _ in range(8):
+            step()
+        assert hip.hipStreamEndCapture(side.cuda_stream, ctypes.byref(graph)) == 0
+    assert hip.hipGraphInstantiate(ctypes.byref(exe), graph, None, None, 0) == 0
+    try:
+        for r in range(3):
+            out.fill_(float("nan"))
+            d["k_cache"].view(torch.int16)[0, 0, 0, 0] += 0  # eager work between replays
+            torch.cuda.synchronize()
+            assert hip.hipGraphLaunch(exe, side.cuda_stream) == 0
+            torch.cuda.synchronize()
+            assert torch.equal(out, eager), f"replay {r}"
+        assert np.array_equal(wl.to_bits(d["k_cache"]), eager_kc)
+        assert np.array_equal(wl.to_bits(d["v_cache"]), eager_vc)
+    finally:
+        hip.hipGraphExecDestroy(exe)
+        hip.hipGraphDestroy(graph)
+
+
 # ------------------------------------------------------- multi-query causal (prefill)
 _PCASES = {}
 
