@@ -45,7 +45,8 @@ def parse_args():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="c5")
-    p.add_argument("--kernel", default="auto", choices=["auto", "valu", "mfma", "mfma_hw"])
+    p.add_argument("--kernel", default="auto",
+                   choices=["auto", "valu", "mfma", "mfma_hw", "mfma_sk"])
     p.add_argument("--partition", type=int, default=0,
                    help="tokens per partition (multi-query workloads: keys per partition of a "
                         "query tile, a multiple of 32): 0 automatic, -1 never split")
@@ -94,6 +95,12 @@ def parse_args():
     p.add_argument("--copy-calibration-mib", type=int, default=0,
                    help="run one plain device-to-device copy of this many MiB before the "
                         "steps (reference dispatch for hardware byte counters)")
+    p.add_argument("--record-traffic", default=None, metavar="DIR",
+                   help="no GPU run: read the FETCH_SIZE and WRITE_SIZE counter passes under "
+                        "DIR/FETCH_SIZE and DIR/WRITE_SIZE (rocprofv3 csv of this script with "
+                        "--copy-calibration-mib 1024), scale them by the copy's readings and "
+                        "store the workload's HBM bytes per attention launch in "
+                        "profiles/decode_traffic.json")
     args = p.parse_args()
     if args.block_size < 16 or args.block_size % 16:
         p.error(f"--block-size {args.block_size}: a multiple of 16 tokens")
@@ -186,11 +193,15 @@ def hip_graph_replay_ms(args, torch, dev, step):
         hip.hipGraphDestroy(graph)
 
 
-def kernel_source_hash(kernel: str) -> str:
-    """Hash of the code (comments and blank lines removed) of the sources a decode kernel
-    family is built from: a recorded traffic figure stays valid across comment edits only."""
+KERNEL_SOURCES = {"valu": "decode_valu.hip", "mfma": "decode_mfma.hip",
+                  "mfma_hw": "decode_mfma.hip", "mfma_sk": "decode_sk.hip"}
+KERNEL_SYMBOLS = {"valu": "decode_valu_kernel<", "mfma": "decode_mfma_kernel<",
+                  "mfma_hw": "decode_mfma_hw_kernel<", "mfma_sk": "decode_mfma_sk_kernel<"}
+
+
+def _code_hash(files) -> str:
+    """Hash of the code of these csrc files with comments and blank lines removed."""
     csrc = os.path.join(HERE, "paged_kv_decode_write_amd", "csrc")
-    files = ["device_common.h", "launch.h", "mfma_tiles.h", "decode_%s.hip" % kernel.split("_")[0]]
     h = hashlib.sha256()
     for f in files:
         with open(os.path.join(csrc, f), encoding="utf-8") as fh:
@@ -200,6 +211,75 @@ def kernel_source_hash(kernel: str) -> str:
             if code.strip():
                 h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
+
+
+def kernel_source_hash(kernel: str) -> str:
+    """Hash of the code of the sources a decode kernel family is built from: a recorded
+    traffic figure stays valid across comment edits only."""
+    return _code_hash(["device_common.h", "launch.h", "mfma_tiles.h", "decode_step.h",
+                       KERNEL_SOURCES[kernel]])
+
+
+def library_source_hash() -> str:
+    """Hash of the code of every source the library is built from."""
+    csrc = os.path.join(HERE, "paged_kv_decode_write_amd", "csrc")
+    return _code_hash(sorted(f for f in os.listdir(csrc) if f.endswith((".h", ".hip", ".cpp"))))
+
+
+def record_traffic(args):
+    """HBM bytes per attention launch from two rocprofv3 counter passes of this script
+    (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled so that the plain copy of
+    --copy-calibration-mib 1024 run in the same pass reads and writes exactly 1 GiB; the
+    figure is stored with the hash of the kernel's sources, and a later run reports it only
+    while that hash still matches."""
+    import csv
+    import statistics
+    copy_mib = 1024
+    copy_grid = 131072  # work items of the runtime's copyBuffer dispatch for a 1 GiB copy
+    per, copy = {}, {}
+    for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+        path = os.path.join(args.record_traffic, counter, "run_counter_collection.csv")
+        with open(path, newline="") as f:
+            rows = [r for r in csv.DictReader(f) if r["Counter_Name"] == counter]
+        if args.kernel == "auto":
+            counts = {k: sum(sym in r["Kernel_Name"] for r in rows)
+                      for k, sym in KERNEL_SYMBOLS.items()}
+            kernel = max(counts, key=counts.get)
+        else:
+            kernel = args.kernel
+        per[counter] = [float(r["Counter_Value"]) for r in rows
+                        if KERNEL_SYMBOLS[kernel] in r["Kernel_Name"]]
+        copies = [float(r["Counter_Value"]) for r in rows
+                  if "copyBuffer" in r["Kernel_Name"] and int(r["Grid_Size"]) == copy_grid]
+        if not per[counter] or not copies:
+            raise SystemExit(f"{path}: no {kernel} dispatch or no {copy_mib} MiB copy")
+        copy[counter] = copies[0]
+    fetch_scale = (copy_mib << 10) / copy["FETCH_SIZE"]
+    write_scale = (copy_mib << 10) / copy["WRITE_SIZE"]
+    fetch = statistics.fmean(per["FETCH_SIZE"]) * 1024 * fetch_scale
+    write = statistics.fmean(per["WRITE_SIZE"]) * 1024 * write_scale
+    cmd = ("rocprofv3 --pmc {c} --output-format csv -d {d}/{c} -o run -- python -u bench.py "
+           "--workload {w} --steps 3 --warmup 1 --no-cpu-baseline --no-read-probe "
+           "--copy-calibration-mib 1024")
+    rec = {"kernel": kernel, "kernel_source": kernel_source_hash(kernel),
+           "bytes_per_launch": int(round(fetch + write)),
+           "fetch_bytes_per_launch": int(round(fetch)), "write_bytes_per_launch": int(round(write)),
+           "fetch_scale": round(fetch_scale, 5), "write_scale": round(write_scale, 5),
+           "launches": len(per["FETCH_SIZE"]),
+           "fetch_kib_per_launch": per["FETCH_SIZE"], "write_kib_per_launch": per["WRITE_SIZE"],
+           "copy_fetch_kib": copy["FETCH_SIZE"], "copy_write_kib": copy["WRITE_SIZE"],
+           "commands": [cmd.format(c=c, d=args.record_traffic, w=args.workload)
+                        for c in ("FETCH_SIZE", "WRITE_SIZE")]}
+    table = {}
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            table = json.load(f)
+    table[args.workload] = rec
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(table, f, indent=1)
+        f.write("\n")
+    print(json.dumps({k: rec[k] for k in ("kernel", "bytes_per_launch", "fetch_scale",
+                                          "write_scale", "launches")}))
 
 
 def resolved_kernel(pk, w, requested):
@@ -370,7 +450,7 @@ def _environment(torch):
             "compute_units": props.multi_processor_count, "rocm": rocm,
             "hip": torch.version.hip, "torch": torch.__version__,
             "host_cores": len(os.sched_getaffinity(0)),
-            "kernel_source": kernel_source_hash("mfma_hw")}
+            "library_source": library_source_hash()}
 
 
 def _input_sha256(d):
@@ -565,6 +645,9 @@ def bench_prefill(args, torch, pk, wl):
 
 def main():
     args = parse_args()
+    if args.record_traffic:
+        record_traffic(args)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the path has no "
               "multi-GPU leg to time.", file=sys.stderr)
