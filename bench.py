@@ -214,10 +214,13 @@ def _code_hash(files) -> str:
 
 
 def kernel_source_hash(kernel: str) -> str:
-    """Hash of the code of the sources a decode kernel family is built from: a recorded
-    traffic figure stays valid across comment edits only."""
-    return _code_hash(["device_common.h", "launch.h", "mfma_tiles.h", "decode_step.h",
-                       KERNEL_SOURCES[kernel]])
+    """Hash of the code of the sources the decode kernel families `kernel` ("a" or "a+b") are
+    built from: a recorded traffic figure stays valid across comment edits only."""
+    files = ["device_common.h", "launch.h", "mfma_tiles.h", "decode_step.h"]
+    for k in kernel.split("+"):
+        if KERNEL_SOURCES[k] not in files:
+            files.append(KERNEL_SOURCES[k])
+    return _code_hash(files)
 
 
 def library_source_hash() -> str:
@@ -241,14 +244,14 @@ def record_traffic(args):
         path = os.path.join(args.record_traffic, counter, "run_counter_collection.csv")
         with open(path, newline="") as f:
             rows = [r for r in csv.DictReader(f) if r["Counter_Name"] == counter]
-        if args.kernel == "auto":
-            counts = {k: sum(sym in r["Kernel_Name"] for r in rows)
-                      for k, sym in KERNEL_SYMBOLS.items()}
-            kernel = max(counts, key=counts.get)
-        else:
-            kernel = args.kernel
-        per[counter] = [float(r["Counter_Value"]) for r in rows
-                        if KERNEL_SYMBOLS[kernel] in r["Kernel_Name"]]
+        # every attention dispatch, in order (the merge kernels are not among these)
+        fam = [next((k for k, sym in KERNEL_SYMBOLS.items() if sym in r["Kernel_Name"]), None)
+               for r in rows]
+        used = [k for k in dict.fromkeys(fam) if k is not None]
+        if args.kernel != "auto":
+            used = [args.kernel]
+        kernel = "+".join(used)
+        per[counter] = [float(r["Counter_Value"]) for r, k in zip(rows, fam) if k in used]
         copies = [float(r["Counter_Value"]) for r in rows
                   if "copyBuffer" in r["Kernel_Name"] and int(r["Grid_Size"]) == copy_grid]
         if not per[counter] or not copies:
@@ -280,13 +283,6 @@ def record_traffic(args):
         f.write("\n")
     print(json.dumps({k: rec[k] for k in ("kernel", "bytes_per_launch", "fetch_scale",
                                           "write_scale", "launches")}))
-
-
-def resolved_kernel(pk, w, requested):
-    if requested != "auto":
-        return requested
-    return pk.decode_plan(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.max_blocks,
-                          w.block_size, 0, "auto", with_kernel=True)[2]
 
 
 def read_probe(torch, dev, nbytes, reps=5):
@@ -893,7 +889,7 @@ def main():
     launch_bytes = sum(d["bytes"]["attention"] for d in subs) / len(subs)
     launch_s = sum(p["attn_kernel_us_mean"] for p in per) / len(per) * 1e-6
     achieved = launch_bytes / launch_s / 1e9
-    kernel = resolved_kernel(pk, subs[0]["workload"], args.kernel)
+    kernel = "+".join(dict.fromkeys(p["kernel"] for p in per))
 
     traffic = None
     if os.path.exists(TRAFFIC_FILE):

@@ -213,8 +213,8 @@ typedef enum {
   PAGEDKV_KERNEL_AUTO = 0,  /* the library's choice for the shape (the default path): for
                                contexts over 1024 tokens MFMA_HEADWAVE, or MFMA_STREAM when
                                batch * num_kv_heads exceeds a quarter of the compute units and
-                               the head-per-wave plan would leave a partial last round of
-                               workgroups; for shorter contexts MFMA */
+                               the head-per-wave plan would have more workgroups than compute
+                               units; for shorter contexts MFMA */
   PAGEDKV_KERNEL_VALU = 1,  /* fp32 vector-ALU dot products and accumulation; a workgroup's
                                4 waves split one (sequence, KV head) partition */
   PAGEDKV_KERNEL_MFMA = 2,  /* bf16 matrix-core (MFMA) tiles, fp32 accumulation; a
@@ -222,7 +222,7 @@ typedef enum {
   PAGEDKV_KERNEL_MFMA_HEADWAVE = 3, /* MFMA tiles; a workgroup's 4 waves take 4 KV heads of
                                one (sequence, partition), one wave per head */
   PAGEDKV_KERNEL_MFMA_STREAM = 4  /* MFMA tiles, one wave per KV head as in MFMA_HEADWAVE; a
-                               persistent grid (two workgroups per compute unit) counts the
+                               persistent grid (one workgroup per compute unit) counts the
                                batch's work on the device from context_lens and gives every
                                workgroup an equal contiguous slice of it (32-token pairs of
                                (sequence, 4 KV heads)), so ragged batches stay balanced; a

@@ -132,11 +132,13 @@ int make_plan(int32_t batch, int32_t num_kv_heads, int32_t max_blocks, int32_t b
 // that many partial slots. Automatically the slots are at most kStreamSlots (min_pairs from the
 // table width alone, so the workspace bound needs no device; and never below 256 tokens, below
 // which a slice costs more in start-up than it gains in balance); partition_tokens > 0 sets
-// min_pairs to that many tokens instead. The grid is two workgroups per compute unit (the
-// kernel's registers allow two), kStreamGroupsPerCU.
+// min_pairs to that many tokens instead. The grid is one workgroup (four waves, one per SIMD)
+// per compute unit: with two resident per CU (the registers allow two), the second one's
+// loads were served only after most of the first one's, so on a ragged batch the second
+// finished a quarter of the dispatch later, and the whole kernel ran 5-6% slower.
 constexpr int64_t kStreamSlots = 16;
 constexpr int64_t kStreamPairTokens = 32;
-constexpr int kStreamGroupsPerCU = 2;
+constexpr int kStreamGroupsPerCU = 1;
 
 struct StreamPlan {
   int32_t min_pairs;
@@ -318,14 +320,16 @@ int select_kernel(int32_t kernel, int D, int G, int bs, int64_t max_len, int* ch
 // partial slots and minimum tokens per workgroup) and, for the stream family, the grid.
 // An automatic choice of the head-per-wave kernel becomes the stream family when the caller
 // left the split to the library, the (sequence, KV head) units exceed a quarter of the compute
-// units, and the head-per-wave plan would not fill the device in whole rounds of workgroups
-// (more workgroups than resident slots, two per compute unit, and not a multiple of them): its
-// last, partial round then runs as a tail while most of the device idles, and the stream family,
-// which always makes exactly one round of equal slices, is faster (ragged or not). A plan in
-// whole rounds keeps the head-per-wave kernel: on uniform batches of full-width tables it is
-// about 1% faster (the stream family spends one more memory round trip reading the lengths
-// before it can read the block ids), and the host cannot see whether the batch is ragged
-// without reading context_lens, which would need a synchronisation.
+// units, and the head-per-wave plan has more workgroups than compute units. The head-per-wave
+// plan then keeps two workgroups on a compute unit, and the second one's loads are served
+// mostly after the first one's: it finishes a quarter of the dispatch later, with its compute
+// unit half idle meanwhile; on a ragged batch the plan also leaves partitions empty or short.
+// The stream family runs one workgroup per compute unit on equal slices and measured faster
+// on ragged batches (13%) and on uniform long ones (1.5%). With fewer workgroups than compute
+// units (few, short contexts) the head-per-wave kernel stays: the stream family's extra
+// memory round trip (it reads the lengths before it can read the block ids) costs more there
+// than the balance gains (10% on 16 x 2048 tokens of head_dim 64). The host cannot see the
+// lengths without reading context_lens, which would need a synchronisation.
 struct DecodePlan {
   int kernel;
   Plan plan;
@@ -346,8 +350,7 @@ int plan_decode(int32_t requested, int chosen, int32_t batch, int32_t num_q_head
                              plan_granule(chosen, kKernelBlock), &hw);
     if (st) return st;
     const int64_t groups = (int64_t)batch * ceil_div(num_kv_heads, kHeadsPerGroup) * hw.nparts;
-    const int64_t slots = (int64_t)kStreamGroupsPerCU * cus;
-    if (groups > slots && groups % slots) chosen = PAGEDKV_KERNEL_MFMA_STREAM;
+    if (groups > cus) chosen = PAGEDKV_KERNEL_MFMA_STREAM;
   }
   out->kernel = chosen;
   out->min_pairs = 0;

@@ -31,6 +31,16 @@
 
 namespace pagedkv {
 
+// Pairs in flight per wave (three measured 3% slower than two on the ragged and the uniform
+// long batches), and the least waves per SIMD the registers are sized for (the grid holds
+// one workgroup per compute unit, one wave per SIMD).
+#ifndef PAGEDKV_STREAM_NBUF
+#define PAGEDKV_STREAM_NBUF 2
+#endif
+#ifndef PAGEDKV_STREAM_MINW
+#define PAGEDKV_STREAM_MINW 1
+#endif
+
 __device__ __forceinline__ int wave_sum_i32(int v) {
 #pragma unroll
   for (int s = 32; s >= 1; s >>= 1) v += __shfl_xor(v, s, 64);
@@ -172,7 +182,7 @@ __global__ void __launch_bounds__(HPW * 64, MINW)
 decode_mfma_sk_kernel(const DecodeArgs a, const int32_t* __restrict__ tables,
                       const int32_t* __restrict__ lens, const int64_t* __restrict__ slots,
                       const int32_t* __restrict__ positions) {
-  static_assert(NBUF == 2, "the stream kernel keeps two pairs in flight");
+  static_assert(NBUF == 2 || NBUF == 3, "two or three pairs in flight");
   constexpr int BS = 16, PT = 2 * BS;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -267,41 +277,50 @@ decode_mfma_sk_kernel(const DecodeArgs a, const int32_t* __restrict__ tables,
     const auto head_ld = [&](const SkPos& p) { return min(head(p), Hkv - 1); };
 
     // One continuous pipeline over the slice's pairs, across segment boundaries: pair j is
-    // computed from buffer j % 2 while pair j + 1 is loaded into the other, with block ids read
-    // one pair further ahead, as in the head-per-wave kernel. When pair j ends a segment, the
-    // next segment's q and new rows are loaded right after pair j's scores (q is not needed
-    // again), and its first pair is already in flight, so the boundary costs no round trip.
-    SkPos pc = pos_at(lo, __builtin_amdgcn_readfirstlane(b0),
-                      __builtin_amdgcn_readfirstlane(S0));
-    SkPos p1 = pos_next(pc);
-    SkPos p2 = pos_next(p1);
-    PairTile<NCH, EPL> t[2];
-    int2 idc = sk_ids<D>(sk_ctx<D>(a, tables, pc, head_ld(pc), n16, kg), pc);
-    load_q(pc.b, head_ld(pc));
-    int2 id1 = sk_ids<D>(sk_ctx<D>(a, tables, p1, head_ld(p1), n16, kg), p1);
-    {
-      const PairCtx<D> c = sk_ctx<D>(a, tables, pc, head_ld(pc), n16, kg);
-      pair_issue(t[0], c, idc, 2 * pc.k);
-      pair_valid(t[0], c, idc, 2 * pc.k);
+    // computed from buffer j % NBUF while pairs j + 1 .. j + NBUF - 1 are in flight in the
+    // others, with block ids read one pair further ahead, as in the head-per-wave kernel. When
+    // pair j ends a segment, the next segment's q and new rows are loaded right after pair j's
+    // scores (q is not needed again), and its first pairs are already in flight, so the
+    // boundary costs no round trip. pp[0] is the pair computed next, pp[i] the i-th after it;
+    // ids[i] holds pp[i]'s block ids.
+    SkPos pp[NBUF + 1];
+    pp[0] = pos_at(lo, __builtin_amdgcn_readfirstlane(b0), __builtin_amdgcn_readfirstlane(S0));
+#pragma unroll
+    for (int i = 1; i <= NBUF; ++i) pp[i] = pos_next(pp[i - 1]);
+    PairTile<NCH, EPL> t[NBUF];
+    int2 ids[NBUF];
+    ids[0] = sk_ids<D>(sk_ctx<D>(a, tables, pp[0], head_ld(pp[0]), n16, kg), pp[0]);
+    load_q(pp[0].b, head_ld(pp[0]));
+#pragma unroll
+    for (int i = 1; i < NBUF; ++i)
+      ids[i] = sk_ids<D>(sk_ctx<D>(a, tables, pp[i], head_ld(pp[i]), n16, kg), pp[i]);
+    const int P = hi - lo;
+#pragma unroll
+    for (int i = 0; i + 1 < NBUF; ++i) {  // past the slice's end: pair 0's addresses again
+      const SkPos& pi = i < P ? pp[i] : pp[0];
+      const PairCtx<D> c = sk_ctx<D>(a, tables, pi, head_ld(pi), n16, kg);
+      pair_issue(t[i], c, i < P ? ids[i] : ids[0], 2 * pi.k);
+      pair_valid(t[i], c, i < P ? ids[i] : ids[0], 2 * pi.k);
     }
     WaveState<EPL> st;
     int sub_pos = -1;
     const float sl2 = a.scale_log2;
-    const int P = hi - lo;
-    for (int j = 0; j < P; j += 2) {
+    for (int j = 0; j < P; j += NBUF) {
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
+      for (int u = 0; u < NBUF; ++u) {
         const int jj = j + u;
-        // Issue pair jj + 1 (past the end: repeat pair jj's addresses, never computed).
+        // Issue pair jj + NBUF - 1 (past the end: repeat pair jj's addresses, never computed).
         {
-          const bool more = jj + 1 < P;
-          const SkPos& pi = more ? p1 : pc;
-          const int2 ii = more ? id1 : idc;
+          const bool more = jj + NBUF - 1 < P;
+          const SkPos& pi = more ? pp[NBUF - 1] : pp[0];
+          const int2 ii = more ? ids[NBUF - 1] : ids[0];
           const PairCtx<D> c = sk_ctx<D>(a, tables, pi, head_ld(pi), n16, kg);
-          pair_issue(t[1 - u], c, ii, 2 * pi.k);
-          pair_valid(t[1 - u], c, ii, 2 * pi.k);
+          pair_issue(t[(u + NBUF - 1) % NBUF], c, ii, 2 * pi.k);
+          pair_valid(t[(u + NBUF - 1) % NBUF], c, ii, 2 * pi.k);
         }
-        const int2 id2 = sk_ids<D>(sk_ctx<D>(a, tables, p2, head_ld(p2), n16, kg), p2);
+        const int2 idn = sk_ids<D>(sk_ctx<D>(a, tables, pp[NBUF], head_ld(pp[NBUF]), n16, kg),
+                                   pp[NBUF]);
+        const SkPos& pc = pp[0];
         if (jj < P) {
           if (pc.k == pc.k0) {  // the segment starts: fresh state
             st.m_run = kNegInf;
@@ -321,7 +340,7 @@ decode_mfma_sk_kernel(const DecodeArgs a, const int32_t* __restrict__ tables,
           // the next segment's load right away. With RoPE the close stores them (rotated), so
           // they load after it.
           if constexpr (!ROPE)
-            if (closes && jj + 1 < P) load_q(p1.b, head_ld(p1));
+            if (closes && jj + 1 < P) load_q(pp[1].b, head_ld(pp[1]));
           pair_finish<KT>(t[u], st, sc, kg);
           if (closes) {
             const int g = head(pc);
@@ -329,14 +348,15 @@ decode_mfma_sk_kernel(const DecodeArgs a, const int32_t* __restrict__ tables,
               sk_close<D, NCH, EPL, ROPE>(a, slots, pc, g, w - pc.first / q, st, qb, nrow,
                                           lane);
             if constexpr (ROPE)
-              if (jj + 1 < P) load_q(p1.b, head_ld(p1));
+              if (jj + 1 < P) load_q(pp[1].b, head_ld(pp[1]));
           }
         }
-        pc = p1;
-        p1 = p2;
-        p2 = pos_next(p2);
-        idc = id1;
-        id1 = id2;
+#pragma unroll
+        for (int i = 0; i < NBUF; ++i) pp[i] = pp[i + 1];
+        pp[NBUF] = pos_next(pp[NBUF]);
+#pragma unroll
+        for (int i = 0; i + 1 < NBUF; ++i) ids[i] = ids[i + 1];
+        ids[NBUF - 1] = idn;
       }
     }
   }
@@ -351,7 +371,8 @@ decode_mfma_sk_kernel(const DecodeArgs a, const int32_t* __restrict__ tables,
 
 hipError_t launch_decode_mfma_sk(const DecodeArgs& a, int workgroups, hipStream_t stream) {
   constexpr int HPW = kHeadsPerGroup;
-  constexpr int NBUF = 2;
+  constexpr int NBUF = PAGEDKV_STREAM_NBUF;
+  constexpr int MINW = PAGEDKV_STREAM_MINW;
   return with_formats(a.kv_dtype, a.out_dtype, [&](auto kt, auto ot) {
     constexpr int KT = decltype(kt)::value, OT = decltype(ot)::value;
     constexpr bool kRope = KT == kDtBf16;  // bf16 inputs only, as in the other launches
@@ -359,19 +380,19 @@ hipError_t launch_decode_mfma_sk(const DecodeArgs& a, int workgroups, hipStream_
     if (rope && !kRope) return hipErrorInvalidValue;
     const dim3 grid(workgroups), block(HPW * 64);
     if (a.head_dim == 128 && rope)
-      hipLaunchKernelGGL((decode_mfma_sk_kernel<128, HPW, NBUF, 2, KT, OT, kRope>), grid, block,
+      hipLaunchKernelGGL((decode_mfma_sk_kernel<128, HPW, NBUF, MINW, KT, OT, kRope>), grid, block,
                          0, stream, a, a.block_tables, a.context_lens, a.slot_mapping,
                          a.positions);
     else if (a.head_dim == 128)
-      hipLaunchKernelGGL((decode_mfma_sk_kernel<128, HPW, NBUF, 2, KT, OT, false>), grid, block,
+      hipLaunchKernelGGL((decode_mfma_sk_kernel<128, HPW, NBUF, MINW, KT, OT, false>), grid, block,
                          0, stream, a, a.block_tables, a.context_lens, a.slot_mapping,
                          a.positions);
     else if (a.head_dim == 64 && rope)
-      hipLaunchKernelGGL((decode_mfma_sk_kernel<64, HPW, NBUF, 2, KT, OT, kRope>), grid, block,
+      hipLaunchKernelGGL((decode_mfma_sk_kernel<64, HPW, NBUF, MINW, KT, OT, kRope>), grid, block,
                          0, stream, a, a.block_tables, a.context_lens, a.slot_mapping,
                          a.positions);
     else if (a.head_dim == 64)
-      hipLaunchKernelGGL((decode_mfma_sk_kernel<64, HPW, NBUF, 2, KT, OT, false>), grid, block,
+      hipLaunchKernelGGL((decode_mfma_sk_kernel<64, HPW, NBUF, MINW, KT, OT, false>), grid, block,
                          0, stream, a, a.block_tables, a.context_lens, a.slot_mapping,
                          a.positions);
     else

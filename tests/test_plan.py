@@ -3,8 +3,9 @@ without a device: PAGEDKV_CU_COUNT stands in for the device's compute-unit count
 MI355X). Expected values are worked out by hand from the planning rule documented in the
 library (comments of make_plan and select_kernel in csrc/api.cpp):
   * contexts over 1024 tokens (max_blocks * block_size) use the one-wave-per-KV-head MFMA
-    kernel, or the stream family when batch * kv_heads exceeds a quarter of the CUs and the
-    split is left automatic; shorter ones the split-wave MFMA kernel;
+    kernel, or the stream family when batch * kv_heads exceeds a quarter of the CUs, the
+    split is left automatic and the head-per-wave plan has more workgroups than CUs; shorter
+    ones the split-wave MFMA kernel;
   * target work: 4 workgroups per CU (split-wave), 8 waves per CU (head-wave), or 4 when the
     batch * kv_heads units are at most a quarter of the CUs;
   * n = min(ceil(target / units), ceil(max_len / 256)), tokens per partition rounded up to the
@@ -35,15 +36,16 @@ def plan(monkeypatch):
 #  c1: 128 tokens -> mfma; n = min(ceil(1024/8), ceil(128/256)=1) = 1, P = 128
 #  c2: 512 -> mfma; n = min(32, 2) = 2, P = roundup(256, 128) = 256
 #  c3: 2048 -> mfma_hw; units 128 (x4 > 256): n = min(ceil(2048/128)=16, 8) = 8, P = 256;
-#      16 x 2 head groups x 8 = 256 workgroups, within the 512 slots: kept
+#      16 x 2 head groups x 8 = 256 workgroups, not more than the 256 CUs: kept
 #  c4: 4096, units 384: head-per-wave n = min(ceil(2048/384)=6, 16) = 6 gives 48 x 2 x 6 = 576
-#      workgroups, a partial second round over 512 slots: the stream family, whose slots and
-#      least pairs per workgroup come from pairs_max = max_len / 32 alone:
+#      workgroups, more than the CUs: the stream family, whose slots and least pairs per
+#      workgroup come from pairs_max = max_len / 32 alone:
 #      q = max(8, ceil((pairs_max - 1) / 14)) = 10, slots (128 - 1) // 10 + 2 = 14, 320 tokens
-#  c5a: 8192 -> mfma_hw; units 512: n = min(4, 32) = 4, P = 2048; 64 x 2 x 4 = 512: one round
+#  c5a: 8192, units 512: head-per-wave n = min(4, 32) = 4 gives 64 x 2 x 4 = 512 workgroups:
+#      the stream family, q = max(8, ceil(255 / 14)) = 19, slots 255 // 19 + 2 = 15, 608 tokens
 #  c5b: 32768 -> mfma_hw; units 16 (x4 <= 256): n = min(ceil(1024/16)=64, 128) = 64, P = 512
 EXPECTED = {"c1": (1, 128, "mfma"), "c2": (2, 256, "mfma"), "c3": (8, 256, "mfma_hw"),
-            "c4": (14, 320, "mfma_sk"), "c5a": (4, 2048, "mfma_hw"),
+            "c4": (14, 320, "mfma_sk"), "c5a": (15, 608, "mfma_sk"),
             "c5b": (64, 512, "mfma_hw")}
 
 
@@ -76,13 +78,15 @@ def test_plan_scales_with_the_compute_units(plan, monkeypatch):
     # c5b's 16 units (x4 <= 128): head-per-wave, 4 * 128 waves -> n = 32, P = 1024
     assert plan(wl.WORKLOADS["c5b"]) == (32, 1024, "mfma_hw")
     # with 24 CUs the 16 units exceed a quarter of them; head-per-wave targets 8 * 24 waves ->
-    # n = 12 (P = 2752 -> n = 12), 2 x 2 x 12 = 48 workgroups, one full round of 48 slots: kept
+    # n = 12 (P = 2752 -> n = 12), 2 x 2 x 12 = 48 workgroups, more than the 24 CUs: the
+    # stream family, pairs_max 1024, q = max(8, ceil(1023 / 14)) = 74, slots 1023 // 74 + 2 =
+    # 15, 2368 tokens
     monkeypatch.setenv("PAGEDKV_CU_COUNT", "24")
-    assert plan(wl.WORKLOADS["c5b"]) == (12, 2752, "mfma_hw")
-    # with 20 CUs: n = ceil(160 / 16) = 10 (P = 3296 -> n = 10), 40 workgroups over 40 slots:
-    # kept; with 28: n = 14 (P = 2368 -> 14), 56 over 56: kept; with 36: n = 18 (P = 1824 ->
-    # n = 18), 72 over 72: kept -- c5b's plan always fills whole rounds, so the c4 workload
-    # stands for the switch (test_automatic_plan_of_each_workload)
+    assert plan(wl.WORKLOADS["c5b"]) == (15, 2368, "mfma_sk")
+    assert plan(wl.WORKLOADS["c5b"], 0, "mfma_hw") == (12, 2752, "mfma_hw")
+    # with 64 CUs: 16 units are exactly a quarter: head-per-wave, 4 * 64 waves -> n = 16
+    monkeypatch.setenv("PAGEDKV_CU_COUNT", "64")
+    assert plan(wl.WORKLOADS["c5b"]) == (16, 2048, "mfma_hw")
 
 
 def test_stream_family_forced(plan):
