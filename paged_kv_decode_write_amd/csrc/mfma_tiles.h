@@ -105,40 +105,40 @@ constexpr float kRescaleSlack = 8.f;
 // carries the same factor, so it cancels in acc / l and in the partition merge.
 template <int KT> constexpr float kWeightLift = KT == kDtF16 ? 7.f : 0.f;
 
-// Weights p[0..7] (token slots of the P^T operand) as hi + lo in the input format, with
-// p = hi + lo + O(2^-16 p). bf16: hi is p rounded to nearest even, two per v_cvt_pk; the
+// Two weights a, b (neighbouring token slots of the P^T operand) as hi + lo in the input
+// format, with p = hi + lo + O(2^-16 p). bf16: hi is p rounded to nearest even, two per v_cvt_pk; the
 // remainders p - hi come from v_dot2c_f32_bf16 against (-1, 0) and (0, -1), one instruction
 // each (p - hi is exact in fp32, and the other product is 0), and lo is them rounded. fp16: hi
 // is p rounded toward zero (v_cvt_pkrtz_f16_f32), lo the remainder likewise.
 template <int KT>
-__device__ __forceinline__ void split_weights(const float (&p)[8], uint4& hi, uint4& lo) {
-  uint32_t hw[4], lw[4];
-  // (-1, 0) and (0, -1) as packed bf16, held in scalar registers: written as constants, the
-  // first one became the inline constant -1.0, which the instruction reads as (0, -1).
-  uint32_t neg_first = 0x0000bf80u, neg_second = 0xbf800000u;
-  if constexpr (KT == kDtBf16) {
+__device__ __forceinline__ void split_weight_pair(float a, float b, uint32_t& hi, uint32_t& lo) {
+  if constexpr (KT == kDtF16) {
+    const fp16x2 h = __builtin_amdgcn_cvt_pkrtz(a, b);
+    const fp16x2 l = __builtin_amdgcn_cvt_pkrtz(a - (float)h[0], b - (float)h[1]);
+    hi = __builtin_bit_cast(uint32_t, h);
+    lo = __builtin_bit_cast(uint32_t, l);
+  } else {
+    // (-1, 0) and (0, -1) as packed bf16, held in scalar registers: written as constants, the
+    // first one became the inline constant -1.0, which the instruction reads as (0, -1).
+    uint32_t neg_first = 0x0000bf80u, neg_second = 0xbf800000u;
     asm("" : "+s"(neg_first));
     asm("" : "+s"(neg_second));
+    const floatx2 v = {a, b};
+    const bf16x2 h = __builtin_convertvector(v, bf16x2);
+    const floatx2 r = {
+        __builtin_amdgcn_fdot2_f32_bf16(h, __builtin_bit_cast(bf16x2, neg_first), a, false),
+        __builtin_amdgcn_fdot2_f32_bf16(h, __builtin_bit_cast(bf16x2, neg_second), b, false)};
+    hi = __builtin_bit_cast(uint32_t, h);
+    lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2));
   }
+}
+
+// All eight weights p[0..7] of a lane, as the hi and lo P^T operands.
+template <int KT>
+__device__ __forceinline__ void split_weights(const float (&p)[8], uint4& hi, uint4& lo) {
+  uint32_t hw[4], lw[4];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    if constexpr (KT == kDtF16) {
-      const fp16x2 h = __builtin_amdgcn_cvt_pkrtz(p[2 * q], p[2 * q + 1]);
-      const fp16x2 l = __builtin_amdgcn_cvt_pkrtz(p[2 * q] - (float)h[0],
-                                                  p[2 * q + 1] - (float)h[1]);
-      hw[q] = __builtin_bit_cast(uint32_t, h);
-      lw[q] = __builtin_bit_cast(uint32_t, l);
-    } else {
-      const floatx2 v = {p[2 * q], p[2 * q + 1]};
-      const bf16x2 h = __builtin_convertvector(v, bf16x2);
-      const floatx2 r = {
-          __builtin_amdgcn_fdot2_f32_bf16(h, __builtin_bit_cast(bf16x2, neg_first), v[0], false),
-          __builtin_amdgcn_fdot2_f32_bf16(h, __builtin_bit_cast(bf16x2, neg_second), v[1],
-                                          false)};
-      hw[q] = __builtin_bit_cast(uint32_t, h);
-      lw[q] = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2));
-    }
-  }
+  for (int q = 0; q < 4; ++q) split_weight_pair<KT>(p[2 * q], p[2 * q + 1], hw[q], lw[q]);
   hi = make_uint4(hw[0], hw[1], hw[2], hw[3]);
   lo = make_uint4(lw[0], lw[1], lw[2], lw[3]);
 }

@@ -175,6 +175,28 @@ __device__ __forceinline__ void read_pair(uint4 (&ka)[NCH], uint4 (&kb)[NCH], ui
 
 }  // namespace
 
+// Maxima of scores without the canonicalising v_max x, x that IEEE mode puts in front of fmaxf
+// on values the compiler cannot prove quiet (the masked scores and the cross-lane exchanges
+// here): no operand is a signalling NaN, and only the rescale decision reads the result.
+__device__ __forceinline__ float max3_raw(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+__device__ __forceinline__ float max8_raw(const float (&x)[8]) {
+  return max3_raw(max3_raw(x[0], x[1], x[2]), max3_raw(x[3], x[4], x[5]),
+                  max3_raw(x[6], x[7], x[7]));
+}
+// The maximum over the 4 lanes n16 + 16 kg of a row (the cross-lane exchange of row4_max).
+__device__ __forceinline__ float row4_max_raw(float v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  v = max3_raw(__uint_as_float(a[0]), __uint_as_float(a[1]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return max3_raw(__uint_as_float(b[0]), __uint_as_float(b[1]), __uint_as_float(b[1]));
+}
+
 // Several N blocks of 16 query rows against one pair of key blocks, from operands already in
 // registers: the K rows of both blocks as the A operand of q.K, and vt[e], the V^T operand of
 // output-column group e. Every (pair, block) shares them, so one pass over the keys feeds
@@ -188,7 +210,9 @@ __device__ __forceinline__ void read_pair(uint4 (&ka)[NCH], uint4 (&kb)[NCH], ui
 // maximum did not move multiplies by exactly 1, so the results are those of one update per
 // block), then each block's weights and P.V. With no branch between one block's products and
 // the next block's exponentials, the compiler can issue the vector work of block nb + 1 while
-// the matrix products of block nb run.
+// the matrix products of block nb run. (Scaling inside the exponent's fused multiply-add,
+// 2^(raw * scale_log2 - m), saves one instruction per score but loses the exact weight 1 of a
+// row's largest score, and with it the exact value row of a row that sees one key.)
 template <int KT, int NCH, int EPL, int NB>
 __device__ __forceinline__ void pair_compute_rows(const uint4 (&ka)[NCH], const uint4 (&kb)[NCH],
                                                   const uint4 (&vt)[EPL],
@@ -208,7 +232,7 @@ __device__ __forceinline__ void pair_compute_rows(const uint4 (&ka)[NCH], const 
       sB[nb] = mfma16x16x32<KT>(kb[ch], qb[nb][ch], sB[nb]);
     }
   }
-  float s[NB][8];
+  float s[NB][8];  // scores in log2 units; -inf past a row's position
   float mn[NB];
   bool upd[NB];
   bool any_upd = false;
@@ -226,11 +250,8 @@ __device__ __forceinline__ void pair_compute_rows(const uint4 (&ka)[NCH], const 
         s[nb][4 + i] = key0 + BS + 4 * kg + i <= row_pos[nb] ? s[nb][4 + i] : kNegInf;
       }
     }
-    float mx = s[nb][0];
-#pragma unroll
-    for (int i = 1; i < 8; ++i) mx = fmaxf(mx, s[nb][i]);
-    mx = row4_max(mx);
-    mn[nb] = fmaxf(st[nb].m_run, mx);
+    const float mx = row4_max_raw(max8_raw(s[nb]));
+    mn[nb] = max3_raw(st[nb].m_run, mx, mx);
     upd[nb] = mn[nb] > st[nb].m_run + kRescaleSlack;  // also true while m_run is -inf
     any_upd = any_upd || upd[nb];
   }
