@@ -28,7 +28,10 @@
  *     context lengths) is the caller's contract and is not checked on the host, because
  *     that would need a device-to-host copy; the kernels stay memory-safe on invalid data
  *     (out-of-range slots are not written, out-of-range block ids are not read, lengths are
- *     clamped to the table width) but the results for such entries are unspecified.
+ *     clamped to the table width) but the results for such entries are unspecified. The
+ *     checked build of the library (libpagedkv_checked.so, compiled with PAGEDKV_CHECKED)
+ *     validates that data on the device before each call's kernels and records the first
+ *     violation for paged_kv_check_status.
  *
  * Cache layout (both pools): [num_blocks][block_size][num_kv_heads][head_dim], 16-bit
  * elements (bf16, or fp16 where a call takes a pagedkv_dtype).
@@ -47,7 +50,7 @@
 extern "C" {
 #endif
 
-#define PAGED_KV_ABI_VERSION 5
+#define PAGED_KV_ABI_VERSION 6
 
 typedef enum {
   PAGEDKV_OK = 0,
@@ -82,6 +85,41 @@ const char* paged_kv_status_string(int status);
 /* Text of the last error raised on the calling thread (argument problem or HIP error
  * string); "" if none. Valid until the thread's next call into the library. */
 const char* paged_kv_last_error(void);
+
+/*
+ * Checked build. A paged kernel's result is defined by the dense attention over the blocks
+ * its table names (the mini-vLLM README tests its paged kernel against dense attention on
+ * scattered blocks), so a wrong slot or block id or length silently changes the answer. In a
+ * library built with PAGEDKV_CHECKED, every call first launches, on its own stream, kernels
+ * that validate the data it is about to read: slot ids (below num_blocks * block_size, or
+ * negative for padding), context lengths (0 .. max_blocks_per_seq * block_size), the block
+ * ids each context covers (the first ceil(L / block_size) table entries, in [0, num_blocks)),
+ * and for the multi-query calls the query spans. The first violation found on a device is kept
+ * in a per-device record until cleared; the calls themselves then proceed as in the unchecked
+ * build (memory-safe, result unspecified).
+ */
+typedef enum {
+  PAGEDKV_CHECK_NONE = 0,
+  PAGEDKV_CHECK_SLOT = 1,   /* index: token t; value: slot_mapping[t] >= num_blocks * block_size */
+  PAGEDKV_CHECK_LENGTH = 2, /* index: sequence b; value: context_lens[b] < 0 or past the table */
+  PAGEDKV_CHECK_BLOCK = 3,  /* index: b * max_blocks_per_seq + j; value: the block id outside
+                               [0, num_blocks) of table entry j < ceil(L_b / block_size) */
+  PAGEDKV_CHECK_QUERY = 4   /* index: sequence b; value: its span cu[b + 1] - cu[b], which is
+                               negative, reaches past num_tokens, or exceeds L_b or max_q_len */
+} pagedkv_check_code;
+
+/* 1 if this library was built with PAGEDKV_CHECKED, else 0. Host only. */
+int paged_kv_checked_build(void);
+
+/*
+ * Synchronises the current device (hipDeviceSynchronize), then reads its check record:
+ * *code a pagedkv_check_code (PAGEDKV_CHECK_NONE if no violation was recorded since the last
+ * clear), *index and *value (either may be NULL) as listed above. clear != 0 resets the record
+ * afterwards. Which of several concurrent violations is recorded is unspecified.
+ * Errors: PAGEDKV_ERR_UNSUPPORTED in the unchecked build; PAGEDKV_ERR_NULL for a NULL code;
+ * PAGEDKV_ERR_HIP if the synchronisation or the copy fails (including an earlier kernel fault).
+ */
+int paged_kv_check_status(int32_t* code, int64_t* index, int64_t* value, int32_t clear);
 
 /*
  * paged_kv_write -- store each new token's K and V rows into its slot of the paged pools

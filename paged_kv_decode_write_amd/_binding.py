@@ -16,6 +16,7 @@ import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_NAME = "libpagedkv.so"
+CHECKED_LIB_NAME = "libpagedkv_checked.so"
 
 STATUS_NAMES = {0: "PAGEDKV_OK", 1: "PAGEDKV_ERR_NULL", 2: "PAGEDKV_ERR_SHAPE",
                 3: "PAGEDKV_ERR_UNSUPPORTED", 4: "PAGEDKV_ERR_WORKSPACE", 5: "PAGEDKV_ERR_HIP",
@@ -42,6 +43,72 @@ def library_path() -> str:
     return os.environ.get("PAGEDKV_LIBRARY", os.path.join(_HERE, LIB_NAME))
 
 
+def _declare(lib: ctypes.CDLL) -> ctypes.CDLL:
+    """Declare the C signatures of every entry point on a loaded library."""
+    P, I32, I64, SZ, F32 = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
+                            ctypes.c_size_t, ctypes.c_float)
+    lib.paged_kv_abi_version.restype = ctypes.c_int
+    lib.paged_kv_abi_version.argtypes = []
+    lib.paged_kv_status_string.restype = ctypes.c_char_p
+    lib.paged_kv_status_string.argtypes = [ctypes.c_int]
+    lib.paged_kv_last_error.restype = ctypes.c_char_p
+    lib.paged_kv_last_error.argtypes = []
+    lib.paged_kv_write.restype = ctypes.c_int
+    lib.paged_kv_write.argtypes = [P, P, P, I64, P, P, I64, I32, I32, I32, P]
+    lib.paged_decode_workspace_bytes.restype = SZ
+    lib.paged_decode_workspace_bytes.argtypes = [I32, I32, I32, I32, I32, I32]
+    attn = [P, P, P, P, I32, P, I32, I32, I32, I32, I32, I64, F32, P, P, SZ, I32]
+    lib.paged_decode_attention.restype = ctypes.c_int
+    lib.paged_decode_attention.argtypes = attn + [P]
+    typed = attn[:13] + [I32, P, I32, P, SZ, I32]
+    lib.paged_decode_attention_typed.restype = ctypes.c_int
+    lib.paged_decode_attention_typed.argtypes = typed + [P]
+    lib.paged_decode_attention_ex.restype = ctypes.c_int
+    lib.paged_decode_attention_ex.argtypes = typed + [I32, P, P, P]
+    lib.paged_decode_step.restype = ctypes.c_int
+    lib.paged_decode_step.argtypes = [P, P, P, P, P, P, P, I32, P, I32, I32, I32, I32, I32,
+                                      I64, F32, I32, P, I32, P, SZ, I32, I32, P, P, P]
+    lib.paged_decode_step_noalloc.restype = ctypes.c_int
+    lib.paged_decode_step_noalloc.argtypes = [P, P, P, P, P, P, P, I32, P, I32, I32, I32,
+                                              I32, I32, I64, F32, I32, P, I32, I32, I32, P,
+                                              P, P]
+    lib.paged_decode_step_rope.restype = ctypes.c_int
+    lib.paged_decode_step_rope.argtypes = [P, P, P, P, P, I32, P, P, P, P, P, I32, P, I32,
+                                           I32, I32, I32, I32, I64, F32, I32, P, I32, P, SZ,
+                                           I32, I32, P, P, P]
+    lib.paged_kv_write_rope.restype = ctypes.c_int
+    lib.paged_kv_write_rope.argtypes = [P, P, P, P, P, I32, P, I64, P, P, P, I64, I32, I32,
+                                        I32, I32, P]
+    lib.paged_prefill_attention.restype = ctypes.c_int
+    lib.paged_prefill_attention.argtypes = [P, P, I64, I32, P, P, P, I32, P, I32, I32, I32,
+                                            I32, I32, I64, F32, P, P]
+    lib.paged_prefill_attention_ex.restype = ctypes.c_int
+    lib.paged_prefill_attention_ex.argtypes = [P, P, I64, I32, P, P, P, I32, P, I32, I32,
+                                               I32, I32, I32, I64, F32, I32, P, I32, I32,
+                                               P]
+    lib.paged_decode_plan.restype = ctypes.c_int
+    lib.paged_decode_plan.argtypes = [I32, I32, I32, I32, I32, I32, I32, I32,
+                                      ctypes.POINTER(I32), ctypes.POINTER(I32),
+                                      ctypes.POINTER(I32)]
+    lib.paged_prefill_attention_split.restype = ctypes.c_int
+    lib.paged_prefill_attention_split.argtypes = [P, P, I64, I32, P, P, P, I32, P, I32, I32,
+                                                  I32, I32, I32, I64, F32, I32, P, I32, I32,
+                                                  P, SZ, I32, P]
+    lib.paged_prefill_workspace_bytes.restype = SZ
+    lib.paged_prefill_workspace_bytes.argtypes = [I64, I32, I32, I32, I32, I32]
+    lib.paged_prefill_plan.restype = ctypes.c_int
+    lib.paged_prefill_plan.argtypes = [I64, I32, I32, I32, I32, I32, I32, I32, I32, I32,
+                                       ctypes.POINTER(I32), ctypes.POINTER(I32),
+                                       ctypes.POINTER(I32)]
+    lib.paged_kv_checked_build.restype = ctypes.c_int
+    lib.paged_kv_checked_build.argtypes = []
+    lib.paged_kv_check_status.restype = ctypes.c_int
+    lib.paged_kv_check_status.argtypes = [ctypes.POINTER(ctypes.c_int32),
+                                          ctypes.POINTER(ctypes.c_int64),
+                                          ctypes.POINTER(ctypes.c_int64), ctypes.c_int32]
+    return lib
+
+
 def load_library() -> ctypes.CDLL:
     """Load libpagedkv.so (after torch, so both share one HIP runtime) and declare the
     C signatures. Raises FileNotFoundError if it has not been built."""
@@ -53,64 +120,47 @@ def load_library() -> ctypes.CDLL:
         if not os.path.exists(path):
             raise FileNotFoundError(
                 f"{path} is missing: build it first (python -m paged_kv_decode_write_amd.build)")
-        lib = ctypes.CDLL(path)
-        P, I32, I64, SZ, F32 = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
-                                ctypes.c_size_t, ctypes.c_float)
-        lib.paged_kv_abi_version.restype = ctypes.c_int
-        lib.paged_kv_abi_version.argtypes = []
-        lib.paged_kv_status_string.restype = ctypes.c_char_p
-        lib.paged_kv_status_string.argtypes = [ctypes.c_int]
-        lib.paged_kv_last_error.restype = ctypes.c_char_p
-        lib.paged_kv_last_error.argtypes = []
-        lib.paged_kv_write.restype = ctypes.c_int
-        lib.paged_kv_write.argtypes = [P, P, P, I64, P, P, I64, I32, I32, I32, P]
-        lib.paged_decode_workspace_bytes.restype = SZ
-        lib.paged_decode_workspace_bytes.argtypes = [I32, I32, I32, I32, I32, I32]
-        attn = [P, P, P, P, I32, P, I32, I32, I32, I32, I32, I64, F32, P, P, SZ, I32]
-        lib.paged_decode_attention.restype = ctypes.c_int
-        lib.paged_decode_attention.argtypes = attn + [P]
-        typed = attn[:13] + [I32, P, I32, P, SZ, I32]
-        lib.paged_decode_attention_typed.restype = ctypes.c_int
-        lib.paged_decode_attention_typed.argtypes = typed + [P]
-        lib.paged_decode_attention_ex.restype = ctypes.c_int
-        lib.paged_decode_attention_ex.argtypes = typed + [I32, P, P, P]
-        lib.paged_decode_step.restype = ctypes.c_int
-        lib.paged_decode_step.argtypes = [P, P, P, P, P, P, P, I32, P, I32, I32, I32, I32, I32,
-                                          I64, F32, I32, P, I32, P, SZ, I32, I32, P, P, P]
-        lib.paged_decode_step_noalloc.restype = ctypes.c_int
-        lib.paged_decode_step_noalloc.argtypes = [P, P, P, P, P, P, P, I32, P, I32, I32, I32,
-                                                  I32, I32, I64, F32, I32, P, I32, I32, I32, P,
-                                                  P, P]
-        lib.paged_decode_step_rope.restype = ctypes.c_int
-        lib.paged_decode_step_rope.argtypes = [P, P, P, P, P, I32, P, P, P, P, P, I32, P, I32,
-                                               I32, I32, I32, I32, I64, F32, I32, P, I32, P, SZ,
-                                               I32, I32, P, P, P]
-        lib.paged_kv_write_rope.restype = ctypes.c_int
-        lib.paged_kv_write_rope.argtypes = [P, P, P, P, P, I32, P, I64, P, P, P, I64, I32, I32,
-                                            I32, I32, P]
-        lib.paged_prefill_attention.restype = ctypes.c_int
-        lib.paged_prefill_attention.argtypes = [P, P, I64, I32, P, P, P, I32, P, I32, I32, I32,
-                                                I32, I32, I64, F32, P, P]
-        lib.paged_prefill_attention_ex.restype = ctypes.c_int
-        lib.paged_prefill_attention_ex.argtypes = [P, P, I64, I32, P, P, P, I32, P, I32, I32,
-                                                   I32, I32, I32, I64, F32, I32, P, I32, I32,
-                                                   P]
-        lib.paged_decode_plan.restype = ctypes.c_int
-        lib.paged_decode_plan.argtypes = [I32, I32, I32, I32, I32, I32, I32, I32,
-                                          ctypes.POINTER(I32), ctypes.POINTER(I32),
-                                          ctypes.POINTER(I32)]
-        lib.paged_prefill_attention_split.restype = ctypes.c_int
-        lib.paged_prefill_attention_split.argtypes = [P, P, I64, I32, P, P, P, I32, P, I32, I32,
-                                                      I32, I32, I32, I64, F32, I32, P, I32, I32,
-                                                      P, SZ, I32, P]
-        lib.paged_prefill_workspace_bytes.restype = SZ
-        lib.paged_prefill_workspace_bytes.argtypes = [I64, I32, I32, I32, I32, I32]
-        lib.paged_prefill_plan.restype = ctypes.c_int
-        lib.paged_prefill_plan.argtypes = [I64, I32, I32, I32, I32, I32, I32, I32, I32, I32,
-                                           ctypes.POINTER(I32), ctypes.POINTER(I32),
-                                           ctypes.POINTER(I32)]
-        _lib = lib
-        return lib
+        _lib = _declare(ctypes.CDLL(path))
+        return _lib
+
+
+_checked_lib: Optional[ctypes.CDLL] = None
+
+
+def checked_library_path() -> str:
+    return os.path.join(_HERE, CHECKED_LIB_NAME)
+
+
+def load_checked_library() -> ctypes.CDLL:
+    """Load the checked build, libpagedkv_checked.so (the same entry points, each call
+    validating its slot ids, block ids, lengths and query spans on the device first), as a
+    library of its own: call its entry points directly and read the result with
+    check_status(lib)."""
+    global _checked_lib
+    with _lock:
+        if _checked_lib is not None:
+            return _checked_lib
+        path = checked_library_path()
+        if not os.path.exists(path):
+            raise FileNotFoundError(
+                f"{path} is missing: build it first (python -m paged_kv_decode_write_amd.build)")
+        _checked_lib = _declare(ctypes.CDLL(path, mode=os.RTLD_LOCAL))
+        return _checked_lib
+
+
+CHECK_CODES = {0: "none", 1: "slot", 2: "length", 3: "block", 4: "query"}
+
+
+def check_status(lib: Optional[ctypes.CDLL] = None, clear: bool = True):
+    """Synchronise the current device and return the checked build's record as
+    (code name, index, value); `clear` resets it."""
+    lib = lib or load_checked_library()
+    code, index, value = ctypes.c_int32(0), ctypes.c_int64(0), ctypes.c_int64(0)
+    st = lib.paged_kv_check_status(ctypes.byref(code), ctypes.byref(index), ctypes.byref(value),
+                                   1 if clear else 0)
+    if st != 0:
+        raise PagedKVError(st, lib.paged_kv_last_error().decode(errors="replace"))
+    return CHECK_CODES.get(code.value, code.value), index.value, value.value
 
 
 def abi_version() -> int:

@@ -20,11 +20,13 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(HERE, "libpagedkv.so")
+CHECKED_OUT = os.path.join(HERE, "libpagedkv_checked.so")  # PAGEDKV_CHECKED: device-side checks
 PROBE_OUT = os.path.join(HERE, "libpagedkv_probe.so")
 PROBE_SOURCES = ["read_probe.hip"]  # measurement utility, a library of its own
 
-SOURCES = ["api.cpp", "kv_write.hip", "decode_valu.hip", "decode_mfma.hip", "decode_sk.hip", "decode_reduce.hip",
-           "prefill_mfma.hip", "kv_write_rope.hip", "block_table.hip"]
+SOURCES = ["api.cpp", "kv_write.hip", "decode_valu.hip", "decode_mfma.hip", "decode_sk.hip",
+           "decode_reduce.hip", "prefill_mfma.hip", "kv_write_rope.hip", "block_table.hip",
+           "check.hip"]
 ARCH = os.environ.get("PAGEDKV_ARCH", "gfx950")
 
 
@@ -75,6 +77,12 @@ def build(out: str = OUT, jobs: int = 8, extra=()) -> str:
     return link(SOURCES, out, jobs, extra)
 
 
+def build_checked(out: str = CHECKED_OUT, jobs: int = 8) -> str:
+    """Build libpagedkv_checked.so: the same library with PAGEDKV_CHECKED, which validates
+    each call's slot ids, block ids, lengths and query spans on the device first."""
+    return link(SOURCES, out, jobs, extra=("-DPAGEDKV_CHECKED",))
+
+
 def build_probe(out: str = PROBE_OUT) -> str:
     """Build libpagedkv_probe.so (the streaming-read measurement utility)."""
     return link(PROBE_SOURCES, out)
@@ -82,4 +90,5 @@ def build_probe(out: str = PROBE_OUT) -> str:
 
 if __name__ == "__main__":
     print(build())
+    print(build_checked())
     print(build_probe())

@@ -465,6 +465,37 @@ int scratch_address(void** out) {
 }
 
 // Decode attention, optionally fused with the step's KV write (sw non-null).
+// The checked build (PAGEDKV_CHECKED) validates a call's data on the device before its
+// kernels, on the same stream; the unchecked build launches nothing here.
+#ifdef PAGEDKV_CHECKED
+constexpr bool kChecked = true;
+#else
+constexpr bool kChecked = false;
+#endif
+
+int check_slots(const int64_t* slots, int64_t n, int64_t num_slots, hipStream_t stream) {
+  if (!kChecked) return PAGEDKV_OK;
+  const hipError_t e = launch_check_slots(slots, n, num_slots, stream);
+  return e == hipSuccess ? PAGEDKV_OK : hip_fail(e, "slot check launch");
+}
+
+int check_tables(const int32_t* tables, const int32_t* lens, int32_t batch, int32_t max_blocks,
+                 int32_t block_size, int64_t num_blocks, hipStream_t stream) {
+  if (!kChecked) return PAGEDKV_OK;
+  const hipError_t e =
+      launch_check_tables(tables, lens, batch, max_blocks, block_size, num_blocks, stream);
+  return e == hipSuccess ? PAGEDKV_OK : hip_fail(e, "block table check launch");
+}
+
+int check_queries(const int32_t* cu, const int32_t* lens, int32_t batch, int32_t max_blocks,
+                  int32_t block_size, int64_t num_tokens, int32_t max_q_len,
+                  hipStream_t stream) {
+  if (!kChecked) return PAGEDKV_OK;
+  const hipError_t e = launch_check_queries(cu, lens, batch, max_blocks, block_size, num_tokens,
+                                            max_q_len, stream);
+  return e == hipSuccess ? PAGEDKV_OK : hip_fail(e, "query span check launch");
+}
+
 int decode_impl(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache,
                 const int32_t* block_tables, int32_t max_blocks_per_seq,
                 const int32_t* context_lens, int32_t batch, int32_t num_q_heads,
@@ -577,6 +608,13 @@ int decode_impl(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_ca
     a.ws_ml = reinterpret_cast<float*>(base + acc_bytes(batch, num_q_heads, head_dim, plan.nparts));
   }
 
+  st = check_tables(block_tables, context_lens, batch, max_blocks_per_seq, block_size,
+                    num_blocks, stream);
+  if (st) return st;
+  if (sw) {
+    st = check_slots(sw->slot_mapping, batch, num_blocks * block_size, stream);
+    if (st) return st;
+  }
   hipError_t e;
   if (sw && chosen == PAGEDKV_KERNEL_VALU && sw->positions) {
     // The vector-ALU kernel has no fused write: rotate and store first, then attend over the
@@ -662,6 +700,23 @@ const char* paged_kv_status_string(int status) {
 
 const char* paged_kv_last_error(void) { return g_last_error.c_str(); }
 
+int paged_kv_checked_build(void) { return kChecked ? 1 : 0; }
+
+int paged_kv_check_status(int32_t* code, int64_t* index, int64_t* value, int32_t clear) {
+  g_last_error.clear();
+  if (!kChecked)
+    return fail(PAGEDKV_ERR_UNSUPPORTED,
+                "this library does not validate data on the device (build with PAGEDKV_CHECKED)");
+  if (!code) return fail(PAGEDKV_ERR_NULL, "code must be non-NULL");
+  long long rec[3] = {0, 0, 0};
+  const hipError_t e = read_check_record(rec, clear != 0);
+  if (e != hipSuccess) return hip_fail(e, "reading the check record");
+  *code = (int32_t)rec[0];
+  if (index) *index = rec[1];
+  if (value) *value = rec[2];
+  return PAGEDKV_OK;
+}
+
 int paged_kv_write(const uint16_t* k, const uint16_t* v, const int64_t* slot_mapping,
                    int64_t num_tokens, uint16_t* k_cache, uint16_t* v_cache,
                    int64_t num_blocks, int32_t block_size, int32_t num_kv_heads,
@@ -683,6 +738,8 @@ int paged_kv_write(const uint16_t* k, const uint16_t* v, const int64_t* slot_map
   if (!aligned(k, 16) || !aligned(v, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
       !aligned(slot_mapping, 8))
     return fail(PAGEDKV_ERR_ALIGN, "k, v, k_cache, v_cache need 16-byte alignment");
+  const int st = check_slots(slot_mapping, num_tokens, num_blocks * block_size, stream);
+  if (st) return st;
   hipError_t e = launch_kv_write(k, v, slot_mapping, num_tokens, k_cache, v_cache,
                                  num_blocks * block_size, (int32_t)row, stream);
   if (e != hipSuccess) return hip_fail(e, "kv_write launch");
@@ -734,6 +791,8 @@ int paged_kv_write_rope(const uint16_t* q, const uint16_t* k, const uint16_t* v,
   a.num_kv_heads = num_kv_heads;
   a.head_dim = head_dim;
   a.interleaved = interleaved;
+  const int st = check_slots(slot_mapping, num_tokens, num_blocks * block_size, stream);
+  if (st) return st;
   hipError_t e = launch_kv_write_rope(a, stream);
   if (e != hipSuccess) return hip_fail(e, "rope + kv_write launch");
   return PAGEDKV_OK;
@@ -962,6 +1021,12 @@ int paged_prefill_attention_split(const uint16_t* q, const int32_t* cu_seqlens_q
     a.ws_ml = reinterpret_cast<float*>(
         base + acc_bytes(num_tokens, num_q_heads, head_dim, plan.nparts));
   }
+  st = check_tables(block_tables, context_lens, batch, max_blocks_per_seq, block_size,
+                    num_blocks, stream);
+  if (st) return st;
+  st = check_queries(cu_seqlens_q, context_lens, batch, max_blocks_per_seq, block_size,
+                     num_tokens, max_q_len, stream);
+  if (st) return st;
   hipError_t e = launch_prefill_mfma(a, stream);
   if (e != hipSuccess) return hip_fail(e, "prefill attention launch");
   if (plan.nparts > 1) {

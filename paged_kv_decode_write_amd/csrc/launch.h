@@ -137,6 +137,25 @@ hipError_t launch_kv_write(const uint16_t* k, const uint16_t* v, const int64_t* 
                            int64_t num_tokens, uint16_t* k_cache, uint16_t* v_cache,
                            int64_t num_slots, int32_t row_elems, hipStream_t stream);
 
+// Device-side validation (launched by the checked build before a call's kernels): codes of
+// the first violation recorded, as paged_kv_check_status reports them.
+constexpr int kCheckSlot = 1;    // slot id at or past the end of the pool
+constexpr int kCheckLength = 2;  // context length negative or past the table width
+constexpr int kCheckBlock = 3;   // a block id the context covers lies outside the pool
+constexpr int kCheckQuery = 4;   // a query span that is negative, past num_tokens, longer
+                                 // than its context or than max_q_len
+hipError_t launch_check_slots(const int64_t* slots, int64_t n, int64_t num_slots,
+                              hipStream_t stream);
+hipError_t launch_check_tables(const int32_t* tables, const int32_t* lens, int32_t batch,
+                               int32_t max_blocks, int32_t block_size, int64_t num_blocks,
+                               hipStream_t stream);
+hipError_t launch_check_queries(const int32_t* cu, const int32_t* lens, int32_t batch,
+                                int32_t max_blocks, int32_t block_size, int64_t num_tokens,
+                                int32_t max_q_len, hipStream_t stream);
+// Synchronises the current device, then reads (and with `clear` zeroes) its record:
+// {code, index, value}.
+hipError_t read_check_record(long long rec[3], bool clear);
+
 // Waves per workgroup of the decode kernels; partitions are multiples of
 // kWavesPerGroup * block_size tokens when split automatically.
 constexpr int kWavesPerGroup = 4;

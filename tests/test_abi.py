@@ -35,7 +35,8 @@ def test_header_declares_the_entry_points():
                  "paged_prefill_attention_ex", "paged_kv_write_rope", "paged_decode_step", "paged_decode_step_rope",
                  "paged_decode_workspace_bytes", "paged_kv_status_string", "paged_kv_abi_version",
                  "paged_kv_last_error", "paged_decode_plan", "paged_prefill_attention_split",
-                 "paged_prefill_workspace_bytes", "paged_prefill_plan"):
+                 "paged_prefill_workspace_bytes", "paged_prefill_plan", "paged_kv_checked_build",
+                 "paged_kv_check_status"):
         assert want in names
 
 
@@ -49,7 +50,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.paged_kv_abi_version() == 5
+    assert lib.paged_kv_abi_version() == 6
     assert lib.paged_kv_status_string(OK) == b"PAGEDKV_OK"
     assert lib.paged_kv_status_string(ERR_WORKSPACE) == b"PAGEDKV_ERR_WORKSPACE"
     assert lib.paged_kv_status_string(99) == b"PAGEDKV_UNKNOWN_STATUS"
@@ -274,3 +275,29 @@ def test_decode_step_noalloc_host_checks(lib, monkeypatch):
     assert _step_noalloc(lib, B=64, MB=512, NB=32768, part=16) == ERR_WORKSPACE
     msg = lib.paged_kv_last_error()
     assert b"static scratch" in msg and str(64 * 32 * 512 * 130 * 4).encode() in msg
+
+
+def test_unchecked_build_has_no_check_record(lib):
+    """The default library validates nothing on the device: it says so, and the status call
+    refuses before touching the device."""
+    assert lib.paged_kv_checked_build() == 0
+    code = ctypes.c_int32(-1)
+    assert lib.paged_kv_check_status(ctypes.byref(code), None, None, 1) == ERR_UNSUPPORTED
+    assert code.value == -1
+
+
+def test_checked_build_loads_and_exports_everything():
+    """libpagedkv_checked.so (PAGEDKV_CHECKED) is built beside the default library, exports
+    every declared symbol, reports itself checked, and checks its arguments on the host."""
+    path = _binding.checked_library_path()
+    if not os.path.exists(path):
+        pytest.skip("libpagedkv_checked.so not built")
+    ck = _binding.load_checked_library()
+    assert ck.paged_kv_checked_build() == 1
+    assert ck.paged_kv_abi_version() == 6
+    for name in declared_functions():
+        assert hasattr(ck, name), name
+    assert ck.paged_kv_check_status(None, None, None, 1) == ERR_NULL
+    # host-side argument checks are the same as in the default build
+    assert _write(ck, T=-1) == ERR_SHAPE
+    assert _write(ck, k=None) == ERR_NULL
