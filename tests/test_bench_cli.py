@@ -1,4 +1,7 @@
-"""bench.py's command line without a GPU: it measures one GPU only and says so for more."""
+"""bench.py without a GPU: its command line (one GPU only, and it says so for more) and the
+traffic record it builds from rocprofv3 counter passes."""
+import argparse
+import json
 import os
 import subprocess
 import sys
@@ -33,3 +36,46 @@ def test_block_size_must_be_a_multiple_of_16():
         assert "multiple of 16" in res.stderr, res.stderr
         assert res.stdout == ""
 
+
+
+def _counter_csv(path, counter, rows):
+    os.makedirs(path, exist_ok=True)
+    cols = ["Dispatch_Id", "Grid_Size", "Kernel_Name", "Counter_Name", "Counter_Value"]
+    with open(os.path.join(path, "run_counter_collection.csv"), "w") as f:
+        f.write(",".join(cols) + "\n")
+        for i, (grid, name, value) in enumerate(rows):
+            f.write(f'{i},{grid},"{name}",{counter},{value}\n')
+
+
+def test_record_traffic_scales_by_the_copy_and_averages_the_attention_launches(tmp_path,
+                                                                                monkeypatch):
+    """--record-traffic reads the two counter passes, takes the scale from the 1 GiB copy
+    (FETCH_SIZE reads half of its bytes here, WRITE_SIZE all of them), averages every attention
+    dispatch of the decode families it finds (not the merge), and stamps the record with the
+    hash of those families' sources."""
+    sys.path.insert(0, ROOT)
+    import bench
+
+    copy = (131072, "__amd_rocclr_copyBuffer", None)
+    sk = "void pagedkv::decode_mfma_sk_kernel<128, 4, 2, 1, 0, 2, false>(pagedkv::DecodeArgs)"
+    hw = "void pagedkv::decode_mfma_hw_kernel<128, 4, 2, 2, 0, 2, false>(pagedkv::DecodeArgs)"
+    merge = "void pagedkv::decode_reduce_split_kernel<2, 16, 4, false>(pagedkv::DecodeArgs)"
+    fetch = [(copy[0], copy[1], 524288.0), (65536, sk, 1000.0), (8192, merge, 77.0),
+             (65536, hw, 3000.0)]
+    write = [(copy[0], copy[1], 1048576.0), (65536, sk, 10.0), (8192, merge, 5.0),
+             (65536, hw, 30.0)]
+    _counter_csv(str(tmp_path / "FETCH_SIZE"), "FETCH_SIZE", fetch)
+    _counter_csv(str(tmp_path / "WRITE_SIZE"), "WRITE_SIZE", write)
+    out = tmp_path / "traffic.json"
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(out))
+    args = argparse.Namespace(record_traffic=str(tmp_path), kernel="auto", workload="c5")
+    bench.record_traffic(args)
+    rec = json.loads(out.read_text())["c5"]
+    assert rec["kernel"] == "mfma_sk+mfma_hw"
+    assert rec["fetch_scale"] == 2.0 and rec["write_scale"] == 1.0
+    assert rec["launches"] == 2
+    assert rec["fetch_bytes_per_launch"] == 2000 * 1024 * 2
+    assert rec["write_bytes_per_launch"] == 20 * 1024
+    assert rec["bytes_per_launch"] == 2000 * 1024 * 2 + 20 * 1024
+    assert rec["kernel_source"] == bench.kernel_source_hash("mfma_sk+mfma_hw")
+    assert rec["kernel_source"] != bench.kernel_source_hash("mfma_hw")
