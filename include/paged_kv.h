@@ -468,7 +468,7 @@ int paged_prefill_attention_ex(const uint16_t* q, const int32_t* cu_seqlens_q,
  *                  Calls that may overlap (other streams) need their own workspace.
  *   partition_tokens  keys per partition: 0 lets the library choose (it splits only when the
  *                  query tiles cannot fill the device and contexts may exceed 2048 keys, into
- *                  at most 4 partitions of at least 512 keys), -1 never splits, > 0 forces
+ *                  at most 3 partitions of at least 512 keys), -1 never splits, > 0 forces
  *                  that size, which must be a multiple of 32 (else PAGEDKV_ERR_SHAPE).
  *   Other arguments as in paged_prefill_attention_ex. A split adds a second launch (the
  *   merge) on `stream`. Results agree with the unsplit call up to fp32 rounding of the same

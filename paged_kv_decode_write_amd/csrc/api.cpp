@@ -210,8 +210,13 @@ size_t view_table_bytes(int64_t batch, int64_t max_blocks, int32_t sub) {
 // batches) fill fewer than two residency rounds and the contexts may exceed
 // kPrefillSplitMinKeys; it cuts them into at most kPrefillMaxAutoParts partitions of at least
 // kPrefillMinPartKeys keys. Partitions are multiples of the 32 keys one staged pair holds.
+// Three partitions measured best on the ragged mix of short chunks and full prefills up to
+// 4000 keys (75 us per call, against 87 with four partitions of 1024 keys and 93 with two of
+// 2048): each split workgroup pays its start (block ids, the first staged pair) once, and a
+// fourth partition adds more workgroups and merge input than it removes from the longest
+// chain.
 constexpr int64_t kPrefillSplitMinKeys = 2048;
-constexpr int64_t kPrefillMaxAutoParts = 4;
+constexpr int64_t kPrefillMaxAutoParts = 3;
 constexpr int64_t kPrefillMinPartKeys = 512;
 constexpr int64_t kPrefillPairKeys = 32;
 // Workgroups of the one- and two-block kernels one CU holds (their registers allow two); a

@@ -178,14 +178,15 @@ def test_prefill_workspace_bytes(lib):
     f = lib.paged_prefill_workspace_bytes
     assert f(100, 24, 128, 256, 16, -1) == 0                # never split
     assert f(100, 24, 128, 128, 16, 0) == 0                 # 2048 keys: auto never splits
-    # auto over 4096 keys: at most 4 partitions of 1024 keys
-    acc = 100 * 24 * 4 * 128 * 4
-    ml = 100 * 24 * 4 * 2 * 4
+    # auto over 4096 keys: at most 3 partitions (of 1376 keys)
+    acc = 100 * 24 * 128 * 4
+    ml = 100 * 24 * 2 * 4
     r = lambda x: (x + 255) // 256 * 256
-    assert f(100, 24, 128, 256, 16, 0) == r(acc) + r(ml)
-    assert f(100, 24, 128, 256, 16, 1024) == r(acc) + r(ml)
+    assert f(100, 24, 128, 256, 16, 0) == r(3 * acc) + r(3 * ml)
+    assert f(100, 24, 128, 256, 16, 1376) == r(3 * acc) + r(3 * ml)
+    assert f(100, 24, 128, 256, 16, 1024) == r(4 * acc) + r(4 * ml)
     # forced 512-key partitions: 8 of them
-    assert f(100, 24, 128, 256, 16, 512) == r(2 * acc) + r(2 * ml)
+    assert f(100, 24, 128, 256, 16, 512) == r(8 * acc) + r(8 * ml)
     assert f(100, 24, 128, 256, 16, 48) == 0                # not a multiple of 32
     assert f(0, 24, 128, 256, 16, 0) == 0
 

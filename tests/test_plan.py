@@ -104,12 +104,12 @@ def test_stream_family_forced(plan):
 
 # Multi-query (prefill) plans, from the rule documented beside make_prefill_plan: split when
 # kv_heads * ceil(num_tokens / tokens per workgroup) < 2 * 2 * CUs and the contexts may exceed
-# 2048 keys, into ceil(max_len / P) partitions, P = max(512, roundup(ceil(max_len / 4), 32)).
+# 2048 keys, into ceil(max_len / P) partitions, P = max(512, roundup(ceil(max_len / 3), 32)).
 # row_blocks is passed explicitly (its automatic choice asks the device for occupancy).
 #  p1: 8 kv heads * ceil(4096 / 32) = 1024 workgroups, not < 1024: no split
-#  p2: 8 * ceil(1438 / 20) = 576 < 1024 and 4096 keys: P = 1024, 4 partitions
+#  p2: 8 * ceil(1438 / 20) = 576 < 1024 and 4096 keys: P = roundup(1366, 32) = 1376, 3 partitions
 #  p3: 2048 keys: never split automatically
-PREFILL_EXPECTED = {"p1": (2, 1, 4096), "p2": (1, 4, 1024), "p3": (1, 1, 2048)}
+PREFILL_EXPECTED = {"p1": (2, 1, 4096), "p2": (1, 3, 1376), "p3": (1, 1, 2048)}
 
 
 def _prefill_plan(w, row_blocks, partition=0):
@@ -133,7 +133,7 @@ def test_prefill_plan_forced_and_scaled(plan, monkeypatch):
         _prefill_plan(w, 1, 48)                                    # not a multiple of 32
     # four times the compute units: p1's 1024 workgroups no longer fill two rounds
     monkeypatch.setenv("PAGEDKV_CU_COUNT", "1024")
-    assert _prefill_plan(wl.PREFILL_WORKLOADS["p1"], 2) == (2, 4, 1024)
+    assert _prefill_plan(wl.PREFILL_WORKLOADS["p1"], 2) == (2, 3, 1376)
 
 
 @pytest.mark.parametrize("name", ["c2", "c4", "c5b"])
