@@ -14,8 +14,10 @@
 // set the time. Here the work is counted on the device and cut into equal slices:
 //   items = (sequence b, group of HPW KV heads, pair k of 32 tokens), b-major, then the head
 //   group, then k; sequence b holds ngrp * ceil(L_b / 32) items, W in all.
-// Workgroup w of N takes items [w*q, (w+1)*q), q = max(min_pairs, ceil(W / N)); each of its
-// HPW waves streams one KV head of those items. Where the slice crosses from one (sequence,
+// Workgroup w of N (one per compute unit: a second resident workgroup's loads were served
+// after most of the first one's, and it finished a quarter of the dispatch later) takes items
+// [w*q, (w+1)*q), q = max(min_pairs, ceil(W / N)); each of its HPW waves streams one KV head
+// of those items. Where the slice crosses from one (sequence,
 // head group) to the next, the wave closes the first as a segment and starts the next: each
 // segment leaves a partial softmax result (unnormalised output, reference max, sum) in slot
 // j = w - (first workgroup of that (sequence, head group)) of the split workspace, and the
