@@ -23,6 +23,11 @@ OUT = os.path.join(HERE, "libpagedkv.so")
 CHECKED_OUT = os.path.join(HERE, "libpagedkv_checked.so")  # PAGEDKV_CHECKED: device-side checks
 PROBE_OUT = os.path.join(HERE, "libpagedkv_probe.so")
 PROBE_SOURCES = ["read_probe.hip"]  # measurement utility, a library of its own
+# A native C++ caller of the C ABI (eager step, HIP stream capture of several steps, replay),
+# built against each library; tests/test_native_abi.py runs it.
+NATIVE_SRC = os.path.join(ROOT, "tests", "native", "decode_step_graph.cpp")
+NATIVE_OUT = {"libpagedkv.so": os.path.join(HERE, "decode_step_graph"),
+              "libpagedkv_checked.so": os.path.join(HERE, "decode_step_graph_checked")}
 
 SOURCES = ["api.cpp", "kv_write.hip", "decode_valu.hip", "decode_mfma.hip", "decode_sk.hip",
            "decode_reduce.hip", "prefill_mfma.hip", "kv_write_rope.hip", "block_table.hip",
@@ -88,7 +93,25 @@ def build_probe(out: str = PROBE_OUT) -> str:
     return link(PROBE_SOURCES, out)
 
 
+def build_native(lib_name: str = "libpagedkv.so") -> str:
+    """Build the native C-ABI test program against `lib_name` (already built next to this
+    file); the program finds the library through an $ORIGIN run path."""
+    out = NATIVE_OUT[lib_name]
+    # -l (not a path) so the program records the bare file name and the run path finds it
+    lib_flag = "-l" + lib_name[len("lib"):-len(".so")]
+    cmd = [hipcc(), *common_flags(), "-x", "hip", NATIVE_SRC, f"-L{HERE}", lib_flag,
+           "-Wl,-rpath,$ORIGIN", "-o", out + ".tmp"]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(" ".join(cmd) + "\n" + res.stdout + res.stderr)
+        raise RuntimeError(f"building {os.path.basename(out)} failed")
+    os.replace(out + ".tmp", out)
+    return out
+
+
 if __name__ == "__main__":
     print(build())
     print(build_checked())
     print(build_probe())
+    for name in NATIVE_OUT:
+        print(build_native(name))
