@@ -39,11 +39,39 @@ TRAFFIC_FILE = os.path.join(HERE, "profiles", "decode_traffic.json")
 OUT_TORCH = {"f32": "float32", "bf16": "bfloat16", "f16": "float16"}  # torch dtype names
 
 
+def warm_up(args, torch, step):
+    """The untimed warm-up: args.warmup steps when given; otherwise at least 5 and until
+    args.warmup_seconds of them have run. Sets args.warmup to the number done."""
+    if args.warmup is not None:
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        return args.warmup
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        for _ in range(5):
+            step()
+        n += 5
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= args.warmup_seconds:
+            break
+    args.warmup = n
+    return n
+
+
 def parse_args():
     p = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--warmup", type=int, default=None,
+                   help="untimed warm-up steps (default: at least 5, and as many as run in "
+                        "--warmup-seconds; the JSON line reports the number done)")
+    p.add_argument("--warmup-seconds", type=float, default=0.5,
+                   help="without --warmup: keep warming up until the GPU has run the step "
+                        "this long (its clocks rise over the first tens of milliseconds of "
+                        "sustained work: a p1 prefill call measured 473 us after 5 warm-up "
+                        "calls and 383 us after 100)")
     p.add_argument("--workload", default="c5")
     p.add_argument("--kernel", default="auto",
                    choices=["auto", "valu", "mfma", "mfma_hw", "mfma_sk"])
@@ -178,7 +206,7 @@ def hip_graph_replay_ms(args, torch, dev, step):
     if hip.hipGraphInstantiate(ctypes.byref(exe), graph, None, None, 0):
         raise RuntimeError("hipGraphInstantiate failed")
     try:
-        for _ in range(args.warmup):
+        for _ in range(min(args.warmup, 20)):
             hip.hipGraphLaunch(exe, handle)
         torch.cuda.synchronize()
         reps = max(1, args.steps // args.graph_steps)
@@ -601,9 +629,7 @@ def bench_prefill(args, torch, pk, wl):
         if ev is not None:
             ev[1].record()
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    warm_up(args, torch, step)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]
     t0 = time.perf_counter()
@@ -772,9 +798,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    warm_up(args, torch, step)
 
     # Even steps time the attention kernel (events recorded by the library around it), odd
     # steps the whole call (events around the call only); both kinds are in the timed region.
@@ -819,7 +843,7 @@ def main():
     graph_ms = hip_graph_ms = eager_ms = None
     if args.graph:
         # The same steps, plain, with no timing events: the reference for the replays.
-        for _ in range(args.warmup):
+        for _ in range(min(args.warmup, 20)):
             step()
         torch.cuda.synchronize()
         e0 = time.perf_counter()
@@ -838,7 +862,7 @@ def main():
         with torch.cuda.graph(graph):
             for _ in range(args.graph_steps):
                 step()
-        for _ in range(args.warmup):
+        for _ in range(min(args.warmup, 20)):
             graph.replay()
         torch.cuda.synchronize()
         reps = max(1, args.steps // args.graph_steps)
@@ -864,7 +888,7 @@ def main():
                 call()
 
         def per_step_ms(fn):
-            for _ in range(args.warmup):
+            for _ in range(min(args.warmup, 20)):
                 fn()
             torch.cuda.synchronize()
             t = time.perf_counter()
