@@ -75,11 +75,17 @@ __device__ __forceinline__ int sub_block_id(const int32_t* table, int j, int sh,
 template <int D> struct Stager {
   static constexpr int kCPR = D / 8;                           // pieces per row
   static constexpr int kPieces = kPairRows * kCPR / 256;      // per thread: D 64 -> 1, 128 -> 2
-  uint4 k[kPieces], v[kPieces];
   uint32_t goff[kPieces];  // byte offset of the piece inside its block (row, head, column)
   uint32_t loff[kPieces];  // byte offset of the piece in an LdsPair buffer
   int row[kPieces];        // r
   int blk[kPieces];        // 0 or 1: block of the pair (uniform over the wave)
+
+  // One staged pair in flight: the thread's pieces and the pair's edge state.
+  struct Regs {
+    uint4 k[kPieces], v[kPieces];
+    int zero_a, zero_b;  // uniform: block A / B of the pair is absent or invalid
+    int tail_from;       // rows r >= tail_from of the pair are zero (32: none)
+  };
 
   __device__ __forceinline__ void init(int wave, size_t row_stride, size_t head_off) {
 #pragma unroll
@@ -93,48 +99,48 @@ template <int D> struct Stager {
     }
   }
 
-  // Load pair `pair`. The loads are only issued here; the data is first used by commit(),
-  // after the current pair's compute, so their latency hides behind it. A block id outside the
-  // pool reads block 0 instead, and such a block, and rows at or past tok1 (only in the last
-  // pair), are stored as zeros by commit().
-  int zero_a, zero_b;   // uniform: block A / B of the staged pair is absent or invalid
-  int tail_from;        // rows r >= tail_from of the staged pair are zero (32: none)
-  __device__ __forceinline__ void load(const PrefillArgs& a, const int32_t* table, int nblk,
-                                       int tok1, size_t row_stride, int pair) {
+  // Load pair `pair` into r. The loads are only issued here; the data is first used by
+  // commit(), two pairs' compute later, so their latency hides behind it. A block id outside
+  // the pool reads block 0 instead, and such a block, and rows at or past tok1 (only in the
+  // last pair), are stored as zeros by commit().
+  __device__ __forceinline__ void load(Regs& rg, const PrefillArgs& a, const int32_t* table,
+                                       int nblk, int tok1, size_t row_stride, int pair) const {
     const int jA = 2 * pair;
     const int sh = __builtin_ctz((unsigned)a.block_size) - 4;  // block_size = 16 << sh
     const int idA = sub_block_id(table, jA, sh, a.num_blocks);
     const int idB = jA + 1 < nblk ? sub_block_id(table, jA + 1, sh, a.num_blocks) : -1;
     const bool okA = idA >= 0;
     const bool okB = idB >= 0;
-    zero_a = !okA;
-    zero_b = !okB;
-    tail_from = min(tok1 - 32 * pair, 32);
+    rg.zero_a = !okA;
+    rg.zero_b = !okB;
+    rg.tail_from = min(tok1 - 32 * pair, 32);
     const size_t bbytes = (size_t)16 * row_stride * 2;  // bytes of one block
     const char* kc = reinterpret_cast<const char*>(a.k_cache);
     const char* vc = reinterpret_cast<const char*>(a.v_cache);
+    const int safe_a = okA ? idA : 0, safe_b = okB ? idB : 0;
 #pragma unroll
     for (int x = 0; x < kPieces; ++x) {
-      const bool okb = blk[x] ? okB : okA;
-      const size_t base = (size_t)(okb ? (blk[x] ? idB : idA) : 0) * bbytes;
-      k[x] = *reinterpret_cast<const uint4*>(kc + base + goff[x]);
-      v[x] = *reinterpret_cast<const uint4*>(vc + base + goff[x]);
+      // The block is the same for the whole wave; its id taken from the first lane stays in a
+      // scalar register (a per-lane select of it cost more vector instructions per pair).
+      const int id = __builtin_amdgcn_readfirstlane(blk[x] ? safe_b : safe_a);
+      rg.k[x] = *reinterpret_cast<const uint4*>(kc + (size_t)id * bbytes + goff[x]);
+      rg.v[x] = *reinterpret_cast<const uint4*>(vc + (size_t)id * bbytes + goff[x]);
     }
   }
 
-  __device__ __forceinline__ void commit(LdsPair<D>& p) {
-    if (zero_a || zero_b || tail_from < 32) {  // uniform: only an edge pair
+  __device__ __forceinline__ void commit(Regs& rg, LdsPair<D>& p) const {
+    if (rg.zero_a || rg.zero_b || rg.tail_from < 32) {  // uniform: only an edge pair
 #pragma unroll
       for (int x = 0; x < kPieces; ++x) {
-        const bool ok = !(blk[x] ? zero_b : zero_a) && row[x] < tail_from;
-        k[x] = select4(ok, k[x], make_uint4(0, 0, 0, 0));
-        v[x] = select4(ok, v[x], make_uint4(0, 0, 0, 0));
+        const bool ok = !(blk[x] ? rg.zero_b : rg.zero_a) && row[x] < rg.tail_from;
+        rg.k[x] = select4(ok, rg.k[x], make_uint4(0, 0, 0, 0));
+        rg.v[x] = select4(ok, rg.v[x], make_uint4(0, 0, 0, 0));
       }
     }
 #pragma unroll
     for (int x = 0; x < kPieces; ++x) {
-      *reinterpret_cast<uint4*>(p.k + loff[x]) = k[x];
-      *reinterpret_cast<uint4*>(p.v + loff[x]) = v[x];
+      *reinterpret_cast<uint4*>(p.k + loff[x]) = rg.k[x];
+      *reinterpret_cast<uint4*>(p.v + loff[x]) = rg.v[x];
     }
   }
 };
@@ -392,23 +398,31 @@ prefill_mfma_kernel(const PrefillArgs a) {
   }
 
   if (pair_lo < pair_hi) {
+    // Two pairs in flight: while pair k is computed from LDS, pair k + 1 waits in registers
+    // (loaded during pair k - 1) and pair k + 2's loads are issued. The loop is unrolled by
+    // two so that each of the two register sets keeps fixed registers.
     Stager<D> s;
+    typename Stager<D>::Regs r0, r1;
     s.init(wave, row_stride, head_off);
-    s.load(a, table, nblk, tok1, row_stride, pair_lo);
-    s.commit(buf[0]);
+    s.load(r0, a, table, nblk, tok1, row_stride, pair_lo);
+    if (pair_lo + 1 < pair_hi) s.load(r1, a, table, nblk, tok1, row_stride, pair_lo + 1);
+    s.commit(r0, buf[0]);
     __syncthreads();
-    for (int k = pair_lo; k < pair_hi; ++k) {
-      const bool more = k + 1 < pair_hi;  // uniform
+    auto step = [&](int k, typename Stager<D>::Regs& next, typename Stager<D>::Regs& spare) {
       const int cur = (k - pair_lo) & 1;
-      if (more) s.load(a, table, nblk, tok1, row_stride, k + 1);
+      if (k + 2 < pair_hi) s.load(spare, a, table, nblk, tok1, row_stride, k + 2);  // uniform
       const int key0 = 32 * k;
       if (wave_rows && key0 <= p_max) {
         uint4 ka[NCH], kb[NCH], vt[EPL];
         read_pair<D>(ka, kb, vt, buf[cur], n16, kg);
         pair_compute_rows<KT>(ka, kb, vt, st, qb, sl2, kg, row_pos, key0, key0 + 31 > p_min);
       }
-      if (more) s.commit(buf[cur ^ 1]);
+      if (k + 1 < pair_hi) s.commit(next, buf[cur ^ 1]);
       __syncthreads();
+    };
+    for (int k = pair_lo; k < pair_hi; k += 2) {
+      step(k, r1, r0);
+      if (k + 1 < pair_hi) step(k + 1, r0, r1);
     }
   }
 
