@@ -314,24 +314,30 @@ def record_traffic(args):
 
 
 def read_probe(torch, dev, nbytes, reps=5):
-    """Achievable streaming-read rate at this byte count: a grid-stride read kernel
-    (libpagedkv_probe.so) over a buffer of nbytes, cold (a 1 GiB buffer is read in between so
-    neither L2 nor the MALL holds it), timed with events, once with plain loads and once with
-    the non-temporal hint. Returns the faster as (median us, GB/s), and both rates."""
+    """Achievable streaming-read rate at this byte count: read kernels (libpagedkv_probe.so)
+    over a buffer of nbytes, cold (a 1 GiB buffer is read in between so neither L2 nor the MALL
+    holds it), timed with events: grid-stride with plain loads, grid-stride with the
+    non-temporal hint, and contiguous chunks per workgroup with the hint (four workgroups per
+    CU: the fastest simple read measured on this part). Returns the fastest as (median us,
+    GB/s), and every rate."""
     import ctypes
     lib = ctypes.CDLL(os.path.join(HERE, "paged_kv_decode_write_amd", "libpagedkv_probe.so"))
-    for fn in (lib.pagedkv_read_probe, lib.pagedkv_read_probe_nt):
+    for fn in (lib.pagedkv_read_probe, lib.pagedkv_read_probe_nt,
+               lib.pagedkv_read_probe_chunked_nt):
         fn.restype = ctypes.c_int
         fn.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int32,
                        ctypes.c_void_p]
     grid = 256 * 16
+    chunk_grid = 4 * torch.cuda.get_device_properties(dev).multi_processor_count
     nbytes = (nbytes + 15) // 16 * 16
     buf = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
     flush = torch.ones((1 << 30) // 4, dtype=torch.float32, device=dev)
     sink = torch.zeros(grid, dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream(dev).cuda_stream
     rates = {}
-    for name, fn in (("plain", lib.pagedkv_read_probe), ("nontemporal", lib.pagedkv_read_probe_nt)):
+    for name, fn, g in (("plain", lib.pagedkv_read_probe, grid),
+                        ("nontemporal", lib.pagedkv_read_probe_nt, grid),
+                        ("chunked_nontemporal", lib.pagedkv_read_probe_chunked_nt, chunk_grid)):
         times = []
         for i in range(reps + 1):
             if lib.pagedkv_read_probe(flush.data_ptr(), flush.numel() * 4, sink.data_ptr(), grid,
@@ -339,7 +345,7 @@ def read_probe(torch, dev, nbytes, reps=5):
                 raise RuntimeError("read probe launch failed")
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record()
-            if fn(buf.data_ptr(), nbytes, sink.data_ptr(), grid, stream):
+            if fn(buf.data_ptr(), nbytes, sink.data_ptr(), g, stream):
                 raise RuntimeError("read probe launch failed")
             b.record()
             torch.cuda.synchronize()

@@ -302,3 +302,18 @@ def test_checked_build_loads_and_exports_everything():
     # host-side argument checks are the same as in the default build
     assert _write(ck, T=-1) == ERR_SHAPE
     assert _write(ck, k=None) == ERR_NULL
+
+
+def test_probe_library_exports_its_declared_symbols():
+    """The measurement utility libpagedkv_probe.so exports every call paged_kv_probe.h
+    declares (the benchmark's read probe loads them by name)."""
+    path = os.path.join(os.path.dirname(_binding.library_path()), "libpagedkv_probe.so")
+    if not os.path.exists(path):
+        pytest.skip("libpagedkv_probe.so not built")
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "paged_kv_probe.h")).read(),
+                  flags=re.S)
+    declared = set(re.findall(r"\b(pagedkv_\w+)\s*\(", text))
+    assert {"pagedkv_read_probe", "pagedkv_read_probe_nt", "pagedkv_read_probe_chunked_nt"} <= declared
+    out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True,
+                         check=True).stdout
+    assert declared <= set(re.findall(r"\bT (pagedkv_\w+)", out))
