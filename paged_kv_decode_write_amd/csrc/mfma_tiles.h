@@ -109,12 +109,21 @@ template <int KT> constexpr float kWeightLift = KT == kDtF16 ? 7.f : 0.f;
 // format, with p = hi + lo + O(2^-16 p). bf16: hi is p rounded to nearest even, two per v_cvt_pk; the
 // remainders p - hi come from v_dot2c_f32_bf16 against (-1, 0) and (0, -1), one instruction
 // each (p - hi is exact in fp32, and the other product is 0), and lo is them rounded. fp16: hi
-// is p rounded toward zero (v_cvt_pkrtz_f16_f32), lo the remainder likewise.
+// is p rounded toward zero (v_cvt_pkrtz_f16_f32), the remainders likewise from
+// v_dot2_f32_f16, and lo is them rounded toward zero.
 template <int KT>
 __device__ __forceinline__ void split_weight_pair(float a, float b, uint32_t& hi, uint32_t& lo) {
   if constexpr (KT == kDtF16) {
+    // (-1, 0) and (0, -1) as packed fp16, in scalar registers as for bf16 below
+    uint32_t neg_first = 0x0000bc00u, neg_second = 0xbc000000u;
+    asm("" : "+s"(neg_first));
+    asm("" : "+s"(neg_second));
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
     const fp16x2 h = __builtin_amdgcn_cvt_pkrtz(a, b);
-    const fp16x2 l = __builtin_amdgcn_cvt_pkrtz(a - (float)h[0], b - (float)h[1]);
+    const h2 hh = __builtin_bit_cast(h2, h);
+    const fp16x2 l = __builtin_amdgcn_cvt_pkrtz(
+        __builtin_amdgcn_fdot2(hh, __builtin_bit_cast(h2, neg_first), a, false),
+        __builtin_amdgcn_fdot2(hh, __builtin_bit_cast(h2, neg_second), b, false));
     hi = __builtin_bit_cast(uint32_t, h);
     lo = __builtin_bit_cast(uint32_t, l);
   } else {
