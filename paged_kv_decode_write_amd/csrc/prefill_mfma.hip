@@ -100,7 +100,7 @@ template <int D> struct Stager {
   }
 
   // Load pair `pair` into r. The loads are only issued here; the data is first used by
-  // commit(), two pairs' compute later, so their latency hides behind it. A block id outside
+  // commit(), after the current pair's compute, so their latency hides behind it. A block id outside
   // the pool reads block 0 instead, and such a block, and rows at or past tok1 (only in the
   // last pair), are stored as zeros by commit().
   __device__ __forceinline__ void load(Regs& rg, const PrefillArgs& a, const int32_t* table,
@@ -398,9 +398,11 @@ prefill_mfma_kernel(const PrefillArgs a) {
   }
 
   if (pair_lo < pair_hi) {
-    // Two pairs in flight: while pair k is computed from LDS, pair k + 1 waits in registers
-    // (loaded during pair k - 1) and pair k + 2's loads are issued. The loop is unrolled by
-    // two so that each of the two register sets keeps fixed registers.
+    // Two register sets, the loop unrolled by two: pair k + 2's loads are issued while pair
+    // k is computed from LDS and pair k + 1 waits in the other set. (The compiler's wait
+    // counting, merging the paths around the conditional loads and commits, still waits for
+    // both sets at each commit, so mostly one pair is in flight; unconditional loads and
+    // commits fixed the commit waits but not the loop head's, and measured the same.)
     Stager<D> s;
     typename Stager<D>::Regs r0, r1;
     s.init(wave, row_stride, head_off);
