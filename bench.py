@@ -60,6 +60,19 @@ def warm_up(args, torch, step):
     return n
 
 
+def event_steps(steps, per_kind):
+    """Indices of the timed steps that carry kernel events and of those that carry call
+    events: per_kind of each, spread evenly over the steps (every step, alternating, when
+    there are not enough steps for both kinds; a single step times the kernel)."""
+    if steps <= 1:
+        return [0], []
+    if per_kind <= 0 or 2 * per_kind >= steps:
+        return list(range(0, steps, 2)), list(range(1, steps, 2))
+    kern = [int((j + 0.25) * steps / per_kind) for j in range(per_kind)]
+    call = [int((j + 0.75) * steps / per_kind) for j in range(per_kind)]
+    return kern, call
+
+
 def parse_args():
     p = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     p.add_argument("--gpus", type=int, default=1)
@@ -67,6 +80,10 @@ def parse_args():
     p.add_argument("--warmup", type=int, default=None,
                    help="untimed warm-up steps (default: at least 5, and as many as run in "
                         "--warmup-seconds; the JSON line reports the number done)")
+    p.add_argument("--event-steps", type=int, default=4,
+                   help="decode workloads: timed steps that carry the kernel's timing events, "
+                        "and as many that carry the whole call's; the other timed steps carry "
+                        "none (0, or too few steps for both: every step, alternating)")
     p.add_argument("--warmup-seconds", type=float, default=0.5,
                    help="without --warmup: keep warming up until the GPU has run the step "
                         "this long (its clocks rise over the first tens of milliseconds of "
@@ -806,21 +823,24 @@ def main():
 
     warm_up(args, torch, step)
 
-    # Even steps time the attention kernel (events recorded by the library around it), odd
-    # steps the whole call (events around the call only); both kinds are in the timed region.
-    evs = [[(hip.create(), hip.create()) for _ in subs] for _ in range(args.steps)]
+    # Some timed steps time the attention kernel (events the library records around it),
+    # others the whole call (events around the call only), spread over the timed region; the
+    # rest carry no events, since each event record costs the GPU about 2 us between kernels
+    # (the c5 step measured 370.2 us with none, 377.7 with four per step).
+    kern_steps, call_steps = event_steps(args.steps, args.event_steps)
+    evs = {i: [(hip.create(), hip.create()) for _ in subs] for i in kern_steps + call_steps}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(evs[i], kernel_events=(i % 2 == 0) or args.steps == 1)
+        step(evs.get(i), kernel_events=i in kern_steps)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
 
     per = []
     for j, d in enumerate(subs):
-        kern = sorted(hip.elapsed_ms(*evs[i][j]) for i in range(0, args.steps, 2))
-        call = sorted(hip.elapsed_ms(*evs[i][j]) for i in range(1, args.steps, 2)) or kern
+        kern = sorted(hip.elapsed_ms(*evs[i][j]) for i in kern_steps)
+        call = sorted(hip.elapsed_ms(*evs[i][j]) for i in call_steps) or kern
         kmean = sum(kern) / len(kern)
         cmean = sum(call) / len(call)
         w = d["workload"]
@@ -942,6 +962,8 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": args.in_dtype if kernel.startswith("mfma") else "fp32",
+        "event_steps": {"kernel": len(kern_steps), "call": len(call_steps),
+                        "none": args.steps - len(kern_steps) - len(call_steps)},
         "data": (f"synthetic (seeded N(0,1) {args.in_dtype} K/V pools, shuffled block tables), "
                  "resident in HBM"),
         "config": {

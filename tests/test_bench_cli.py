@@ -79,3 +79,19 @@ def test_record_traffic_scales_by_the_copy_and_averages_the_attention_launches(t
     assert rec["bytes_per_launch"] == 2000 * 1024 * 2 + 20 * 1024
     assert rec["kernel_source"] == bench.kernel_source_hash("mfma_sk+mfma_hw")
     assert rec["kernel_source"] != bench.kernel_source_hash("mfma_hw")
+
+
+def test_event_steps_are_disjoint_spread_and_in_range():
+    """The timed steps that carry timing events: disjoint kernel and call sets inside the
+    timed steps, spread over them, every step alternating when there are too few."""
+    import bench
+    for steps, per in ((20, 4), (100, 4), (10, 2), (5, 4), (20, 0), (1, 4), (2, 1)):
+        kern, call = bench.event_steps(steps, per)
+        assert kern, (steps, per)
+        assert not set(kern) & set(call)
+        assert all(0 <= i < steps for i in kern + call)
+        if steps > 1 and 0 < per and 2 * per < steps:
+            assert len(kern) == len(call) == per
+            assert kern[0] < steps // per and kern[-1] >= steps - steps // per
+        elif steps > 1:
+            assert sorted(kern + call) == list(range(steps))
