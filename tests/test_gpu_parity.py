@@ -1230,3 +1230,34 @@ def test_concurrent_calls_on_two_streams(dev):
         torch.cuda.synchronize()
         for name in names:
             assert torch.equal(outs[name], alone[name]), (rep, name)
+
+
+def test_concurrent_steps_on_two_streams_match_sequential(dev):
+    """Two decode steps with their own pools and workspaces, issued on two streams before
+    either is waited for (c4 on the stream kernel, c5b on the split head-per-wave kernel and its
+    merge), give the same bits as the same steps run one after the other, three times over."""
+    data = {n: to_dev(wl.make_inputs(wl.WORKLOADS[n]), dev) for n in ("c4", "c5b")}
+    ref = {}
+    for n, d in data.items():
+        e = dict(d)
+        e["k_cache"], e["v_cache"] = d["k_cache"].clone(), d["v_cache"].clone()
+        ref[n] = (run_step(e), e["k_cache"], e["v_cache"])
+    torch.cuda.synchronize()
+    streams = {"c4": torch.cuda.Stream(dev), "c5b": torch.cuda.Stream(dev)}
+    for rep in range(3):
+        runs = {}
+        for n, d in data.items():
+            e = dict(d)
+            e["k_cache"], e["v_cache"] = d["k_cache"].clone(), d["v_cache"].clone()
+            runs[n] = e
+        torch.cuda.synchronize()
+        outs = {}
+        for n, e in runs.items():
+            with torch.cuda.stream(streams[n]):
+                outs[n] = run_step(e)
+        torch.cuda.synchronize()
+        for n, e in runs.items():
+            out, kc, vc = ref[n]
+            assert torch.equal(outs[n], out), (n, rep)
+            assert torch.equal(e["k_cache"].view(torch.int16), kc.view(torch.int16)), (n, rep)
+            assert torch.equal(e["v_cache"].view(torch.int16), vc.view(torch.int16)), (n, rep)
