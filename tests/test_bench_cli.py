@@ -95,3 +95,27 @@ def test_event_steps_are_disjoint_spread_and_in_range():
             assert kern[0] < steps // per and kern[-1] >= steps - steps // per
         elif steps > 1:
             assert sorted(kern + call) == list(range(steps))
+
+
+def test_warm_up_counts_steps_and_stops_on_time():
+    """Without --warmup the warm-up runs whole groups of five steps until --warmup-seconds
+    have passed and records the count; with --warmup it runs exactly that many."""
+    import types
+    import bench
+
+    class FakeCuda:
+        def synchronize(self):
+            pass
+
+    torch_stub = types.SimpleNamespace(cuda=FakeCuda())
+    calls = []
+    args = types.SimpleNamespace(warmup=None, warmup_seconds=0.0)
+    n = bench.warm_up(args, torch_stub, lambda: calls.append(1))
+    assert n == 5 and args.warmup == 5 and len(calls) == 5  # at least one group of five
+    calls.clear()
+    args = types.SimpleNamespace(warmup=None, warmup_seconds=0.05)
+    n = bench.warm_up(args, torch_stub, lambda: (calls.append(1), __import__("time").sleep(0.002)))
+    assert n % 5 == 0 and n >= 15 and args.warmup == n == len(calls)
+    calls.clear()
+    args = types.SimpleNamespace(warmup=3, warmup_seconds=10.0)
+    assert bench.warm_up(args, torch_stub, lambda: calls.append(1)) == 3 and len(calls) == 3
