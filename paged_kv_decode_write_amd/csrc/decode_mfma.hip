@@ -109,8 +109,10 @@ decode_mfma_kernel(const DecodeArgs a) {
   ctx.n16 = n16;
   ctx.kg = kg;
   // Fused step: the new row of this head, loaded unconditionally (from pool slot 0 when there
-  // is no step write, then never used) so no memory operation waits behind a branch.
-  const int sub_pos = step_sub_pos(a, table, b, L);
+  // is no step write, then never used) so no memory operation waits behind a branch; the slot
+  // is read once, for the position test here and the store at the end.
+  const int64_t slot = step_slot(a, b);
+  const int sub_pos = step_sub_pos_at(a, slot, table, L);
   NewRow<NCH, EPL> nrow;
   load_new_row(nrow, new_k_row(a, b, g, D), new_v_row(a, b, g, D), n16, kg);
   if constexpr (ROPE)
@@ -147,10 +149,10 @@ decode_mfma_kernel(const DecodeArgs a) {
 
   // The step's store comes after every block-table read, so the compiler can keep those reads
   // on the scalar path (no earlier store may have changed the table).
-  if (a.k_new && wave == 0 && (L > 0 ? L - 1 < tok1 : part == 0)) {
-    if constexpr (ROPE) step_store_regs<D>(a, a.slot_mapping, b, g, nrow, n16, kg);
-    else step_store<D>(a, a.slot_mapping, b, g, lane);
-  }
+  // It stores from the registers that hold the new rows (rotated key with RoPE), at the slot
+  // read above, so it waits on no read.
+  if (a.k_new && wave == 0 && (L > 0 ? L - 1 < tok1 : part == 0))
+    step_store_regs_at<D>(a, slot, g, nrow, n16, kg);
   if constexpr (ROPE)
     if (wave == 0 && part == 0) store_q_out<D>(a, qb, b, g, G, n16, kg);
 
@@ -265,6 +267,7 @@ decode_mfma_hw_kernel(const DecodeArgs a) {
   // before the first pair so that waiting for it never waits for the pair.
   NewRow<NCH, EPL> nrow;
   load_new_row(nrow, new_k_row(a, b, g, D), new_v_row(a, b, g, D), n16, kg);
+  const int64_t slot = step_slot(a, b);  // read once: the position test and the store
   // The first pair's K / V loads go out with q's, before the context length arrives: a
   // partition that then turns out empty discards them; every other one saves a round trip.
   PairTile<NCH, EPL> t[NBUF];
@@ -293,7 +296,7 @@ decode_mfma_hw_kernel(const DecodeArgs a) {
 #pragma unroll
   for (int e = 0; e < EPL; ++e) st.acc[e] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  const int sub_pos = step_sub_pos(a, table, b, L);
+  const int sub_pos = step_sub_pos_at(a, slot, table, L);
   if constexpr (ROPE)
     rope_pieces<KT>(qb, nrow.k, (float)a.positions[b], a.inv_freq, a.interleaved != 0, kg,
                     lane);
@@ -330,11 +333,10 @@ decode_mfma_hw_kernel(const DecodeArgs a) {
     }
   }
 
-  // The step's store comes after every block-table read (see the split-wave kernel).
-  if (a.k_new && (L > 0 ? L - 1 < tok1 : part == 0)) {
-    if constexpr (ROPE) step_store_regs<D>(a, a.slot_mapping, b, g, nrow, n16, kg);
-    else step_store<D>(a, a.slot_mapping, b, g, lane);
-  }
+  // The step's store comes after every block-table read (see the split-wave kernel), from
+  // the registers that hold the new rows, at the slot read above.
+  if (a.k_new && (L > 0 ? L - 1 < tok1 : part == 0))
+    step_store_regs_at<D>(a, slot, g, nrow, n16, kg);
   if constexpr (ROPE)
     if (part == 0) store_q_out<D>(a, qb, b, g, G, n16, kg);
 

@@ -80,6 +80,15 @@ struct SkPos {
   int b, S, hg, L, pairs, k, k0, kend, first;
 };
 
+// The fused step's facts of a segment, read ahead with its first pair's block ids: the new
+// token's slot (-1 when the segment does not end its sequence, or without new rows), the block
+// table's entry for position L - 1, and with RoPE the sequence's position.
+struct SegFacts {
+  int64_t slot;
+  int entry;
+  float pos;
+};
+
 // One wave's K / V tile of pair p for KV head g: the context a pair load needs.
 template <int D>
 __device__ __forceinline__ PairCtx<D> sk_ctx(const DecodeArgs& a, const int32_t* tables,
@@ -108,20 +117,16 @@ __device__ __forceinline__ int2 sk_ids(const PairCtx<D>& c, const SkPos& p) {
 }
 
 // Writes the partial of the segment that ends with pair p (slot w - first / q) and, when it
-// ends its (sequence, head group), marks that sequence's remaining slots empty and stores the
-// step's new rows; with RoPE the segment that starts the sequence stores the rotated q.
+// ends its (sequence, head group), marks that sequence's remaining slots empty; with RoPE the
+// segment that starts the sequence stores the rotated q. (The step's new rows are stored by
+// the kernel's loop when the segment's last pair is scored.)
 template <int D, int NCH, int EPL, bool ROPE>
-__device__ __forceinline__ void sk_close(const DecodeArgs& a, const int64_t* slots,
-                                         const SkPos& p, int g, int slot,
+__device__ __forceinline__ void sk_close(const DecodeArgs& a, const SkPos& p, int g, int slot,
                                          const WaveState<EPL>& st, const uint4 (&qb)[NCH],
-                                         const NewRow<NCH, EPL>& nrow, int lane) {
+                                         int lane) {
   const int n16 = lane & 15, kg = lane >> 4;
   const int G = a.num_q_heads / a.num_kv_heads;
   const bool last = p.kend == p.pairs;
-  if (a.k_new && last) {
-    if constexpr (ROPE) step_store_regs<D>(a, slots, p.b, g, nrow, n16, kg);
-    else step_store<D>(a, slots, p.b, g, lane);
-  }
   if constexpr (ROPE)
     if (p.k0 == 0) store_q_out<D>(a, qb, p.b, g, G, n16, kg);
   const float l_run = row4_sum(st.l_run);
@@ -277,6 +282,24 @@ decode_mfma_sk_kernel(const DecodeArgs a, const int32_t* __restrict__ tables,
     };
     const auto head = [&](const SkPos& p) { return p.hg * HPW + wave; };
     const auto head_ld = [&](const SkPos& p) { return min(head(p), Hkv - 1); };
+    const auto load_ids = [&](const SkPos& p) {
+      return sk_ids<D>(sk_ctx<D>(a, tables, p, head_ld(p), n16, kg), p);
+    };
+    // The fused step's facts of the segment that pair p starts, read with p's block ids, NBUF
+    // pairs before p is computed, so that neither the segment's start nor its close waits on a
+    // read of its own: with RoPE the position; for the segment that ends its sequence, the new
+    // token's slot and the table's entry for position L - 1.
+    const auto seg_facts = [&](const SkPos& p) {
+      SegFacts f{-1, 0, 0.f};
+      if (p.k == p.k0) {
+        if (a.k_new && p.kend == p.pairs) {
+          f.slot = slots[p.b];
+          f.entry = tables[(size_t)p.b * a.max_blocks + (p.L - 1) / BS];
+        }
+        if constexpr (ROPE) f.pos = (float)positions[p.b];
+      }
+      return f;
+    };
 
     // One continuous pipeline over the slice's pairs, across segment boundaries: pair j is
     // computed from buffer j % NBUF while pairs j + 1 .. j + NBUF - 1 are in flight in the
@@ -284,28 +307,34 @@ decode_mfma_sk_kernel(const DecodeArgs a, const int32_t* __restrict__ tables,
     // pair j ends a segment, the next segment's q and new rows are loaded right after pair j's
     // scores (q is not needed again), and its first pairs are already in flight, so the
     // boundary costs no round trip. pp[0] is the pair computed next, pp[i] the i-th after it;
-    // ids[i] holds pp[i]'s block ids.
+    // ids[i] and sf[i] hold pp[i]'s block ids and segment facts.
     SkPos pp[NBUF + 1];
     pp[0] = pos_at(lo, __builtin_amdgcn_readfirstlane(b0), __builtin_amdgcn_readfirstlane(S0));
 #pragma unroll
     for (int i = 1; i <= NBUF; ++i) pp[i] = pos_next(pp[i - 1]);
     PairTile<NCH, EPL> t[NBUF];
     int2 ids[NBUF];
-    ids[0] = sk_ids<D>(sk_ctx<D>(a, tables, pp[0], head_ld(pp[0]), n16, kg), pp[0]);
+    SegFacts sf[NBUF];
+    ids[0] = load_ids(pp[0]);
+    sf[0] = seg_facts(pp[0]);
     load_q(pp[0].b, head_ld(pp[0]));
 #pragma unroll
-    for (int i = 1; i < NBUF; ++i)
-      ids[i] = sk_ids<D>(sk_ctx<D>(a, tables, pp[i], head_ld(pp[i]), n16, kg), pp[i]);
+    for (int i = 1; i < NBUF; ++i) {
+      ids[i] = load_ids(pp[i]);
+      sf[i] = seg_facts(pp[i]);
+    }
     const int P = hi - lo;
 #pragma unroll
     for (int i = 0; i + 1 < NBUF; ++i) {  // past the slice's end: pair 0's addresses again
       const SkPos& pi = i < P ? pp[i] : pp[0];
       const PairCtx<D> c = sk_ctx<D>(a, tables, pi, head_ld(pi), n16, kg);
-      pair_issue(t[i], c, i < P ? ids[i] : ids[0], 2 * pi.k);
-      pair_valid(t[i], c, i < P ? ids[i] : ids[0], 2 * pi.k);
+      const int2 ii = i < P ? ids[i] : ids[0];
+      pair_issue(t[i], c, ii, 2 * pi.k);
+      pair_valid(t[i], c, ii, 2 * pi.k);
     }
     WaveState<EPL> st;
     int sub_pos = -1;
+    int64_t seg_slot = -1;  // the current segment's new-token slot (-1: it stores nothing)
     const float sl2 = a.scale_log2;
     for (int j = 0; j < P; j += NBUF) {
 #pragma unroll
@@ -320,8 +349,8 @@ decode_mfma_sk_kernel(const DecodeArgs a, const int32_t* __restrict__ tables,
           pair_issue(t[(u + NBUF - 1) % NBUF], c, ii, 2 * pi.k);
           pair_valid(t[(u + NBUF - 1) % NBUF], c, ii, 2 * pi.k);
         }
-        const int2 idn = sk_ids<D>(sk_ctx<D>(a, tables, pp[NBUF], head_ld(pp[NBUF]), n16, kg),
-                                   pp[NBUF]);
+        const int2 idn = load_ids(pp[NBUF]);
+        const SegFacts sfn = seg_facts(pp[NBUF]);
         const SkPos& pc = pp[0];
         if (jj < P) {
           if (pc.k == pc.k0) {  // the segment starts: fresh state
@@ -329,15 +358,20 @@ decode_mfma_sk_kernel(const DecodeArgs a, const int32_t* __restrict__ tables,
             st.l_run = 0.f;
 #pragma unroll
             for (int e = 0; e < EPL; ++e) st.acc[e] = floatx4{0.f, 0.f, 0.f, 0.f};
-            sub_pos = step_sub_pos(a, slots, tables + (size_t)pc.b * a.max_blocks, pc.b, pc.L);
+            seg_slot = sf[0].slot;
+            sub_pos = sub_pos_of(a, sf[0].slot, sf[0].entry, pc.L);
             if constexpr (ROPE)
-              rope_pieces<KT>(qb, nrow.k, (float)positions[pc.b], a.inv_freq,
-                              a.interleaved != 0, kg, lane);
+              rope_pieces<KT>(qb, nrow.k, sf[0].pos, a.inv_freq, a.interleaved != 0, kg, lane);
           }
           use_new_row(t[u], nrow, sub_pos, n16, kg);
           float sc[8];
           pair_scores<KT>(t[u], qb, sl2, sc);
           const bool closes = pc.k + 1 == pc.kend;
+          // The sequence's last segment stores the step's new rows from registers (as loaded,
+          // or the rotated key), at the slot read with its first pair, before the next
+          // segment's loads replace them.
+          if (closes && pc.kend == pc.pairs && head(pc) < Hkv)
+            step_store_regs_at<D>(a, seg_slot, head(pc), nrow, n16, kg);
           // Without RoPE, q and the new row are dead once the closing pair's scores are taken:
           // the next segment's load right away. With RoPE the close stores them (rotated), so
           // they load after it.
@@ -347,8 +381,7 @@ decode_mfma_sk_kernel(const DecodeArgs a, const int32_t* __restrict__ tables,
           if (closes) {
             const int g = head(pc);
             if (g < Hkv)
-              sk_close<D, NCH, EPL, ROPE>(a, slots, pc, g, w - pc.first / q, st, qb, nrow,
-                                          lane);
+              sk_close<D, NCH, EPL, ROPE>(a, pc, g, w - pc.first / q, st, qb, lane);
             if constexpr (ROPE)
               if (jj + 1 < P) load_q(pp[1].b, head_ld(pp[1]));
           }
@@ -357,8 +390,12 @@ decode_mfma_sk_kernel(const DecodeArgs a, const int32_t* __restrict__ tables,
         for (int i = 0; i < NBUF; ++i) pp[i] = pp[i + 1];
         pp[NBUF] = pos_next(pp[NBUF]);
 #pragma unroll
-        for (int i = 0; i + 1 < NBUF; ++i) ids[i] = ids[i + 1];
+        for (int i = 0; i + 1 < NBUF; ++i) {
+          ids[i] = ids[i + 1];
+          sf[i] = sf[i + 1];
+        }
         ids[NBUF - 1] = idn;
+        sf[NBUF - 1] = sfn;
       }
     }
   }

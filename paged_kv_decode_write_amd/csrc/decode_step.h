@@ -13,18 +13,29 @@ namespace pagedkv {
 // instead of the cache, or -1. That is position L - 1 when the slot the step writes for
 // sequence b is the one its block table gives for that position (the decode-step layout);
 // otherwise the cache is read as it stands.
-// `slots` is the step's slot mapping (a.slot_mapping, or the same array through a pointer the
-// caller knows no store reaches, so the read stays a scalar load).
+// sub_pos_of takes the values already read (slot = slots[b], entry = table[(L - 1) / 16]);
+// step_sub_pos reads them. `slots` is the step's slot mapping (a.slot_mapping, or the same
+// array through a pointer the caller knows no store reaches, so the read stays a scalar load).
+__device__ __forceinline__ int sub_pos_of(const DecodeArgs& a, int64_t slot, int32_t entry,
+                                          int L) {
+  if (!a.k_new || L <= 0) return -1;
+  const int64_t want = (int64_t)entry * 16 + (L - 1) % 16;
+  return slot >= 0 && slot == want && slot < a.num_blocks * 16 ? L - 1 : -1;
+}
 __device__ __forceinline__ int step_sub_pos(const DecodeArgs& a, const int64_t* slots,
                                             const int32_t* table, int b, int L) {
   if (!a.k_new || L <= 0) return -1;
-  const int64_t slot = slots[b];
-  const int64_t want = (int64_t)table[(L - 1) / 16] * 16 + (L - 1) % 16;
-  return slot >= 0 && slot == want && slot < a.num_blocks * 16 ? L - 1 : -1;
+  return sub_pos_of(a, slots[b], table[(L - 1) / 16], L);
 }
-__device__ __forceinline__ int step_sub_pos(const DecodeArgs& a, const int32_t* table, int b,
-                                            int L) {
-  return step_sub_pos(a, a.slot_mapping, table, b, L);
+// The new token's slot, read once by a kernel that both tests it and stores there (-1
+// without new rows), and the test on it.
+__device__ __forceinline__ int64_t step_slot(const DecodeArgs& a, int b) {
+  return a.k_new ? a.slot_mapping[b] : -1;
+}
+__device__ __forceinline__ int step_sub_pos_at(const DecodeArgs& a, int64_t slot,
+                                               const int32_t* table, int L) {
+  if (!a.k_new || L <= 0) return -1;
+  return sub_pos_of(a, slot, table[(L - 1) / 16], L);
 }
 
 // Rows the fused step's new-row loads read for KV head g of sequence b: the step's new K / V
@@ -57,14 +68,12 @@ __device__ __forceinline__ void step_store(const DecodeArgs& a, const int64_t* s
   }
 }
 
-// The same store from a wave's registers (the rotated key row of a RoPE step): the lanes with
-// n16 == 0 hold the whole K row (chunks 32ch + 8kg), the lanes with kg == 0 the whole V row
-// (EPL columns at EPL * n16).
+// The same store from a wave's registers (the new rows as loaded, or the rotated key row of a
+// RoPE step), at a slot already read: the lanes with n16 == 0 hold the whole K row (chunks
+// 32ch + 8kg), the lanes with kg == 0 the whole V row (EPL columns at EPL * n16).
 template <int D, int NCH, int EPL>
-__device__ __forceinline__ void step_store_regs(const DecodeArgs& a, const int64_t* slots,
-                                                int b, int g, const NewRow<NCH, EPL>& r,
-                                                int n16, int kg) {
-  const int64_t slot = slots[b];
+__device__ __forceinline__ void step_store_regs_at(const DecodeArgs& a, int64_t slot, int g,
+                                                   const NewRow<NCH, EPL>& r, int n16, int kg) {
   if (slot < 0 || slot >= a.num_blocks * 16) return;
   const size_t dst = ((size_t)slot * a.num_kv_heads + g) * D;
   if (n16 == 0) {
@@ -73,6 +82,12 @@ __device__ __forceinline__ void step_store_regs(const DecodeArgs& a, const int64
       *reinterpret_cast<uint4*>(a.k_cache_w + dst + 32 * ch + 8 * kg) = r.k[ch];
   }
   if (kg == 0) r.v.store(a.v_cache_w + dst + EPL * n16);
+}
+template <int D, int NCH, int EPL>
+__device__ __forceinline__ void step_store_regs(const DecodeArgs& a, const int64_t* slots,
+                                                int b, int g, const NewRow<NCH, EPL>& r,
+                                                int n16, int kg) {
+  step_store_regs_at<D>(a, slots[b], g, r, n16, kg);
 }
 
 // RoPE step, part 2 (part 1 is rope_pieces on the loaded q and new-key pieces): the rotated q
