@@ -1205,6 +1205,61 @@ def test_many_short_ragged_sequences(dev):
             assert np.array_equal(wl.to_bits(f["k_cache"]), kc_ref)
 
 
+def test_stream_kernel_many_segments_per_slice(dev):
+    """The stream kernel on 600 short sequences (0..160 tokens) with a 1280-token table, so
+    that every slice crosses several sequences and closes several segments (each with its
+    new-token slot read ahead and its new rows stored from registers). Some slots are
+    negative. For three slice sizes, the plain and the rotary fused step equal their separate
+    calls bit for bit, the pools equal the oracle's, and the output is within the bound."""
+    B = 600
+    rng = np.random.default_rng(4242)
+    lengths = [int(x) for x in rng.integers(1, 161, size=B)]
+    for b in (0, 17, 301, 599):
+        lengths[b] = 0
+    nblocks = sum((L + 15) // 16 for L in lengths)
+    w = wl.Workload("sk_short", batch=B, num_q_heads=24, num_kv_heads=8, head_dim=128,
+                    block_size=16, num_blocks=nblocks + 64, max_blocks=80, seed=4243,
+                    context_len=1)
+    inp = wl.make_inputs(w, poison=True, lengths=lengths)
+    inp["slot_mapping"][[3, 50, 420]] = -1
+    host = wl.to_host_numpy(inp)
+    ref, kc_ref, vc_ref = oracle.decode_step(host)
+    pos_np = np.maximum(host["context_lens"] - 1, 0).astype(np.int32)
+    inv_np = llama_inv_freq(w.head_dim)
+    q_rr, kc_rr, vc_rr = oracle.kv_write_rope(host["q"], host["k_new"], host["v_new"], pos_np,
+                                              inv_np, False, host["slot_mapping"],
+                                              host["k_cache"], host["v_cache"])
+    ref_r = oracle.decode_attention(q_rr, kc_rr, vc_rr, host["block_tables"],
+                                    host["context_lens"], host["scale"])
+    pos = torch.from_numpy(pos_np).to(dev)
+    inv = torch.from_numpy(inv_np).to(dev)
+    for partition in (0, 64, 1024):  # slices of 12, 12 and 32 pairs
+        print(f"[case] sk_short p{partition}", flush=True)
+        f, s_ = to_dev(inp, dev), to_dev(inp, dev)
+        out_f = run_step(f, "mfma_sk", partition)
+        run_write(s_)
+        out_s = run_attention(s_, "mfma_sk", partition)
+        torch.cuda.synchronize()
+        assert torch.equal(out_f, out_s), partition
+        assert np.array_equal(wl.to_bits(f["k_cache"]), kc_ref), partition
+        assert np.array_equal(wl.to_bits(f["v_cache"]), vc_ref), partition
+        err = np.abs(out_f.cpu().double().numpy() - ref).max()
+        record(f"sk_short/step/p{partition}", err)
+        assert err <= ATOL, (partition, err)
+        f, s_ = to_dev(inp, dev), to_dev(inp, dev)
+        q_f, out_f = run_step_rope(f, pos, inv, False, "mfma_sk", partition)
+        q_s, out_s = run_rope_separate(s_, pos, inv, False, "mfma_sk", partition)
+        torch.cuda.synchronize()
+        assert torch.equal(q_f.view(torch.int16), q_s.view(torch.int16)), partition
+        assert torch.equal(f["k_cache"].view(torch.int16), s_["k_cache"].view(torch.int16))
+        assert torch.equal(f["v_cache"].view(torch.int16), s_["v_cache"].view(torch.int16))
+        assert torch.equal(out_f, out_s), partition
+        assert np.array_equal(wl.to_bits(f["v_cache"]), vc_rr), partition
+        err = np.abs(out_f.cpu().double().numpy() - ref_r).max()
+        record(f"sk_short/step_rope/p{partition}", err)
+        assert np.isfinite(err) and err <= ATOL, (partition, err)
+
+
 def test_concurrent_calls_on_two_streams(dev):
     """Two split decode calls of different workloads run at the same time on two streams, each
     with the workspace the binding keeps for its stream: both equal their results computed
