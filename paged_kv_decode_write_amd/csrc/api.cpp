@@ -139,6 +139,9 @@ int make_plan(int32_t batch, int32_t num_kv_heads, int32_t max_blocks, int32_t b
 constexpr int64_t kStreamSlots = 16;
 constexpr int64_t kStreamPairTokens = 32;
 constexpr int kStreamGroupsPerCU = 1;
+// Compute units of a whole MI355X / MI350X (8 XCDs of 32), where the stream kernel weights its
+// slices by XCD (see decode_sk.hip).
+constexpr int kXcdWeightedCUs = 256;
 
 struct StreamPlan {
   int32_t min_pairs;
@@ -587,6 +590,9 @@ int decode_impl(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_ca
   a.kv_dtype = kv_dtype;
   a.out_dtype = out_dtype;
   a.sk_min_pairs = dp.min_pairs;
+  // The stream family's XCD-weighted slices assume the whole device: 8 XCDs of 32 CUs, to
+  // which the dispatcher deals workgroups in turn.
+  a.sk_xcd_weights = chosen == PAGEDKV_KERNEL_MFMA_STREAM && cus == kXcdWeightedCUs;
   const size_t split_need = split_workspace_bytes(batch, num_q_heads, head_dim, plan.nparts);
   const size_t table_need = view_table_bytes(batch, max_blocks_per_seq, sub);
   if (static_scratch) {

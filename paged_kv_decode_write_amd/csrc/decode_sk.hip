@@ -15,9 +15,11 @@
 //   items = (sequence b, group of HPW KV heads, pair k of 32 tokens), b-major, then the head
 //   group, then k; sequence b holds ngrp * ceil(L_b / 32) items, W in all.
 // Workgroup w of N (one per compute unit: a second resident workgroup's loads were served
-// after most of the first one's, and it finished a quarter of the dispatch later) takes items
-// [w*q, (w+1)*q), q = max(min_pairs, ceil(W / N)); each of its HPW waves streams one KV head
-// of those items. Where the slice crosses from one (sequence,
+// after most of the first one's, and it finished a quarter of the dispatch later) takes the
+// slice [start(w), start(w+1)) of the items: equal slices of q = max(min_pairs, ceil(W / N)),
+// or on the whole device slices weighted by the XCD the workgroup runs on (SkDivision below);
+// each of its HPW waves streams one KV head of those items. Where the slice crosses from one
+// (sequence,
 // head group) to the next, the wave closes the first as a segment and starts the next: each
 // segment leaves a partial softmax result (unnormalised output, reference max, sum) in slot
 // j = w - (first workgroup of that (sequence, head group)) of the split workspace, and the
@@ -78,6 +80,45 @@ __device__ __forceinline__ void mark_slots_empty(const DecodeArgs& a, int b, int
 // of (b, hg). All wave-uniform.
 struct SkPos {
   int b, S, hg, L, pairs, k, k0, kend, first;
+};
+
+// The division of the batch's W items among the N workgroups: slice v is [start(v), start(v+1)).
+// Uniform: slices of q = max(min_pairs, ceil(W / N)) items. XCD-weighted: the dispatcher deals
+// workgroup v to XCD v mod 8, and on MI355X the odd-numbered XCDs stream about 2.8% slower than
+// the even ones (per-workgroup wall-clock stamps of this kernel on three parts, for pools
+// allocated in different places, two seeds and a ragged batch; the same on each). Slices then
+// get the weights kSkEven and kSkOdd by v's parity, start(v) = round(W c(v) / c(N)) with c(v) the
+// weight of workgroups 0 .. v-1, so that every XCD finishes at about the same time (each slice
+// within one item of its share: on the 64 x 8192 batch 130 and 126 items instead of 128). They
+// are used only when even an odd slice keeps at least min_pairs items, which keeps the planned
+// number of partial slots sufficient.
+constexpr int kSkEven = 507, kSkOdd = 493;
+struct SkDivision {
+  int W, N, q;
+  bool weighted;
+  long long cN;
+  __device__ __forceinline__ static long long c(int v) {
+    return (long long)(v >> 1) * (kSkEven + kSkOdd) + (v & 1) * kSkEven;
+  }
+  __device__ __forceinline__ void init(int W_, int N_, int min_pairs, bool xcd) {
+    W = W_;
+    N = N_;
+    q = max(min_pairs, (W + N - 1) / N);
+    cN = c(N);
+    weighted = xcd && (long long)W * kSkOdd >= (long long)(min_pairs + 1) * cN;
+  }
+  __device__ __forceinline__ int start(int v) const {
+    return weighted ? (int)(((long long)W * c(v) + cN / 2) / cN)
+                    : (int)min((long long)v * q, (long long)W);
+  }
+  // The slice holding item x (0 <= x < W).
+  __device__ __forceinline__ int slice_of(int x) const {
+    if (!weighted) return x / q;
+    int v = (int)((long long)x * N / W);
+    while (v + 1 < N && start(v + 1) <= x) ++v;
+    while (v > 0 && start(v) > x) --v;
+    return v;
+  }
 };
 
 // The fused step's facts of a segment, read ahead with its first pair's block ids: the new
@@ -226,10 +267,10 @@ decode_mfma_sk_kernel(const DecodeArgs a, const int32_t* __restrict__ tables,
     return b < 64 ? __builtin_amdgcn_readlane(Lv, b) : clamp_len(lens[b], Lmax);
   };
   const int W = __builtin_amdgcn_readfirstlane(wave_sum_i32(mine)) * ngrp;
-  const int q = max(a.sk_min_pairs, (W + N - 1) / N);
-  const long long lo64 = (long long)w * q;
-  if (lo64 < W) {
-    const int lo = (int)lo64, hi = (int)min(lo64 + q, (long long)W);
+  SkDivision dv;
+  dv.init(W, N, a.sk_min_pairs, a.sk_xcd_weights != 0);
+  const int lo = dv.start(w), hi = dv.start(w + 1);
+  if (lo < hi) {
     // The sequence holding item lo, and the first item of that sequence: a scan of the items
     // per sequence, 64 sequences at a time.
     int b0 = 0, S0 = 0;
@@ -381,7 +422,7 @@ decode_mfma_sk_kernel(const DecodeArgs a, const int32_t* __restrict__ tables,
           if (closes) {
             const int g = head(pc);
             if (g < Hkv)
-              sk_close<D, NCH, EPL, ROPE>(a, pc, g, w - pc.first / q, st, qb, lane);
+              sk_close<D, NCH, EPL, ROPE>(a, pc, g, w - dv.slice_of(pc.first), st, qb, lane);
             if constexpr (ROPE)
               if (jj + 1 < P) load_q(pp[1].b, head_ld(pp[1]));
           }

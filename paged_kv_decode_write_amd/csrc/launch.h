@@ -45,6 +45,8 @@ struct DecodeArgs {
   // Evenly divided (stream-K) launch: a workgroup takes at least this many 32-token pairs of
   // the batch's work; nparts is then the number of partial slots per (sequence, KV head).
   int32_t sk_min_pairs;
+  // Nonzero: the slices are weighted by the XCD each workgroup runs on (the device whole).
+  int32_t sk_xcd_weights;
 };
 
 // Arguments of one multi-query causal (prefill) launch, already validated.

@@ -2,13 +2,16 @@
 library plans (paged_decode_plan, host logic) must suffice for every batch the kernel may see.
 
 The kernel (csrc/decode_sk.hip) counts items = 32-token pairs of (sequence, group of 4 KV heads),
-sequence-major, gives workgroup w of N the slice [w q, (w + 1) q) with q = max(min_pairs,
-ceil(W / N)), and writes the segment of (sequence b, head group) that slice w holds into slot
-w - first_item(b, head group) // q; the workgroup closing a (sequence, head group) marks its
-later slots empty. This test replays that division with the planned (slots, min_pairs) and
-checks, over random ragged batches (empty, partial-block and over-long contexts included), that
-every pair is covered exactly once, every slot index is in range and every slot is written
-exactly once per call.
+sequence-major, gives workgroup w of N the slice [start(w), start(w + 1)), and writes the
+segment of (sequence b, head group) that slice w holds into slot w - (the slice holding
+first_item(b, head group)); the workgroup closing a (sequence, head group) marks its later slots
+empty. Equal slices: start(w) = min(w q, W), q = max(min_pairs, ceil(W / N)). XCD-weighted
+slices (the whole device): weights 507 for even w and 493 for odd w, start(w) = round(W c(w) /
+c(N)) with c(w) the weight of workgroups 0 .. w-1, used only when W * 493 >= (min_pairs + 1) *
+c(N). This test replays both divisions with the planned (slots, min_pairs) and checks, over
+random ragged batches (empty, partial-block and over-long contexts included), that every pair
+is covered exactly once, every slot index is in range, every slot is written exactly once per
+call and every weighted slice holds at least min_pairs items.
 """
 import os
 import random
@@ -34,13 +37,36 @@ def plan(monkeypatch):
     return f
 
 
-def replay(lens, Hkv, MB, N, slots, min_pairs):
+EVEN, ODD = 507, 493
+
+
+def division(W, N, min_pairs, xcd):
+    """start(v) of the kernel's slices, and whether the weighted form applies."""
+    q = max(min_pairs, -(-W // N))
+
+    def c(v):
+        return (v // 2) * (EVEN + ODD) + (v % 2) * EVEN
+    weighted = xcd and W * ODD >= (min_pairs + 1) * c(N)
+    if weighted:
+        return (lambda v: (W * c(v) + c(N) // 2) // c(N)), True
+    return (lambda v: min(v * q, W)), False
+
+
+def replay(lens, Hkv, MB, N, slots, min_pairs, xcd=False):
     Lmax = MB * 16
     ngrp = -(-Hkv // HPW)
     cl = [max(0, min(L, Lmax)) for L in lens]
     pairs = [-(-L // PT) for L in cl]
     W = sum(pairs) * ngrp
-    q = max(min_pairs, -(-W // N))
+    start, weighted = division(W, N, min_pairs, xcd)
+    bounds = [start(v) for v in range(N + 1)]
+    assert bounds[0] == 0 and bounds[N] == W
+    assert all(bounds[v] <= bounds[v + 1] for v in range(N))
+    if weighted:
+        assert all(bounds[v + 1] - bounds[v] >= min_pairs for v in range(N))
+
+    def slice_of(x):  # the slice holding item x, by search
+        return next(v for v in range(N) if bounds[v] <= x < bounds[v + 1])
     written, covered = {}, set()
     first_of = {}
     S = 0
@@ -54,7 +80,7 @@ def replay(lens, Hkv, MB, N, slots, min_pairs):
                 for s in range(slots):
                     written[(b, g, s)] = written.get((b, g, s), 0) + 1
     for w in range(N):
-        lo, hi = w * q, min(w * q + q, W)
+        lo, hi = bounds[w], bounds[w + 1]
         item = lo
         while item < hi:
             # the (sequence, head group) holding `item`
@@ -62,7 +88,7 @@ def replay(lens, Hkv, MB, N, slots, min_pairs):
                          if pairs[b] and f <= item < f + pairs[b])
             first = first_of[(b, hg)]
             e = min(hi, first + pairs[b])
-            slot = w - first // q
+            slot = w - slice_of(first)
             assert 0 <= slot < slots, (slot, slots)
             for g in range(hg * HPW, min(hg * HPW + HPW, Hkv)):
                 written[(b, g, slot)] = written.get((b, g, slot), 0) + 1
@@ -89,11 +115,29 @@ def test_planned_slots_cover_random_batches(plan):
         slots, min_pairs = plan(B, Hkv, MB, part)
         lens = [rng.choice([0, 1, 15, 16, 17, 31, 32, 33, rng.randint(0, MB * 16), MB * 16,
                             MB * 16 + 5]) for _ in range(B)]
-        N = rng.choice([1, 3, 64, 512])
+        N = rng.choice([1, 3, 64, 256, 512])
         replay(lens, Hkv, MB, N, slots, min_pairs)
+        replay(lens, Hkv, MB, N, slots, min_pairs, xcd=True)
 
 
 def test_automatic_slots_are_at_most_sixteen(plan):
     for MB in (65, 128, 256, 512, 2048, 8192):
         slots, min_pairs = plan(8, 8, MB, 0)
         assert slots <= 16 and min_pairs >= 8
+
+
+def test_weighted_slices_balance_the_xcds():
+    """The weighted division gives every slice its share W * weight / c(N) within one item
+    (slices on even XCDs 507/493 of those on odd ones), and applies to the benchmark-sized
+    batches: on the 64 x 8192 batch (32768 items) 130 and 126 items."""
+    for W in (32768, 6912, 4096):
+        start, weighted = division(W, 256, 8, True)
+        assert weighted
+        cN = 128 * (EVEN + ODD)
+        for v in range(256):
+            share = W * (EVEN if v % 2 == 0 else ODD) / cN
+            assert abs(start(v + 1) - start(v) - share) < 1, (W, v)
+    start, _ = division(32768, 256, 8, True)
+    assert (start(1), start(2) - start(1)) == (130, 126)
+    start, weighted = division(2000, 256, 8, True)  # slices would fall below min_pairs
+    assert not weighted and start(1) == 8
