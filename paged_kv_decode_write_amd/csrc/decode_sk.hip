@@ -19,14 +19,14 @@
 // slice [start(w), start(w+1)) of the items: equal slices of q = max(min_pairs, ceil(W / N)),
 // or on the whole device slices weighted by the XCD the workgroup runs on (SkDivision below);
 // each of its HPW waves streams one KV head of those items. Where the slice crosses from one
-// (sequence,
-// head group) to the next, the wave closes the first as a segment and starts the next: each
-// segment leaves a partial softmax result (unnormalised output, reference max, sum) in slot
-// j = w - (first workgroup of that (sequence, head group)) of the split workspace, and the
-// workgroup that closes the last segment of a (sequence, head group) marks its remaining slots
-// empty. Every slot is therefore written on every call, and the partition merge (the
-// log-sum-exp rule of decode_reduce.hip) combines them. min_pairs bounds the slots a
-// (sequence, head group) can need: with pairs_max pairs at most, ceil(pairs_max / q) + 1.
+// (sequence, head group) to the next, the wave closes the first as a segment and starts the
+// next: each segment leaves a partial softmax result (unnormalised output, reference max, sum)
+// in slot j = w - (first workgroup of that (sequence, head group)) of the split workspace, and
+// the workgroup that closes the last segment of a (sequence, head group) marks its remaining
+// slots empty. Every slot is therefore written on every call, and the partition merge (the
+// log-sum-exp rule of decode_reduce.hip) combines them. Every slice holds at least min_pairs
+// items, which bounds the slots a (sequence, head group) of at most pairs_max pairs can need:
+// (pairs_max - 1) / min_pairs + 2.
 // Sequences of length 0 hold no items; workgroup b mod N marks their slots and does their
 // part of the fused step.
 #include "decode_step.h"
@@ -157,7 +157,7 @@ __device__ __forceinline__ int2 sk_ids(const PairCtx<D>& c, const SkPos& p) {
   return make_int2(c.table[jA], jA + 1 < c.blk1 ? c.table[jA + 1] : -1);
 }
 
-// Writes the partial of the segment that ends with pair p (slot w - first / q) and, when it
+// Writes the partial of the segment that ends with pair p (slot w - slice_of(first)) and, when it
 // ends its (sequence, head group), marks that sequence's remaining slots empty; with RoPE the
 // segment that starts the sequence stores the rotated q. (The step's new rows are stored by
 // the kernel's loop when the segment's last pair is scored.)
