@@ -1209,8 +1209,9 @@ def test_stream_kernel_many_segments_per_slice(dev):
     """The stream kernel on 600 short sequences (0..160 tokens) with a 1280-token table, so
     that every slice crosses several sequences and closes several segments (each with its
     new-token slot read ahead and its new rows stored from registers). Some slots are
-    negative. For three slice sizes, the plain and the rotary fused step equal their separate
-    calls bit for bit, the pools equal the oracle's, and the output is within the bound."""
+    negative. For five slice settings (both sides of the point where the slices stop being
+    weighted by XCD), the plain and the rotary fused step equal their separate calls bit for
+    bit, the pools equal the oracle's, and the output is within the bound."""
     B = 600
     rng = np.random.default_rng(4242)
     lengths = [int(x) for x in rng.integers(1, 161, size=B)]
@@ -1233,7 +1234,9 @@ def test_stream_kernel_many_segments_per_slice(dev):
                                     host["context_lens"], host["scale"])
     pos = torch.from_numpy(pos_np).to(dev)
     inv = torch.from_numpy(inv_np).to(dev)
-    for partition in (0, 64, 1024):  # slices of 12, 12 and 32 pairs
+    # 3564 items: on the whole device (256 CUs) slices of about 14 pairs, XCD-weighted for
+    # min_pairs up to 12 (384 tokens) and equal from 13 (416 tokens) on; 1024 tokens: 32 pairs.
+    for partition in (0, 64, 384, 416, 1024):
         print(f"[case] sk_short p{partition}", flush=True)
         f, s_ = to_dev(inp, dev), to_dev(inp, dev)
         out_f = run_step(f, "mfma_sk", partition)
